@@ -1,0 +1,81 @@
+"""Element codecs for the KV cache -- test infrastructure only (oracle).
+
+The pages name 16-bit KV caches and an 8-bit float KV cache ("AI Inference
+Serving at Scale", section 6: FP8 halves the KV footprint; "vLLM &
+High-Throughput Serving", section 5 engine arguments).  They do not define
+the bit formats, so these follow the public format definitions:
+
+* bfloat16: the upper 16 bits of an IEEE-754 binary32 value.
+* FP8 E4M3 in the OCP "FN" variant: 1 sign bit, 4 exponent bits with bias
+  7, 3 mantissa bits; exponent field 0 holds subnormals m/8 * 2**-6; the
+  single pattern S.1111.111 is NaN; there are no infinities; the largest
+  finite magnitude is 1.75 * 2**8 = 448.
+
+Everything returns numpy float64, in which both formats are exact.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to float64, exactly.
+
+    A bfloat16 is the high half of a binary32, so placing the 16 bits in
+    the top of a 32-bit word gives the identical binary32 value.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Decode OCP E4M3FN codes (uint8) to float64, from the field layout."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    exp = (c >> 3) & 0xF
+    man = (c & 0x7).astype(np.float64)
+    normal = (1.0 + man / 8.0) * np.exp2(exp.astype(np.float64) - 7.0)
+    subnormal = (man / 8.0) * 2.0 ** -6
+    mag = np.where(exp == 0, subnormal, normal)
+    mag = np.where((exp == 0xF) & ((c & 0x7) == 0x7), np.nan, mag)
+    return sign * mag
+
+
+def _e4m3_positive_table() -> tuple[np.ndarray, np.ndarray]:
+    """All non-negative finite E4M3FN values in increasing order, with codes."""
+    codes = np.arange(0, 0x7F, dtype=np.uint8)  # 0x7F is NaN
+    return e4m3_to_f64(codes), codes
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Round float values to E4M3FN codes: nearest, ties to even, saturating.
+
+    Rounding is to the nearest representable magnitude; on an exact tie the
+    code with an even mantissa (even last bit) wins, which is IEEE
+    round-to-nearest-even.  Magnitudes above 448 saturate to 448 instead of
+    becoming NaN; NaN input gives the NaN code with the input's sign.  The
+    input is taken at its float64 value (callers pass the float32 quotient
+    of value by scale, so the quotient's own rounding is binary32's).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    vals, codes = _e4m3_positive_table()
+    mag = np.abs(x)
+    neg = np.signbit(x)
+    clipped = np.minimum(mag, E4M3_MAX)
+    hi = np.searchsorted(vals, clipped, side="left")  # first vals >= clipped
+    hi = np.minimum(hi, len(vals) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = vals[hi] - clipped
+    d_lo = clipped - vals[lo]
+    pick_hi = d_hi < d_lo
+    tie = d_hi == d_lo
+    hi_even = (codes[hi] & 1) == 0
+    pick_hi = np.where(tie, hi_even, pick_hi)
+    out = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
+    out = np.where(vals[hi] == clipped, codes[hi], out).astype(np.uint8)
+    out = out | np.where(neg, np.uint8(0x80), np.uint8(0)).astype(np.uint8)
+    nan_code = np.where(neg, np.uint8(0xFF), np.uint8(0x7F)).astype(np.uint8)
+    return np.where(np.isnan(x), nan_code, out).astype(np.uint8)

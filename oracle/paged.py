@@ -1,0 +1,281 @@
+"""Paged KV cache and decode attention, written as plain definitions.
+
+TEST INFRASTRUCTURE ONLY (oracle): see the package docstring for who may
+import this.  No blocking, fusion or reordering beyond the definitions.
+
+Pool layout (the library's documented layout, restated here from its
+definition, not shared with it):
+
+* K pool: ``[num_blocks, num_kv_heads, block_size, head_dim]`` -- inside a
+  (block, head) tile, token-major rows of ``head_dim`` elements.
+* V pool: ``[num_blocks, num_kv_heads, head_dim, block_size]`` -- inside a
+  (block, head) tile, dimension-major rows of ``block_size`` tokens.
+
+Storage is raw: ``"f32"`` arrays are float32, ``"bf16"`` arrays hold
+bfloat16 bit patterns as uint16, ``"fp8_e4m3"`` arrays hold E4M3FN codes as
+uint8 with one float32 scale per KV head.
+
+Token t of a sequence lives in physical block ``table[t // B]`` at offset
+``t % B`` ("vLLM & High-Throughput Serving", section 2, block-table
+equation; "AI Inference Serving at Scale", section 3, logical-to-physical
+block table).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import codecs
+
+DTYPES = ("f32", "bf16", "fp8_e4m3")
+
+
+# --------------------------------------------------------------------------
+# element storage
+# --------------------------------------------------------------------------
+
+def to_f64(raw: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen raw storage of ``dtype`` to float64 (exact for all three)."""
+    if dtype == "f32":
+        return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return codecs.bf16_bits_to_f64(raw)
+    if dtype == "fp8_e4m3":
+        return codecs.e4m3_to_f64(raw)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def source_to_f32(raw: np.ndarray, dtype: str) -> np.ndarray:
+    """New K/V rows arrive as f32 or bf16; both are exact in float32."""
+    if dtype == "f32":
+        return np.asarray(raw, dtype=np.float32)
+    if dtype == "bf16":
+        return codecs.bf16_bits_to_f64(raw).astype(np.float32)
+    raise ValueError(f"new K/V rows must be f32 or bf16, not {dtype!r}")
+
+
+# --------------------------------------------------------------------------
+# block table: index map and gather
+# --------------------------------------------------------------------------
+
+def slot_of(table_row: np.ndarray, t: int, block_size: int) -> tuple[int, int]:
+    """Physical (block, offset) of logical token ``t``.
+
+    Logical block ``i = floor(t / B)`` and offset ``j = t mod B``
+    ("vLLM & High-Throughput Serving", section 2, block-table equation);
+    the block table maps ``i`` to a physical block id ("AI Inference
+    Serving at Scale", section 3).
+    """
+    i, j = divmod(int(t), int(block_size))
+    return int(table_row[i]), j
+
+
+def gather(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarray,
+           length: int, block_size: int) -> tuple[np.ndarray, np.ndarray]:
+    """Copy one sequence's K and V out of the pool into contiguous arrays.
+
+    Returns raw-storage arrays ``[length, num_kv_heads, head_dim]`` in
+    token order, the contiguous per-sequence layout of "vLLM &
+    High-Throughput Serving", section 1.  The paged kernel gathers K and V
+    from non-adjacent blocks ("How LLM Inference Engines Work", section on
+    PagedAttention); here the gather is one token at a time.
+    """
+    n_kv, head_dim = k_pool.shape[1], k_pool.shape[3]
+    k = np.empty((length, n_kv, head_dim), dtype=k_pool.dtype)
+    v = np.empty((length, n_kv, head_dim), dtype=v_pool.dtype)
+    for t in range(length):
+        blk, off = slot_of(table_row, t, block_size)
+        k[t] = k_pool[blk, :, off, :]
+        v[t] = v_pool[blk, :, :, off]
+    return k, v
+
+
+# --------------------------------------------------------------------------
+# append (cache write)
+# --------------------------------------------------------------------------
+
+def write_tokens(k_pool: np.ndarray, v_pool: np.ndarray,
+                 k_new: np.ndarray, v_new: np.ndarray,
+                 slot_mapping: np.ndarray, block_size: int,
+                 src_dtype: str, cache_dtype: str,
+                 k_scale: np.ndarray | None = None,
+                 v_scale: np.ndarray | None = None
+                 ) -> tuple[np.ndarray, np.ndarray]:
+    """Store new tokens' K and V rows at their slots; return new pools.
+
+    Token n goes to slot ``s = slot_mapping[n]``: block ``s // B``, offset
+    ``s % B`` (the block-table equation of "vLLM & High-Throughput
+    Serving", section 2, applied to a flat slot number).  The engine
+    appends each generated token's K/V into the sequence's current block
+    ("AI Inference Serving at Scale", section 3, on-demand allocation).
+    A negative slot marks a padding token and is skipped.  Two tokens with
+    the same slot are a caller error and raise.
+
+    Same-type caches store the bits unchanged.  An E4M3 cache stores
+    ``e4m3_encode(float32(x) / float32(scale[h]))`` per KV head h: the
+    quotient rounded once in binary32, then rounded to nearest-even E4M3
+    with saturation at +-448 (the pages give FP8 KV caches without a
+    rounding rule; this is the plain reading).
+    """
+    slot_mapping = np.asarray(slot_mapping, dtype=np.int64)
+    live = slot_mapping[slot_mapping >= 0]
+    if len(np.unique(live)) != len(live):
+        raise ValueError("duplicate slot in slot_mapping")
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    n_kv = k_pool.shape[1]
+    for n, s in enumerate(slot_mapping):
+        if s < 0:
+            continue
+        blk, off = divmod(int(s), int(block_size))
+        for h in range(n_kv):
+            if cache_dtype == "fp8_e4m3":
+                kx = source_to_f32(k_new[n, h], src_dtype)
+                vx = source_to_f32(v_new[n, h], src_dtype)
+                kq = kx / np.float32(k_scale[h])
+                vq = vx / np.float32(v_scale[h])
+                k_out[blk, h, off, :] = codecs.e4m3_encode(kq)
+                v_out[blk, h, :, off] = codecs.e4m3_encode(vq)
+            else:
+                if src_dtype != cache_dtype:
+                    raise ValueError("non-fp8 caches store the source bits")
+                k_out[blk, h, off, :] = k_new[n, h]
+                v_out[blk, h, :, off] = v_new[n, h]
+    return k_out, v_out
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+              scale: float) -> np.ndarray:
+    """Textbook single-query attention of one sequence, in float64.
+
+    ``q``: ``[Hq, d]``; ``k``, ``v``: ``[L, Hkv, d]`` (contiguous).
+    Query head ``hq`` uses KV head ``hq // (Hq / Hkv)``: consecutive query
+    heads share one KV head (grouped-query attention, "AI Inference
+    Serving at Scale", section 6).  For each query head the weights are
+    ``softmax(scale * K q)`` over all L cached tokens and the output is the
+    weighted sum of the V rows (dot-product attention against all preceding
+    tokens, same page, section 2).  The maximum is subtracted before exp,
+    which leaves the softmax unchanged.  An empty context gives zeros.
+    """
+    n_q, d = q.shape
+    length, n_kv, _ = k.shape
+    group = n_q // n_kv
+    out = np.zeros((n_q, d), dtype=np.float64)
+    if length == 0:
+        return out
+    for hq in range(n_q):
+        h = hq // group
+        z = scale * (k[:, h, :] @ q[hq])
+        e = np.exp(z - z.max())
+        p = e / e.sum()
+        out[hq] = p @ v[:, h, :]
+    return out
+
+
+def sequence_kv_f64(k_pool, v_pool, table_row, length, block_size,
+                    cache_dtype, k_scale=None, v_scale=None):
+    """Gather one sequence and widen it to float64 (times the FP8 scales)."""
+    kr, vr = gather(k_pool, v_pool, table_row, length, block_size)
+    k = to_f64(kr, cache_dtype)
+    v = to_f64(vr, cache_dtype)
+    if cache_dtype == "fp8_e4m3":
+        k = k * np.asarray(k_scale, dtype=np.float32).astype(np.float64)[None, :, None]
+        v = v * np.asarray(v_scale, dtype=np.float32).astype(np.float64)[None, :, None]
+    return k, v
+
+
+def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+           block_tables: np.ndarray, context_lens: np.ndarray,
+           block_size: int, scale: float, q_dtype: str, cache_dtype: str,
+           k_scale=None, v_scale=None, seqs=None) -> np.ndarray:
+    """Decode-phase attention for a batch: gather, then textbook attention.
+
+    One query token per sequence attends to its ``context_lens[b]`` cached
+    tokens, reached through ``block_tables[b]``.  Returns float64
+    ``[S, Hq, d]`` (rows of sequences not in ``seqs`` are left zero when a
+    subset is asked for).  ``scale`` is taken at its float32 value.
+    """
+    q64 = to_f64(q, q_dtype)
+    s_count = q64.shape[0]
+    out = np.zeros(q64.shape, dtype=np.float64)
+    scale = float(np.float32(scale))
+    for b in (range(s_count) if seqs is None else seqs):
+        k, v = sequence_kv_f64(k_pool, v_pool, block_tables[b],
+                               int(context_lens[b]), block_size,
+                               cache_dtype, k_scale, v_scale)
+        out[b] = attention(q64[b], k, v, scale)
+    return out
+
+
+# --------------------------------------------------------------------------
+# split context: partial softmax states and their merge
+# --------------------------------------------------------------------------
+
+def partial(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+            t0: int, t1: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Softmax state of one query over the token range ``[t0, t1)``.
+
+    Returns, per query head: ``m`` = max of ``scale * K q`` over the range,
+    ``l`` = sum of ``exp(scale * K q - m)``, ``o`` = the range's own
+    normalised attention output (sum of ``exp(.. - m) * v`` divided by l).
+    This is the state a context split keeps for later merging.
+    """
+    n_q, d = q.shape
+    group = n_q // k.shape[1]
+    m = np.empty(n_q)
+    l = np.empty(n_q)
+    o = np.empty((n_q, d))
+    for hq in range(n_q):
+        h = hq // group
+        z = scale * (k[t0:t1, h, :] @ q[hq])
+        m[hq] = z.max()
+        e = np.exp(z - m[hq])
+        l[hq] = e.sum()
+        o[hq] = (e @ v[t0:t1, h, :]) / l[hq]
+    return m, l, o
+
+
+def merge(ms: np.ndarray, ls: np.ndarray, os_: np.ndarray) -> np.ndarray:
+    """Combine softmax states of disjoint token ranges into the output.
+
+    With ``M = max_p m_p`` and ``w_p = l_p * exp(m_p - M)``:
+    ``out = sum_p w_p o_p / sum_p w_p``.  Each range's exp terms are
+    rescaled to the common maximum, so this equals softmax over the union.
+    ``ms``, ``ls``: ``[P]``; ``os_``: ``[P, d]``.
+    """
+    big_m = ms.max()
+    w = ls * np.exp(ms - big_m)
+    return (w[:, None] * os_).sum(axis=0) / w.sum()
+
+
+def decode_partials(q, k_pool, v_pool, block_tables, context_lens,
+                    block_size, scale, q_dtype, cache_dtype, partition_size,
+                    k_scale=None, v_scale=None, seqs=None):
+    """Per-partition softmax states of a split decode.
+
+    Partition p of sequence b covers tokens ``[p*P, min((p+1)*P, L_b))``.
+    Returns ``(m, l, o)`` shaped ``[S, Hq, maxP]``, ``[S, Hq, maxP]``,
+    ``[S, Hq, maxP, d]`` with ``maxP = ceil(max L / P)``; entries of
+    partitions a sequence does not have are NaN.
+    """
+    q64 = to_f64(q, q_dtype)
+    s_count, n_q, d = q64.shape
+    scale = float(np.float32(scale))
+    lens = np.asarray(context_lens, dtype=np.int64)
+    max_p = max(1, int(-(-int(lens.max()) // partition_size))) if len(lens) else 1
+    m = np.full((s_count, n_q, max_p), np.nan)
+    l = np.full((s_count, n_q, max_p), np.nan)
+    o = np.full((s_count, n_q, max_p, d), np.nan)
+    for b in (range(s_count) if seqs is None else seqs):
+        length = int(lens[b])
+        k, v = sequence_kv_f64(k_pool, v_pool, block_tables[b], length,
+                               block_size, cache_dtype, k_scale, v_scale)
+        for p in range(-(-length // partition_size)):
+            t0 = p * partition_size
+            t1 = min(t0 + partition_size, length)
+            m[b, :, p], l[b, :, p], o[b, :, p] = partial(q64[b], k, v, scale, t0, t1)
+    return m, l, o

@@ -1,0 +1,37 @@
+"""Shared test configuration.
+
+Tests marked ``gpu`` need an MI355X and the built HIP library; everything
+else runs on the CPU (the oracle against its pins, host-side logic, and
+loading the C-ABI library without launching anything).
+"""
+
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: large CPU-side case")
+
+
+def _gpu_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+def pytest_collection_modifyitems(config, items):
+    if _gpu_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU in this environment")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

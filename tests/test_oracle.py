@@ -1,0 +1,588 @@
+"""The oracle against what the pages and the mathematics fix (CPU only).
+
+Every pin is a function of the implementation it checks, so the last
+section can run the same pins against deliberately broken copies of the
+oracle and show that each plausible mistake is caught.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import codecs, paged
+from workloads import (WORKLOADS, contiguous_layout, host_view, make_batch,
+                       permute_blocks, unshare)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _impl(**over):
+    """The oracle's functions as a namespace, optionally with replacements."""
+    ns = dict(slot_of=paged.slot_of, gather=paged.gather,
+              write_tokens=paged.write_tokens, attention=paged.attention,
+              decode=paged.decode, partial=paged.partial, merge=paged.merge,
+              e4m3_to_f64=codecs.e4m3_to_f64, e4m3_encode=codecs.e4m3_encode)
+    ns.update(over)
+    return types.SimpleNamespace(**ns)
+
+
+ORACLE = _impl()
+
+
+def _host(batch):
+    return dict(q=host_view(batch.q), k=host_view(batch.k_pool),
+                v=host_view(batch.v_pool), kn=host_view(batch.k_new),
+                vn=host_view(batch.v_new),
+                ks=None if batch.k_scale is None else batch.k_scale.numpy(),
+                vs=None if batch.v_scale is None else batch.v_scale.numpy())
+
+
+def _decode_batch(impl, batch, k=None, v=None):
+    h = _host(batch)
+    w = batch.workload
+    return impl.decode(h["q"], h["k"] if k is None else k, h["v"] if v is None else v,
+                       batch.block_tables, batch.context_lens, w.block_size,
+                       batch.scale, w.q_dtype, w.cache_dtype, h["ks"], h["vs"])
+
+
+def _scatter_contiguous(k_c, v_c, block_size, table, k_pool, v_pool):
+    """Place contiguous [L, Hkv, d] rows into pool tiles with explicit index
+    arrays (the inverse of a gather, built without the oracle)."""
+    length = k_c.shape[0]
+    t = np.arange(length)
+    blk = np.asarray(table)[t // block_size]
+    off = t % block_size
+    k_pool[blk, :, off, :] = k_c
+    for tt in range(length):  # V tiles are dimension-major
+        v_pool[blk[tt], :, :, off[tt]] = v_c[tt]
+
+
+# ==========================================================================
+# pins (each takes an implementation namespace)
+# ==========================================================================
+
+def pin_golden_index(impl):
+    table, bsz, rows = None, None, []
+    with open(os.path.join(GOLDEN, "block_table_index.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            if line.startswith("block_size:"):
+                bsz = int(line.split(":")[1])
+            elif line.startswith("table:"):
+                table = [int(x) for x in line.split(":")[1].split()]
+            else:
+                rows.append([int(x) for x in line.split()])
+    assert table == [5, 0, 3] and bsz == 16 and len(rows) == 8
+    for t, i, j, phys in rows:
+        assert impl.slot_of(np.array(table), t, bsz) == (phys, j)
+        assert table[i] == phys
+
+
+def pin_gather_roundtrip(impl):
+    rng = np.random.default_rng(1)
+    bsz, hkv, d, nb = 4, 2, 3, 9
+    length = 11
+    table = rng.permutation(nb)[:3]
+    k_c = rng.standard_normal((length, hkv, d)).astype(np.float32)
+    v_c = rng.standard_normal((length, hkv, d)).astype(np.float32)
+    k_pool = np.full((nb, hkv, bsz, d), np.nan, np.float32)
+    v_pool = np.full((nb, hkv, d, bsz), np.nan, np.float32)
+    _scatter_contiguous(k_c, v_c, bsz, table, k_pool, v_pool)
+    kg, vg = impl.gather(k_pool, v_pool, table, length, bsz)
+    assert np.array_equal(kg, k_c) and np.array_equal(vg, v_c)
+
+
+def pin_write_whole_pool(impl):
+    """Whole-pool check of an append: every targeted slot holds the new row,
+    every other slot is unchanged, padding tokens write nothing."""
+    rng = np.random.default_rng(2)
+    bsz, hkv, d, nb = 16, 3, 8, 7
+    k_pool = rng.integers(0, 2**16, (nb, hkv, bsz, d)).astype(np.uint16)
+    v_pool = rng.integers(0, 2**16, (nb, hkv, d, bsz)).astype(np.uint16)
+    kn = rng.integers(0, 2**16, (5, hkv, d)).astype(np.uint16)
+    vn = rng.integers(0, 2**16, (5, hkv, d)).astype(np.uint16)
+    slots = np.array([3 * 16 + 5, -1, 0, 6 * 16 + 15, 2 * 16 + 9], np.int64)
+    k2, v2 = impl.write_tokens(k_pool, v_pool, kn, vn, slots, bsz, "bf16", "bf16")
+    kexp, vexp = k_pool.copy(), v_pool.copy()
+    for n, where in enumerate([(3, 5), None, (0, 0), (6, 15), (2, 9)]):
+        if where is None:
+            continue
+        blk, off = where
+        kexp[blk, :, off, :] = kn[n]
+        vexp[blk, :, :, off] = vn[n]
+    assert np.array_equal(k2, kexp) and np.array_equal(v2, vexp)
+    assert np.array_equal(k_pool[1], k2[1])  # input untouched
+
+
+def pin_write_then_gather(impl):
+    """Appending token L through its slot extends the gathered sequence by
+    exactly that row (the engine's append, then the block-table read)."""
+    w = WORKLOADS[1]
+    batch = make_batch(w)
+    h = _host(batch)
+    for b in range(w.num_seqs):
+        length = int(batch.context_lens[b])
+        k_old, v_old = impl.gather(h["k"], h["v"], batch.block_tables[b],
+                                   length - 1, w.block_size)
+        k2, v2 = impl.write_tokens(h["k"], h["v"], h["kn"][b:b + 1], h["vn"][b:b + 1],
+                                   batch.slot_mapping[b:b + 1], w.block_size,
+                                   "f32", "f32")
+        k_new, v_new = impl.gather(k2, v2, batch.block_tables[b], length, w.block_size)
+        assert np.array_equal(k_new[:-1], k_old) and np.array_equal(v_new[:-1], v_old)
+        assert np.array_equal(k_new[-1], h["kn"][b]) and np.array_equal(v_new[-1], h["vn"][b])
+
+
+def pin_single_token(impl):
+    """L = 1: softmax of one score is 1, the output is that V row exactly."""
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((4, 16))
+    k = rng.standard_normal((1, 2, 16))
+    v = rng.standard_normal((1, 2, 16))
+    out = impl.attention(q, k, v, 0.25)
+    assert np.array_equal(out, v[0, np.arange(4) // 2])
+
+
+def pin_two_tokens(impl):
+    """L = 2: out = v0 + sigmoid(z1 - z0) (v1 - v0), z_t = scale * q.k_t."""
+    rng = np.random.default_rng(4)
+    d = 8
+    q = rng.standard_normal((2, d))
+    k = rng.standard_normal((2, 1, d))
+    v = rng.standard_normal((2, 1, d))
+    scale = 0.37
+    out = impl.attention(q, k, v, scale)
+    for hq in range(2):
+        z = [scale * math.fsum(q[hq, i] * k[t, 0, i] for i in range(d)) for t in range(2)]
+        sig = 1.0 / (1.0 + math.exp(-(z[1] - z[0])))
+        want = v[0, 0] + sig * (v[1, 0] - v[0, 0])
+        np.testing.assert_allclose(out[hq], want, rtol=1e-13, atol=1e-14)
+
+
+def pin_identical_keys_mean(impl):
+    """Identical keys (or q = 0) make every weight 1/L: out = mean of V."""
+    rng = np.random.default_rng(5)
+    length, d = 37, 16
+    q = rng.standard_normal((3, d))
+    krow = rng.standard_normal(d)
+    k = np.tile(krow, (length, 1, 1))
+    v = rng.standard_normal((length, 1, d))
+    out = impl.attention(q, k, v, 1.3)
+    mean = np.array([math.fsum(v[:, 0, i]) / length for i in range(d)])
+    np.testing.assert_allclose(out, np.tile(mean, (3, 1)), rtol=1e-13, atol=1e-14)
+    out0 = impl.attention(np.zeros((3, d)), rng.standard_normal((length, 1, d)), v, 1.0)
+    np.testing.assert_allclose(out0, np.tile(mean, (3, 1)), rtol=1e-13, atol=1e-14)
+
+
+def pin_saturation(impl):
+    """One key aligned with q and scaled up dominates: out -> that V row."""
+    rng = np.random.default_rng(6)
+    d, length = 16, 20
+    q = rng.standard_normal((1, d))
+    k = rng.standard_normal((length, 1, d)) * 0.01
+    k[7, 0] = 200.0 * q[0] / np.linalg.norm(q[0])
+    v = rng.standard_normal((length, 1, d))
+    out = impl.attention(q, k, v, 1.0)
+    np.testing.assert_allclose(out[0], v[7, 0], rtol=0, atol=1e-12)
+
+
+def pin_gqa_equals_repeated_mha(impl):
+    """Query head hq reads KV head hq // G: GQA equals MHA whose KV heads
+    are each repeated G times (consecutive grouping)."""
+    rng = np.random.default_rng(7)
+    length, d, hkv, g = 9, 8, 3, 4
+    q = rng.standard_normal((hkv * g, d))
+    k = rng.standard_normal((length, hkv, d))
+    v = rng.standard_normal((length, hkv, d))
+    gqa = impl.attention(q, k, v, 0.5)
+    mha = impl.attention(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), 0.5)
+    assert np.array_equal(gqa, mha)
+    # and each head against a single-head call on its own KV head
+    for hq in range(hkv * g):
+        one = impl.attention(q[hq:hq + 1], k[:, hq // g:hq // g + 1], v[:, hq // g:hq // g + 1], 0.5)
+        assert np.array_equal(one[0], gqa[hq])
+
+
+def pin_library_sdpa(impl):
+    """Special case reducing to a library routine: torch's scaled dot-product
+    attention in float64 on the CPU, KV heads repeated per group."""
+    rng = np.random.default_rng(8)
+    for length, hq, hkv, d in [(1, 4, 4, 8), (50, 8, 2, 16), (300, 6, 3, 32)]:
+        q = rng.standard_normal((hq, d))
+        k = rng.standard_normal((length, hkv, d))
+        v = rng.standard_normal((length, hkv, d))
+        scale = 1.0 / math.sqrt(d)
+        out = impl.attention(q, k, v, scale)
+        g = hq // hkv
+        kt = torch.from_numpy(np.repeat(k, g, axis=1)).permute(1, 0, 2)[None].contiguous()
+        vt = torch.from_numpy(np.repeat(v, g, axis=1)).permute(1, 0, 2)[None].contiguous()
+        qt = torch.from_numpy(q)[None, :, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+        np.testing.assert_allclose(out, ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def _brute_decode(q, k_pool, v_pool, tables, lens, bsz, scale, group):
+    """Pure-Python loops: gather by the index map, then softmax and sum."""
+    out = []
+    for b in range(len(lens)):
+        rows = []
+        for hq in range(len(q[b])):
+            h = hq // group
+            ks, vs = [], []
+            for t in range(lens[b]):
+                blk = tables[b][t // bsz]
+                off = t % bsz
+                ks.append([float(k_pool[blk][h][off][i]) for i in range(len(q[b][hq]))])
+                vs.append([float(v_pool[blk][h][i][off]) for i in range(len(q[b][hq]))])
+            z = [scale * sum(float(q[b][hq][i]) * kk[i] for i in range(len(kk))) for kk in ks]
+            zmax = max(z)
+            e = [math.exp(x - zmax) for x in z]
+            tot = sum(e)
+            rows.append([sum(e[t] * vs[t][i] for t in range(len(e))) / tot
+                         for i in range(len(q[b][hq]))])
+        out.append(rows)
+    return np.array(out)
+
+
+def pin_brute_force(impl):
+    rng = np.random.default_rng(9)
+    bsz, hkv, g, d, nb = 2, 2, 2, 4, 12
+    lens = [1, 2, 3, 5]
+    tables = [list(rng.permutation(nb)[:3]) for _ in lens]
+    q = rng.standard_normal((4, hkv * g, d)).astype(np.float32)
+    k_pool = rng.standard_normal((nb, hkv, bsz, d)).astype(np.float32)
+    v_pool = rng.standard_normal((nb, hkv, d, bsz)).astype(np.float32)
+    got = impl.decode(q, k_pool, v_pool, np.array(tables), np.array(lens), bsz,
+                      0.5, "f32", "f32")
+    want = _brute_decode(q, k_pool, v_pool, tables, lens, bsz, 0.5, g)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def pin_brute_force_tiny_workload(impl):
+    """Brute force on the tiny fp32 workload at a reduced size."""
+    w = WORKLOADS[1]
+    batch = make_batch(w, lens=np.array([1, 3, 17, 33]))
+    h = _host(batch)
+    k2, v2 = impl.write_tokens(h["k"], h["v"], h["kn"], h["vn"], batch.slot_mapping,
+                               w.block_size, "f32", "f32")
+    got = impl.decode(h["q"], k2, v2, batch.block_tables, batch.context_lens,
+                      w.block_size, batch.scale, "f32", "f32")
+    want = _brute_decode(h["q"], k2, v2, batch.block_tables, batch.context_lens,
+                         w.block_size, float(np.float32(batch.scale)), w.group)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def pin_paged_equals_unpaged(impl):
+    """Paged attention equals attention on the contiguous per-sequence
+    layout, bit for bit ("AI Inference Serving at Scale", FAQ)."""
+    rng = np.random.default_rng(10)
+    bsz, hkv, g, d, nb, length = 16, 2, 4, 32, 10, 70
+    k_c = rng.standard_normal((length, hkv, d)).astype(np.float32)
+    v_c = rng.standard_normal((length, hkv, d)).astype(np.float32)
+    q = rng.standard_normal((1, hkv * g, d)).astype(np.float32)
+    table = rng.permutation(nb)[:5]
+    k_pool = np.full((nb, hkv, bsz, d), np.nan, np.float32)
+    v_pool = np.full((nb, hkv, d, bsz), np.nan, np.float32)
+    _scatter_contiguous(k_c, v_c, bsz, table, k_pool, v_pool)
+    paged_out = impl.decode(q, k_pool, v_pool, table[None], np.array([length]), bsz,
+                            0.125, "f32", "f32")
+    flat = impl.attention(q[0].astype(np.float64), k_c.astype(np.float64),
+                          v_c.astype(np.float64), 0.125)
+    assert np.array_equal(paged_out[0], flat)
+
+
+def pin_block_permutation(impl):
+    """Relabelling physical blocks (moving the data along) changes no bit."""
+    for idx in (1, 2):
+        w = WORKLOADS[idx]
+        batch = make_batch(w, num_seqs=3, lens=None if idx == 1 else np.array([40, 77, 130]))
+        base = _decode_batch(impl, batch)
+        perm = np.random.default_rng(11).permutation(batch.num_blocks)
+        moved = _decode_batch(impl, permute_blocks(batch, perm))
+        assert np.array_equal(base, moved)
+        cont = _decode_batch(impl, contiguous_layout(batch))
+        assert np.array_equal(base, cont)
+
+
+def pin_shared_prefix(impl):
+    """Sequences pointing at shared prefix blocks equal private copies."""
+    w = WORKLOADS[4]
+    rng = np.random.default_rng(12)
+    lens = 2048 + rng.integers(1, 40, size=3)
+    batch = make_batch(w, num_seqs=3, lens=lens)
+    small = batch.replace(q=batch.q[:, :4].contiguous(),
+                          k_pool=batch.k_pool[:, :1].contiguous(),
+                          v_pool=batch.v_pool[:, :1].contiguous())
+    small = small.replace(workload=dataclasses.replace(w, num_q_heads=4, num_kv_heads=1))
+    assert np.all(small.ref_counts[small.block_tables[0, :128]] == 3)
+    shared = _decode_batch(impl, small)
+    copied = unshare(small)
+    assert copied.num_blocks == small.num_blocks + 3 * 128
+    assert np.all(copied.ref_counts[copied.ref_counts > 0] == 1)
+    assert np.array_equal(shared, _decode_batch(impl, copied))
+
+
+def pin_split_merge(impl):
+    """Merging softmax states of any split equals the unsplit result."""
+    rng = np.random.default_rng(13)
+    length, hq, hkv, d = 300, 4, 2, 16
+    q = rng.standard_normal((hq, d))
+    k = rng.standard_normal((length, hkv, d)) * 2.0
+    v = rng.standard_normal((length, hkv, d))
+    full = impl.attention(q, k, v, 0.7)
+    for part in (16, 32, 112, 256, 512):
+        bounds = list(range(0, length, part)) + [length]
+        states = [impl.partial(q, k, v, 0.7, a, b) for a, b in zip(bounds[:-1], bounds[1:])]
+        for hh in range(hq):
+            ms = np.array([s[0][hh] for s in states])
+            ls = np.array([s[1][hh] for s in states])
+            os_ = np.array([s[2][hh] for s in states])
+            np.testing.assert_allclose(impl.merge(ms, ls, os_), full[hh], rtol=1e-12, atol=1e-13)
+    m, l, o = impl.partial(q, k, v, 0.7, 0, length)
+    np.testing.assert_allclose(o, full, rtol=1e-13, atol=1e-14)
+    for hh in range(hq):
+        assert np.array_equal(impl.merge(m[hh:hh + 1], l[hh:hh + 1], o[hh:hh + 1]), o[hh])
+
+
+def pin_e4m3_decode_table(impl):
+    """All 256 E4M3FN codes against torch's float8_e4m3fn dtype."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = impl.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9 and mine[0x08] == 2.0 ** -6
+
+
+def pin_e4m3_encode(impl):
+    """Round-to-nearest-even against torch's cast, inside the finite range;
+    exact for every representable value and for midpoints (ties to even)."""
+    rng = np.random.default_rng(14)
+    x = np.concatenate([rng.standard_normal(20000) * 50.0,
+                        rng.uniform(-448, 448, 20000),
+                        rng.standard_normal(20000) * 1e-2]).astype(np.float32)
+    mine = impl.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+    vals = impl.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    assert np.array_equal(impl.e4m3_encode(vals), np.arange(0x7F, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    ref_mid = torch.from_numpy(mids).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(impl.e4m3_encode(mids), ref_mid)
+    assert np.all(impl.e4m3_encode(np.array([449.0, 1e6, -1e9])) == [0x7E, 0x7E, 0xFE])
+    assert impl.e4m3_encode(np.array([np.nan]))[0] & 0x7F == 0x7F
+
+
+def pin_bf16_widen():
+    rng = np.random.default_rng(15)
+    bits = rng.integers(0, 2**16, 50000).astype(np.uint16)
+    mine = codecs.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+
+
+def pin_fp8_write_then_decode(impl):
+    """An FP8 append stores the codes of x / scale; the decode multiplies the
+    scale back, so a one-token sequence returns the dequantised new row."""
+    rng = np.random.default_rng(16)
+    hkv, d, bsz, nb = 2, 16, 32, 3
+    k_pool = np.zeros((nb, hkv, bsz, d), np.uint8)
+    v_pool = np.zeros((nb, hkv, d, bsz), np.uint8)
+    kn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    ks = np.array([0.01, 0.02], np.float32)
+    vs = np.array([0.015, 0.005], np.float32)
+    k2, v2 = impl.write_tokens(k_pool, v_pool, kn, vn, np.array([2 * bsz]), bsz,
+                               "f32", "fp8_e4m3", ks, vs)
+    ref = torch.from_numpy(vn[0] / vs[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(v2[2, :, :, 0], ref)
+    q = rng.standard_normal((1, 4, d)).astype(np.float32)
+    out = impl.decode(q, k2, v2, np.array([[2]]), np.array([1]), bsz, 0.25,
+                      "f32", "fp8_e4m3", ks, vs)
+    deq = impl.e4m3_to_f64(ref) * vs[:, None].astype(np.float64)
+    assert np.array_equal(out[0], deq[np.arange(4) // 2])
+
+
+# ==========================================================================
+# the pins on the oracle
+# ==========================================================================
+
+PINS = [pin_golden_index, pin_gather_roundtrip, pin_write_whole_pool,
+        pin_write_then_gather, pin_single_token, pin_two_tokens,
+        pin_identical_keys_mean, pin_saturation, pin_gqa_equals_repeated_mha,
+        pin_library_sdpa, pin_brute_force, pin_brute_force_tiny_workload,
+        pin_paged_equals_unpaged, pin_block_permutation, pin_shared_prefix,
+        pin_split_merge, pin_e4m3_decode_table, pin_e4m3_encode,
+        pin_fp8_write_then_decode]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(ORACLE)
+
+
+def test_bf16_widen():
+    pin_bf16_widen()
+
+
+def test_oracle_decode_partials_contract():
+    """decode_partials fills exactly the partitions each sequence has."""
+    w = WORKLOADS[2]
+    batch = make_batch(w, num_seqs=3, lens=np.array([33, 64, 100]))
+    h = _host(batch)
+    m, l, o = paged.decode_partials(h["q"], h["k"], h["v"], batch.block_tables,
+                                    batch.context_lens, 16, batch.scale, "bf16",
+                                    "bf16", 32)
+    assert m.shape == (3, 32, 4) and o.shape == (3, 32, 4, 128)
+    assert np.isnan(m[0, :, 2:]).all() and not np.isnan(m[0, :, :2]).any()
+    assert not np.isnan(m[2]).any()
+    full = _decode_batch(ORACLE, batch)
+    for b in range(3):
+        n = -(-int(batch.context_lens[b]) // 32)
+        for hq in range(32):
+            np.testing.assert_allclose(
+                paged.merge(m[b, hq, :n], l[b, hq, :n], o[b, hq, :n]),
+                full[b, hq], rtol=1e-12, atol=1e-13)
+
+
+def test_oracle_rejects_duplicate_slots():
+    k = np.zeros((2, 1, 16, 4), np.float32)
+    v = np.zeros((2, 1, 4, 16), np.float32)
+    rows = np.ones((2, 1, 4), np.float32)
+    with pytest.raises(ValueError):
+        paged.write_tokens(k, v, rows, rows, np.array([3, 3]), 16, "f32", "f32")
+
+
+def test_oracle_empty_context_is_zero():
+    out = paged.attention(np.ones((2, 4)), np.zeros((0, 1, 4)), np.zeros((0, 1, 4)), 1.0)
+    assert np.array_equal(out, np.zeros((2, 4)))
+
+
+def test_oracle_package_header_says_test_only():
+    assert "TEST INFRASTRUCTURE ONLY" in oracle.__doc__
+
+
+# ==========================================================================
+# planted mistakes: each broken copy of the oracle must fail some pin
+# ==========================================================================
+
+def _bad_slot_of(table_row, t, block_size):
+    i, j = divmod(int(t) + 1, int(block_size))  # off by one
+    return int(table_row[i]), j
+
+
+def _bad_gather_v_layout(k_pool, v_pool, table_row, length, block_size):
+    k, _ = paged.gather(k_pool, v_pool, table_row, length, block_size)
+    v = np.empty_like(k)
+    for t in range(length):  # reads V as if it were token-major like K
+        blk, off = paged.slot_of(table_row, t, block_size)
+        v[t] = v_pool.reshape(v_pool.shape[0], v_pool.shape[1], block_size, -1)[blk, :, off, :]
+    return k, v
+
+
+def _bad_attention_no_scale(q, k, v, scale):
+    return paged.attention(q, k, v, 1.0)
+
+
+def _bad_attention_gqa_modulo(q, k, v, scale):
+    n_q = q.shape[0]
+    out = np.zeros_like(q, dtype=np.float64)
+    for hq in range(n_q):
+        h = hq % k.shape[1]  # interleaved instead of consecutive grouping
+        z = scale * (k[:, h, :] @ q[hq])
+        e = np.exp(z - z.max())
+        out[hq] = (e / e.sum()) @ v[:, h, :]
+    return out
+
+
+def _bad_attention_sign(q, k, v, scale):
+    return paged.attention(-q, k, v, scale)
+
+
+def _bad_attention_drop_last(q, k, v, scale):
+    return paged.attention(q, k[:-1], v[:-1], scale) if k.shape[0] > 1 else paged.attention(q, k, v, scale)
+
+
+def _bad_merge_no_rescale(ms, ls, os_):
+    return (ls[:, None] * os_).sum(axis=0) / ls.sum()
+
+
+def _bad_e4m3_bias(codes):
+    return paged.codecs.e4m3_to_f64(codes) * 2.0
+
+
+def _bad_encode_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    vals = codecs.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mag = np.minimum(np.abs(x), 448.0)
+    idx = np.searchsorted(vals, mag, side="right") - 1
+    return (idx.astype(np.uint8) | np.where(np.signbit(x), 0x80, 0).astype(np.uint8))
+
+
+def _bad_write_skip_v(k_pool, v_pool, k_new, v_new, slot_mapping, block_size,
+                      src_dtype, cache_dtype, k_scale=None, v_scale=None):
+    k2, _ = paged.write_tokens(k_pool, v_pool, k_new, v_new, slot_mapping, block_size,
+                               src_dtype, cache_dtype, k_scale, v_scale)
+    return k2, v_pool.copy()
+
+
+def _mk_decode(**over):
+    """decode() rebuilt on top of possibly broken parts."""
+    impl = _impl(**over)
+
+    def decode(q, k_pool, v_pool, block_tables, context_lens, block_size, scale,
+               q_dtype, cache_dtype, k_scale=None, v_scale=None, seqs=None):
+        q64 = paged.to_f64(q, q_dtype)
+        out = np.zeros(q64.shape)
+        scale = float(np.float32(scale))
+        for b in range(q64.shape[0]):
+            kr, vr = impl.gather(k_pool, v_pool, block_tables[b], int(context_lens[b]), block_size)
+            k = paged.to_f64(kr, cache_dtype)
+            v = paged.to_f64(vr, cache_dtype)
+            if cache_dtype == "fp8_e4m3":
+                k = k * np.asarray(k_scale, np.float64)[None, :, None]
+                v = v * np.asarray(v_scale, np.float64)[None, :, None]
+            out[b] = impl.attention(q64[b], k, v, scale)
+        return out
+    return decode
+
+
+MUTANTS = {
+    "index-off-by-one": dict(slot_of=_bad_slot_of),
+    "v-layout-transposed": dict(gather=_bad_gather_v_layout),
+    "scale-dropped": dict(attention=_bad_attention_no_scale),
+    "gqa-interleaved": dict(attention=_bad_attention_gqa_modulo),
+    "score-sign": dict(attention=_bad_attention_sign),
+    "last-token-dropped": dict(attention=_bad_attention_drop_last),
+    "merge-no-rescale": dict(merge=_bad_merge_no_rescale),
+    "e4m3-exponent-bias": dict(e4m3_to_f64=_bad_e4m3_bias),
+    "e4m3-truncating": dict(e4m3_encode=_bad_encode_truncate),
+    "write-drops-v": dict(write_tokens=_bad_write_skip_v),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    over = MUTANTS[name]
+    impl = _impl(**over)
+    if "gather" in over or "attention" in over:
+        impl.decode = _mk_decode(**over)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(impl)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name!r}"

@@ -1,0 +1,14 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+Holds input drawing, the host block allocator, block-level relayouts and
+byte accounting -- none of the attention arithmetic.  The oracle and the
+HIP library both consume what this package produces; neither is imported
+here.
+"""
+
+from .accounting import (ELEMENT_BYTES, decode_bytes, kv_bytes,  # noqa: F401
+                         kv_bytes_per_token, write_bytes)
+from .allocator import BlockManager, Sequence  # noqa: F401
+from .batch import (WORKLOADS, Batch, Workload, contiguous_layout,  # noqa: F401
+                    draw_lens, extract_sequences, host_view, make_batch,
+                    permute_blocks, unshare)

@@ -1,0 +1,61 @@
+"""Byte accounting for KV caches and for one decode step.
+
+The KV footprint per token is two tensors (K and V) times layers times KV
+heads times head dimension times bytes per element ("vLLM &
+High-Throughput Serving", section 1, memory-per-token equation; "How LLM
+Inference Engines Work", KV cache per layer formula).  "AI Inference
+Serving at Scale", section 2, writes a formula with one more factor of 2,
+but its own 2.6 MB-per-token figure omits that factor; the figures, not
+the garbled formula, are what the tests pin.
+
+``decode_bytes`` / ``write_bytes`` give the algorithmic HBM traffic of one
+launch: every byte the operation must read or write at least once.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+ELEMENT_BYTES = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}
+
+
+def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int,
+                       bytes_per_element: int) -> int:
+    """K and V bytes one token occupies across all layers."""
+    return 2 * layers * kv_heads * head_dim * bytes_per_element
+
+
+def kv_bytes(tokens: int, layers: int, kv_heads: int, head_dim: int,
+             bytes_per_element: int) -> int:
+    return tokens * kv_bytes_per_token(layers, kv_heads, head_dim,
+                                       bytes_per_element)
+
+
+def decode_bytes(context_lens, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, block_size: int, cache_dtype: str,
+                 q_dtype: str) -> dict:
+    """Algorithmic bytes of one decode over a batch (one layer).
+
+    K and V of every valid token, each read once; q read and out written
+    once; the used block-table entries and the lengths read once; one
+    float32 scale per KV head for K and for V when the cache is FP8.
+    """
+    lens = np.asarray(context_lens, dtype=np.int64)
+    elt = ELEMENT_BYTES[cache_dtype]
+    qb = ELEMENT_BYTES[q_dtype]
+    tokens = int(lens.sum())
+    kv = tokens * 2 * num_kv_heads * head_dim * elt
+    s = len(lens)
+    q_out = 2 * s * num_q_heads * head_dim * qb
+    tables = int((-(-lens // block_size)).sum()) * 4 + s * 4
+    scales = 2 * num_kv_heads * 4 if cache_dtype == "fp8_e4m3" else 0
+    return {"kv": kv, "q_out": q_out, "tables": tables, "scales": scales,
+            "total": kv + q_out + tables + scales, "tokens": tokens}
+
+
+def write_bytes(num_tokens: int, num_kv_heads: int, head_dim: int,
+                src_dtype: str, cache_dtype: str) -> int:
+    """Algorithmic bytes of one cache append: read new rows, write slots."""
+    rows = num_tokens * 2 * num_kv_heads * head_dim
+    return (rows * ELEMENT_BYTES[src_dtype] + rows * ELEMENT_BYTES[cache_dtype]
+            + num_tokens * 8)
