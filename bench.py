@@ -1,0 +1,245 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+One step = the whole hot path over one synthetic batch already resident in
+HBM: append each sequence's new K/V token (``pa_kv_cache_write``), then
+decode attention over the paged cache (``pa_decode``, plus
+``pa_decode_reduce`` when the context is split).  Default workload: the
+Llama-3-8B-shaped decode batch (64 sequences, 32 query / 8 KV heads, head
+dim 128, 16-token blocks, bf16 KV, lengths U[512, 4096]).
+
+Prints one JSON line on stdout.  ``value`` is the step's algorithmic HBM
+bytes divided by the step time (GB/s); ``roofline`` is the decode kernel
+alone, timed with HIP events on the stream it runs on; ``cpu_baseline`` is
+the fp64 CPU oracle on a bounded sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD public spec
+KERNEL_SOURCES = ["decode_mfma.hip", "decode_valu.hip", "pa_device.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_253_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str, partition: int, launches_per_step: int):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, or
+    None when there are none for this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_sha() or rec.get("partition") != partition:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(batch, seconds: float) -> dict:
+    """Time the oracle (single-threaded BLAS) on whole sequences of the batch
+    until ``seconds`` of CPU work have been spent."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged
+    from workloads import decode_bytes, extract_sequences
+
+    w = batch.workload
+    order = np.random.default_rng(0).permutation(len(batch.context_lens))
+    done, spent, nbytes, tokens = [], 0.0, 0, 0
+    with threadpool_limits(limits=1):
+        for b in order:
+            sub = extract_sequences(batch, [int(b)])
+            t = time.perf_counter()
+            paged.decode(sub["q"], sub["k_pool"], sub["v_pool"], sub["block_tables"],
+                         sub["context_lens"], w.block_size, batch.scale, w.q_dtype,
+                         w.cache_dtype, sub["k_scale"], sub["v_scale"])
+            spent += time.perf_counter() - t
+            done.append(int(b))
+            acct = decode_bytes(sub["context_lens"], w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                w.block_size, w.cache_dtype, w.q_dtype)
+            nbytes += acct["total"]
+            tokens += acct["tokens"]
+            if spent >= seconds:
+                break
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": tokens / spent, "seconds": round(spent, 2),
+            "sample": f"{len(done)} of {len(batch.context_lens)} sequences "
+                      f"({tokens} context tokens), fp64 numpy oracle, 1 BLAS thread"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="context split in tokens (-1: the library default)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_cache_253_amd as pk
+    from workloads import WORKLOADS, decode_bytes, make_batch, write_bytes
+
+    w = WORKLOADS[args.workload]
+    dev = "cuda"
+    t_gen = time.perf_counter()
+    batch = make_batch(w, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] workload {w.index} {w.name}: {len(batch.context_lens)} seqs, "
+        f"{int(batch.context_lens.sum())} tokens, pool {batch.num_blocks} blocks "
+        f"(generated in {time.perf_counter() - t_gen:.1f}s)")
+
+    part = w.partition_size if args.partition < 0 and w.partition_size else args.partition
+    if part < 0:
+        part = pk.default_partition_size(batch.max_context_len)
+    bt = torch.from_numpy(batch.block_tables).to(dev)
+    cl = torch.from_numpy(batch.context_lens).to(dev)
+    slots = torch.from_numpy(batch.slot_mapping).to(dev)
+    out = torch.empty_like(batch.q)
+    s, hq, d = batch.q.shape
+    ws = None
+    if part:
+        ws = torch.empty(pk.workspace_size(s, hq, d, batch.max_context_len, part),
+                         dtype=torch.uint8, device=dev)
+
+    ev = {}
+
+    def rec(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        ev.setdefault(name, []).append(e)
+
+    def step(timed: bool):
+        if timed:
+            rec("write0")
+        pk.kv_cache_write(batch.k_new, batch.v_new, batch.k_pool, batch.v_pool, slots,
+                          batch.k_scale, batch.v_scale)
+        if timed:
+            rec("write1")
+        if part:
+            pk.decode_partitions(batch.q, batch.k_pool, batch.v_pool, bt, cl,
+                                 batch.max_context_len, part, batch.scale, batch.k_scale,
+                                 batch.v_scale, ws)
+            if timed:
+                rec("decode1")
+            pk.decode_reduce(out, ws, cl, batch.max_context_len, part)
+            if timed:
+                rec("reduce1")
+        else:
+            pk.decode(batch.q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len,
+                      batch.scale, batch.k_scale, batch.v_scale, 0, out=out)
+            if timed:
+                rec("decode1")
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps (partition {part})")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step(True)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    def span(a, b):
+        return [x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]
+
+    write_ms = float(np.mean(span("write0", "write1")))
+    decode_ms_list = span("write1", "decode1")
+    decode_ms = float(np.mean(decode_ms_list))
+    reduce_ms = float(np.mean(span("decode1", "reduce1"))) if part else 0.0
+
+    dec = decode_bytes(batch.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                       w.block_size, w.cache_dtype, w.q_dtype)
+    wr = write_bytes(len(batch.context_lens), w.num_kv_heads, w.head_dim, w.src_dtype,
+                     w.cache_dtype)
+    step_bytes = dec["total"] + wr
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = dec["total"] / (decode_ms * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us (write {write_ms * 1e3:.1f}, decode "
+        f"{decode_ms * 1e3:.1f}, reduce {reduce_ms * 1e3:.1f}); decode {achieved:.0f} GB/s "
+        f"= {100 * achieved / PEAK_HBM_GBS:.1f}% of peak")
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 1 GiB device copies done")
+
+    traffic = measured_traffic(w.name, part, 1)
+    result = {
+        "metric": "paged decode attention: achieved HBM GB/s (% of peak) and context tokens/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8_e4m3", "f32": "f32"}[w.cache_dtype],
+        "data": "synthetic",
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "context_tokens_per_s": round(dec["tokens"] / (ms_per_step * 1e-3), 1),
+        "config": {"workload": w.name, "num_seqs": len(batch.context_lens),
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size,
+                   "kv_dtype": w.cache_dtype, "context_tokens": dec["tokens"],
+                   "partition_size": part, "step": "kv_cache_write + decode"
+                   + (" + reduce" if part else "")},
+        "kernels_us": {"kv_cache_write": round(write_ms * 1e3, 2),
+                       "decode": round(decode_ms * 1e3, 2),
+                       "decode_reduce": round(reduce_ms * 1e3, 2)},
+        "roofline": {"bound": "hbm", "kernel": "pa_decode", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": dec["total"],
+                     "traffic": traffic},
+    }
+    if not args.no_cpu:
+        log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f}s")
+        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

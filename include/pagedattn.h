@@ -1,0 +1,226 @@
+/*
+ * pagedattn.h -- C ABI of the paged decode-attention library (AMD MI355X, gfx950).
+ *
+ * What it computes (restated from the pages it follows):
+ *
+ *   - A KV cache lives in a pre-allocated pool of fixed-size physical blocks
+ *     of B tokens; each sequence reaches its blocks through a block table
+ *     ("AI Inference Serving at Scale", section 3: physical block pool,
+ *     logical-to-physical block table, on-demand allocation; "How LLM
+ *     Inference Engines Work", PagedAttention section: pages of 16 or 32
+ *     tokens).  Token t of a sequence is at offset t mod B of the physical
+ *     block named by table entry floor(t / B) ("vLLM & High-Throughput
+ *     Serving", section 2, block-table equation).  Several tables may name
+ *     the same physical block (prefix sharing, same sections).
+ *   - Decode-phase attention: one new query token per sequence attends to
+ *     every cached token of that sequence ("AI Inference Serving at Scale",
+ *     sections 1 and 2); the kernel gathers K and V from the non-adjacent
+ *     blocks ("How LLM Inference Engines Work", PagedAttention section).
+ *     Query head hq reads KV head hq / (Hq / Hkv) (grouped-query attention,
+ *     "AI Inference Serving at Scale", section 6).  The result equals plain,
+ *     un-paged attention (same page, FAQ).
+ *   - An FP8 KV cache ("AI Inference Serving at Scale", section 6) stores
+ *     OCP E4M3FN codes with one float32 scale per KV head: value = code *
+ *     scale.
+ *
+ * Conventions for every entry point:
+ *
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The
+ *     library allocates no memory and keeps no state between calls.
+ *   - Work is enqueued on `stream` (0 = the null stream) and is
+ *     asynchronous; no call synchronizes the device or copies to the host.
+ *   - Arguments are checked on the host before anything is launched; on
+ *     failure the call returns a non-zero pa_status, launches nothing and
+ *     leaves every buffer untouched.  A launch failure reported by the HIP
+ *     runtime returns PA_ERR_HIP.  No C++ exception crosses this interface.
+ *   - Contents of device arrays cannot be checked without a device sync;
+ *     they are the caller's contract.  The kernels keep every memory access
+ *     inside the buffers described here even when that contract is broken
+ *     (see each call), but the results are then meaningless.
+ *   - Calls that share no output buffers may run concurrently on different
+ *     streams.
+ *
+ * Pool layout (one pool for K, one for V, `num_blocks` blocks each):
+ *
+ *   K cache: [num_blocks][num_kv_heads][block_size][head_dim]
+ *            (inside a (block, head) tile: one row of head_dim per token)
+ *   V cache: [num_blocks][num_kv_heads][head_dim][block_size]
+ *            (inside a (block, head) tile: one row of block_size tokens per
+ *            dimension)
+ *
+ * Supported shapes: head_dim 64 or 128; block_size 16 or 32; element types
+ * as listed per call.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, negative count, inconsistent sizes */
+  PA_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (shape / type / group) */
+  PA_ERR_WORKSPACE = 3,   /* split decode given too small a workspace */
+  PA_ERR_HIP = 4          /* the HIP runtime reported an error */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,      /* IEEE binary32 */
+  PA_BF16 = 1,     /* bfloat16 (upper half of a binary32) */
+  PA_FP8_E4M3 = 2  /* OCP FP8 E4M3FN code, one byte, with a per-KV-head scale */
+} pa_dtype;
+
+/*
+ * pa_kv_cache_write -- append new tokens' K and V rows into the pool.
+ *
+ * Follows "AI Inference Serving at Scale", section 3 (each generated
+ * token's K/V goes into its sequence's current block) and the block-table
+ * equation of "vLLM & High-Throughput Serving", section 2 applied to a flat
+ * slot number: token n is stored at block slot_mapping[n] / block_size,
+ * offset slot_mapping[n] % block_size, for every KV head.
+ *
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim], element src_dtype
+ *   k_cache        K pool, element cache_dtype (layout above)
+ *   v_cache        V pool, element cache_dtype (layout above)
+ *   slot_mapping   [num_tokens] int64; a negative slot marks a padding token
+ *                  and writes nothing
+ *   num_blocks     pool size in blocks
+ *   src_dtype      PA_F32 or PA_BF16
+ *   cache_dtype    equal to src_dtype (the bits are copied unchanged), or
+ *                  PA_FP8_E4M3: each element x of KV head h is stored as
+ *                  round_to_nearest_even_e4m3(fp32(x) / k_scale[h]) (V with
+ *                  v_scale), saturated to +-448; NaN stays NaN
+ *   k_scale, v_scale  [num_kv_heads] float32, device; required for an FP8
+ *                  cache, ignored otherwise (may be NULL)
+ *
+ * Caller contract: two tokens must not share a slot (the stored row is then
+ * one of them, unspecified which).  A slot at or beyond
+ * num_blocks * block_size is skipped.  num_tokens == 0 is a no-op.
+ */
+pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache,
+                            const int64_t* slot_mapping, int num_tokens,
+                            int num_kv_heads, int head_dim, int block_size,
+                            int64_t num_blocks,
+                            pa_dtype src_dtype, pa_dtype cache_dtype,
+                            const float* k_scale, const float* v_scale,
+                            hipStream_t stream);
+
+/*
+ * pa_decode -- single-query attention of every sequence over its paged
+ * context (the decode phase of "AI Inference Serving at Scale", section 1;
+ * the gather of "How LLM Inference Engines Work", PagedAttention section).
+ *
+ * For sequence b and query head hq, with G = num_q_heads / num_kv_heads,
+ * h = hq / G, L = context_lens[b] and k_t, v_t the K/V rows of token t
+ * (read through block_tables[b] by the block-table equation):
+ *
+ *   z_t = scale * dot(q[b][hq], k_t)              (FP8: k_t = code * k_scale[h])
+ *   out[b][hq] = sum_t softmax(z)_t * v_t          (FP8: v_t = code * v_scale[h])
+ *
+ * accumulated in float32.  L == 0 gives zeros.
+ *
+ *   out            [num_seqs][num_q_heads][head_dim], element q_dtype; written
+ *                  only when partition_size == 0 (may be NULL otherwise)
+ *   q              [num_seqs][num_q_heads][head_dim], element q_dtype
+ *   k_cache, v_cache   the pools (layout above), element cache_dtype
+ *   block_tables   [num_seqs][max_blocks_per_seq] int32 physical block ids;
+ *                  only entries below ceil(L / block_size) are read
+ *   context_lens   [num_seqs] int32, device
+ *   max_context_len    host-side upper bound of context_lens (sizes the
+ *                  launch and the workspace without a device sync)
+ *   num_blocks     pool size in blocks
+ *   scale          softmax scale (typically 1 / sqrt(head_dim))
+ *   q_dtype / cache_dtype  (PA_F32, PA_F32), (PA_BF16, PA_BF16) or
+ *                  (PA_BF16, PA_FP8_E4M3)
+ *   k_scale, v_scale   [num_kv_heads] float32, device; FP8 cache only
+ *   partition_size 0: each (sequence, KV head) is handled whole and `out`
+ *                  is written.  > 0 (a multiple of 32): flash-decoding
+ *                  split -- partition p of sequence b covers tokens
+ *                  [p * P, min((p + 1) * P, L)); each partition's softmax
+ *                  state goes to `workspace` (layout at
+ *                  pa_decode_workspace_size) and `out` is NOT written;
+ *                  pa_decode_reduce then merges the partitions into `out`.
+ *   workspace, workspace_bytes  device scratch for the split; at least
+ *                  pa_decode_workspace_size(...) bytes, 256-byte aligned;
+ *                  ignored when partition_size == 0
+ *
+ * Group sizes: any G <= 16 for a bf16 or FP8 cache; G in {1, 2, 4, 8} for
+ * an f32 cache.
+ *
+ * Caller contract: context_lens[b] <= max_context_len and <=
+ * max_blocks_per_seq * block_size, and the table entries read are in
+ * [0, num_blocks).  If not, the kernels clamp L to those bounds and read
+ * block 0 in place of an out-of-range id, so no access leaves the buffers.
+ */
+pa_status pa_decode(void* out, const void* q,
+                    const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, int max_context_len,
+                    int num_seqs, int num_q_heads, int num_kv_heads,
+                    int head_dim, int block_size, int64_t num_blocks,
+                    float scale, pa_dtype q_dtype, pa_dtype cache_dtype,
+                    const float* k_scale, const float* v_scale,
+                    int partition_size, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * pa_decode_workspace_size -- bytes of workspace a split pa_decode needs
+ * (0 when partition_size == 0; SIZE_MAX for invalid arguments).
+ *
+ * Layout, with maxP = max(1, ceil(max_context_len / partition_size)) and
+ * align(x) = x rounded up to a multiple of 256:
+ *
+ *   float part_out[num_seqs][num_q_heads][maxP][head_dim]   at 0
+ *   float part_max[num_seqs][num_q_heads][maxP]  at align(|part_out|)
+ *   float part_sum[num_seqs][num_q_heads][maxP]  at that + align(|part_max|)
+ *
+ * For partition p of sequence b and query head hq, with z_t as in
+ * pa_decode over the partition's tokens: part_max = max_t z_t, part_sum =
+ * sum_t exp(z_t - part_max), part_out = sum_t exp(z_t - part_max) v_t /
+ * part_sum.  Entries of partitions a sequence does not have are unused.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
+                                int max_context_len, int partition_size);
+
+/*
+ * pa_decode_reduce -- merge the partitions of a split decode into `out`.
+ *
+ * The partitions of one (sequence, query head) are disjoint token ranges;
+ * rescaling each range's exp-sum to the common maximum and weighting the
+ * range outputs by it gives softmax over the whole context (the split-
+ * context merge of flash decoding; the pages' un-paged attention is the
+ * target it must reproduce):
+ *
+ *   M = max_p part_max[p];  w_p = part_sum[p] * exp(part_max[p] - M)
+ *   out = sum_p w_p * part_out[p] / sum_p w_p,    p < ceil(L / P)
+ *
+ * in float32, partitions merged in increasing p.  L == 0 gives zeros.
+ *
+ *   out            [num_seqs][num_q_heads][head_dim], element out_dtype
+ *                  (PA_F32 or PA_BF16, rounded to nearest even)
+ *   workspace      as filled by pa_decode with the same num_seqs,
+ *                  num_q_heads, head_dim, max_context_len, partition_size
+ *   context_lens   [num_seqs] int32, device (clamped to max_context_len)
+ */
+pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                           const int32_t* context_lens, int max_context_len,
+                           int num_seqs, int num_q_heads, int head_dim,
+                           int partition_size, pa_dtype out_dtype,
+                           hipStream_t stream);
+
+/* pa_status_string -- static, human-readable name of a status code. */
+const char* pa_status_string(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,219 @@
+"""Python binding of ``libpagedattn`` -- paged decode attention on MI355X.
+
+Argument marshalling only: torch tensors become device pointers and torch's
+current HIP stream becomes the ``hipStream_t``; every step of the
+computation runs in the library's HIP kernels (C ABI in
+``include/pagedattn.h``).  There is no CPU fallback: when the shared library
+is missing or a call fails, these functions raise.
+
+Pool layout (the library's): K ``[num_blocks, Hkv, B, D]``, V
+``[num_blocks, Hkv, D, B]``; bf16 / f32 pools hold ``torch.bfloat16`` /
+``torch.float32``, an FP8 pool holds E4M3FN codes as ``torch.uint8`` (or
+``torch.float8_e4m3fn``) with float32 scales per KV head.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["PagedAttnError", "load", "kv_cache_write", "decode", "decode_partitions",
+           "decode_reduce", "workspace_size", "workspace_views", "default_partition_size",
+           "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+_STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
+           3: "PA_ERR_WORKSPACE", 4: "PA_ERR_HIP"}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        super().__init__(f"{call} failed: {_STATUS.get(status, status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the shared library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m paged_kv_cache_253_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, szt = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                              ctypes.c_float, ctypes.c_size_t)
+    lib.pa_kv_cache_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, i32,
+                                      vp, vp, vp]
+    lib.pa_kv_cache_write.restype = i32
+    lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i64,
+                              f32, i32, i32, vp, vp, i32, vp, szt, vp]
+    lib.pa_decode.restype = i32
+    lib.pa_decode_reduce.argtypes = [vp, vp, szt, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_decode_reduce.restype = i32
+    lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.pa_decode_workspace_size.restype = szt
+    lib.pa_status_string.argtypes = [i32]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(call: str, status: int) -> None:
+    if status != 0:
+        raise PagedAttnError(call, status)
+
+
+def workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
+                   partition_size: int) -> int:
+    n = load().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                        partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid workspace arguments")
+    return int(n)
+
+
+def workspace_views(workspace: torch.Tensor, num_seqs: int, num_q_heads: int, head_dim: int,
+                    max_context_len: int, partition_size: int):
+    """(part_out, part_max, part_sum) float32 views of a split-decode
+    workspace, in the layout documented at ``pa_decode_workspace_size``."""
+    parts = max(1, -(-max_context_len // partition_size))
+    rows = num_seqs * num_q_heads * parts
+
+    def align(x):
+        return (x + 255) // 256 * 256
+
+    out_b = align(rows * head_dim * 4)
+    max_b = align(rows * 4)
+    flat = workspace.view(torch.uint8)
+    part_out = flat[:rows * head_dim * 4].view(torch.float32).view(num_seqs, num_q_heads, parts, head_dim)
+    part_max = flat[out_b:out_b + rows * 4].view(torch.float32).view(num_seqs, num_q_heads, parts)
+    part_sum = flat[out_b + max_b:out_b + max_b + rows * 4].view(torch.float32).view(
+        num_seqs, num_q_heads, parts)
+    return part_out, part_max, part_sum
+
+
+def default_partition_size(max_context_len: int) -> int:
+    """Context split used when the caller gives none: 512-token partitions
+    once contexts are longer than that, else unsplit."""
+    return 512 if max_context_len > 512 else 0
+
+
+def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                   v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_scale: torch.Tensor | None = None,
+                   v_scale: torch.Tensor | None = None) -> None:
+    """``pa_kv_cache_write``: store row n of k_new/v_new at slot_mapping[n]."""
+    n, hkv, d = k_new.shape
+    nb, hkv2, bsz, d2 = k_cache.shape
+    if (hkv2, d2) != (hkv, d) or tuple(v_cache.shape) != (nb, hkv, d, bsz):
+        raise ValueError("cache shapes do not match the new rows")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != n:
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    st = load().pa_kv_cache_write(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(slot_mapping), n, hkv, d, bsz, nb,
+                                  _dtype_code(k_new), _dtype_code(k_cache),
+                                  _ptr(k_scale), _ptr(v_scale), _stream(k_cache))
+    _check("pa_kv_cache_write", st)
+
+
+def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                 scale, k_scale, v_scale, partition_size, workspace):
+    s, hq, d = q.shape
+    nb, hkv, bsz, _ = k_cache.shape
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                          block_tables.shape[1], _ptr(context_lens), int(max_context_len), s, hq,
+                          hkv, d, bsz, nb, float(scale), _dtype_code(q), _dtype_code(k_cache),
+                          _ptr(k_scale), _ptr(v_scale), int(partition_size), _ptr(workspace),
+                          ws_bytes, _stream(q))
+    _check("pa_decode", st)
+
+
+def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                      partition_size, scale=None, k_scale=None, v_scale=None,
+                      workspace=None) -> torch.Tensor:
+    """Split ``pa_decode`` only: fill and return the workspace."""
+    s, hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        n = workspace_size(s, hq, d, max_context_len, partition_size)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _decode_call(None, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                 k_scale, v_scale, partition_size, workspace)
+    return workspace
+
+
+def decode_reduce(out: torch.Tensor, workspace: torch.Tensor, context_lens: torch.Tensor,
+                  max_context_len: int, partition_size: int) -> torch.Tensor:
+    """``pa_decode_reduce``: merge the workspace's partitions into ``out``."""
+    s, hq, d = out.shape
+    st = load().pa_decode_reduce(_ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 _ptr(context_lens), int(max_context_len), s, hq, d,
+                                 int(partition_size), _dtype_code(out), _stream(out))
+    _check("pa_decode_reduce", st)
+    return out
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+           scale: float | None = None, k_scale: torch.Tensor | None = None,
+           v_scale: torch.Tensor | None = None, partition_size: int | None = None,
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None
+           ) -> torch.Tensor:
+    """Decode attention over the paged cache; returns ``out [S, Hq, D]``.
+
+    ``partition_size`` 0 runs unsplit; > 0 runs the split decode followed by
+    the merge; None picks ``default_partition_size(max_context_len)``.
+    """
+    s, hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if partition_size is None:
+        partition_size = default_partition_size(max_context_len)
+    if out is None:
+        out = torch.empty_like(q)
+    if partition_size == 0:
+        _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                     scale, k_scale, v_scale, 0, None)
+        return out
+    workspace = decode_partitions(q, k_cache, v_cache, block_tables, context_lens,
+                                  max_context_len, partition_size, scale, k_scale, v_scale,
+                                  workspace)
+    return decode_reduce(out, workspace, context_lens, max_context_len, partition_size)

@@ -1,0 +1,329 @@
+// Paged decode attention on the matrix cores (bf16 or FP8-E4M3 KV cache).
+//
+// One wavefront owns one (sequence, KV head, context partition).  It walks
+// the partition in steps of 32 tokens (two 16-token blocks or one 32-token
+// block), reaching each block through the sequence's block table (the
+// block-table equation of "vLLM & High-Throughput Serving", section 2), and
+// keeps the next step's K and V tiles in flight while it computes the
+// current one.  Per step:
+//
+//   S^T = K q^T      two v_mfma_f32_16x16x32_bf16 chains (16 tokens each)
+//                    over head_dim; rows = tokens, columns = the G query
+//                    heads of this KV head (zero columns beyond G)
+//   online softmax   per query head, in the MFMA output registers; the step
+//                    maximum needs two permlane swaps, no LDS
+//   O^T += V^T P^T   head_dim/16 MFMAs; V tiles are stored dimension-major
+//                    so each lane's 8 tokens of one dimension are one 16-byte
+//                    load, and P comes straight from the S^T registers
+//
+// MFMA operand layouts (16x16x32, wave64; checked on hardware): lane l holds
+// row/column l % 16 and k-slots 8*(l/16) .. 8*(l/16)+7 of A and B; the f32
+// result row is 4*(l/16) + r (r = 0..3), column l % 16.  The token assigned
+// to QK row i of group m is 8*(i/4) + 4*m + i%4, so a lane's QK results are
+// exactly the 8 tokens 8*(l/16) .. +7 that its PV k-slots need.
+//
+// The same head mapping (column = query head) holds in S^T and O^T, so every
+// softmax statistic a lane keeps is the one its output registers need.
+#include "pa_device.hpp"
+#include "pa_internal.hpp"
+
+namespace pa {
+namespace {
+
+constexpr int kStep = 32;
+
+template <bool FP8, int D, int BS>
+struct Cfg {
+  static constexpr int kElt = FP8 ? 1 : 2;
+  static constexpr int kChunks = D / 32;            // QK MFMAs per token group
+  static constexpr int kDTiles = D / 16;            // PV MFMAs per step
+  static constexpr int kKLoads = FP8 ? D / 64 : D / 32;  // 16-byte K loads per token group
+  static constexpr int kRowK = D * kElt;            // bytes of one K row (token)
+  static constexpr int kRowV = BS * kElt;           // bytes of one V row (dimension)
+  static constexpr int kTile = BS * D * kElt;       // bytes of one (block, head) tile
+  static constexpr int kBlocksPerStep = kStep / BS;
+};
+
+template <bool FP8>
+struct VRaw;
+template <>
+struct VRaw<false> { u32x4 w; };  // 8 bf16 tokens
+template <>
+struct VRaw<true> { u32x2 w; };   // 8 e4m3 tokens
+
+template <bool FP8, int D, int BS>
+struct StepBuf {
+  using C = Cfg<FP8, D, BS>;
+  u32x4 k[2][C::kKLoads];
+  VRaw<FP8> v[C::kDTiles];
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+// 8 e4m3 codes (two words) -> 8 bf16, order kept
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  bf16x2 a, b, c, d;
+  fp8x4_to_bf16(w0, a, b);
+  fp8x4_to_bf16(w1, c, d);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// K operand of QK chunk c for token group m
+template <bool FP8, int D, int BS>
+__device__ __forceinline__ bf16x8 k_operand(const StepBuf<FP8, D, BS>& sb, int m, int c) {
+  if constexpr (FP8) {
+    const u32x4 w = sb.k[m][c >> 1];
+    return (c & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+  } else {
+    return as_bf16x8(sb.k[m][c]);
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ bf16x8 v_operand(const VRaw<FP8>& r) {
+  if constexpr (FP8) return fp8x8_to_bf16x8(r.w[0], r.w[1]);
+  else return as_bf16x8(r.w);
+}
+
+// Zero the V elements of k-slots whose token is past the range end.
+template <bool FP8>
+__device__ __forceinline__ void mask_v(VRaw<FP8>& r, int valid) {  // valid = tokens kept, 0..8
+  if constexpr (FP8) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      int n = valid - 4 * w;
+      uint32_t keep = n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (0xffffffffu >> (32 - 8 * n)));
+      r.w[w] &= keep;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      int n = valid - 2 * w;
+      uint32_t keep = n >= 2 ? 0xffffffffu : (n == 1 ? 0x0000ffffu : 0u);
+      r.w[w] &= keep;
+    }
+  }
+}
+
+template <bool FP8, int D, int BS>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
+  using C = Cfg<FP8, D, BS>;
+  const int part = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int col = lane & 15;   // query head within the group (QK/PV column)
+  const int grp = lane >> 4;   // k-slot group: tokens 8*grp .. 8*grp+7 of a step
+
+  int len = a.context_lens[b];
+  len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+  const int t0 = a.partition ? part * a.partition : 0;
+  const int t1 = a.partition ? min(t0 + a.partition, len) : len;
+  const int G = a.group;
+  const int hq = h * G + col;
+  const bool head_ok = col < G;
+
+  if (t0 >= t1) {
+    // An unsplit launch of an empty context writes zeros; a split launch has
+    // no partition here (the merge never reads it).
+    if (a.partition == 0 && head_ok) {
+      __bf16* o = reinterpret_cast<__bf16*>(a.out) + ((size_t)b * a.num_q_heads + hq) * D;
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[dt * 16 + grp * 4 + r] = (__bf16)0.0f;
+    }
+    return;
+  }
+
+  // ---- q operand (B of QK): head `col`, the 8 dims of k-slot group `grp` --
+  bf16x8 qop[C::kChunks];
+  {
+    const __bf16* qrow = reinterpret_cast<const __bf16*>(a.q) + ((size_t)b * a.num_q_heads + hq) * D;
+#pragma unroll
+    for (int c = 0; c < C::kChunks; ++c) {
+      // dims of chunk c held by this lane; K rows use the same map
+      const int d0 = FP8 ? (c >> 1) * 64 + grp * 16 + (c & 1) * 8 : c * 32 + grp * 8;
+      if (head_ok) {
+        qop[c] = *reinterpret_cast<const bf16x8*>(qrow + d0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qop[c][e] = (__bf16)0.0f;
+      }
+    }
+  }
+
+  float kscale = 1.0f, vscale = 1.0f;
+  if constexpr (FP8) { kscale = a.k_scale[h]; vscale = a.v_scale[h]; }
+  const float c2 = a.scale * kscale * kLog2e;  // q.k -> log2 units
+
+  // ---- per-lane byte offsets inside the step's tiles ----------------------
+  // K: QK row i = col of group m is token 8*(col/4) + 4*m + col%4 of the step.
+  const int ktok = 8 * (col >> 2) + (col & 3);             // + 4*m
+  const int kblk = (BS == 16) ? (ktok >> 4) : 0;            // which block of the step
+  const int krow = (BS == 16) ? (ktok & 15) : ktok;
+  const uint32_t koff = (uint32_t)krow * C::kRowK + (uint32_t)grp * 16;
+  // V: dimension dt*16 + col, tokens 8*grp .. +7 of the step.
+  const int vblk = (BS == 16) ? (grp >> 1) : 0;
+  const uint32_t vtok = (BS == 16) ? (uint32_t)(8 * (grp & 1)) : (uint32_t)(8 * grp);
+  const uint32_t voff = (uint32_t)col * C::kRowV + vtok * C::kElt;
+
+  const char* kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache);
+  const int32_t* table = a.block_tables + (size_t)b * a.max_blocks;
+  const int nsteps = (t1 - t0 + kStep - 1) / kStep;
+  const int lb_first = t0 / BS;
+  const int lb_last = (t1 - 1) / BS;  // last logical block with a token in range
+
+  // block-table window: lane i holds entry chunk_base + i
+  int chunk_base = lb_first;
+  int tbl = (chunk_base + lane <= lb_last) ? table[chunk_base + lane] : 0;
+
+  auto phys_of = [&](int lb) -> int64_t {
+    int p = readlane(tbl, lb - chunk_base);
+    return (p < 0 || (int64_t)p >= a.num_blocks) ? 0 : (int64_t)p;
+  };
+
+  auto issue = [&](StepBuf<FP8, D, BS>& sb, int step) {
+    const int lb0 = (t0 + step * kStep) / BS;
+    const int lb1 = min(lb0 + C::kBlocksPerStep - 1, lb_last);
+    if (lb1 - chunk_base >= 64) {  // slide the table window (long unsplit ranges)
+      chunk_base = lb0;
+      tbl = (chunk_base + lane <= lb_last) ? table[chunk_base + lane] : 0;
+    }
+    const int64_t p0 = phys_of(lb0);
+    const int64_t p1 = (C::kBlocksPerStep == 2) ? phys_of(lb1) : p0;
+    const int64_t tile0 = (p0 * a.num_kv_heads + h) * C::kTile;
+    const int64_t tile1 = (p1 * a.num_kv_heads + h) * C::kTile;
+    const char* kp = kc + (kblk ? tile1 : tile0) + koff;
+    const char* vp = vc + (vblk ? tile1 : tile0) + voff;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < C::kKLoads; ++j)
+        sb.k[m][j] = *reinterpret_cast<const u32x4*>(kp + (BS == 16 ? 4 * m : 4 * m) * C::kRowK + j * 64);
+#pragma unroll
+    for (int dt = 0; dt < C::kDTiles; ++dt) {
+      if constexpr (FP8) sb.v[dt].w = *reinterpret_cast<const u32x2*>(vp + dt * 16 * C::kRowV);
+      else sb.v[dt].w = *reinterpret_cast<const u32x4*>(vp + dt * 16 * C::kRowV);
+    }
+  };
+
+  f32x4 acc[C::kDTiles];
+#pragma unroll
+  for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max of z = c2 * q.k for head `col`
+  float l_run = 0.f;        // this lane's share of sum 2^(z - m_run)
+
+  auto compute = [&](StepBuf<FP8, D, BS>& sb, int step) {
+    const int base = t0 + step * kStep;
+    const bool partial = base + kStep > t1;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C::kChunks; ++c) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(sb, 0, c), qop[c], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(sb, 1, c), qop[c], s1, 0, 0, 0);
+    }
+    // scores in log2 units: z = s * c2, so exp(scale*q.k - max) = 2^(z - m)
+    const int tok0 = base + 8 * grp;  // token of k-slot 0 of this lane
+    const int valid = partial ? min(max(t1 - tok0, 0), 8) : 8;
+    float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (i < valid) ? __fmul_rn(z[i], c2) : -INFINITY;
+    if (partial) {
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<FP8>(sb.v[dt], valid);
+    }
+    float mx = z[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
+    mx = xlane<OpMax, 16, 32>(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (wave_any(m_new > m_run)) {
+      const float alpha = exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] *= alpha;
+      m_run = m_new;
+    }
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = (i < valid) ? exp2f(z[i] - m_run) : 0.f;
+      l_run += p[i];
+    }
+    bf16x8 pop;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pop[i] = (__bf16)p[i];
+#pragma unroll
+    for (int dt = 0; dt < C::kDTiles; ++dt)
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<FP8>(sb.v[dt]), pop, acc[dt], 0, 0, 0);
+  };
+
+  StepBuf<FP8, D, BS> bufA, bufB;
+  issue(bufA, 0);
+  for (int step = 0; step < nsteps; step += 2) {
+    issue(bufB, min(step + 1, nsteps - 1));
+    compute(bufA, step);
+    if (step + 1 >= nsteps) break;
+    issue(bufA, min(step + 2, nsteps - 1));
+    compute(bufB, step + 1);
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  const float l_tot = xlane<OpSum, 16, 32>(l_run);
+  const float inv = vscale / l_tot;
+  if (!head_ok) return;
+  if (a.partition == 0) {
+    __bf16* o = reinterpret_cast<__bf16*>(a.out) + ((size_t)b * a.num_q_heads + hq) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::kDTiles; ++dt) {
+      bf16x2 lo, hi;
+      lo[0] = (__bf16)(acc[dt][0] * inv); lo[1] = (__bf16)(acc[dt][1] * inv);
+      hi[0] = (__bf16)(acc[dt][2] * inv); hi[1] = (__bf16)(acc[dt][3] * inv);
+      u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      *reinterpret_cast<u32x2*>(o + dt * 16 + grp * 4) = w;
+    }
+  } else {
+    const size_t slot = ((size_t)b * a.num_q_heads + hq) * a.max_parts + part;
+    float* o = a.part_out + slot * D;
+#pragma unroll
+    for (int dt = 0; dt < C::kDTiles; ++dt)
+      *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = acc[dt] * inv;
+    if (grp == 0) {
+      a.part_max[slot] = m_run * kLn2;  // back to natural units
+      a.part_sum[slot] = l_tot;
+    }
+  }
+}
+
+template <bool FP8, int D, int BS>
+hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+  const int parts = a.partition ? a.max_parts : 1;
+  dim3 grid(parts, a.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, BS>), grid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool FP8>
+hipError_t dispatch_shape(const DecodeArgs& a, int head_dim, int block_size, hipStream_t s) {
+  if (head_dim == 128 && block_size == 16) return launch<FP8, 128, 16>(a, s);
+  if (head_dim == 128 && block_size == 32) return launch<FP8, 128, 32>(a, s);
+  if (head_dim == 64 && block_size == 16) return launch<FP8, 64, 16>(a, s);
+  if (head_dim == 64 && block_size == 32) return launch<FP8, 64, 32>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, Elem cache, int head_dim, int block_size,
+                              hipStream_t stream) {
+  if (cache == Elem::BF16) return dispatch_shape<false>(a, head_dim, block_size, stream);
+  if (cache == Elem::FP8) return dispatch_shape<true>(a, head_dim, block_size, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

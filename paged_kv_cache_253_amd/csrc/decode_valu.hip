@@ -1,0 +1,297 @@
+// Paged decode attention on the vector ALUs.
+//
+// Used where the per-KV-head query group is too small for the matrix cores
+// to pay (multi-head attention, G = 1) and for float32 caches.  Same work
+// split and pipeline as the MFMA kernel: one wavefront per (sequence, KV
+// head, partition), 32-token steps through the block table ("vLLM &
+// High-Throughput Serving", section 2), next step's tiles in flight during
+// the current one.
+//
+// QK: each K row (one token) is read by D/VEC lanes with 16-byte loads
+// (VEC elements each); the lanes' partial dot products are combined with DPP
+// row operations, leaving every lane of the row with the score.
+// PV: V tiles are dimension-major, so a lane reads VPT consecutive tokens of
+// one dimension per 16-byte load and accumulates them with the matching
+// softmax weights, which it takes from a 32-entry LDS row per query head.
+// Lanes sharing a dimension are summed once at the end.
+#include "pa_device.hpp"
+#include "pa_internal.hpp"
+
+namespace pa {
+namespace {
+
+constexpr int kStep = 32;
+
+template <Elem E> struct ElemBytes;
+template <> struct ElemBytes<Elem::F32> { static constexpr int v = 4; };
+template <> struct ElemBytes<Elem::BF16> { static constexpr int v = 2; };
+template <> struct ElemBytes<Elem::FP8> { static constexpr int v = 1; };
+
+// 16 bytes of cache elements -> floats
+template <Elem E>
+__device__ __forceinline__ void widen16(u32x4 w, float* out) {
+  if constexpr (E == Elem::F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+  } else if constexpr (E == Elem::BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { out[2 * i] = bf16lo_to_f32(w[i]); out[2 * i + 1] = bf16hi_to_f32(w[i]); }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fp8x4_to_f32(w[i], out + 4 * i);
+  }
+}
+
+template <typename QT>
+__device__ __forceinline__ float load_q(const QT* p) { return (float)*p; }
+
+template <typename QT, Elem E, int D, int BS, int G>
+__global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeArgs a) {
+  constexpr int ELT = ElemBytes<E>::v;
+  constexpr int VEC = 16 / ELT;          // elements per 16-byte load
+  constexpr int LPT = D / VEC;           // lanes per K row
+  constexpr int TPL = 64 / LPT;          // K rows per load instruction
+  constexpr int NK = kStep / TPL;        // K loads per lane per step
+  constexpr int VPT = VEC;               // tokens per 16-byte V load
+  constexpr int CPR = kStep / VPT;       // V loads per dimension per step
+  constexpr int NV = D * CPR / 64;       // V loads per lane per step
+  constexpr int DSTRIDE = 64 / CPR;      // dimension stride between a lane's V loads
+  constexpr int TILE = BS * D * ELT;
+  constexpr int BPS = kStep / BS;        // blocks per step
+  static_assert(LPT <= 64 && NK >= 1 && NV >= 1, "shape");
+
+  __shared__ float plds[2][G][kStep];
+
+  const int part = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x;
+
+  int len = a.context_lens[b];
+  len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+  const int t0 = a.partition ? part * a.partition : 0;
+  const int t1 = a.partition ? min(t0 + a.partition, len) : len;
+  QT* out = reinterpret_cast<QT*>(a.out);
+
+  const int tc = lane % CPR;               // V token chunk of this lane
+  if (t0 >= t1) {
+    if (a.partition == 0 && tc == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          out[((size_t)b * a.num_q_heads + h * G + g) * D + i * DSTRIDE + lane / CPR] = (QT)0.0f;
+    }
+    return;
+  }
+
+  // q slice of this lane for every head of the group
+  const int dsl = (lane % LPT) * VEC;
+  float qf[G][VEC];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const QT* qrow = reinterpret_cast<const QT*>(a.q) + ((size_t)b * a.num_q_heads + h * G + g) * D + dsl;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qf[g][e] = load_q(qrow + e);
+  }
+
+  float kscale = 1.0f, vscale = 1.0f;
+  if constexpr (E == Elem::FP8) { kscale = a.k_scale[h]; vscale = a.v_scale[h]; }
+  const float c2 = a.scale * kscale * kLog2e;  // q.k -> log2 units
+
+  // byte offsets inside the step's tiles
+  const int ktok = lane / LPT;  // + i*TPL
+  uint32_t koff[NK];
+  int kblk[NK];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int tok = i * TPL + ktok;
+    kblk[i] = tok / BS;
+    koff[i] = (uint32_t)(tok % BS) * D * ELT + (uint32_t)dsl * ELT;
+  }
+  const int vtok = tc * VPT;                 // first token of this lane's V chunk
+  const int vblk = vtok / BS;
+  const uint32_t voff = (uint32_t)(lane / CPR) * BS * ELT + (uint32_t)(vtok % BS) * ELT;
+
+  const char* kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache);
+  const int32_t* table = a.block_tables + (size_t)b * a.max_blocks;
+  const int nsteps = (t1 - t0 + kStep - 1) / kStep;
+  const int lb_first = t0 / BS;
+  const int lb_last = (t1 - 1) / BS;
+  int chunk_base = lb_first;
+  int tbl = (chunk_base + lane <= lb_last) ? table[chunk_base + lane] : 0;
+
+  auto phys_of = [&](int lb) -> int64_t {
+    int p = readlane(tbl, lb - chunk_base);
+    return (p < 0 || (int64_t)p >= a.num_blocks) ? 0 : (int64_t)p;
+  };
+
+  struct Buf { u32x4 k[NK]; u32x4 v[NV]; };
+
+  auto issue = [&](Buf& sb, int step) {
+    const int lb0 = (t0 + step * kStep) / BS;
+    const int lbl = min(lb0 + BPS - 1, lb_last);
+    if (lbl - chunk_base >= 64) {
+      chunk_base = lb0;
+      tbl = (chunk_base + lane <= lb_last) ? table[chunk_base + lane] : 0;
+    }
+    int64_t tiles[BPS];
+#pragma unroll
+    for (int j = 0; j < BPS; ++j) tiles[j] = (phys_of(min(lb0 + j, lbl)) * a.num_kv_heads + h) * TILE;
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+      sb.k[i] = *reinterpret_cast<const u32x4*>(kc + tiles[kblk[i]] + koff[i]);
+    const char* vp = vc + tiles[vblk] + voff;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      sb.v[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)i * DSTRIDE * BS * ELT);
+  };
+
+  float acc[G][NV];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[g][i] = 0.f;
+  float m_run[G], l_run[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) { m_run[g] = -INFINITY; l_run[g] = 0.f; }
+
+  int parity = 0;
+  auto compute = [&](Buf& sb, int step) {
+    const int base = t0 + step * kStep;
+    const bool partial = base + kStep > t1;
+    float s[G][NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      float kv[VEC];
+      widen16<E>(sb.k[i], kv);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float part_dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) part_dot = fmaf(qf[g][e], kv[e], part_dot);
+        s[g][i] = xlane<OpSum, 1, LPT / 2>(part_dot);
+      }
+    }
+    bool valid[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) valid[i] = !partial || (base + i * TPL + ktok < t1);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      // scores in log2 units: z = s * c2, so exp(scale*q.k - max) = 2^(z - m)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        s[g][i] = valid[i] ? __fmul_rn(s[g][i], c2) : -INFINITY;
+        mx = fmaxf(mx, s[g][i]);
+      }
+      if constexpr (LPT < 64) mx = xlane<OpMax, LPT, 32>(mx);
+      const float m_new = fmaxf(m_run[g], mx);
+      if (wave_any(m_new > m_run[g])) {
+        const float alpha = exp2f(m_run[g] - m_new);
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[g][i] *= alpha;
+        m_run[g] = m_new;
+      }
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const float p = valid[i] ? exp2f(s[g][i] - m_run[g]) : 0.f;
+        l_run[g] += p;
+        if (lane % LPT == 0) plds[parity][g][i * TPL + ktok] = p;
+      }
+    }
+    __syncthreads();
+    // V: tokens vtok .. vtok+VPT-1 of the step, dimension i*DSTRIDE + lane/CPR
+    const int vvalid = partial ? min(max(t1 - (base + vtok), 0), VPT) : VPT;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float vv[VPT];
+      widen16<E>(sb.v[i], vv);
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) vv[e] = (e < vvalid) ? vv[e] : 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float sum = acc[g][i];
+#pragma unroll
+        for (int e = 0; e < VPT; ++e) sum = fmaf(plds[parity][g][vtok + e], vv[e], sum);
+        acc[g][i] = sum;
+      }
+    }
+    parity ^= 1;
+  };
+
+  Buf bufA, bufB;
+  issue(bufA, 0);
+  for (int step = 0; step < nsteps; step += 2) {
+    issue(bufB, min(step + 1, nsteps - 1));
+    compute(bufA, step);
+    if (step + 1 >= nsteps) break;
+    issue(bufA, min(step + 2, nsteps - 1));
+    compute(bufB, step + 1);
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float l_tot = l_run[g];
+    if constexpr (LPT < 64) l_tot = xlane<OpSum, LPT, 32>(l_tot);
+    const float inv = vscale / l_tot;
+    const int hq = h * G + g;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float v = acc[g][i];
+      if constexpr (CPR > 1) v = xlane<OpSum, 1, CPR / 2>(v);
+      v *= inv;
+      if (tc == 0) {
+        const int d = i * DSTRIDE + lane / CPR;
+        if (a.partition == 0) {
+          out[((size_t)b * a.num_q_heads + hq) * D + d] = (QT)v;
+        } else {
+          a.part_out[(((size_t)b * a.num_q_heads + hq) * a.max_parts + part) * D + d] = v;
+        }
+      }
+    }
+    if (a.partition != 0 && lane == 0) {
+      const size_t slot = ((size_t)b * a.num_q_heads + hq) * a.max_parts + part;
+      a.part_max[slot] = m_run[g] * kLn2;  // back to natural units
+      a.part_sum[slot] = l_tot;
+    }
+  }
+}
+
+template <typename QT, Elem E, int D, int BS>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  const int parts = a.partition ? a.max_parts : 1;
+  dim3 grid(parts, a.num_kv_heads, a.num_seqs);
+  switch (a.group) {
+    case 1: hipLaunchKernelGGL((decode_valu_kernel<QT, E, D, BS, 1>), grid, dim3(64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_valu_kernel<QT, E, D, BS, 2>), grid, dim3(64), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_valu_kernel<QT, E, D, BS, 4>), grid, dim3(64), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_valu_kernel<QT, E, D, BS, 8>), grid, dim3(64), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename QT, Elem E>
+hipError_t launch_shape(const DecodeArgs& a, int head_dim, int block_size, hipStream_t s) {
+  if (head_dim == 128 && block_size == 16) return launch_g<QT, E, 128, 16>(a, s);
+  if (head_dim == 128 && block_size == 32) return launch_g<QT, E, 128, 32>(a, s);
+  if (head_dim == 64 && block_size == 16) return launch_g<QT, E, 64, 16>(a, s);
+  if (head_dim == 64 && block_size == 32) return launch_g<QT, E, 64, 32>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_valu(const DecodeArgs& a, Elem q, Elem cache, int head_dim,
+                              int block_size, hipStream_t stream) {
+  if (q == Elem::F32 && cache == Elem::F32) return launch_shape<float, Elem::F32>(a, head_dim, block_size, stream);
+  if (q == Elem::BF16 && cache == Elem::BF16) return launch_shape<__bf16, Elem::BF16>(a, head_dim, block_size, stream);
+  if (q == Elem::BF16 && cache == Elem::FP8) return launch_shape<__bf16, Elem::FP8>(a, head_dim, block_size, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,226 @@
+// C ABI: argument checks, kernel choice, launch on the caller's stream.
+// Declared and documented in include/pagedattn.h.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "pa_internal.hpp"
+#include "pagedattn.h"
+
+using pa::Elem;
+
+namespace {
+
+constexpr int kStepTokens = 32;  // kernels walk the context in 32-token steps
+
+bool supported_dim(int head_dim) { return head_dim == 64 || head_dim == 128; }
+bool supported_block(int block_size) { return block_size == 16 || block_size == 32; }
+
+bool to_elem(pa_dtype t, Elem* e) {
+  switch (t) {
+    case PA_F32: *e = Elem::F32; return true;
+    case PA_BF16: *e = Elem::BF16; return true;
+    case PA_FP8_E4M3: *e = Elem::FP8; return true;
+  }
+  return false;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t out_bytes, max_bytes, total;
+  int max_parts;
+};
+
+bool workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
+                      int partition_size, Layout* l) {
+  if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || max_context_len < 0 || partition_size <= 0)
+    return false;
+  const long long parts = std::max(1LL, ((long long)max_context_len + partition_size - 1) / partition_size);
+  const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)parts;
+  l->max_parts = (int)parts;
+  l->out_bytes = align256(rows * head_dim * sizeof(float));
+  l->max_bytes = align256(rows * sizeof(float));
+  l->total = l->out_bytes + 2 * l->max_bytes;
+  return true;
+}
+
+// "valu" / "mfma" forces a decode kernel family (tuning and cross-checks).
+int forced_path() {
+  const char* e = std::getenv("PA_FORCE_PATH");
+  if (!e) return 0;
+  if (std::strcmp(e, "valu") == 0) return 1;
+  if (std::strcmp(e, "mfma") == 0) return 2;
+  return 0;
+}
+
+bool log_enabled() {
+  const char* e = std::getenv("PA_LOG");
+  return e && e[0] == '1';
+}
+
+pa_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  if (log_enabled()) std::fprintf(stderr, "[pagedattn] HIP error: %s\n", hipGetErrorString(e));
+  return PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
+                                int partition_size) {
+  if (partition_size == 0 && num_seqs >= 0 && num_q_heads >= 1 && head_dim >= 1 && max_context_len >= 0)
+    return 0;
+  Layout l;
+  if (!workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_size, &l))
+    return SIZE_MAX;
+  return l.total;
+}
+
+pa_status pa_kv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                            int head_dim, int block_size, int64_t num_blocks, pa_dtype src_dtype,
+                            pa_dtype cache_dtype, const float* k_scale, const float* v_scale,
+                            hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads < 1 || num_blocks < 1) return PA_ERR_INVALID_ARG;
+  Elem src, cache;
+  if (!to_elem(src_dtype, &src) || !to_elem(cache_dtype, &cache)) return PA_ERR_INVALID_ARG;
+  if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
+  if (src == Elem::FP8) return PA_ERR_UNSUPPORTED;
+  if (cache != src && cache != Elem::FP8) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (cache == Elem::FP8 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  pa::WriteArgs a;
+  a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.slots = slot_mapping; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.num_slots = num_blocks * block_size;
+  a.num_tokens = num_tokens; a.num_kv_heads = num_kv_heads;
+  return from_hip(pa::launch_cache_write(a, src, cache, head_dim, block_size, stream));
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, int max_context_len, int num_seqs,
+                    int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                    int64_t num_blocks, float scale, pa_dtype q_dtype, pa_dtype cache_dtype,
+                    const float* k_scale, const float* v_scale, int partition_size,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0 ||
+      max_blocks_per_seq < 1 || num_blocks < 1 || partition_size < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (!(std::isfinite(scale) && scale > 0.0f)) return PA_ERR_INVALID_ARG;
+  Elem qe, ce;
+  if (!to_elem(q_dtype, &qe) || !to_elem(cache_dtype, &ce)) return PA_ERR_INVALID_ARG;
+  if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
+  const bool combo_ok = (qe == Elem::F32 && ce == Elem::F32) || (qe == Elem::BF16 && ce == Elem::BF16) ||
+                        (qe == Elem::BF16 && ce == Elem::FP8);
+  if (!combo_ok) return PA_ERR_UNSUPPORTED;
+  if (partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (partition_size == 0 && !out) return PA_ERR_INVALID_ARG;
+  if (ce == Elem::FP8 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+
+  const int group = num_q_heads / num_kv_heads;
+  const bool valu_group = group == 1 || group == 2 || group == 4 || group == 8;
+  const int force = forced_path();
+  bool use_mfma;
+  if (ce == Elem::F32) {
+    if (force == 2 || !valu_group) return PA_ERR_UNSUPPORTED;
+    use_mfma = false;
+  } else if (force == 1) {
+    if (!valu_group) return PA_ERR_UNSUPPORTED;
+    use_mfma = false;
+  } else if (force == 2) {
+    if (group > 16) return PA_ERR_UNSUPPORTED;
+    use_mfma = true;
+  } else {
+    if (group > 16) return PA_ERR_UNSUPPORTED;
+    use_mfma = group > 1;
+  }
+
+  pa::DecodeArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.out = out; a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.block_tables = block_tables; a.context_lens = context_lens;
+  a.k_scale = k_scale; a.v_scale = v_scale;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  const long long cap = (long long)max_blocks_per_seq * block_size;
+  a.max_len = (int)std::min<long long>(max_context_len, cap);
+  a.num_seqs = num_seqs; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.partition = partition_size;
+  a.scale = scale;
+  if (partition_size > 0) {
+    Layout l;
+    if (!workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_size, &l))
+      return PA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+      return PA_ERR_WORKSPACE;
+    char* w = static_cast<char*>(workspace);
+    a.part_out = reinterpret_cast<float*>(w);
+    a.part_max = reinterpret_cast<float*>(w + l.out_bytes);
+    a.part_sum = reinterpret_cast<float*>(w + l.out_bytes + l.max_bytes);
+    a.max_parts = l.max_parts;
+  } else {
+    a.max_parts = 1;
+  }
+  if (num_seqs == 0) return PA_OK;
+  if (log_enabled())
+    std::fprintf(stderr, "[pagedattn] decode path=%s S=%d Hq=%d Hkv=%d G=%d D=%d B=%d P=%d parts=%d\n",
+                 use_mfma ? "mfma" : "valu", num_seqs, num_q_heads, num_kv_heads, group, head_dim,
+                 block_size, partition_size, a.max_parts);
+  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, ce, head_dim, block_size, stream)
+                          : pa::launch_decode_valu(a, qe, ce, head_dim, block_size, stream);
+  return from_hip(e);
+}
+
+pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                           const int32_t* context_lens, int max_context_len, int num_seqs,
+                           int num_q_heads, int head_dim, int partition_size, pa_dtype out_dtype,
+                           hipStream_t stream) {
+  if (num_seqs < 0 || num_q_heads < 1 || max_context_len < 0 || partition_size <= 0)
+    return PA_ERR_INVALID_ARG;
+  Elem oe;
+  if (!to_elem(out_dtype, &oe)) return PA_ERR_INVALID_ARG;
+  if (oe == Elem::FP8 || !supported_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (!out || !workspace || !context_lens) return PA_ERR_INVALID_ARG;
+  Layout l;
+  if (!workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_size, &l))
+    return PA_ERR_INVALID_ARG;
+  if (workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return PA_ERR_WORKSPACE;
+  if (num_seqs == 0) return PA_OK;
+  const char* w = static_cast<const char*>(workspace);
+  pa::ReduceArgs a;
+  a.out = out;
+  a.part_out = reinterpret_cast<const float*>(w);
+  a.part_max = reinterpret_cast<const float*>(w + l.out_bytes);
+  a.part_sum = reinterpret_cast<const float*>(w + l.out_bytes + l.max_bytes);
+  a.context_lens = context_lens;
+  a.max_len = max_context_len;
+  a.num_seqs = num_seqs; a.num_q_heads = num_q_heads;
+  a.partition = partition_size; a.max_parts = l.max_parts;
+  return from_hip(pa::launch_reduce(a, oe, head_dim, stream));
+}
+
+}  // extern "C"

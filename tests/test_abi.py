@@ -1,0 +1,149 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host (no kernel is launched by
+any call here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+LIB = os.path.join(ROOT, "paged_kv_cache_253_amd", "libpagedattn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libpagedattn.so not built")
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+F32, BF16, FP8 = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import paged_kv_cache_253_amd as pk
+    return pk.load()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["pa_decode", "pa_decode_reduce", "pa_decode_workspace_size",
+                                    "pa_kv_cache_write", "pa_status_string"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(lib):
+    assert lib.pa_status_string(0) == b"PA_OK"
+    assert lib.pa_status_string(3) == b"PA_ERR_WORKSPACE"
+    assert lib.pa_status_string(99) == b"PA_ERR_UNKNOWN"
+
+
+def test_workspace_size_follows_documented_layout(lib):
+    def align(x):
+        return (x + 255) // 256 * 256
+    for s, hq, d, maxlen, p in [(64, 32, 128, 4096, 512), (8, 32, 128, 131072, 512),
+                                (3, 5, 64, 100, 32), (1, 1, 64, 0, 64)]:
+        parts = max(1, -(-maxlen // p))
+        rows = s * hq * parts
+        want = align(rows * d * 4) + 2 * align(rows * 4)
+        assert lib.pa_decode_workspace_size(s, hq, d, maxlen, p) == want
+    assert lib.pa_decode_workspace_size(4, 8, 64, 200, 0) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 64, 200, -32) == ctypes.c_size_t(-1).value
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+
+
+def _decode(lib, **kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, maxb=8, cl=FAKE, maxlen=128, s=2,
+                hq=8, hkv=2, d=128, bs=16, nb=64, scale=0.088, qdt=BF16, cdt=BF16, ks=None,
+                vs=None, p=0, ws=None, wsb=0)
+    args.update(kw)
+    a = args
+    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["maxb"], a["cl"],
+                         a["maxlen"], a["s"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
+                         a["scale"], a["qdt"], a["cdt"], a["ks"], a["vs"], a["p"], a["ws"],
+                         a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID),
+    (dict(bt=None), INVALID),
+    (dict(cl=None), INVALID),
+    (dict(out=None), INVALID),                 # unsplit decode needs out
+    (dict(hq=6, hkv=4), INVALID),               # heads not a multiple of KV heads
+    (dict(scale=0.0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(s=-1), INVALID),
+    (dict(maxb=0), INVALID),
+    (dict(d=96), UNSUPPORTED),
+    (dict(bs=8), UNSUPPORTED),
+    (dict(qdt=F32, cdt=BF16), UNSUPPORTED),
+    (dict(cdt=FP8), INVALID),                   # fp8 cache without scales
+    (dict(p=48), UNSUPPORTED),                  # split not a multiple of 32 tokens
+    (dict(p=-32), INVALID),
+    (dict(p=64, ws=None), WORKSPACE),
+    (dict(p=64, ws=FAKE, wsb=16), WORKSPACE),
+    (dict(p=64, ws=ctypes.c_void_p(0x1010), wsb=1 << 30), WORKSPACE),  # misaligned
+    (dict(hq=64, hkv=2), UNSUPPORTED),          # group 32 > 16
+    (dict(qdt=F32, cdt=F32, hq=6, hkv=2), UNSUPPORTED),  # f32 cache, group 3
+    (dict(qdt=7), INVALID),
+])
+def test_decode_rejects(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_decode_reduce_rejects(lib):
+    r = lib.pa_decode_reduce
+    assert r(FAKE, FAKE, 1 << 30, FAKE, 128, 2, 8, 128, 0, BF16, None) == INVALID
+    assert r(FAKE, FAKE, 1 << 30, FAKE, 128, 2, 8, 96, 64, BF16, None) == UNSUPPORTED
+    assert r(FAKE, FAKE, 1 << 30, FAKE, 128, 2, 8, 128, 64, FP8, None) == UNSUPPORTED
+    assert r(None, FAKE, 1 << 30, FAKE, 128, 2, 8, 128, 64, BF16, None) == INVALID
+    assert r(FAKE, FAKE, 16, FAKE, 128, 2, 8, 128, 64, BF16, None) == WORKSPACE
+
+
+def test_cache_write_rejects(lib):
+    w = lib.pa_kv_cache_write
+    ok = dict(kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, sm=FAKE, n=4, hkv=2, d=128, bs=16, nb=64,
+              src=BF16, cache=BF16, ks=None, vs=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return w(a["kn"], a["vn"], a["kc"], a["vc"], a["sm"], a["n"], a["hkv"], a["d"], a["bs"],
+                 a["nb"], a["src"], a["cache"], a["ks"], a["vs"], None)
+    assert call(kn=None) == INVALID
+    assert call(sm=None) == INVALID
+    assert call(n=-1) == INVALID
+    assert call(d=80) == UNSUPPORTED
+    assert call(bs=64) == UNSUPPORTED
+    assert call(src=F32, cache=BF16) == UNSUPPORTED
+    assert call(src=FP8, cache=FP8) == UNSUPPORTED
+    assert call(cache=FP8) == INVALID          # fp8 cache needs scales
+    assert call(n=0) == 0                       # empty append is a no-op
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import paged_kv_cache_253_amd as pk
+    monkeypatch.setattr(pk, "_lib", None)
+    monkeypatch.setattr(pk, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        pk.load()
+
+
+def test_product_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "paged_kv_cache_253_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text, f

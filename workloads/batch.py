@@ -216,8 +216,8 @@ def make_batch(w: Workload, seed: int | None = None, device="cpu",
     refs = np.array([mgr.ref_count(i) for i in range(num_blocks)], dtype=np.int32)
     new_pos = lens.astype(np.int64) - 1
     slot_mapping = np.array(
-        [tables[b, p // bsz] * bsz + p % bsz for b, p in enumerate(new_pos)],
-        dtype=np.int64)
+        [tables[b, p // bsz] * bsz + p % bsz if p >= 0 else -1 for b, p in enumerate(new_pos)],
+        dtype=np.int64)  # an empty context has no new token
 
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
