@@ -77,6 +77,9 @@ typedef enum pa_dtype {
   PA_FP8_E4M3 = 2  /* OCP FP8 E4M3FN code, one byte, with a per-KV-head scale */
 } pa_dtype;
 
+/* partition_size value selecting the balanced context split (see pa_decode). */
+#define PA_PARTITION_AUTO (-1)
+
 /*
  * pa_kv_cache_write -- append new tokens' K and V rows into the pool.
  *
@@ -127,8 +130,9 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
  *
  * accumulated in float32.  L == 0 gives zeros.
  *
- *   out            [num_seqs][num_q_heads][head_dim], element q_dtype; written
- *                  only when partition_size == 0 (may be NULL otherwise)
+ *   out            [num_seqs][num_q_heads][head_dim], element q_dtype; see
+ *                  partition_size for which rows this call writes (may be
+ *                  NULL for fixed partitions)
  *   q              [num_seqs][num_q_heads][head_dim], element q_dtype
  *   k_cache, v_cache   the pools (layout above), element cache_dtype
  *   block_tables   [num_seqs][max_blocks_per_seq] int32 physical block ids;
@@ -141,14 +145,24 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
  *   q_dtype / cache_dtype  (PA_F32, PA_F32), (PA_BF16, PA_BF16) or
  *                  (PA_BF16, PA_FP8_E4M3)
  *   k_scale, v_scale   [num_kv_heads] float32, device; FP8 cache only
- *   partition_size 0: each (sequence, KV head) is handled whole and `out`
- *                  is written.  > 0 (a multiple of 32): flash-decoding
- *                  split -- partition p of sequence b covers tokens
- *                  [p * P, min((p + 1) * P, L)); each partition's softmax
- *                  state goes to `workspace` (layout at
- *                  pa_decode_workspace_size) and `out` is NOT written;
- *                  pa_decode_reduce then merges the partitions into `out`.
- *   workspace, workspace_bytes  device scratch for the split; at least
+ *   partition_size selects how contexts are cut into ranges, one range per
+ *                  wavefront (split-context decoding; a wavefront's softmax
+ *                  state over its range is merged with the others afterwards):
+ *                  0: unsplit -- each (sequence, KV head) is one range and
+ *                     `out` is written; no workspace.
+ *                  P > 0 (a multiple of 32): fixed partitions -- partition p
+ *                     of sequence b covers tokens [p*P, min((p+1)*P, L)); the
+ *                     softmax state of every partition goes to `workspace`
+ *                     and `out` is NOT written; pa_decode_reduce merges.
+ *                  PA_PARTITION_AUTO: balanced -- every (sequence, KV head)
+ *                     is a run of ceil(L / 32) 32-token steps (one step for
+ *                     L == 0); the runs of the batch, KV head major, are cut
+ *                     into equal slices for 8 wavefronts per compute unit of
+ *                     the current device.  Runs one slice covers whole are
+ *                     written to `out` here; the state of each run cut by a
+ *                     slice boundary goes to `workspace`, and pa_decode_reduce
+ *                     (same arguments) writes those runs' output.
+ *   workspace, workspace_bytes  device scratch for the split modes; at least
  *                  pa_decode_workspace_size(...) bytes, 256-byte aligned;
  *                  ignored when partition_size == 0
  *
@@ -173,46 +187,61 @@ pa_status pa_decode(void* out, const void* q,
 
 /*
  * pa_decode_workspace_size -- bytes of workspace a split pa_decode needs
- * (0 when partition_size == 0; SIZE_MAX for invalid arguments).
+ * (0 when partition_size == 0; SIZE_MAX for invalid arguments, or for
+ * PA_PARTITION_AUTO when the current HIP device cannot be queried).
  *
- * Layout, with maxP = max(1, ceil(max_context_len / partition_size)) and
- * align(x) = x rounded up to a multiple of 256:
+ * Layout: a header of H bytes, then R rows of partial softmax state,
+ * align(x) = x rounded up to a multiple of 256,
  *
- *   float part_out[num_seqs][num_q_heads][maxP][head_dim]   at 0
- *   float part_max[num_seqs][num_q_heads][maxP]  at align(|part_out|)
- *   float part_sum[num_seqs][num_q_heads][maxP]  at that + align(|part_max|)
+ *   float part_out[R][head_dim]   at H
+ *   float part_max[R]             at H + align(R * head_dim * 4)
+ *   float part_sum[R]             at that + align(R * 4)
  *
- * For partition p of sequence b and query head hq, with z_t as in
- * pa_decode over the partition's tokens: part_max = max_t z_t, part_sum =
- * sum_t exp(z_t - part_max), part_out = sum_t exp(z_t - part_max) v_t /
- * part_sum.  Entries of partitions a sequence does not have are unused.
+ * Fixed partitions: H = 0, R = num_seqs * num_q_heads * maxP with
+ * maxP = max(1, ceil(max_context_len / partition_size)); the state of
+ * partition p of sequence b, query head hq is row (b * num_q_heads + hq) *
+ * maxP + p; rows of partitions a sequence does not have are unused.
+ * PA_PARTITION_AUTO: H = 256 (pa_decode stores its slice count there, as an
+ * int32 at offset 0), R = 4 * CUs * 2 * G (CUs = compute units of the
+ * current device, G = num_q_heads / num_kv_heads; a decode uses at most
+ * 4 * CUs slices); slice s keeps the state of its first run in rows
+ * (2s) * G + g and of its last run in rows (2s + 1) * G + g, for the
+ * group's query heads g, when those runs are cut.
+ *
+ * A state over tokens T of a query head, with z_t as in pa_decode:
+ * part_max = max_{t in T} z_t, part_sum = sum_t exp(z_t - part_max),
+ * part_out = sum_t exp(z_t - part_max) v_t / part_sum.
  */
-size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim,
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                 int max_context_len, int partition_size);
 
 /*
- * pa_decode_reduce -- merge the partitions of a split decode into `out`.
+ * pa_decode_reduce -- merge the partial states of a split decode into `out`.
  *
- * The partitions of one (sequence, query head) are disjoint token ranges;
- * rescaling each range's exp-sum to the common maximum and weighting the
- * range outputs by it gives softmax over the whole context (the split-
- * context merge of flash decoding; the pages' un-paged attention is the
- * target it must reproduce):
+ * The ranges of one (sequence, query head) are disjoint; rescaling each
+ * range's exp-sum to the common maximum and weighting the range outputs by
+ * it gives softmax over the whole context (the split-context merge of flash
+ * decoding; the pages' un-paged attention is the result it must reproduce):
  *
  *   M = max_p part_max[p];  w_p = part_sum[p] * exp(part_max[p] - M)
- *   out = sum_p w_p * part_out[p] / sum_p w_p,    p < ceil(L / P)
+ *   out = sum_p w_p * part_out[p] / sum_p w_p
  *
- * in float32, partitions merged in increasing p.  L == 0 gives zeros.
+ * in float32, ranges added in a fixed order (identical bits on every call).
+ * Fixed partitions: every row of `out` is written (L == 0 gives zeros).
+ * PA_PARTITION_AUTO: only the rows of runs that pa_decode left cut are
+ * written; pa_decode wrote the others.
  *
  *   out            [num_seqs][num_q_heads][head_dim], element out_dtype
  *                  (PA_F32 or PA_BF16, rounded to nearest even)
- *   workspace      as filled by pa_decode with the same num_seqs,
- *                  num_q_heads, head_dim, max_context_len, partition_size
+ *   workspace      as filled by pa_decode called with the same num_seqs,
+ *                  num_q_heads, num_kv_heads, head_dim, max_context_len,
+ *                  partition_size (and, for PA_PARTITION_AUTO, on the same
+ *                  device and stream order)
  *   context_lens   [num_seqs] int32, device (clamped to max_context_len)
  */
 pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
                            const int32_t* context_lens, int max_context_len,
-                           int num_seqs, int num_q_heads, int head_dim,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                            int partition_size, pa_dtype out_dtype,
                            hipStream_t stream);
 

@@ -22,11 +22,12 @@ import torch
 
 __all__ = ["PagedAttnError", "load", "kv_cache_write", "decode", "decode_partitions",
            "decode_reduce", "workspace_size", "workspace_views", "default_partition_size",
-           "LIB_PATH"]
+           "PARTITION_AUTO", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PARTITION_AUTO = -1  # balanced context split (PA_PARTITION_AUTO)
 _STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
            3: "PA_ERR_WORKSPACE", 4: "PA_ERR_HIP"}
 
@@ -57,9 +58,9 @@ def load() -> ctypes.CDLL:
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i64,
                               f32, i32, i32, vp, vp, i32, vp, szt, vp]
     lib.pa_decode.restype = i32
-    lib.pa_decode_reduce.argtypes = [vp, vp, szt, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_decode_reduce.argtypes = [vp, vp, szt, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_decode_reduce.restype = i32
-    lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_decode_workspace_size.restype = szt
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -96,10 +97,10 @@ def _check(call: str, status: int) -> None:
         raise PagedAttnError(call, status)
 
 
-def workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
-                   partition_size: int) -> int:
-    n = load().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
-                                        partition_size)
+def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                   max_context_len: int, partition_size: int) -> int:
+    n = load().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        max_context_len, partition_size)
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid workspace arguments")
     return int(n)
@@ -107,7 +108,7 @@ def workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_context_l
 
 def workspace_views(workspace: torch.Tensor, num_seqs: int, num_q_heads: int, head_dim: int,
                     max_context_len: int, partition_size: int):
-    """(part_out, part_max, part_sum) float32 views of a split-decode
+    """(part_out, part_max, part_sum) float32 views of a fixed-partition
     workspace, in the layout documented at ``pa_decode_workspace_size``."""
     parts = max(1, -(-max_context_len // partition_size))
     rows = num_seqs * num_q_heads * parts
@@ -126,9 +127,8 @@ def workspace_views(workspace: torch.Tensor, num_seqs: int, num_q_heads: int, he
 
 
 def default_partition_size(max_context_len: int) -> int:
-    """Context split used when the caller gives none: 512-token partitions
-    once contexts are longer than that, else unsplit."""
-    return 512 if max_context_len > 512 else 0
+    """Context split used when the caller gives none: the balanced split."""
+    return PARTITION_AUTO
 
 
 def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
@@ -166,26 +166,33 @@ def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
 
 def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                       partition_size, scale=None, k_scale=None, v_scale=None,
-                      workspace=None) -> torch.Tensor:
-    """Split ``pa_decode`` only: fill and return the workspace."""
+                      workspace=None, out=None) -> torch.Tensor:
+    """Split ``pa_decode`` only (fixed partitions, or the balanced split,
+    which also writes the rows of ``out`` it finishes); returns the
+    workspace."""
     s, hq, d = q.shape
+    hkv = k_cache.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        n = workspace_size(s, hq, d, max_context_len, partition_size)
+        n = workspace_size(s, hq, hkv, d, max_context_len, partition_size)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
-    _decode_call(None, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+    _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                  k_scale, v_scale, partition_size, workspace)
     return workspace
 
 
 def decode_reduce(out: torch.Tensor, workspace: torch.Tensor, context_lens: torch.Tensor,
-                  max_context_len: int, partition_size: int) -> torch.Tensor:
-    """``pa_decode_reduce``: merge the workspace's partitions into ``out``."""
+                  max_context_len: int, partition_size: int,
+                  num_kv_heads: int | None = None) -> torch.Tensor:
+    """``pa_decode_reduce``: merge the workspace's states into ``out``.
+    ``num_kv_heads`` defaults to the query heads (it only matters for the
+    balanced split)."""
     s, hq, d = out.shape
+    hkv = hq if num_kv_heads is None else int(num_kv_heads)
     st = load().pa_decode_reduce(_ptr(out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(),
-                                 _ptr(context_lens), int(max_context_len), s, hq, d,
+                                 _ptr(context_lens), int(max_context_len), s, hq, hkv, d,
                                  int(partition_size), _dtype_code(out), _stream(out))
     _check("pa_decode_reduce", st)
     return out
@@ -199,7 +206,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            ) -> torch.Tensor:
     """Decode attention over the paged cache; returns ``out [S, Hq, D]``.
 
-    ``partition_size`` 0 runs unsplit; > 0 runs the split decode followed by
+    ``partition_size`` 0 runs unsplit; > 0 (fixed partitions) or
+    ``PARTITION_AUTO`` (balanced split) runs the split decode followed by
     the merge; None picks ``default_partition_size(max_context_len)``.
     """
     s, hq, d = q.shape
@@ -215,5 +223,6 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         return out
     workspace = decode_partitions(q, k_cache, v_cache, block_tables, context_lens,
                                   max_context_len, partition_size, scale, k_scale, v_scale,
-                                  workspace)
-    return decode_reduce(out, workspace, context_lens, max_context_len, partition_size)
+                                  workspace, out=out)
+    return decode_reduce(out, workspace, context_lens, max_context_len, partition_size,
+                         k_cache.shape[1])

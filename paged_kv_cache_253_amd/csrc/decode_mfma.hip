@@ -24,8 +24,13 @@
 //
 // The same head mapping (column = query head) holds in S^T and O^T, so every
 // softmax statistic a lane keeps is the one its output registers need.
+//
+// Two entry kernels share the per-range body: a grid of one wavefront per
+// (partition, KV head, sequence), and a persistent grid that walks balanced
+// slices of the whole batch (see pa_split.hpp).
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
+#include "pa_split.hpp"
 
 namespace pa {
 namespace {
@@ -71,9 +76,9 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-// K operand of QK chunk c for token group m
-template <bool FP8, int D, int BS>
-__device__ __forceinline__ bf16x8 k_operand(const StepBuf<FP8, D, BS>& sb, int m, int c) {
+// K operand of QK chunk c for token group m (from a buffer with k[2][..])
+template <bool FP8, class Buf>
+__device__ __forceinline__ bf16x8 k_operand(const Buf& sb, int m, int c) {
   if constexpr (FP8) {
     const u32x4 w = sb.k[m][c >> 1];
     return (c & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
@@ -108,28 +113,31 @@ __device__ __forceinline__ void mask_v(VRaw<FP8>& r, int valid) {  // valid = to
   }
 }
 
+// Where a range's result goes: the final output rows, or partial softmax
+// states (rows of part_out/part_max/part_sum; row of query head g of the
+// group = row0 + g * row_stride).
+struct Target {
+  bool final_out;
+  size_t row0;
+  size_t row_stride;
+};
+
+// Attention of the G query heads of KV head h of sequence b over tokens
+// [t0, t1) (t0 a multiple of 32).  An empty range writes zeros (final only).
 template <bool FP8, int D, int BS>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const int h, const int t0,
+                                       int t1, const Target tgt) {
   using C = Cfg<FP8, D, BS>;
-  const int part = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  t1 = min(t1, a.cap_len);  // never walk past the table row
   const int lane = threadIdx.x;
   const int col = lane & 15;   // query head within the group (QK/PV column)
   const int grp = lane >> 4;   // k-slot group: tokens 8*grp .. 8*grp+7 of a step
-
-  int len = a.context_lens[b];
-  len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
-  const int t0 = a.partition ? part * a.partition : 0;
-  const int t1 = a.partition ? min(t0 + a.partition, len) : len;
   const int G = a.group;
   const int hq = h * G + col;
   const bool head_ok = col < G;
 
   if (t0 >= t1) {
-    // An unsplit launch of an empty context writes zeros; a split launch has
-    // no partition here (the merge never reads it).
-    if (a.partition == 0 && head_ok) {
+    if (tgt.final_out && head_ok) {
       __bf16* o = reinterpret_cast<__bf16*>(a.out) + ((size_t)b * a.num_q_heads + hq) * D;
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt)
@@ -204,11 +212,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int j = 0; j < C::kKLoads; ++j)
-        sb.k[m][j] = *reinterpret_cast<const u32x4*>(kp + (BS == 16 ? 4 * m : 4 * m) * C::kRowK + j * 64);
+        sb.k[m][j] = stream_load<u32x4>(kp + 4 * m * C::kRowK + j * 64);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt) {
-      if constexpr (FP8) sb.v[dt].w = *reinterpret_cast<const u32x2*>(vp + dt * 16 * C::kRowV);
-      else sb.v[dt].w = *reinterpret_cast<const u32x4*>(vp + dt * 16 * C::kRowV);
+      if constexpr (FP8) sb.v[dt].w = stream_load<u32x2>(vp + dt * 16 * C::kRowV);
+      else sb.v[dt].w = stream_load<u32x4>(vp + dt * 16 * C::kRowV);
     }
   };
 
@@ -224,8 +232,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < C::kChunks; ++c) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(sb, 0, c), qop[c], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(sb, 1, c), qop[c], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(sb, 0, c), qop[c], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(sb, 1, c), qop[c], s1, 0, 0, 0);
     }
     // scores in log2 units: z = s * c2, so exp(scale*q.k - max) = 2^(z - m)
     const int tok0 = base + 8 * grp;  // token of k-slot 0 of this lane
@@ -277,7 +285,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
   const float l_tot = xlane<OpSum, 16, 32>(l_run);
   const float inv = vscale / l_tot;
   if (!head_ok) return;
-  if (a.partition == 0) {
+  if (tgt.final_out) {
     __bf16* o = reinterpret_cast<__bf16*>(a.out) + ((size_t)b * a.num_q_heads + hq) * D;
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt) {
@@ -288,23 +296,289 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
       *reinterpret_cast<u32x2*>(o + dt * 16 + grp * 4) = w;
     }
   } else {
-    const size_t slot = ((size_t)b * a.num_q_heads + hq) * a.max_parts + part;
-    float* o = a.part_out + slot * D;
+    const size_t row = tgt.row0 + (size_t)col * tgt.row_stride;
+    float* o = a.part_out + row * D;
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
       *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = acc[dt] * inv;
     if (grp == 0) {
-      a.part_max[slot] = m_run * kLn2;  // back to natural units
-      a.part_sum[slot] = l_tot;
+      a.part_max[row] = m_run * kLn2;  // back to natural units
+      a.part_sum[row] = l_tot;
+    }
+  }
+}
+
+// One wavefront per (partition, KV head, sequence); unsplit launches have a
+// single partition covering the whole context.
+template <bool FP8, int D, int BS>
+__global__ __launch_bounds__(64) void decode_mfma_grid(const DecodeArgs a) {
+  const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int len = clamp_len(a.context_lens[b], a.max_len);
+  if (a.partition == 0) {
+    attend<FP8, D, BS>(a, b, h, 0, len, Target{true, 0, 0});
+    return;
+  }
+  const int t0 = part * a.partition;
+  const int t1 = min(t0 + a.partition, len);
+  if (t0 >= t1) return;  // the sequence has no such partition
+  const size_t row0 = ((size_t)b * a.num_q_heads + (size_t)h * a.group) * a.max_parts + part;
+  attend<FP8, D, BS>(a, b, h, t0, t1, Target{false, row0, (size_t)a.max_parts});
+}
+
+// ---------------------------------------------------------------------------
+// Balanced split: one persistent wavefront per SIMD streams its slice of the
+// batch as one sequence of 32-token steps, whatever runs (sequence, KV head)
+// the steps belong to.  A ring of kRing step slots holds the K, V and q tiles
+// of the next steps; the issue side runs kRing - 1 steps ahead of the
+// compute side, across run boundaries, so the memory pipeline never drains
+// inside a slice.  Every slot issues the same loads, so the wait before a
+// slot's compute is exact.  Block-table entries and lengths are read with
+// scalar loads (separate wait counter from the tile loads).  A run the slice
+// covers whole is finished here; the slice's first and last runs, when cut
+// by a slice boundary, leave partial states in rows (2r)*G.. and (2r+1)*G..
+// ---------------------------------------------------------------------------
+
+constexpr int kFirst = 1, kLast = 2, kFinal = 4;
+// Ring of 4 step slots: each wavefront keeps 3 steps of tiles in flight.
+// Wavefronts per compute unit by step size (measured on MI355X): with 16 KiB
+// steps (bf16, head_dim 128) two wavefronts per CU (~48 KiB ahead each, ~24
+// MiB over the chip) read the scattered tiles fastest; fewer, deeper streams
+// beat more, shallower ones there.  Smaller steps (FP8 or head_dim 64) do
+// best with four.
+constexpr int kRing = 4;
+
+template <bool FP8, int D>
+constexpr int stream_waves_per_cu() {
+  return kStep * 2 * D * (FP8 ? 1 : 2) >= 16 * 1024 ? 2 : 4;
+}
+
+typedef const __attribute__((address_space(4))) int32_t* const_i32;
+typedef const __attribute__((address_space(4))) float* const_f32;
+
+template <bool FP8, int D, int BS>
+struct Slot {
+  using C = Cfg<FP8, D, BS>;
+  u32x4 k[2][C::kKLoads];
+  VRaw<FP8> v[C::kDTiles];
+  bf16x8 q[C::kChunks];
+  // segment descriptor (wave-uniform)
+  int base;   // first token of the step
+  int t1;     // end of the run's tokens inside this segment
+  int b, h;
+  int flags;  // kFirst / kLast step of its segment; kFinal output (else partial state)
+  int row0;   // partial state: row of the group's first query head
+};
+
+template <bool FP8, int D, int BS>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_mfma_stream(const DecodeArgs a) {
+  using C = Cfg<FP8, D, BS>;
+  using S = Slot<FP8, D, BS>;
+  const int lane = threadIdx.x;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int G = a.group;
+  if (blockIdx.x == 0 && lane == 0) *a.header = a.slices;  // for the merge
+  const int r = slice_of_wave(blockIdx.x, a.slices);
+  const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, a.slices);
+  const int64_t g0 = (int64_t)r * sp.per;
+  const int64_t g_end = min(g0 + sp.per, sp.total);
+  if (g0 >= g_end) return;
+  const int total_steps = (int)(g_end - g0);
+
+  const const_i32 lens = (const_i32)a.context_lens;
+  const const_i32 tables = (const_i32)a.block_tables;
+
+  // ---- issue-side cursor over the slice's runs --------------------------
+  int cb, ci;  // run (sequence cb, KV head ch) and its step index
+  int ch = (int)(g0 / sp.per_head);
+  locate_step(a.context_lens, a.num_seqs, a.max_len, g0 - (int64_t)ch * sp.per_head, cb, ci);
+  int clen = clamp_len(lens[cb], a.max_len);
+  int cn = steps_of_len(clen);
+  int left = total_steps;                   // slice steps not yet issued
+  int cseg_end = min(cn, ci + left);        // end step (in the run) of this segment
+  int cseg_start = ci;
+  int cflags_run = (ci == 0 && cseg_end == cn) ? kFinal : 0;
+  int crow0 = r * 2 * G;                    // the slice's first run -> rows (2r)*G..
+
+  // per-lane offsets inside a step's tiles (see attend)
+  const int ktok = 8 * (col >> 2) + (col & 3);
+  const int kblk = (BS == 16) ? (ktok >> 4) : 0;
+  const int krow = (BS == 16) ? (ktok & 15) : ktok;
+  const uint32_t koff = (uint32_t)krow * C::kRowK + (uint32_t)grp * 16;
+  const int vblk = (BS == 16) ? (grp >> 1) : 0;
+  const uint32_t vtok = (BS == 16) ? (uint32_t)(8 * (grp & 1)) : (uint32_t)(8 * grp);
+  const uint32_t voff = (uint32_t)col * C::kRowV + vtok * C::kElt;
+  const int qhead = min(col, G - 1);        // lanes past the group read a real row; unused
+  const char* kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* vc = reinterpret_cast<const char*>(a.v_cache);
+  const __bf16* qbase = reinterpret_cast<const __bf16*>(a.q);
+
+  const char* kp = kc;
+  const char* vp = vc;
+  const __bf16* qp = qbase;
+
+  auto issue = [&](S& sl, const bool real) {
+    if (real) {
+      if (ci == cseg_end) {  // next run of the slice
+        if (++cb == a.num_seqs) { cb = 0; ++ch; }
+        clen = clamp_len(lens[cb], a.max_len);
+        cn = steps_of_len(clen);
+        ci = 0;
+        cseg_start = 0;
+        cseg_end = min(cn, left);
+        cflags_run = (cseg_end == cn) ? kFinal : 0;
+        crow0 = (r * 2 + 1) * G;
+      }
+      sl.base = ci * kStepTokens;
+      sl.t1 = min(min(cseg_end * kStepTokens, clen), a.cap_len);
+      sl.b = cb;
+      sl.h = ch;
+      sl.flags = cflags_run | (ci == cseg_start ? kFirst : 0) | (ci + 1 == cseg_end ? kLast : 0);
+      sl.row0 = crow0;
+      // physical blocks of the step (an empty run reads block 0, all masked)
+      const int lb0 = sl.base / BS;
+      const int lb_last = sl.t1 > 0 ? (sl.t1 - 1) / BS : 0;
+      const int64_t row = (int64_t)cb * a.max_blocks;
+      int p0 = sl.t1 > sl.base ? tables[row + lb0] : 0;
+      int p1 = (C::kBlocksPerStep == 2 && lb0 + 1 <= lb_last) ? tables[row + lb0 + 1] : p0;
+      p0 = (p0 < 0 || (int64_t)p0 >= a.num_blocks) ? 0 : p0;
+      p1 = (p1 < 0 || (int64_t)p1 >= a.num_blocks) ? 0 : p1;
+      const int64_t tile0 = ((int64_t)p0 * a.num_kv_heads + ch) * C::kTile;
+      const int64_t tile1 = ((int64_t)p1 * a.num_kv_heads + ch) * C::kTile;
+      kp = kc + (kblk ? tile1 : tile0) + koff;
+      vp = vc + (vblk ? tile1 : tile0) + voff;
+      qp = qbase + ((size_t)cb * a.num_q_heads + (size_t)ch * G + qhead) * D;
+      ++ci;
+      --left;
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < C::kKLoads; ++j)
+        sl.k[m][j] = stream_load<u32x4>(kp + 4 * m * C::kRowK + j * 64);
+#pragma unroll
+    for (int dt = 0; dt < C::kDTiles; ++dt) {
+      if constexpr (FP8) sl.v[dt].w = stream_load<u32x2>(vp + dt * 16 * C::kRowV);
+      else sl.v[dt].w = stream_load<u32x4>(vp + dt * 16 * C::kRowV);
+    }
+#pragma unroll
+    for (int c = 0; c < C::kChunks; ++c) {
+      const int d0 = FP8 ? (c >> 1) * 64 + grp * 16 + (c & 1) * 8 : c * 32 + grp * 8;
+      sl.q[c] = *reinterpret_cast<const bf16x8*>(qp + d0);
+    }
+  };
+
+  // ---- compute side ---------------------------------------------------------
+  f32x4 acc[C::kDTiles];
+  float m_run = -INFINITY, l_run = 0.f, c2 = 0.f;
+
+  auto compute = [&](S& sl) {
+    if (sl.flags & kFirst) {
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run = -INFINITY;
+      l_run = 0.f;
+      float kscale = 1.0f;
+      if constexpr (FP8) kscale = ((const_f32)a.k_scale)[sl.h];
+      c2 = a.scale * kscale * kLog2e;
+    }
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < C::kChunks; ++c) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(sl, 0, c), sl.q[c], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(sl, 1, c), sl.q[c], s1, 0, 0, 0);
+    }
+    const bool partial = sl.base + kStepTokens > sl.t1;
+    const int tok0 = sl.base + 8 * grp;
+    const int valid = partial ? min(max(sl.t1 - tok0, 0), 8) : 8;
+    float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (i < valid) ? __fmul_rn(z[i], c2) : -INFINITY;
+    if (partial) {
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<FP8>(sl.v[dt], valid);
+    }
+    float mx = z[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
+    mx = xlane<OpMax, 16, 32>(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (wave_any(m_new > m_run)) {
+      const float alpha = exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] *= alpha;
+      m_run = m_new;
+    }
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = (i < valid) ? exp2f(z[i] - m_run) : 0.f;
+      l_run += p[i];
+    }
+    bf16x8 pop;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pop[i] = (__bf16)p[i];
+#pragma unroll
+    for (int dt = 0; dt < C::kDTiles; ++dt)
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<FP8>(sl.v[dt]), pop, acc[dt], 0, 0, 0);
+
+    if (sl.flags & kLast) {
+      const float l_tot = xlane<OpSum, 16, 32>(l_run);
+      float vscale = 1.0f;
+      if constexpr (FP8) vscale = ((const_f32)a.v_scale)[sl.h];
+      const float inv = l_tot > 0.f ? vscale / l_tot : 0.f;  // an empty run writes zeros
+      if (col < G) {
+        if (sl.flags & kFinal) {
+          __bf16* o = reinterpret_cast<__bf16*>(a.out) +
+                      ((size_t)sl.b * a.num_q_heads + (size_t)sl.h * G + col) * D;
+#pragma unroll
+          for (int dt = 0; dt < C::kDTiles; ++dt) {
+            bf16x2 lo, hi;
+            lo[0] = (__bf16)(acc[dt][0] * inv); lo[1] = (__bf16)(acc[dt][1] * inv);
+            hi[0] = (__bf16)(acc[dt][2] * inv); hi[1] = (__bf16)(acc[dt][3] * inv);
+            u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            *reinterpret_cast<u32x2*>(o + dt * 16 + grp * 4) = w;
+          }
+        } else {
+          const size_t row = (size_t)sl.row0 + col;
+          float* o = a.part_out + row * D;
+#pragma unroll
+          for (int dt = 0; dt < C::kDTiles; ++dt)
+            *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = acc[dt] * inv;
+          if (grp == 0) {
+            a.part_max[row] = m_run * kLn2;
+            a.part_sum[row] = l_tot;
+          }
+        }
+      }
+    }
+  };
+
+  S ring[kRing];
+#pragma unroll
+  for (int j = 0; j < kRing - 1; ++j) issue(ring[j], j < total_steps);
+  for (int k = 0; k < total_steps; k += kRing) {
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+      issue(ring[(j + kRing - 1) % kRing], k + j + kRing - 1 < total_steps);
+      if (k + j < total_steps) compute(ring[j]);
     }
   }
 }
 
 template <bool FP8, int D, int BS>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-  const int parts = a.partition ? a.max_parts : 1;
-  dim3 grid(parts, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<FP8, D, BS>), grid, dim3(64), 0, stream, a);
+  if (a.partition == kAuto) {
+    DecodeArgs b = a;
+    b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : stream_waves_per_cu<FP8, D>());
+    hipLaunchKernelGGL((decode_mfma_stream<FP8, D, BS>), dim3(b.slices), dim3(64), 0, stream, b);
+  } else {
+    const int parts = a.partition ? a.max_parts : 1;
+    dim3 grid(parts, a.num_kv_heads, a.num_seqs);
+    hipLaunchKernelGGL((decode_mfma_grid<FP8, D, BS>), grid, dim3(64), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

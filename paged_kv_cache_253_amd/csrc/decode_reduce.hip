@@ -1,63 +1,165 @@
-// Merge of a split decode's partition states into the output.
+// Merge of partial softmax states into the output.
 //
-// One wavefront per (sequence, query head).  With M the largest partition
-// maximum, partition p carries weight w_p = sum_p * exp(max_p - M); the
-// output is sum_p w_p * out_p / sum_p w_p.  Each partition's exp terms were
-// taken relative to its own maximum, so the rescale by exp(max_p - M) puts
-// all of them on one scale and the result is softmax over the whole context.
-// Partitions are added in increasing p, so the result is deterministic.
+// A partial state of a token range holds its maximum score m, its exp-sum l
+// (taken relative to m) and its normalised output o.  With M the largest m
+// of a (sequence, query head), range p weighs w_p = l_p * exp(m_p - M) and
+// the output is sum_p w_p * o_p / sum_p w_p: each range's exp terms are put
+// on the common scale, so the result is softmax over the union of ranges.
+// Every merge below adds its ranges in a fixed order (deterministic bits).
+//
+//  * reduce_kernel: fixed partitions.  One 256-thread workgroup per
+//    (sequence, query head); 16-byte loads, D/4 threads per partition row,
+//    256/(D/4) rows in flight; the row groups are summed in order at the end.
+//  * auto_fixup_kernel: balanced slices.  One workgroup per slice boundary;
+//    the first boundary that cuts a (sequence, KV head) run merges all of the
+//    run's slice states (see pa_split.hpp), one query head per wavefront,
+//    the pieces' maxima and weights taken by the lanes in parallel.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
+#include "pa_split.hpp"
 
 namespace pa {
 namespace {
 
+constexpr int kReduceThreads = 256;
+constexpr int kWeightChunk = 1024;
+
+template <class Op>
+__device__ __forceinline__ float block_combine(float x, float* scratch) {
+  x = xlane<Op, 1, 32>(x);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[wave] = x;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < kReduceThreads / 64; ++i) r = Op::f(r, scratch[i]);
+  return r;
+}
+
 template <typename OT, int D>
-__global__ __launch_bounds__(64) void reduce_kernel(const ReduceArgs a) {
-  constexpr int PER = D / 64;
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReduceArgs a) {
+  constexpr int TPR = D / 4;                    // threads per partition row
+  constexpr int ROWS = kReduceThreads / TPR;    // rows in flight
+  __shared__ float wbuf[kWeightChunk];
+  __shared__ float part[ROWS][D];
+  __shared__ float scratch[kReduceThreads / 64];
+
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int lane = threadIdx.x;
-  int len = a.context_lens[b];
-  len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+  const int tid = threadIdx.x;
+  const int len = clamp_len(a.context_lens[b], a.max_len);
   const int n = (len + a.partition - 1) / a.partition;
   OT* o = reinterpret_cast<OT*>(a.out) + ((size_t)b * a.num_q_heads + hq) * D;
   if (n == 0) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[lane + 64 * e] = (OT)0.0f;
+    if (tid < D) o[tid] = (OT)0.0f;
     return;
   }
   const size_t base = ((size_t)b * a.num_q_heads + hq) * a.max_parts;
   float mx = -INFINITY;
-  for (int p = lane; p < n; p += 64) mx = fmaxf(mx, a.part_max[base + p]);
-  mx = xlane<OpMax, 1, 32>(mx);
+  for (int p = tid; p < n; p += kReduceThreads) mx = fmaxf(mx, a.part_max[base + p]);
+  mx = block_combine<OpMax>(mx, scratch);
 
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  const int row = tid / TPR;
+  const int q4 = tid % TPR;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int p0 = 0; p0 < n; p0 += 64) {
-    const int p = p0 + lane;
-    const float w = (p < n) ? a.part_sum[base + p] * __expf(a.part_max[base + p] - mx) : 0.f;
-    wsum += w;
-    const int cnt = min(64, n - p0);
-    const float* row = a.part_out + (base + p0) * D + lane;
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = __int_as_float(readlane(__float_as_int(w), j));
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, row[(size_t)j * D + 64 * e], acc[e]);
+  for (int c0 = 0; c0 < n; c0 += kWeightChunk) {
+    const int cn = min(kWeightChunk, n - c0);
+    for (int p = tid; p < cn; p += kReduceThreads) {
+      const float w = a.part_sum[base + c0 + p] * __expf(a.part_max[base + c0 + p] - mx);
+      wbuf[p] = w;
+      wsum += w;
     }
+    __syncthreads();
+    const float* src = a.part_out + (base + c0) * D + q4 * 4;
+#pragma unroll 4
+    for (int p = row; p < cn; p += ROWS)
+      acc += wbuf[p] * *reinterpret_cast<const f32x4*>(src + (size_t)p * D);
+    __syncthreads();
   }
-  const float total = xlane<OpSum, 1, 32>(wsum);
-  const float inv = 1.0f / total;
+  const float total = block_combine<OpSum>(wsum, scratch);
+  *reinterpret_cast<f32x4*>(&part[row][q4 * 4]) = acc;
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) o[lane + 64 * e] = (OT)(acc[e] * inv);
+    for (int r = 0; r < ROWS; ++r) s += part[r][tid];
+    o[tid] = (OT)(s / total);
+  }
+}
+
+constexpr int kFixupThreads = 256;
+
+template <typename OT, int D>
+__global__ __launch_bounds__(kFixupThreads) void auto_fixup_kernel(const ReduceArgs a) {
+  constexpr int PER = D / 64;
+  const int r = blockIdx.x + 1;  // boundary between slices r-1 and r
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slices = *a.header;  // as launched by the decode
+  if (r >= slices) return;
+  // every wavefront of the workgroup derives the same plan
+  const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, slices);
+  const int64_t g = (int64_t)r * sp.per;
+  if (g >= sp.total) return;
+  const int h = (int)(g / sp.per_head);
+  int b, i;
+  locate_step(a.context_lens, a.num_seqs, a.max_len, g - (int64_t)h * sp.per_head, b, i);
+  if (i == 0 || i > sp.per) return;  // not a cut, or an earlier boundary cuts the same run
+  const int n = steps_of_len(clamp_len(a.context_lens[b], a.max_len));
+  const int64_t gs = g - i;           // first step of the run
+  const int64_t ge = gs + n;          // one past its last step
+  const int r_first = r - 1;
+  const int k_first = (gs == (int64_t)r_first * sp.per) ? 0 : 1;
+  const int nparts = (int)((ge - 1) / sp.per) - r_first + 1;  // slices holding a piece
+  const int G = a.num_q_heads / a.num_kv_heads;
+  auto row_of = [&](int j, int gq) -> size_t {  // piece j of the run, in slice order
+    const int rr = r_first + j;
+    return ((size_t)rr * 2 + (j == 0 ? k_first : 0)) * G + gq;
+  };
+  for (int gq = wave; gq < G; gq += kFixupThreads / 64) {
+    // lanes take the pieces' maxima and exp-sums in parallel
+    float mx = -INFINITY;
+    for (int j = lane; j < nparts; j += 64) mx = fmaxf(mx, a.part_max[row_of(j, gq)]);
+    mx = xlane<OpMax, 1, 32>(mx);
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    float wsum = 0.f;
+    for (int j0 = 0; j0 < nparts; j0 += 64) {
+      const int j = j0 + lane;
+      const size_t row = row_of(j < nparts ? j : j0, gq);
+      const float w = j < nparts ? a.part_sum[row] * __expf(a.part_max[row] - mx) : 0.f;
+      wsum += w;
+      const int cnt = min(64, nparts - j0);
+#pragma unroll 4
+      for (int jj = 0; jj < cnt; ++jj) {
+        const float wj = __int_as_float(readlane(__float_as_int(w), jj));
+        const float* src = a.part_out + row_of(j0 + jj, gq) * D + lane;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, src[64 * e], acc[e]);
+      }
+    }
+    const float total = xlane<OpSum, 1, 32>(wsum);
+    OT* o = reinterpret_cast<OT*>(a.out) + ((size_t)b * a.num_q_heads + (size_t)h * G + gq) * D;
+    const float inv = 1.0f / total;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[lane + 64 * e] = (OT)(acc[e] * inv);
+  }
 }
 
 template <typename OT, int D>
 hipError_t launch(const ReduceArgs& a, hipStream_t s) {
   dim3 grid(a.num_q_heads, a.num_seqs);
-  hipLaunchKernelGGL((reduce_kernel<OT, D>), grid, dim3(64), 0, s, a);
+  hipLaunchKernelGGL((reduce_kernel<OT, D>), grid, dim3(kReduceThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename OT, int D>
+hipError_t launch_fixup(const ReduceArgs& a, hipStream_t s) {
+  if (a.slices_max < 2) return hipSuccess;
+  hipLaunchKernelGGL((auto_fixup_kernel<OT, D>), dim3(a.slices_max - 1), dim3(kFixupThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -68,6 +170,14 @@ hipError_t launch_reduce(const ReduceArgs& a, Elem out, int head_dim, hipStream_
   if (out == Elem::BF16 && head_dim == 64) return launch<__bf16, 64>(a, stream);
   if (out == Elem::F32 && head_dim == 128) return launch<float, 128>(a, stream);
   if (out == Elem::F32 && head_dim == 64) return launch<float, 64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_auto_fixup(const ReduceArgs& a, Elem out, int head_dim, hipStream_t stream) {
+  if (out == Elem::BF16 && head_dim == 128) return launch_fixup<__bf16, 128>(a, stream);
+  if (out == Elem::BF16 && head_dim == 64) return launch_fixup<__bf16, 64>(a, stream);
+  if (out == Elem::F32 && head_dim == 128) return launch_fixup<float, 128>(a, stream);
+  if (out == Elem::F32 && head_dim == 64) return launch_fixup<float, 64>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -16,11 +16,12 @@
 // Lanes sharing a dimension are summed once at the end.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
+#include "pa_split.hpp"
 
 namespace pa {
 namespace {
 
-constexpr int kStep = 32;
+constexpr int kStep = kStepTokens;
 
 template <Elem E> struct ElemBytes;
 template <> struct ElemBytes<Elem::F32> { static constexpr int v = 4; };
@@ -45,8 +46,19 @@ __device__ __forceinline__ void widen16(u32x4 w, float* out) {
 template <typename QT>
 __device__ __forceinline__ float load_q(const QT* p) { return (float)*p; }
 
+// Where a range's result goes: the final output rows, or partial softmax
+// states (row of query head g of the group = row0 + g * row_stride).
+struct Target {
+  bool final_out;
+  size_t row0;
+  size_t row_stride;
+};
+
+// Attention of the G query heads of KV head h of sequence b over tokens
+// [t0, t1) (t0 a multiple of 32).  An empty range writes zeros (final only).
 template <typename QT, Elem E, int D, int BS, int G>
-__global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const int h, const int t0,
+                                       int t1, const Target tgt) {
   constexpr int ELT = ElemBytes<E>::v;
   constexpr int VEC = 16 / ELT;          // elements per 16-byte load
   constexpr int LPT = D / VEC;           // lanes per K row
@@ -62,20 +74,13 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeArgs a) {
 
   __shared__ float plds[2][G][kStep];
 
-  const int part = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
   const int lane = threadIdx.x;
-
-  int len = a.context_lens[b];
-  len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
-  const int t0 = a.partition ? part * a.partition : 0;
-  const int t1 = a.partition ? min(t0 + a.partition, len) : len;
+  t1 = min(t1, a.cap_len);  // never walk past the table row
   QT* out = reinterpret_cast<QT*>(a.out);
 
   const int tc = lane % CPR;               // V token chunk of this lane
   if (t0 >= t1) {
-    if (a.partition == 0 && tc == 0) {
+    if (tgt.final_out && tc == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -141,11 +146,11 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeArgs a) {
     for (int j = 0; j < BPS; ++j) tiles[j] = (phys_of(min(lb0 + j, lbl)) * a.num_kv_heads + h) * TILE;
 #pragma unroll
     for (int i = 0; i < NK; ++i)
-      sb.k[i] = *reinterpret_cast<const u32x4*>(kc + tiles[kblk[i]] + koff[i]);
+      sb.k[i] = stream_load<u32x4>(kc + tiles[kblk[i]] + koff[i]);
     const char* vp = vc + tiles[vblk] + voff;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      sb.v[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)i * DSTRIDE * BS * ELT);
+      sb.v[i] = stream_load<u32x4>(vp + (size_t)i * DSTRIDE * BS * ELT);
   };
 
   float acc[G][NV];
@@ -239,6 +244,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeArgs a) {
     if constexpr (LPT < 64) l_tot = xlane<OpSum, LPT, 32>(l_tot);
     const float inv = vscale / l_tot;
     const int hq = h * G + g;
+    const size_t row = tgt.row0 + (size_t)g * tgt.row_stride;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       float v = acc[g][i];
@@ -246,33 +252,86 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeArgs a) {
       v *= inv;
       if (tc == 0) {
         const int d = i * DSTRIDE + lane / CPR;
-        if (a.partition == 0) {
-          out[((size_t)b * a.num_q_heads + hq) * D + d] = (QT)v;
-        } else {
-          a.part_out[(((size_t)b * a.num_q_heads + hq) * a.max_parts + part) * D + d] = v;
-        }
+        if (tgt.final_out) out[((size_t)b * a.num_q_heads + hq) * D + d] = (QT)v;
+        else a.part_out[row * D + d] = v;
       }
     }
-    if (a.partition != 0 && lane == 0) {
-      const size_t slot = ((size_t)b * a.num_q_heads + hq) * a.max_parts + part;
-      a.part_max[slot] = m_run[g] * kLn2;  // back to natural units
-      a.part_sum[slot] = l_tot;
+    if (!tgt.final_out && lane == 0) {
+      a.part_max[row] = m_run[g] * kLn2;  // back to natural units
+      a.part_sum[row] = l_tot;
     }
   }
 }
 
-template <typename QT, Elem E, int D, int BS>
-hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
-  const int parts = a.partition ? a.max_parts : 1;
-  dim3 grid(parts, a.num_kv_heads, a.num_seqs);
-  switch (a.group) {
-    case 1: hipLaunchKernelGGL((decode_valu_kernel<QT, E, D, BS, 1>), grid, dim3(64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_valu_kernel<QT, E, D, BS, 2>), grid, dim3(64), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_valu_kernel<QT, E, D, BS, 4>), grid, dim3(64), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_valu_kernel<QT, E, D, BS, 8>), grid, dim3(64), 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+template <typename QT, Elem E, int D, int BS, int G>
+__global__ __launch_bounds__(64) void decode_valu_grid(const DecodeArgs a) {
+  const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int len = clamp_len(a.context_lens[b], a.max_len);
+  if (a.partition == 0) {
+    attend<QT, E, D, BS, G>(a, b, h, 0, len, Target{true, 0, 0});
+    return;
+  }
+  const int t0 = part * a.partition;
+  const int t1 = min(t0 + a.partition, len);
+  if (t0 >= t1) return;
+  const size_t row0 = ((size_t)b * a.num_q_heads + (size_t)h * G) * a.max_parts + part;
+  attend<QT, E, D, BS, G>(a, b, h, t0, t1, Target{false, row0, (size_t)a.max_parts});
+}
+
+template <typename QT, Elem E, int D, int BS, int G>
+__global__ __launch_bounds__(64) void decode_valu_auto(const DecodeArgs a) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.header = a.slices;  // for the merge
+  const int r = slice_of_wave(blockIdx.x, a.slices);
+  const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, a.slices);
+  int64_t g = (int64_t)r * sp.per;
+  const int64_t g_end = min(g + sp.per, sp.total);
+  if (g >= g_end) return;
+  int h = (int)(g / sp.per_head);
+  int b, i0;
+  locate_step(a.context_lens, a.num_seqs, a.max_len, g - (int64_t)h * sp.per_head, b, i0);
+  bool first = true;
+  while (g < g_end) {
+    const int len = clamp_len(a.context_lens[b], a.max_len);
+    const int n = steps_of_len(len);
+    const int seg = (int)min((int64_t)(n - i0), g_end - g);
+    const int t0 = i0 * kStep;
+    const int t1 = min((i0 + seg) * kStep, len);
+    if (i0 == 0 && seg == n) {
+      attend<QT, E, D, BS, G>(a, b, h, t0, t1, Target{true, 0, 0});
+    } else {
+      const size_t row0 = ((size_t)r * 2 + (first ? 0 : 1)) * G;
+      attend<QT, E, D, BS, G>(a, b, h, t0, t1, Target{false, row0, 1});
+    }
+    g += seg;
+    first = false;
+    i0 = 0;
+    if (++b == a.num_seqs) { b = 0; ++h; }
+  }
+}
+
+template <typename QT, Elem E, int D, int BS, int G>
+hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
+  if (a.partition == kAuto) {
+    DecodeArgs b = a;
+    b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : kAutoMaxWavesPerCU);
+    hipLaunchKernelGGL((decode_valu_auto<QT, E, D, BS, G>), dim3(b.slices), dim3(64), 0, stream, b);
+  } else {
+    const int parts = a.partition ? a.max_parts : 1;
+    dim3 grid(parts, a.num_kv_heads, a.num_seqs);
+    hipLaunchKernelGGL((decode_valu_grid<QT, E, D, BS, G>), grid, dim3(64), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+template <typename QT, Elem E, int D, int BS>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.group) {
+    case 1: return launch_one<QT, E, D, BS, 1>(a, stream);
+    case 2: return launch_one<QT, E, D, BS, 2>(a, stream);
+    case 4: return launch_one<QT, E, D, BS, 4>(a, stream);
+    case 8: return launch_one<QT, E, D, BS, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <typename QT, Elem E>

@@ -1,6 +1,8 @@
 // C ABI: argument checks, kernel choice, launch on the caller's stream.
 // Declared and documented in include/pagedattn.h.
+#include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -29,20 +31,63 @@ bool to_elem(pa_dtype t, Elem* e) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t out_bytes, max_bytes, total;
-  int max_parts;
+  size_t head_bytes, out_bytes, max_bytes, total;
+  int max_parts;   // fixed partitions: partitions per (sequence, query head)
+  int slices_max;  // balanced split: most persistent wavefronts
+  int cus;         // balanced split: compute units
 };
 
-bool workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
-                      int partition_size, Layout* l) {
-  if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || max_context_len < 0 || partition_size <= 0)
+// Wavefronts per compute unit for the balanced split: 0 = each decode
+// kernel's own choice, or PA_AUTO_WAVES_PER_CU (1..kAutoMaxWavesPerCU) for
+// tuning.
+int auto_waves_override() {
+  static const int n = [] {
+    const char* e = std::getenv("PA_AUTO_WAVES_PER_CU");
+    const int v = e ? std::atoi(e) : 0;
+    return (v >= 1 && v <= pa::kAutoMaxWavesPerCU) ? v : 0;
+  }();
+  return n;
+}
+
+// Compute units of the current device, 0 if it cannot be queried.
+int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 0;
+  if (dev < 64) cached[dev] = cus;
+  return cus;
+}
+
+bool workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int max_context_len, int partition_size, Layout* l) {
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads ||
+      head_dim < 1 || max_context_len < 0)
     return false;
-  const long long parts = std::max(1LL, ((long long)max_context_len + partition_size - 1) / partition_size);
-  const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)parts;
-  l->max_parts = (int)parts;
+  size_t rows;
+  l->max_parts = 1;
+  l->slices_max = 0;
+  l->cus = 0;
+  l->head_bytes = 0;
+  if (partition_size == pa::kAuto) {
+    l->cus = device_cus();
+    if (l->cus <= 0) return false;
+    l->slices_max = l->cus * pa::kAutoMaxWavesPerCU;
+    l->head_bytes = pa::kWorkspaceHeader;
+    rows = (size_t)l->slices_max * 2 * (size_t)(num_q_heads / num_kv_heads);
+  } else if (partition_size > 0) {
+    const long long parts = std::max(1LL, ((long long)max_context_len + partition_size - 1) / partition_size);
+    l->max_parts = (int)parts;
+    rows = (size_t)num_seqs * num_q_heads * (size_t)parts;
+  } else {
+    return false;
+  }
   l->out_bytes = align256(rows * head_dim * sizeof(float));
   l->max_bytes = align256(rows * sizeof(float));
-  l->total = l->out_bytes + 2 * l->max_bytes;
+  l->total = l->head_bytes + l->out_bytes + 2 * l->max_bytes;
   return true;
 }
 
@@ -81,12 +126,14 @@ const char* pa_status_string(pa_status status) {
   return "PA_ERR_UNKNOWN";
 }
 
-size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
-                                int partition_size) {
-  if (partition_size == 0 && num_seqs >= 0 && num_q_heads >= 1 && head_dim >= 1 && max_context_len >= 0)
+size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                int max_context_len, int partition_size) {
+  if (partition_size == 0 && num_seqs >= 0 && num_q_heads >= 1 && num_kv_heads >= 1 &&
+      num_q_heads % num_kv_heads == 0 && head_dim >= 1 && max_context_len >= 0)
     return 0;
   Layout l;
-  if (!workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_size, &l))
+  if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                        partition_size, &l))
     return SIZE_MAX;
   return l.total;
 }
@@ -122,7 +169,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     const float* k_scale, const float* v_scale, int partition_size,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0 ||
-      max_blocks_per_seq < 1 || num_blocks < 1 || partition_size < 0)
+      max_blocks_per_seq < 1 || num_blocks < 1 || partition_size < PA_PARTITION_AUTO)
     return PA_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (!(std::isfinite(scale) && scale > 0.0f)) return PA_ERR_INVALID_ARG;
@@ -132,9 +179,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const bool combo_ok = (qe == Elem::F32 && ce == Elem::F32) || (qe == Elem::BF16 && ce == Elem::BF16) ||
                         (qe == Elem::BF16 && ce == Elem::FP8);
   if (!combo_ok) return PA_ERR_UNSUPPORTED;
-  if (partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
-  if (partition_size == 0 && !out) return PA_ERR_INVALID_ARG;
+  if (partition_size <= 0 && !out) return PA_ERR_INVALID_ARG;
   if (ce == Elem::FP8 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
   if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
 
@@ -164,30 +211,36 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   const long long cap = (long long)max_blocks_per_seq * block_size;
-  a.max_len = (int)std::min<long long>(max_context_len, cap);
+  a.cap_len = (int)std::min<long long>(cap, INT32_MAX);
+  a.max_len = partition_size == PA_PARTITION_AUTO ? max_context_len
+                                                  : (int)std::min<long long>(max_context_len, cap);
   a.num_seqs = num_seqs; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads;
   a.group = group;
   a.partition = partition_size;
   a.scale = scale;
-  if (partition_size > 0) {
+  a.max_parts = 1;
+  if (partition_size != 0) {
     Layout l;
-    if (!workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_size, &l))
-      return PA_ERR_INVALID_ARG;
+    if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          partition_size, &l))
+      return partition_size == PA_PARTITION_AUTO ? PA_ERR_HIP : PA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
       return PA_ERR_WORKSPACE;
     char* w = static_cast<char*>(workspace);
+    a.header = reinterpret_cast<int*>(w);
+    w += l.head_bytes;
     a.part_out = reinterpret_cast<float*>(w);
     a.part_max = reinterpret_cast<float*>(w + l.out_bytes);
     a.part_sum = reinterpret_cast<float*>(w + l.out_bytes + l.max_bytes);
     a.max_parts = l.max_parts;
-  } else {
-    a.max_parts = 1;
+    a.cus = l.cus;
+    a.waves_per_cu = auto_waves_override();
   }
   if (num_seqs == 0) return PA_OK;
   if (log_enabled())
-    std::fprintf(stderr, "[pagedattn] decode path=%s S=%d Hq=%d Hkv=%d G=%d D=%d B=%d P=%d parts=%d\n",
+    std::fprintf(stderr, "[pagedattn] decode path=%s S=%d Hq=%d Hkv=%d G=%d D=%d B=%d P=%d parts=%d cus=%d\n",
                  use_mfma ? "mfma" : "valu", num_seqs, num_q_heads, num_kv_heads, group, head_dim,
-                 block_size, partition_size, a.max_parts);
+                 block_size, partition_size, a.max_parts, a.cus);
   hipError_t e = use_mfma ? pa::launch_decode_mfma(a, ce, head_dim, block_size, stream)
                           : pa::launch_decode_valu(a, qe, ce, head_dim, block_size, stream);
   return from_hip(e);
@@ -195,31 +248,39 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
 
 pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
                            const int32_t* context_lens, int max_context_len, int num_seqs,
-                           int num_q_heads, int head_dim, int partition_size, pa_dtype out_dtype,
-                           hipStream_t stream) {
-  if (num_seqs < 0 || num_q_heads < 1 || max_context_len < 0 || partition_size <= 0)
+                           int num_q_heads, int num_kv_heads, int head_dim, int partition_size,
+                           pa_dtype out_dtype, hipStream_t stream) {
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0 ||
+      (partition_size <= 0 && partition_size != PA_PARTITION_AUTO))
     return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   Elem oe;
   if (!to_elem(out_dtype, &oe)) return PA_ERR_INVALID_ARG;
   if (oe == Elem::FP8 || !supported_dim(head_dim)) return PA_ERR_UNSUPPORTED;
-  if (partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
   if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (num_q_heads / num_kv_heads > 16 && partition_size == PA_PARTITION_AUTO) return PA_ERR_UNSUPPORTED;
   if (!out || !workspace || !context_lens) return PA_ERR_INVALID_ARG;
   Layout l;
-  if (!workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, partition_size, &l))
-    return PA_ERR_INVALID_ARG;
+  if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                        partition_size, &l))
+    return partition_size == PA_PARTITION_AUTO ? PA_ERR_HIP : PA_ERR_INVALID_ARG;
   if (workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return PA_ERR_WORKSPACE;
   if (num_seqs == 0) return PA_OK;
   const char* w = static_cast<const char*>(workspace);
   pa::ReduceArgs a;
   a.out = out;
+  a.header = reinterpret_cast<const int*>(w);
+  w += l.head_bytes;
   a.part_out = reinterpret_cast<const float*>(w);
   a.part_max = reinterpret_cast<const float*>(w + l.out_bytes);
   a.part_sum = reinterpret_cast<const float*>(w + l.out_bytes + l.max_bytes);
   a.context_lens = context_lens;
   a.max_len = max_context_len;
-  a.num_seqs = num_seqs; a.num_q_heads = num_q_heads;
-  a.partition = partition_size; a.max_parts = l.max_parts;
+  a.num_seqs = num_seqs; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads;
+  a.partition = partition_size; a.max_parts = l.max_parts; a.slices_max = l.slices_max;
+  if (partition_size == PA_PARTITION_AUTO)
+    return from_hip(pa::launch_auto_fixup(a, oe, head_dim, stream));
   return from_hip(pa::launch_reduce(a, oe, head_dim, stream));
 }
 

@@ -8,6 +8,19 @@ namespace pa {
 
 enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2 };
 
+// Balanced split: most persistent wavefronts per compute unit any decode
+// kernel uses (sizes the workspace and the merge grid), minimum slice length
+// in 32-token steps, the XCD count used to group slices, and the size of the
+// workspace header (the decode kernel records its slice count there).
+constexpr int kAutoMaxWavesPerCU = 4;
+constexpr int kAutoMinSteps = 4;
+constexpr int kXcds = 8;
+constexpr int kWorkspaceHeader = 256;
+
+// Split modes (DecodeArgs::partition): > 0 fixed partitions of that many
+// tokens, 0 unsplit, kAuto balanced slices.
+constexpr int kAuto = -1;
+
 // Everything a decode launch needs; passed by value as the kernel argument.
 struct DecodeArgs {
   void* out;                    // [S][Hq][D] q type (unsplit launches)
@@ -23,10 +36,15 @@ struct DecodeArgs {
   float* part_sum;
   int64_t num_blocks;
   int max_blocks;               // table row length
-  int max_len;                  // clamp for context_lens (host bound and table capacity)
+  int max_len;                  // clamp for context_lens when planning ranges
+  int cap_len;                  // tokens the table rows can address (max_blocks * B)
   int num_seqs, num_q_heads, num_kv_heads, group;
-  int partition;                // tokens per partition, 0 = unsplit
+  int partition;                // tokens per partition, 0 = unsplit, kAuto = balanced
   int max_parts;                // partitions per sequence slot in the workspace
+  int slices;                   // balanced split: persistent wavefronts (set by the launcher)
+  int cus;                      // balanced split: compute units of the device
+  int waves_per_cu;             // balanced split: 0 = the kernel's own choice
+  int* header;                  // balanced split: workspace header (slice count)
   float scale;
 };
 
@@ -48,7 +66,9 @@ struct ReduceArgs {
   const float* part_max;
   const float* part_sum;
   const int32_t* context_lens;
-  int max_len, num_seqs, num_q_heads, partition, max_parts;
+  int max_len, num_seqs, num_q_heads, num_kv_heads, partition, max_parts;
+  int slices_max;               // balanced split: upper bound of the decode's slice count
+  const int* header;            // balanced split: slice count recorded by the decode
 };
 
 // Each launcher returns hipErrorInvalidValue for a shape it has no kernel
@@ -60,5 +80,6 @@ hipError_t launch_decode_valu(const DecodeArgs& a, Elem q, Elem cache, int head_
 hipError_t launch_cache_write(const WriteArgs& a, Elem src, Elem cache, int head_dim,
                               int block_size, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, Elem out, int head_dim, hipStream_t stream);
+hipError_t launch_auto_fixup(const ReduceArgs& a, Elem out, int head_dim, hipStream_t stream);
 
 }  // namespace pa

@@ -1,0 +1,100 @@
+// Work split shared by the decode kernels and the merge kernels.
+//
+// Two ways to cut a batch's contexts into per-wavefront ranges:
+//
+//  * Fixed partitions (flash decoding): range p of (sequence b, KV head h)
+//    covers tokens [p*P, min((p+1)*P, L_b)); one wavefront per range.
+//  * Balanced ("auto"): every (b, h) is a run of 32-token steps
+//    (ceil(L_b / 32), at least 1 so an empty context still has its zero
+//    output written); the runs are laid end to end, KV head major, and a
+//    persistent grid of R wavefronts takes R equal consecutive slices.  A
+//    (b, h) that one slice covers whole is finished by that wavefront; one
+//    that straddles a slice boundary leaves a partial softmax state per
+//    slice, merged afterwards.  Each slice has at most two such states: its
+//    first run ("head", slot 0) and its last run ("tail", slot 1).
+#pragma once
+
+#include "pa_device.hpp"
+#include "pa_internal.hpp"
+
+namespace pa {
+
+constexpr int kStepTokens = 32;
+
+__device__ __forceinline__ int clamp_len(int len, int max_len) {
+  return len < 0 ? 0 : (len > max_len ? max_len : len);
+}
+
+__device__ __forceinline__ int steps_of_len(int len) {
+  return len <= 0 ? 1 : (len + kStepTokens - 1) / kStepTokens;
+}
+
+// Inclusive prefix sum over the 64 lanes of the wavefront.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+struct Split {
+  int64_t per_head;  // steps of one KV head over the whole batch
+  int64_t total;     // steps of the batch (all KV heads)
+  int64_t per;       // steps per slice
+};
+
+// Every wavefront computes the same plan from the lengths (no device-wide
+// communication).  A slice is at least kAutoMinSteps steps, so small batches
+// use fewer wavefronts instead of many tiny slices.
+__device__ __forceinline__ Split plan_split(const int32_t* lens, int num_seqs, int max_len,
+                                            int num_kv_heads, int slices) {
+  const int lane = threadIdx.x & 63;
+  int64_t tot = 0;
+  for (int c = 0; c < num_seqs; c += 64) {
+    const int b = c + lane;
+    const int n = b < num_seqs ? steps_of_len(clamp_len(lens[b], max_len)) : 0;
+    tot += readlane(wave_scan_incl(n), 63);
+  }
+  Split s;
+  s.per_head = tot;
+  s.total = tot * num_kv_heads;
+  const int64_t even = (s.total + slices - 1) / slices;
+  s.per = even > kAutoMinSteps ? even : kAutoMinSteps;
+  return s;
+}
+
+// Sequence b and step offset i of step `rem` (0 <= rem < per_head) of a head.
+__device__ __forceinline__ void locate_step(const int32_t* lens, int num_seqs, int max_len,
+                                            int64_t rem, int& b_out, int& i_out) {
+  const int lane = threadIdx.x & 63;
+  int64_t base = 0;
+  for (int c = 0; c < num_seqs; c += 64) {
+    const int b = c + lane;
+    const int n = b < num_seqs ? steps_of_len(clamp_len(lens[b], max_len)) : 0;
+    const int incl = wave_scan_incl(n);
+    const int chunk = readlane(incl, 63);
+    if (rem < base + chunk) {
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > rem);
+      const int l = __builtin_ctzll(hit);
+      b_out = c + l;
+      i_out = (int)(rem - (base + readlane(incl, l) - readlane(n, l)));
+      return;
+    }
+    base += chunk;
+  }
+  b_out = num_seqs - 1;  // not reached for rem < per_head
+  i_out = 0;
+}
+
+// Slice index of wavefront w: slices handled by one XCD (workgroups are
+// dealt to the XCDs round-robin) are consecutive, so neighbouring work --
+// e.g. sequences sharing prefix blocks -- meets in one L2.
+__device__ __forceinline__ int slice_of_wave(int w, int slices) {
+  if (slices % kXcds != 0) return w;
+  return (w % kXcds) * (slices / kXcds) + w / kXcds;
+}
+
+}  // namespace pa

@@ -55,9 +55,10 @@ def test_workspace_size_follows_documented_layout(lib):
         parts = max(1, -(-maxlen // p))
         rows = s * hq * parts
         want = align(rows * d * 4) + 2 * align(rows * 4)
-        assert lib.pa_decode_workspace_size(s, hq, d, maxlen, p) == want
-    assert lib.pa_decode_workspace_size(4, 8, 64, 200, 0) == 0
-    assert lib.pa_decode_workspace_size(4, 8, 64, 200, -32) == ctypes.c_size_t(-1).value
+        assert lib.pa_decode_workspace_size(s, hq, hq // 4 or 1, d, maxlen, p) == want
+    assert lib.pa_decode_workspace_size(4, 8, 2, 64, 200, 0) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 2, 64, 200, -32) == ctypes.c_size_t(-1).value
+    assert lib.pa_decode_workspace_size(4, 8, 3, 64, 200, 64) == ctypes.c_size_t(-1).value
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
@@ -91,6 +92,7 @@ def _decode(lib, **kw):
     (dict(cdt=FP8), INVALID),                   # fp8 cache without scales
     (dict(p=48), UNSUPPORTED),                  # split not a multiple of 32 tokens
     (dict(p=-32), INVALID),
+    (dict(p=-1, out=None), INVALID),            # the balanced split writes out
     (dict(p=64, ws=None), WORKSPACE),
     (dict(p=64, ws=FAKE, wsb=16), WORKSPACE),
     (dict(p=64, ws=ctypes.c_void_p(0x1010), wsb=1 << 30), WORKSPACE),  # misaligned
@@ -104,11 +106,12 @@ def test_decode_rejects(lib, kw, code):
 
 def test_decode_reduce_rejects(lib):
     r = lib.pa_decode_reduce
-    assert r(FAKE, FAKE, 1 << 30, FAKE, 128, 2, 8, 128, 0, BF16, None) == INVALID
-    assert r(FAKE, FAKE, 1 << 30, FAKE, 128, 2, 8, 96, 64, BF16, None) == UNSUPPORTED
-    assert r(FAKE, FAKE, 1 << 30, FAKE, 128, 2, 8, 128, 64, FP8, None) == UNSUPPORTED
-    assert r(None, FAKE, 1 << 30, FAKE, 128, 2, 8, 128, 64, BF16, None) == INVALID
-    assert r(FAKE, FAKE, 16, FAKE, 128, 2, 8, 128, 64, BF16, None) == WORKSPACE
+    assert r(FAKE, FAKE, 1 << 30, FAKE, 128, 2, 8, 2, 128, 0, BF16, None) == INVALID
+    assert r(FAKE, FAKE, 1 << 30, FAKE, 128, 2, 8, 2, 96, 64, BF16, None) == UNSUPPORTED
+    assert r(FAKE, FAKE, 1 << 30, FAKE, 128, 2, 8, 2, 128, 64, FP8, None) == UNSUPPORTED
+    assert r(None, FAKE, 1 << 30, FAKE, 128, 2, 8, 2, 128, 64, BF16, None) == INVALID
+    assert r(FAKE, FAKE, 16, FAKE, 128, 2, 8, 2, 128, 64, BF16, None) == WORKSPACE
+    assert r(FAKE, FAKE, 1 << 30, FAKE, 128, 2, 8, 3, 128, 64, BF16, None) == INVALID
 
 
 def test_cache_write_rejects(lib):

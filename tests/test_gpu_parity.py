@@ -68,7 +68,7 @@ def test_workload_write_and_decode(idx):
     seqs = _sample(batch, SAMPLE[idx])
     ref = oracle_decode_host(batch, k_ref, v_ref, seqs)
     del k_ref, v_ref
-    splits = [w.partition_size] if w.partition_size else [None, 0]
+    splits = [w.partition_size, -1] if w.partition_size else [-1, 0, 512]
     for p in splits:
         out = gpu_decode(batch, p)
         _sync()
@@ -79,7 +79,7 @@ def test_workload_write_and_decode(idx):
 # layout invariances: identical bits
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("idx,p", [(2, 512), (2, 0), (1, 0), (4, 256)])
+@pytest.mark.parametrize("idx,p", [(2, 512), (2, 0), (2, -1), (1, 0), (1, -1), (4, 256), (4, -1)])
 def test_block_permutation_and_contiguous_layout_bit_identical(idx, p):
     w = WORKLOADS[idx]
     batch = make_batch(w, device=DEV, num_seqs=8 if idx != 1 else None)
@@ -94,7 +94,7 @@ def test_block_permutation_and_contiguous_layout_bit_identical(idx, p):
         assert torch.equal(bits(base), bits(cont))
 
 
-@pytest.mark.parametrize("p", [0, 512])
+@pytest.mark.parametrize("p", [0, 512, -1])
 def test_shared_prefix_equals_private_copies(p):
     w = WORKLOADS[4]
     batch = make_batch(w, device=DEV)
@@ -122,12 +122,30 @@ def test_poisoned_unused_slots_do_not_change_bits(idx):
     assert torch.equal(bits(a), bits(b))
 
 
-def test_repeated_runs_identical():
+@pytest.mark.parametrize("p", [512, -1])
+def test_repeated_runs_identical(p):
     batch = make_batch(WORKLOADS[3], device=DEV, num_seqs=32)
-    a = gpu_decode(batch, 512).clone()
-    b = gpu_decode(batch, 512)
+    a = gpu_decode(batch, p).clone()
+    b = gpu_decode(batch, p)
     _sync()
     assert torch.equal(bits(a), bits(b))
+
+
+@pytest.mark.parametrize("cache,group", [("bf16", 4), ("bf16", 1), ("fp8_e4m3", 4), ("f32", 2)])
+def test_balanced_split_cuts_and_empty_runs(cache, group):
+    """Many short and a few long contexts with empty ones between them: the
+    balanced slices cut long runs several times and start inside runs."""
+    rng = np.random.default_rng(21)
+    lens = rng.integers(1, 90, size=40)
+    lens[[3, 17]] = 0
+    lens[[5, 30]] = [5000, 2500]
+    batch = _custom(cache, 128 if cache != "f32" else 64, 32 if cache == "fp8_e4m3" else 16,
+                    2 * group, 2, lens)
+    k_ref, v_ref = write_and_reference(batch)
+    ref = oracle_decode_host(batch, k_ref, v_ref, range(len(lens)))
+    out = gpu_decode(batch, -1)
+    _sync()
+    compare(widen(out), ref, cache, f"balanced {cache} G={group}")
 
 
 # ---------------------------------------------------------------------------
@@ -156,7 +174,7 @@ def test_shapes_and_groups(cache, head_dim, block, group):
     k_ref, v_ref = write_and_reference(batch)
     seqs = list(range(len(EDGE_LENS)))
     ref = oracle_decode_host(batch, k_ref, v_ref, seqs)
-    for p in (0, 32, 64, 512):
+    for p in (0, 32, 64, 512, -1):
         out = gpu_decode(batch, p)
         _sync()
         compare(widen(out), ref, cache, f"{cache} d={head_dim} B={block} G={group} P={p}")
@@ -167,7 +185,7 @@ def test_matrix_core_path_odd_groups(group):
     batch = _custom("bf16", 128, 16, group * 2, 2, [1, 40, 300, 777])
     k_ref, v_ref = write_and_reference(batch)
     ref = oracle_decode_host(batch, k_ref, v_ref, range(4))
-    for p in (0, 64):
+    for p in (0, 64, -1):
         out = gpu_decode(batch, p)
         _sync()
         compare(widen(out), ref, "bf16", f"G={group} P={p}")
@@ -211,7 +229,7 @@ def test_single_token_returns_that_value_row(cache, group):
             assert np.array_equal(got[b, hq], want), (b, hq)
 
 
-@pytest.mark.parametrize("p", [0, 64])
+@pytest.mark.parametrize("p", [0, 64, -1])
 def test_empty_context_gives_zeros(p):
     batch = _custom("bf16", 128, 16, 8, 2, [0, 5, 0], poison=False)
     out = torch.full_like(batch.q, 7.0)
@@ -258,7 +276,7 @@ def test_reduce_of_oracle_partitions():
                                       host_view(batch.v_pool), batch.block_tables,
                                       batch.context_lens, w.block_size, batch.scale, "bf16",
                                       "bf16", p)
-    n = pk.workspace_size(5, 8, 128, batch.max_context_len, p)
+    n = pk.workspace_size(5, 8, 2, 128, batch.max_context_len, p)
     ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
     po, pm, ps = pk.workspace_views(ws, 5, 8, 128, batch.max_context_len, p)
     po.copy_(torch.from_numpy(np.nan_to_num(o)).float())
