@@ -106,6 +106,8 @@ def main() -> int:
                          "(default: the workload's own, else the library default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as a captured HIP graph (replayed K times)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -183,6 +185,29 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
+    eager_ms_per_step = ms_per_step
+
+    if args.graph:
+        # The same step captured once in a HIP graph and replayed K times.
+        ref = out.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(False)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out.view(torch.int16), ref.view(torch.int16)):
+            raise RuntimeError("graph replay differs from the eager step")
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_per_step = g0.elapsed_time(g1) / args.steps
+        log(f"[bench] graph replay: {ms_per_step * 1e3:.1f} us per step "
+            f"(eager {eager_ms_per_step * 1e3:.1f} us)")
 
     def span(a, b):
         return [x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]
@@ -257,7 +282,9 @@ def main() -> int:
                    "head_dim": w.head_dim, "block_size": w.block_size,
                    "kv_dtype": w.cache_dtype, "context_tokens": dec["tokens"],
                    "partition_size": part, "split": split, "step": "kv_cache_write + decode"
-                   + (" + reduce" if part else "")},
+                   + (" + reduce" if part else ""),
+                   "launch": "hip graph replay" if args.graph else "eager",
+                   "eager_ms_per_step": round(eager_ms_per_step, 4)},
         "kernels_us": {"kv_cache_write": round(write_ms * 1e3, 2),
                        "decode": round(decode_ms_in_step * 1e3, 2),
                        "decode_reduce": round(reduce_ms * 1e3, 2),

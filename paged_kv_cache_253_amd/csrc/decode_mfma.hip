@@ -345,7 +345,10 @@ constexpr int kFirst = 1, kLast = 2, kFinal = 4;
 // MiB over the chip) read the scattered tiles fastest; fewer, deeper streams
 // beat more, shallower ones there.  Smaller steps (FP8 or head_dim 64) do
 // best with four.
-constexpr int kRing = 4;
+#ifndef PA_STREAM_RING
+#define PA_STREAM_RING 4  // build-time tuning knob
+#endif
+constexpr int kRing = PA_STREAM_RING;
 
 template <bool FP8, int D>
 constexpr int stream_waves_per_cu() {
