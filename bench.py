@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD public spec
-KERNEL_SOURCES = ["decode_mfma.hip", "decode_valu.hip", "pa_device.hpp"]
+KERNEL_SOURCES = ["decode_mfma.hip", "decode_valu.hip", "pa_device.hpp", "pa_split.hpp", "pa_internal.hpp"]
 
 
 def log(*a):
@@ -140,8 +140,7 @@ def main() -> int:
     s, hq, d = batch.q.shape
     ws = None
     if part:
-        ws = torch.empty(pk.workspace_size(s, hq, w.num_kv_heads, d, batch.max_context_len, part),
-                         dtype=torch.uint8, device=dev)
+        ws = pk.new_workspace(s, hq, w.num_kv_heads, d, batch.max_context_len, part, dev)
 
     ev = {}
 

@@ -42,8 +42,12 @@
  *
  * Pool layout (one pool for K, one for V, `num_blocks` blocks each):
  *
- *   K cache: [num_blocks][num_kv_heads][block_size][head_dim]
- *            (inside a (block, head) tile: one row of head_dim per token)
+ *   K cache: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
+ *            X = 16 bytes / element size (4 f32, 8 bf16, 16 fp8): inside a
+ *            (block, head) tile the head dimension is cut into 16-byte
+ *            chunks, and chunk row c holds chunk c of every token of the
+ *            block in token order.  Element d of token j's K row sits at
+ *            ((d / X) * block_size + j) * X + d % X within the tile.
  *   V cache: [num_blocks][num_kv_heads][head_dim][block_size]
  *            (inside a (block, head) tile: one row of block_size tokens per
  *            dimension)
@@ -157,14 +161,16 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
  *                  PA_PARTITION_AUTO: balanced -- every (sequence, KV head)
  *                     is a run of ceil(L / 32) 32-token steps (one step for
  *                     L == 0); the runs of the batch, KV head major, are cut
- *                     into equal slices for 8 wavefronts per compute unit of
- *                     the current device.  Runs one slice covers whole are
+ *                     into W equal slices, one per persistent wavefront
+ *                     (W = 2 to 4 per compute unit of the current device, by
+ *                     kernel variant).  Runs one slice covers whole are
  *                     written to `out` here; the state of each run cut by a
  *                     slice boundary goes to `workspace`, and pa_decode_reduce
  *                     (same arguments) writes those runs' output.
  *   workspace, workspace_bytes  device scratch for the split modes; at least
  *                  pa_decode_workspace_size(...) bytes, 256-byte aligned;
- *                  ignored when partition_size == 0
+ *                  ignored when partition_size == 0.  Concurrent calls must
+ *                  not share a workspace.
  *
  * Group sizes: any G <= 16 for a bf16 or FP8 cache; G in {1, 2, 4, 8} for
  * an f32 cache.
@@ -201,11 +207,11 @@ pa_status pa_decode(void* out, const void* q,
  * maxP = max(1, ceil(max_context_len / partition_size)); the state of
  * partition p of sequence b, query head hq is row (b * num_q_heads + hq) *
  * maxP + p; rows of partitions a sequence does not have are unused.
- * PA_PARTITION_AUTO: H = 256 (pa_decode stores its slice count there, as an
- * int32 at offset 0), R = 4 * CUs * 2 * G (CUs = compute units of the
- * current device, G = num_q_heads / num_kv_heads; a decode uses at most
- * 4 * CUs slices); slice s keeps the state of its first run in rows
- * (2s) * G + g and of its last run in rows (2s + 1) * G + g, for the
+ * PA_PARTITION_AUTO: H = 256 (pa_decode stores W there, as an int32 at
+ * offset 0, for pa_decode_reduce), R = 4 * CUs * 2 * G (CUs = compute
+ * units of the current device, G = num_q_heads / num_kv_heads; a decode
+ * uses at most 4 * CUs slices); slice s keeps the state of its first run in
+ * rows (2s) * G + g and of its last run in rows (2s + 1) * G + g, for the
  * group's query heads g, when those runs are cut.
  *
  * A state over tokens T of a query head, with z_t as in pa_decode:

@@ -6,8 +6,11 @@ import this.  No blocking, fusion or reordering beyond the definitions.
 Pool layout (the library's documented layout, restated here from its
 definition, not shared with it):
 
-* K pool: ``[num_blocks, num_kv_heads, block_size, head_dim]`` -- inside a
-  (block, head) tile, token-major rows of ``head_dim`` elements.
+* K pool: ``[num_blocks, num_kv_heads, head_dim // x, block_size, x]`` with
+  ``x = 16 / element bytes`` (4 f32, 8 bf16, 16 E4M3) -- inside a (block,
+  head) tile the head dimension is cut into 16-byte chunks, and each chunk
+  row holds that chunk of every token of the block, token-major.  Token
+  ``j``'s K row is ``pool[blk, h, :, j, :]`` read chunk by chunk.
 * V pool: ``[num_blocks, num_kv_heads, head_dim, block_size]`` -- inside a
   (block, head) tile, dimension-major rows of ``block_size`` tokens.
 
@@ -55,6 +58,26 @@ def source_to_f32(raw: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# K rows in the chunked K pool
+# --------------------------------------------------------------------------
+
+def k_row(k_pool: np.ndarray, blk: int, h: int, off: int) -> np.ndarray:
+    """K row (``head_dim`` elements, raw storage) of the token at offset
+    ``off`` of block ``blk``, KV head ``h``: its chunks in order."""
+    return k_pool[blk, h, :, off, :].reshape(-1)
+
+
+def set_k_row(k_pool: np.ndarray, blk: int, h: int, off: int, row: np.ndarray) -> None:
+    """Store one K row (``head_dim`` elements) at (``blk``, ``h``, ``off``)."""
+    n_chunks, x = k_pool.shape[2], k_pool.shape[4]
+    k_pool[blk, h, :, off, :] = np.asarray(row).reshape(n_chunks, x)
+
+
+def k_head_dim(k_pool: np.ndarray) -> int:
+    return int(k_pool.shape[2] * k_pool.shape[4])
+
+
+# --------------------------------------------------------------------------
 # block table: index map and gather
 # --------------------------------------------------------------------------
 
@@ -80,12 +103,13 @@ def gather(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarray,
     from non-adjacent blocks ("How LLM Inference Engines Work", section on
     PagedAttention); here the gather is one token at a time.
     """
-    n_kv, head_dim = k_pool.shape[1], k_pool.shape[3]
+    n_kv, head_dim = k_pool.shape[1], k_head_dim(k_pool)
     k = np.empty((length, n_kv, head_dim), dtype=k_pool.dtype)
     v = np.empty((length, n_kv, head_dim), dtype=v_pool.dtype)
     for t in range(length):
         blk, off = slot_of(table_row, t, block_size)
-        k[t] = k_pool[blk, :, off, :]
+        for h in range(n_kv):
+            k[t, h] = k_row(k_pool, blk, h, off)
         v[t] = v_pool[blk, :, :, off]
     return k, v
 
@@ -134,12 +158,12 @@ def write_tokens(k_pool: np.ndarray, v_pool: np.ndarray,
                 vx = source_to_f32(v_new[n, h], src_dtype)
                 kq = kx / np.float32(k_scale[h])
                 vq = vx / np.float32(v_scale[h])
-                k_out[blk, h, off, :] = codecs.e4m3_encode(kq)
+                set_k_row(k_out, blk, h, off, codecs.e4m3_encode(kq))
                 v_out[blk, h, :, off] = codecs.e4m3_encode(vq)
             else:
                 if src_dtype != cache_dtype:
                     raise ValueError("non-fp8 caches store the source bits")
-                k_out[blk, h, off, :] = k_new[n, h]
+                set_k_row(k_out, blk, h, off, k_new[n, h])
                 v_out[blk, h, :, off] = v_new[n, h]
     return k_out, v_out
 

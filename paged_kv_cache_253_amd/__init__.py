@@ -21,7 +21,7 @@ import os
 import torch
 
 __all__ = ["PagedAttnError", "load", "kv_cache_write", "decode", "decode_partitions",
-           "decode_reduce", "workspace_size", "workspace_views", "default_partition_size",
+           "decode_reduce", "workspace_size", "new_workspace", "workspace_views", "default_partition_size",
            "PARTITION_AUTO", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
@@ -106,6 +106,15 @@ def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim:
     return int(n)
 
 
+def new_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                  max_context_len: int, partition_size: int, device) -> torch.Tensor:
+    """A zeroed workspace for a split decode (fixed partitions or the
+    balanced split), sized by ``workspace_size``."""
+    n = workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                       partition_size)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+
+
 def workspace_views(workspace: torch.Tensor, num_seqs: int, num_q_heads: int, head_dim: int,
                     max_context_len: int, partition_size: int):
     """(part_out, part_max, part_sum) float32 views of a fixed-partition
@@ -131,13 +140,23 @@ def default_partition_size(max_context_len: int) -> int:
     return PARTITION_AUTO
 
 
+def _k_pool_shape(k_cache: torch.Tensor) -> tuple[int, int, int, int]:
+    """(num_blocks, num_kv_heads, block_size, head_dim) of a K pool laid out
+    ``[nb, Hkv, head_dim / X, block_size, X]`` with X elements = 16 bytes."""
+    if k_cache.dim() != 5 or k_cache.shape[4] * k_cache.element_size() != 16:
+        raise ValueError("K pool must be [num_blocks, num_kv_heads, head_dim/X, block_size, X] "
+                         "with X elements = 16 bytes")
+    nb, hkv, nc, bsz, x = k_cache.shape
+    return int(nb), int(hkv), int(bsz), int(nc * x)
+
+
 def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
                    v_cache: torch.Tensor, slot_mapping: torch.Tensor,
                    k_scale: torch.Tensor | None = None,
                    v_scale: torch.Tensor | None = None) -> None:
     """``pa_kv_cache_write``: store row n of k_new/v_new at slot_mapping[n]."""
     n, hkv, d = k_new.shape
-    nb, hkv2, bsz, d2 = k_cache.shape
+    nb, hkv2, bsz, d2 = _k_pool_shape(k_cache)
     if (hkv2, d2) != (hkv, d) or tuple(v_cache.shape) != (nb, hkv, d, bsz):
         raise ValueError("cache shapes do not match the new rows")
     if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != n:
@@ -152,7 +171,7 @@ def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tens
 def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                  scale, k_scale, v_scale, partition_size, workspace):
     s, hq, d = q.shape
-    nb, hkv, bsz, _ = k_cache.shape
+    nb, hkv, bsz, _ = _k_pool_shape(k_cache)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise ValueError("block_tables and context_lens must be int32")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -175,8 +194,7 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, max_conte
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        n = workspace_size(s, hq, hkv, d, max_context_len, partition_size)
-        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(s, hq, hkv, d, max_context_len, partition_size, q.device)
     _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                  k_scale, v_scale, partition_size, workspace)
     return workspace

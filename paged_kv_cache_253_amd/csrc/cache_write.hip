@@ -2,8 +2,9 @@
 //
 // Token n goes to block slot / B at offset slot % B ("vLLM & High-Throughput
 // Serving", section 2, block-table equation on a flat slot number), one row
-// per KV head: a contiguous head_dim row in the K tile, one element per
-// dimension row in the dimension-major V tile.  Same-type caches copy bits;
+// per KV head: one 16-byte piece per head-dimension chunk in the chunked K
+// tile (element d at chunk d / X, lane d % X of the token, X elements = 16
+// bytes), one element per dimension row in the dimension-major V tile.  Same-type caches copy bits;
 // an FP8 cache stores the E4M3FN code of x / scale[h] (binary32 quotient,
 // then nearest-even E4M3 with saturation).
 #include "pa_device.hpp"
@@ -24,6 +25,8 @@ __global__ __launch_bounds__(64) void cache_write_kernel(const WriteArgs a) {
   const int64_t blk = slot / BS;
   const int off = (int)(slot % BS);
   const int64_t tile = (blk * a.num_kv_heads + h) * (int64_t)(BS * D);  // in elements
+  constexpr int X = CE == Elem::F32 ? 4 : (CE == Elem::BF16 ? 8 : 16);  // K chunk width
+  auto kidx = [&](int d) { return ((d / X) * BS + off) * X + d % X; };
   const ST* kn = reinterpret_cast<const ST*>(a.k_new) + ((int64_t)n * a.num_kv_heads + h) * D;
   const ST* vn = reinterpret_cast<const ST*>(a.v_new) + ((int64_t)n * a.num_kv_heads + h) * D;
   if constexpr (CE == Elem::FP8) {
@@ -31,14 +34,14 @@ __global__ __launch_bounds__(64) void cache_write_kernel(const WriteArgs a) {
     uint8_t* kc = reinterpret_cast<uint8_t*>(a.k_cache) + tile;
     uint8_t* vc = reinterpret_cast<uint8_t*>(a.v_cache) + tile;
     for (int d = threadIdx.x; d < D; d += 64) {
-      kc[off * D + d] = (uint8_t)f32_to_e4m3_sat(__fdiv_rn(to_f32(kn[d]), ks));
+      kc[kidx(d)] = (uint8_t)f32_to_e4m3_sat(__fdiv_rn(to_f32(kn[d]), ks));
       vc[d * BS + off] = (uint8_t)f32_to_e4m3_sat(__fdiv_rn(to_f32(vn[d]), vs));
     }
   } else {
     ST* kc = reinterpret_cast<ST*>(a.k_cache) + tile;
     ST* vc = reinterpret_cast<ST*>(a.v_cache) + tile;
     for (int d = threadIdx.x; d < D; d += 64) {
-      kc[off * D + d] = kn[d];
+      kc[kidx(d)] = kn[d];
       vc[d * BS + off] = vn[d];
     }
   }

@@ -7,20 +7,25 @@
 // keeps the next step's K and V tiles in flight while it computes the
 // current one.  Per step:
 //
-//   S^T = K q^T      two v_mfma_f32_16x16x32_bf16 chains (16 tokens each)
-//                    over head_dim; rows = tokens, columns = the G query
-//                    heads of this KV head (zero columns beyond G)
+//   S^T = K q^T      two v_mfma_f32_16x16x32_bf16 chains (tokens 0-15 and
+//                    16-31 of the step) over head_dim; rows = tokens,
+//                    columns = the G query heads of this KV head (zero
+//                    columns beyond G).  K tiles hold 16-byte head-dim
+//                    chunks token-major, so the A operand of one chunk
+//                    (16 tokens x 4 chunk rows) is one 1 KiB run at B = 16
 //   online softmax   per query head, in the MFMA output registers; the step
 //                    maximum needs two permlane swaps, no LDS
 //   O^T += V^T P^T   head_dim/16 MFMAs; V tiles are stored dimension-major
 //                    so each lane's 8 tokens of one dimension are one 16-byte
-//                    load, and P comes straight from the S^T registers
+//                    load; P comes from the S^T registers through one
+//                    permlane32 and one permlane16 swap per packed word
 //
 // MFMA operand layouts (16x16x32, wave64; checked on hardware): lane l holds
 // row/column l % 16 and k-slots 8*(l/16) .. 8*(l/16)+7 of A and B; the f32
-// result row is 4*(l/16) + r (r = 0..3), column l % 16.  The token assigned
-// to QK row i of group m is 8*(i/4) + 4*m + i%4, so a lane's QK results are
-// exactly the 8 tokens 8*(l/16) .. +7 that its PV k-slots need.
+// result row is 4*(l/16) + r (r = 0..3), column l % 16.  QK row i of group
+// m is token 16*m + i, so lane l holds scores of tokens 4*(l/16) + r and
+// 16 + 4*(l/16) + r; its PV k-slots need tokens 8*(l/16) .. +7, which the
+// two swaps bring in from the lanes 16 and 32 away (p_operand).
 //
 // The same head mapping (column = query head) holds in S^T and O^T, so every
 // softmax statistic a lane keeps is the one its output registers need.
@@ -43,7 +48,7 @@ struct Cfg {
   static constexpr int kChunks = D / 32;            // QK MFMAs per token group
   static constexpr int kDTiles = D / 16;            // PV MFMAs per step
   static constexpr int kKLoads = FP8 ? D / 64 : D / 32;  // 16-byte K loads per token group
-  static constexpr int kRowK = D * kElt;            // bytes of one K row (token)
+  static constexpr int kChunkRow = BS * 16;         // bytes of one K chunk row (16 B per token)
   static constexpr int kRowV = BS * kElt;           // bytes of one V row (dimension)
   static constexpr int kTile = BS * D * kElt;       // bytes of one (block, head) tile
   static constexpr int kBlocksPerStep = kStep / BS;
@@ -86,6 +91,32 @@ __device__ __forceinline__ bf16x8 k_operand(const Buf& sb, int m, int c) {
     return as_bf16x8(sb.k[m][c]);
   }
 }
+
+// Softmax weights in QK register order (p[0..3]: tokens 4*grp + r, p[4..7]:
+// tokens 16 + 4*grp + r) -> PV B operand in k-slot order (tokens 8*grp ..
+// 8*grp + 7).  Packed bf16 pairs A (first four) and B (last four) of lanes
+// in rows 0..3 are exchanged: permlane32_swap leaves rows 0,1 with A of
+// rows {0,2},{1,3} and rows 2,3 with B of rows {0,2},{1,3}; permlane16_swap
+// then gives row k the two quarters of tokens 8k .. 8k + 7.
+__device__ __forceinline__ bf16x8 p_operand(const float* p) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16x2 t;
+    t[0] = (__bf16)p[2 * i];
+    t[1] = (__bf16)p[2 * i + 1];
+    w[i] = __builtin_bit_cast(uint32_t, t);
+  }
+  const auto x0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+  const auto x1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+  const auto y0 = __builtin_amdgcn_permlane16_swap(x0[0], x0[1], false, false);
+  const auto y1 = __builtin_amdgcn_permlane16_swap(x1[0], x1[1], false, false);
+  const u32x4 r = {y0[0], y1[0], y0[1], y1[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// The token of QK result register i (0..7) of lane row grp, within a step.
+__device__ __forceinline__ int qk_token(int grp, int i) { return 4 * grp + (i & 3) + 16 * (i >> 2); }
 
 template <bool FP8>
 __device__ __forceinline__ bf16x8 v_operand(const VRaw<FP8>& r) {
@@ -170,10 +201,9 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
 
   // ---- per-lane byte offsets inside the step's tiles ----------------------
   // K: QK row i = col of group m is token 8*(col/4) + 4*m + col%4 of the step.
-  const int ktok = 8 * (col >> 2) + (col & 3);             // + 4*m
-  const int kblk = (BS == 16) ? (ktok >> 4) : 0;            // which block of the step
-  const int krow = (BS == 16) ? (ktok & 15) : ktok;
-  const uint32_t koff = (uint32_t)krow * C::kRowK + (uint32_t)grp * 16;
+  // K: QK row col of group m is token 16*m + col of the step; load j of the
+  // group reads chunk row 4*j + grp.
+  const uint32_t koff = ((uint32_t)grp * BS + (uint32_t)col) * 16;
   // V: dimension dt*16 + col, tokens 8*grp .. +7 of the step.
   const int vblk = (BS == 16) ? (grp >> 1) : 0;
   const uint32_t vtok = (BS == 16) ? (uint32_t)(8 * (grp & 1)) : (uint32_t)(8 * grp);
@@ -206,13 +236,14 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
     const int64_t p1 = (C::kBlocksPerStep == 2) ? phys_of(lb1) : p0;
     const int64_t tile0 = (p0 * a.num_kv_heads + h) * C::kTile;
     const int64_t tile1 = (p1 * a.num_kv_heads + h) * C::kTile;
-    const char* kp = kc + (kblk ? tile1 : tile0) + koff;
+    const char* kp0 = kc + tile0 + koff;
+    const char* kp1 = (BS == 16) ? kc + tile1 + koff : kp0 + 16 * 16;
     const char* vp = vc + (vblk ? tile1 : tile0) + voff;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int j = 0; j < C::kKLoads; ++j)
-        sb.k[m][j] = stream_load<u32x4>(kp + 4 * m * C::kRowK + j * 64);
+    for (int j = 0; j < C::kKLoads; ++j) {
+      sb.k[0][j] = stream_load<u32x4>(kp0 + j * 4 * C::kChunkRow);
+      sb.k[1][j] = stream_load<u32x4>(kp1 + j * 4 * C::kChunkRow);
+    }
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt) {
       if constexpr (FP8) sb.v[dt].w = stream_load<u32x2>(vp + dt * 16 * C::kRowV);
@@ -236,14 +267,16 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(sb, 1, c), qop[c], s1, 0, 0, 0);
     }
     // scores in log2 units: z = s * c2, so exp(scale*q.k - max) = 2^(z - m)
-    const int tok0 = base + 8 * grp;  // token of k-slot 0 of this lane
-    const int valid = partial ? min(max(t1 - tok0, 0), 8) : 8;
+    bool zok[8];  // token of score register i inside the range
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zok[i] = !partial || base + qk_token(grp, i) < t1;
     float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = (i < valid) ? __fmul_rn(z[i], c2) : -INFINITY;
-    if (partial) {
+    for (int i = 0; i < 8; ++i) z[i] = zok[i] ? __fmul_rn(z[i], c2) : -INFINITY;
+    if (partial) {  // PV k-slots of this lane: tokens 8*grp .. +7
+      const int vvalid = min(max(t1 - (base + 8 * grp), 0), 8);
 #pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<FP8>(sb.v[dt], valid);
+      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<FP8>(sb.v[dt], vvalid);
     }
     float mx = z[0];
 #pragma unroll
@@ -260,12 +293,10 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
     float p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = (i < valid) ? exp2f(z[i] - m_run) : 0.f;
+      p[i] = zok[i] ? exp2f(z[i] - m_run) : 0.f;
       l_run += p[i];
     }
-    bf16x8 pop;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pop[i] = (__bf16)p[i];
+    const bf16x8 pop = p_operand(p);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<FP8>(sb.v[dt]), pop, acc[dt], 0, 0, 0);
@@ -339,14 +370,16 @@ __global__ __launch_bounds__(64) void decode_mfma_grid(const DecodeArgs a) {
 // ---------------------------------------------------------------------------
 
 constexpr int kFirst = 1, kLast = 2, kFinal = 4;
-// Ring of 4 step slots: each wavefront keeps 3 steps of tiles in flight.
+// Ring of 3 step slots: each wavefront keeps up to 3 steps of tiles in
+// flight (60 loads for bf16 head_dim 128, at the hardware's limit of 63
+// outstanding vector memory operations per wavefront, so a deeper ring adds
+// nothing but registers; measured equal to a ring of 4 on MI355X).
 // Wavefronts per compute unit by step size (measured on MI355X): with 16 KiB
-// steps (bf16, head_dim 128) two wavefronts per CU (~48 KiB ahead each, ~24
-// MiB over the chip) read the scattered tiles fastest; fewer, deeper streams
-// beat more, shallower ones there.  Smaller steps (FP8 or head_dim 64) do
-// best with four.
+// steps (bf16, head_dim 128) two wavefronts per CU read the scattered tiles
+// fastest; fewer, deeper streams beat more, shallower ones there.  Smaller
+// steps (FP8 or head_dim 64) do best with four.
 #ifndef PA_STREAM_RING
-#define PA_STREAM_RING 4  // build-time tuning knob
+#define PA_STREAM_RING 3  // build-time tuning knob
 #endif
 constexpr int kRing = PA_STREAM_RING;
 
@@ -370,6 +403,7 @@ struct Slot {
   int b, h;
   int flags;  // kFirst / kLast step of its segment; kFinal output (else partial state)
   int row0;   // partial state: row of the group's first query head
+  bool real;  // false: a filler step (loads repeated, nothing computed)
 };
 
 template <bool FP8, int D, int BS>
@@ -381,34 +415,32 @@ void decode_mfma_stream(const DecodeArgs a) {
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int G = a.group;
-  if (blockIdx.x == 0 && lane == 0) *a.header = a.slices;  // for the merge
-  const int r = slice_of_wave(blockIdx.x, a.slices);
-  const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, a.slices);
-  const int64_t g0 = (int64_t)r * sp.per;
-  const int64_t g_end = min(g0 + sp.per, sp.total);
+  const int W = a.slices;
+  if (blockIdx.x == 0 && lane == 0) a.header[kHdrSlices] = W;  // for the merge
+  const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, W);
+  const int r = slice_of_wave(blockIdx.x, W);
+  int64_t g0, g_end;
+  slice_bounds(sp, r, g0, g_end);
   if (g0 >= g_end) return;
-  const int total_steps = (int)(g_end - g0);
 
   const const_i32 lens = (const_i32)a.context_lens;
   const const_i32 tables = (const_i32)a.block_tables;
 
-  // ---- issue-side cursor over the slice's runs --------------------------
-  int cb, ci;  // run (sequence cb, KV head ch) and its step index
+  // ---- issue-side cursor over the slice's runs ----------------------------
+  int64_t left = g_end - g0;  // slice steps not yet issued
+  int cb, ci;                 // run (sequence cb, KV head ch) and its step index
   int ch = (int)(g0 / sp.per_head);
   locate_step(a.context_lens, a.num_seqs, a.max_len, g0 - (int64_t)ch * sp.per_head, cb, ci);
   int clen = clamp_len(lens[cb], a.max_len);
   int cn = steps_of_len(clen);
-  int left = total_steps;                   // slice steps not yet issued
-  int cseg_end = min(cn, ci + left);        // end step (in the run) of this segment
-  int cseg_start = ci;
+  int cseg_start = ci;                                     // the segment (run part inside the
+  int cseg_end = (int)min((int64_t)cn, (int64_t)ci + left);  // slice), in run steps
   int cflags_run = (ci == 0 && cseg_end == cn) ? kFinal : 0;
-  int crow0 = r * 2 * G;                    // the slice's first run -> rows (2r)*G..
+  int crow0 = r * 2 * G;  // the slice's first run -> rows (2r)*G..
+  int pending = 0;        // real steps issued and not yet computed
 
   // per-lane offsets inside a step's tiles (see attend)
-  const int ktok = 8 * (col >> 2) + (col & 3);
-  const int kblk = (BS == 16) ? (ktok >> 4) : 0;
-  const int krow = (BS == 16) ? (ktok & 15) : ktok;
-  const uint32_t koff = (uint32_t)krow * C::kRowK + (uint32_t)grp * 16;
+  const uint32_t koff = ((uint32_t)grp * BS + (uint32_t)col) * 16;
   const int vblk = (BS == 16) ? (grp >> 1) : 0;
   const uint32_t vtok = (BS == 16) ? (uint32_t)(8 * (grp & 1)) : (uint32_t)(8 * grp);
   const uint32_t voff = (uint32_t)col * C::kRowV + vtok * C::kElt;
@@ -418,10 +450,13 @@ void decode_mfma_stream(const DecodeArgs a) {
   const __bf16* qbase = reinterpret_cast<const __bf16*>(a.q);
 
   const char* kp = kc;
+  const char* kp1 = kc;
   const char* vp = vc;
   const __bf16* qp = qbase;
 
-  auto issue = [&](S& sl, const bool real) {
+  auto issue = [&](S& sl) {
+    const bool real = left > 0;
+    sl.real = real;
     if (real) {
       if (ci == cseg_end) {  // next run of the slice
         if (++cb == a.num_seqs) { cb = 0; ++ch; }
@@ -429,7 +464,7 @@ void decode_mfma_stream(const DecodeArgs a) {
         cn = steps_of_len(clen);
         ci = 0;
         cseg_start = 0;
-        cseg_end = min(cn, left);
+        cseg_end = (int)min((int64_t)cn, left);
         cflags_run = (cseg_end == cn) ? kFinal : 0;
         crow0 = (r * 2 + 1) * G;
       }
@@ -449,17 +484,19 @@ void decode_mfma_stream(const DecodeArgs a) {
       p1 = (p1 < 0 || (int64_t)p1 >= a.num_blocks) ? 0 : p1;
       const int64_t tile0 = ((int64_t)p0 * a.num_kv_heads + ch) * C::kTile;
       const int64_t tile1 = ((int64_t)p1 * a.num_kv_heads + ch) * C::kTile;
-      kp = kc + (kblk ? tile1 : tile0) + koff;
+      kp = kc + tile0 + koff;
+      kp1 = (BS == 16) ? kc + tile1 + koff : kp + 16 * 16;
       vp = vc + (vblk ? tile1 : tile0) + voff;
       qp = qbase + ((size_t)cb * a.num_q_heads + (size_t)ch * G + qhead) * D;
       ++ci;
       --left;
+      ++pending;
     }
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int j = 0; j < C::kKLoads; ++j)
-        sl.k[m][j] = stream_load<u32x4>(kp + 4 * m * C::kRowK + j * 64);
+    for (int j = 0; j < C::kKLoads; ++j) {
+      sl.k[0][j] = stream_load<u32x4>(kp + j * 4 * C::kChunkRow);
+      sl.k[1][j] = stream_load<u32x4>(kp1 + j * 4 * C::kChunkRow);
+    }
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt) {
       if constexpr (FP8) sl.v[dt].w = stream_load<u32x2>(vp + dt * 16 * C::kRowV);
@@ -493,14 +530,16 @@ void decode_mfma_stream(const DecodeArgs a) {
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(sl, 1, c), sl.q[c], s1, 0, 0, 0);
     }
     const bool partial = sl.base + kStepTokens > sl.t1;
-    const int tok0 = sl.base + 8 * grp;
-    const int valid = partial ? min(max(sl.t1 - tok0, 0), 8) : 8;
+    bool zok[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zok[i] = !partial || sl.base + qk_token(grp, i) < sl.t1;
     float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = (i < valid) ? __fmul_rn(z[i], c2) : -INFINITY;
+    for (int i = 0; i < 8; ++i) z[i] = zok[i] ? __fmul_rn(z[i], c2) : -INFINITY;
     if (partial) {
+      const int vvalid = min(max(sl.t1 - (sl.base + 8 * grp), 0), 8);
 #pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<FP8>(sl.v[dt], valid);
+      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<FP8>(sl.v[dt], vvalid);
     }
     float mx = z[0];
 #pragma unroll
@@ -517,12 +556,10 @@ void decode_mfma_stream(const DecodeArgs a) {
     float p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = (i < valid) ? exp2f(z[i] - m_run) : 0.f;
+      p[i] = zok[i] ? exp2f(z[i] - m_run) : 0.f;
       l_run += p[i];
     }
-    bf16x8 pop;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pop[i] = (__bf16)p[i];
+    const bf16x8 pop = p_operand(p);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<FP8>(sl.v[dt]), pop, acc[dt], 0, 0, 0);
@@ -559,14 +596,18 @@ void decode_mfma_stream(const DecodeArgs a) {
     }
   };
 
+  // ---- the ring ------------------------------------------------------------
   S ring[kRing];
 #pragma unroll
-  for (int j = 0; j < kRing - 1; ++j) issue(ring[j], j < total_steps);
-  for (int k = 0; k < total_steps; k += kRing) {
+  for (int j = 0; j < kRing - 1; ++j) issue(ring[j]);
+  while (pending > 0) {
 #pragma unroll
     for (int j = 0; j < kRing; ++j) {
-      issue(ring[(j + kRing - 1) % kRing], k + j + kRing - 1 < total_steps);
-      if (k + j < total_steps) compute(ring[j]);
+      issue(ring[(j + kRing - 1) % kRing]);
+      if (ring[j].real) {
+        compute(ring[j]);
+        --pending;
+      }
     }
   }
 }

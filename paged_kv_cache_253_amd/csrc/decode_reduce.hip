@@ -97,22 +97,26 @@ __global__ __launch_bounds__(kFixupThreads) void auto_fixup_kernel(const ReduceA
   const int r = blockIdx.x + 1;  // boundary between slices r-1 and r
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int slices = *a.header;  // as launched by the decode
+  const int slices = a.header[kHdrSlices];  // as launched by the decode
   if (r >= slices) return;
   // every wavefront of the workgroup derives the same plan
   const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, slices);
-  const int64_t g = (int64_t)r * sp.per;
+  int64_t g, g_unused;
+  slice_bounds(sp, r, g, g_unused);
   if (g >= sp.total) return;
   const int h = (int)(g / sp.per_head);
   int b, i;
   locate_step(a.context_lens, a.num_seqs, a.max_len, g - (int64_t)h * sp.per_head, b, i);
-  if (i == 0 || i > sp.per) return;  // not a cut, or an earlier boundary cuts the same run
-  const int n = steps_of_len(clamp_len(a.context_lens[b], a.max_len));
+  if (i == 0) return;                 // the boundary does not cut a run
   const int64_t gs = g - i;           // first step of the run
+  const int r_first = slice_of_step(sp, gs);
+  if (r != r_first + 1) return;       // an earlier boundary cuts the same run
+  const int n = steps_of_len(clamp_len(a.context_lens[b], a.max_len));
   const int64_t ge = gs + n;          // one past its last step
-  const int r_first = r - 1;
-  const int k_first = (gs == (int64_t)r_first * sp.per) ? 0 : 1;
-  const int nparts = (int)((ge - 1) / sp.per) - r_first + 1;  // slices holding a piece
+  int64_t first_start;
+  slice_bounds(sp, r_first, first_start, g_unused);
+  const int k_first = (gs == first_start) ? 0 : 1;
+  const int nparts = slice_of_step(sp, ge - 1) - r_first + 1;  // slices holding a piece
   const int G = a.num_q_heads / a.num_kv_heads;
   auto row_of = [&](int j, int gq) -> size_t {  // piece j of the run, in slice order
     const int rr = r_first + j;

@@ -7,9 +7,11 @@
 // High-Throughput Serving", section 2), next step's tiles in flight during
 // the current one.
 //
-// QK: each K row (one token) is read by D/VEC lanes with 16-byte loads
-// (VEC elements each); the lanes' partial dot products are combined with DPP
-// row operations, leaving every lane of the row with the score.
+// QK: K tiles hold 16-byte chunks of the head dimension, token-major per
+// chunk.  Lane l takes token l % 16 of a 16-token group and chunk rows
+// 4j + l / 16, so each 16-byte load instruction reads four chunk rows of 16
+// tokens (4 x 256 contiguous bytes); the four lanes of a token finish its dot
+// product with two cross-row swaps, leaving every one of them the score.
 // PV: V tiles are dimension-major, so a lane reads VPT consecutive tokens of
 // one dimension per 16-byte load and accumulates them with the matching
 // softmax weights, which it takes from a 32-entry LDS row per query head.
@@ -61,16 +63,16 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
                                        int t1, const Target tgt) {
   constexpr int ELT = ElemBytes<E>::v;
   constexpr int VEC = 16 / ELT;          // elements per 16-byte load
-  constexpr int LPT = D / VEC;           // lanes per K row
-  constexpr int TPL = 64 / LPT;          // K rows per load instruction
-  constexpr int NK = kStep / TPL;        // K loads per lane per step
+  constexpr int NC = D / VEC;            // 16-byte chunks per K row
+  constexpr int CPL = NC / 4;            // K chunks per lane per 16-token group
+  constexpr int NK = 2 * CPL;            // K loads per lane per step (two groups)
   constexpr int VPT = VEC;               // tokens per 16-byte V load
   constexpr int CPR = kStep / VPT;       // V loads per dimension per step
   constexpr int NV = D * CPR / 64;       // V loads per lane per step
   constexpr int DSTRIDE = 64 / CPR;      // dimension stride between a lane's V loads
   constexpr int TILE = BS * D * ELT;
   constexpr int BPS = kStep / BS;        // blocks per step
-  static_assert(LPT <= 64 && NK >= 1 && NV >= 1, "shape");
+  static_assert(NC % 4 == 0 && NK >= 2 && NV >= 1 && kStep == 32, "shape");
 
   __shared__ float plds[2][G][kStep];
 
@@ -90,30 +92,35 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
     return;
   }
 
-  // q slice of this lane for every head of the group
-  const int dsl = (lane % LPT) * VEC;
-  float qf[G][VEC];
+  // q slices of this lane (chunks 4j + kq) for every head of the group
+  const int ktok = lane & 15;  // token within a 16-token group
+  const int kq = lane >> 4;    // chunk row within each group of four
+  float qf[G][CPL][VEC];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const QT* qrow = reinterpret_cast<const QT*>(a.q) + ((size_t)b * a.num_q_heads + h * G + g) * D + dsl;
+    const QT* qrow = reinterpret_cast<const QT*>(a.q) + ((size_t)b * a.num_q_heads + h * G + g) * D;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) qf[g][e] = load_q(qrow + e);
+    for (int j = 0; j < CPL; ++j)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) qf[g][j][e] = load_q(qrow + (4 * j + kq) * VEC + e);
   }
 
   float kscale = 1.0f, vscale = 1.0f;
   if constexpr (E == Elem::FP8) { kscale = a.k_scale[h]; vscale = a.v_scale[h]; }
   const float c2 = a.scale * kscale * kLog2e;  // q.k -> log2 units
 
-  // byte offsets inside the step's tiles
-  const int ktok = lane / LPT;  // + i*TPL
+  // byte offsets inside the step's tiles: load m*CPL + j reads chunk row
+  // 4j + kq of token 16m + ktok of the step
   uint32_t koff[NK];
   int kblk[NK];
 #pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    const int tok = i * TPL + ktok;
-    kblk[i] = tok / BS;
-    koff[i] = (uint32_t)(tok % BS) * D * ELT + (uint32_t)dsl * ELT;
-  }
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int tok = 16 * m + ktok;
+      kblk[m * CPL + j] = tok / BS;
+      koff[m * CPL + j] = ((uint32_t)(4 * j + kq) * BS + (uint32_t)(tok % BS)) * 16;
+    }
   const int vtok = tc * VPT;                 // first token of this lane's V chunk
   const int vblk = vtok / BS;
   const uint32_t voff = (uint32_t)(lane / CPR) * BS * ELT + (uint32_t)(vtok % BS) * ELT;
@@ -166,32 +173,37 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
   auto compute = [&](Buf& sb, int step) {
     const int base = t0 + step * kStep;
     const bool partial = base + kStep > t1;
-    float s[G][NK];
+    float s[G][2];  // scores of tokens ktok and 16 + ktok of the step
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      float kv[VEC];
-      widen16<E>(sb.k[i], kv);
+    for (int m = 0; m < 2; ++m) {
+      float dot[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float part_dot = 0.f;
+      for (int g = 0; g < G; ++g) dot[g] = 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) part_dot = fmaf(qf[g][e], kv[e], part_dot);
-        s[g][i] = xlane<OpSum, 1, LPT / 2>(part_dot);
+      for (int j = 0; j < CPL; ++j) {
+        float kv[VEC];
+        widen16<E>(sb.k[m * CPL + j], kv);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) dot[g] = fmaf(qf[g][j][e], kv[e], dot[g]);
       }
-    }
-    bool valid[NK];
 #pragma unroll
-    for (int i = 0; i < NK; ++i) valid[i] = !partial || (base + i * TPL + ktok < t1);
+      for (int g = 0; g < G; ++g) s[g][m] = xlane<OpSum, 16, 32>(dot[g]);
+    }
+    bool valid[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) valid[m] = !partial || (base + 16 * m + ktok < t1);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       // scores in log2 units: z = s * c2, so exp(scale*q.k - max) = 2^(z - m)
       float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        s[g][i] = valid[i] ? __fmul_rn(s[g][i], c2) : -INFINITY;
-        mx = fmaxf(mx, s[g][i]);
+      for (int m = 0; m < 2; ++m) {
+        s[g][m] = valid[m] ? __fmul_rn(s[g][m], c2) : -INFINITY;
+        mx = fmaxf(mx, s[g][m]);
       }
-      if constexpr (LPT < 64) mx = xlane<OpMax, LPT, 32>(mx);
+      mx = xlane<OpMax, 1, 8>(mx);  // the 16 lanes of a row hold all 32 tokens
       const float m_new = fmaxf(m_run[g], mx);
       if (wave_any(m_new > m_run[g])) {
         const float alpha = exp2f(m_run[g] - m_new);
@@ -201,10 +213,10 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
         m_run[g] = m_new;
       }
 #pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        const float p = valid[i] ? exp2f(s[g][i] - m_run[g]) : 0.f;
+      for (int m = 0; m < 2; ++m) {
+        const float p = valid[m] ? exp2f(s[g][m] - m_run[g]) : 0.f;
         l_run[g] += p;
-        if (lane % LPT == 0) plds[parity][g][i * TPL + ktok] = p;
+        if (kq == 0) plds[parity][g][16 * m + ktok] = p;
       }
     }
     __syncthreads();
@@ -240,8 +252,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
   // ---- epilogue -------------------------------------------------------------
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float l_tot = l_run[g];
-    if constexpr (LPT < 64) l_tot = xlane<OpSum, LPT, 32>(l_tot);
+    const float l_tot = xlane<OpSum, 1, 8>(l_run[g]);  // rows hold equal copies
     const float inv = vscale / l_tot;
     const int hq = h * G + g;
     const size_t row = tgt.row0 + (size_t)g * tgt.row_stride;
@@ -280,11 +291,11 @@ __global__ __launch_bounds__(64) void decode_valu_grid(const DecodeArgs a) {
 
 template <typename QT, Elem E, int D, int BS, int G>
 __global__ __launch_bounds__(64) void decode_valu_auto(const DecodeArgs a) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.header = a.slices;  // for the merge
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.header[kHdrSlices] = a.slices;  // for the merge
   const int r = slice_of_wave(blockIdx.x, a.slices);
   const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, a.slices);
-  int64_t g = (int64_t)r * sp.per;
-  const int64_t g_end = min(g + sp.per, sp.total);
+  int64_t g, g_end;
+  slice_bounds(sp, r, g, g_end);
   if (g >= g_end) return;
   int h = (int)(g / sp.per_head);
   int b, i0;

@@ -16,6 +16,9 @@ constexpr int kAutoMaxWavesPerCU = 4;
 constexpr int kAutoMinSteps = 4;
 constexpr int kXcds = 8;
 constexpr int kWorkspaceHeader = 256;
+// Workspace header word (int32 index) where the decode records its
+// wavefront count W for the merge.
+constexpr int kHdrSlices = 0;
 
 // Split modes (DecodeArgs::partition): > 0 fixed partitions of that many
 // tokens, 0 unsplit, kAuto balanced slices.
@@ -25,7 +28,7 @@ constexpr int kAuto = -1;
 struct DecodeArgs {
   void* out;                    // [S][Hq][D] q type (unsplit launches)
   const void* q;                // [S][Hq][D]
-  const void* k_cache;          // [nb][Hkv][B][D]
+  const void* k_cache;          // [nb][Hkv][D/X][B][X], X elements = 16 bytes
   const void* v_cache;          // [nb][Hkv][D][B]
   const int32_t* block_tables;  // [S][max_blocks]
   const int32_t* context_lens;  // [S]
@@ -44,7 +47,7 @@ struct DecodeArgs {
   int slices;                   // balanced split: persistent wavefronts (set by the launcher)
   int cus;                      // balanced split: compute units of the device
   int waves_per_cu;             // balanced split: 0 = the kernel's own choice
-  int* header;                  // balanced split: workspace header (slice count)
+  int* header;                  // balanced split: workspace header (kHdrSlices)
   float scale;
 };
 
@@ -67,8 +70,8 @@ struct ReduceArgs {
   const float* part_sum;
   const int32_t* context_lens;
   int max_len, num_seqs, num_q_heads, num_kv_heads, partition, max_parts;
-  int slices_max;               // balanced split: upper bound of the decode's slice count
-  const int* header;            // balanced split: slice count recorded by the decode
+  int slices_max;               // balanced split: upper bound of the decode's wavefront count
+  const int* header;            // balanced split: wavefront count recorded by the decode
 };
 
 // Each launcher returns hipErrorInvalidValue for a shape it has no kernel

@@ -7,7 +7,7 @@
 //  * Balanced ("auto"): every (b, h) is a run of 32-token steps
 //    (ceil(L_b / 32), at least 1 so an empty context still has its zero
 //    output written); the runs are laid end to end, KV head major, and a
-//    persistent grid of R wavefronts takes R equal consecutive slices.  A
+//    persistent grid of W wavefronts takes W equal consecutive slices.  A
 //    (b, h) that one slice covers whole is finished by that wavefront; one
 //    that straddles a slice boundary leaves a partial softmax state per
 //    slice, merged afterwards.  Each slice has at most two such states: its
@@ -44,11 +44,12 @@ struct Split {
   int64_t per_head;  // steps of one KV head over the whole batch
   int64_t total;     // steps of the batch (all KV heads)
   int64_t per;       // steps per slice
+  int slices;        // persistent wavefronts W
 };
 
 // Every wavefront computes the same plan from the lengths (no device-wide
-// communication).  A slice is at least kAutoMinSteps steps, so small batches
-// use fewer wavefronts instead of many tiny slices.
+// communication).  A slice is at least kAutoMinSteps steps, so small
+// batches use fewer wavefronts instead of many tiny slices.
 __device__ __forceinline__ Split plan_split(const int32_t* lens, int num_seqs, int max_len,
                                             int num_kv_heads, int slices) {
   const int lane = threadIdx.x & 63;
@@ -61,10 +62,22 @@ __device__ __forceinline__ Split plan_split(const int32_t* lens, int num_seqs, i
   Split s;
   s.per_head = tot;
   s.total = tot * num_kv_heads;
+  s.slices = slices;
   const int64_t even = (s.total + slices - 1) / slices;
   s.per = even > kAutoMinSteps ? even : kAutoMinSteps;
   return s;
 }
+
+// Steps [g0, g1) of slice c (empty for slices past the batch).
+__device__ __forceinline__ void slice_bounds(const Split& s, int c, int64_t& g0, int64_t& g1) {
+  g0 = (int64_t)c * s.per;
+  g1 = g0 + s.per;
+  if (g1 > s.total) g1 = s.total;
+  if (g0 > g1) g0 = g1;
+}
+
+// Slice holding step g (0 <= g < total).
+__device__ __forceinline__ int slice_of_step(const Split& s, int64_t g) { return (int)(g / s.per); }
 
 // Sequence b and step offset i of step `rem` (0 <= rem < per_head) of a head.
 __device__ __forceinline__ void locate_step(const int32_t* lens, int num_seqs, int max_len,
@@ -89,9 +102,9 @@ __device__ __forceinline__ void locate_step(const int32_t* lens, int num_seqs, i
   i_out = 0;
 }
 
-// Slice index of wavefront w: slices handled by one XCD (workgroups are
-// dealt to the XCDs round-robin) are consecutive, so neighbouring work --
-// e.g. sequences sharing prefix blocks -- meets in one L2.
+// Slice of wavefront w: slices handled by one XCD (workgroups are dealt to
+// the XCDs round-robin) are consecutive, so neighbouring work -- e.g.
+// sequences sharing prefix blocks -- meets in one L2.
 __device__ __forceinline__ int slice_of_wave(int w, int slices) {
   if (slices % kXcds != 0) return w;
   return (w % kXcds) * (slices / kXcds) + w / kXcds;

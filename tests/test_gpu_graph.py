@@ -25,7 +25,7 @@ def test_graph_replays_match_eager(idx, p):
     s, hq, d = batch.q.shape
     ws = None
     if p:
-        ws = torch.empty(pk.workspace_size(s, hq, w.num_kv_heads, d, batch.max_context_len, p),
+        ws = torch.zeros(pk.workspace_size(s, hq, w.num_kv_heads, d, batch.max_context_len, p),
                          dtype=torch.uint8, device=dev)
 
     def step():

@@ -328,7 +328,7 @@ def test_fp8_append_rounding_matches_oracle_on_many_values():
     vn = torch.from_numpy(vals[::-1].copy().reshape(n, hkv, d)).to(torch.bfloat16)
     ks = torch.tensor([0.5, 1.0, 2.0, 0.01], dtype=torch.float32)
     vs = torch.tensor([1.0, 0.25, 3.0, 0.7], dtype=torch.float32)
-    k_pool = torch.zeros(nb, hkv, bsz, d, dtype=torch.uint8)
+    k_pool = torch.zeros(nb, hkv, d // 16, bsz, 16, dtype=torch.uint8)
     v_pool = torch.zeros(nb, hkv, d, bsz, dtype=torch.uint8)
     slots = np.arange(n, dtype=np.int64) * bsz + 7
     k_ref, v_ref = paged.write_tokens(k_pool.numpy(), v_pool.numpy(), host_view(kn), host_view(vn),

@@ -53,14 +53,22 @@ def _decode_batch(impl, batch, k=None, v=None):
                        batch.scale, w.q_dtype, w.cache_dtype, h["ks"], h["vs"])
 
 
+def _k_pool(nb, hkv, bsz, d, x, fill, dtype):
+    """Empty chunked K pool [nb, Hkv, d/x, B, x]."""
+    return np.full((nb, hkv, d // x, bsz, x), fill, dtype)
+
+
 def _scatter_contiguous(k_c, v_c, block_size, table, k_pool, v_pool):
     """Place contiguous [L, Hkv, d] rows into pool tiles with explicit index
-    arrays (the inverse of a gather, built without the oracle)."""
-    length = k_c.shape[0]
+    arrays (the inverse of a gather, built without the oracle).  Element i
+    of a K row sits in chunk i // x at lane i % x of its token."""
+    length, _, d = k_c.shape
+    x = k_pool.shape[4]
     t = np.arange(length)
     blk = np.asarray(table)[t // block_size]
     off = t % block_size
-    k_pool[blk, :, off, :] = k_c
+    for i in range(d):
+        k_pool[blk, :, i // x, off, i % x] = k_c[:, :, i]
     for tt in range(length):  # V tiles are dimension-major
         v_pool[blk[tt], :, :, off[tt]] = v_c[tt]
 
@@ -89,12 +97,12 @@ def pin_golden_index(impl):
 
 def pin_gather_roundtrip(impl):
     rng = np.random.default_rng(1)
-    bsz, hkv, d, nb = 4, 2, 3, 9
+    bsz, hkv, d, nb = 4, 2, 6, 9
     length = 11
     table = rng.permutation(nb)[:3]
     k_c = rng.standard_normal((length, hkv, d)).astype(np.float32)
     v_c = rng.standard_normal((length, hkv, d)).astype(np.float32)
-    k_pool = np.full((nb, hkv, bsz, d), np.nan, np.float32)
+    k_pool = _k_pool(nb, hkv, bsz, d, 2, np.nan, np.float32)
     v_pool = np.full((nb, hkv, d, bsz), np.nan, np.float32)
     _scatter_contiguous(k_c, v_c, bsz, table, k_pool, v_pool)
     kg, vg = impl.gather(k_pool, v_pool, table, length, bsz)
@@ -105,8 +113,8 @@ def pin_write_whole_pool(impl):
     """Whole-pool check of an append: every targeted slot holds the new row,
     every other slot is unchanged, padding tokens write nothing."""
     rng = np.random.default_rng(2)
-    bsz, hkv, d, nb = 16, 3, 8, 7
-    k_pool = rng.integers(0, 2**16, (nb, hkv, bsz, d)).astype(np.uint16)
+    bsz, hkv, d, nb = 16, 3, 16, 7
+    k_pool = rng.integers(0, 2**16, (nb, hkv, d // 8, bsz, 8)).astype(np.uint16)
     v_pool = rng.integers(0, 2**16, (nb, hkv, d, bsz)).astype(np.uint16)
     kn = rng.integers(0, 2**16, (5, hkv, d)).astype(np.uint16)
     vn = rng.integers(0, 2**16, (5, hkv, d)).astype(np.uint16)
@@ -117,7 +125,7 @@ def pin_write_whole_pool(impl):
         if where is None:
             continue
         blk, off = where
-        kexp[blk, :, off, :] = kn[n]
+        kexp[blk, :, :, off, :] = kn[n].reshape(hkv, d // 8, 8)
         vexp[blk, :, :, off] = vn[n]
     assert np.array_equal(k2, kexp) and np.array_equal(v2, vexp)
     assert np.array_equal(k_pool[1], k2[1])  # input untouched
@@ -231,6 +239,7 @@ def pin_library_sdpa(impl):
 
 def _brute_decode(q, k_pool, v_pool, tables, lens, bsz, scale, group):
     """Pure-Python loops: gather by the index map, then softmax and sum."""
+    x = len(k_pool[0][0][0][0])
     out = []
     for b in range(len(lens)):
         rows = []
@@ -240,7 +249,7 @@ def _brute_decode(q, k_pool, v_pool, tables, lens, bsz, scale, group):
             for t in range(lens[b]):
                 blk = tables[b][t // bsz]
                 off = t % bsz
-                ks.append([float(k_pool[blk][h][off][i]) for i in range(len(q[b][hq]))])
+                ks.append([float(k_pool[blk][h][i // x][off][i % x]) for i in range(len(q[b][hq]))])
                 vs.append([float(v_pool[blk][h][i][off]) for i in range(len(q[b][hq]))])
             z = [scale * sum(float(q[b][hq][i]) * kk[i] for i in range(len(kk))) for kk in ks]
             zmax = max(z)
@@ -258,7 +267,7 @@ def pin_brute_force(impl):
     lens = [1, 2, 3, 5]
     tables = [list(rng.permutation(nb)[:3]) for _ in lens]
     q = rng.standard_normal((4, hkv * g, d)).astype(np.float32)
-    k_pool = rng.standard_normal((nb, hkv, bsz, d)).astype(np.float32)
+    k_pool = rng.standard_normal((nb, hkv, d // 2, bsz, 2)).astype(np.float32)
     v_pool = rng.standard_normal((nb, hkv, d, bsz)).astype(np.float32)
     got = impl.decode(q, k_pool, v_pool, np.array(tables), np.array(lens), bsz,
                       0.5, "f32", "f32")
@@ -289,7 +298,7 @@ def pin_paged_equals_unpaged(impl):
     v_c = rng.standard_normal((length, hkv, d)).astype(np.float32)
     q = rng.standard_normal((1, hkv * g, d)).astype(np.float32)
     table = rng.permutation(nb)[:5]
-    k_pool = np.full((nb, hkv, bsz, d), np.nan, np.float32)
+    k_pool = _k_pool(nb, hkv, bsz, d, 4, np.nan, np.float32)
     v_pool = np.full((nb, hkv, d, bsz), np.nan, np.float32)
     _scatter_contiguous(k_c, v_c, bsz, table, k_pool, v_pool)
     paged_out = impl.decode(q, k_pool, v_pool, table[None], np.array([length]), bsz,
@@ -398,7 +407,7 @@ def pin_fp8_write_then_decode(impl):
     scale back, so a one-token sequence returns the dequantised new row."""
     rng = np.random.default_rng(16)
     hkv, d, bsz, nb = 2, 16, 32, 3
-    k_pool = np.zeros((nb, hkv, bsz, d), np.uint8)
+    k_pool = np.zeros((nb, hkv, d // 16, bsz, 16), np.uint8)
     v_pool = np.zeros((nb, hkv, d, bsz), np.uint8)
     kn = rng.standard_normal((1, hkv, d)).astype(np.float32)
     vn = rng.standard_normal((1, hkv, d)).astype(np.float32)
@@ -458,7 +467,7 @@ def test_oracle_decode_partials_contract():
 
 
 def test_oracle_rejects_duplicate_slots():
-    k = np.zeros((2, 1, 16, 4), np.float32)
+    k = np.zeros((2, 1, 1, 16, 4), np.float32)
     v = np.zeros((2, 1, 4, 16), np.float32)
     rows = np.ones((2, 1, 4), np.float32)
     with pytest.raises(ValueError):
@@ -489,6 +498,17 @@ def _bad_gather_v_layout(k_pool, v_pool, table_row, length, block_size):
     for t in range(length):  # reads V as if it were token-major like K
         blk, off = paged.slot_of(table_row, t, block_size)
         v[t] = v_pool.reshape(v_pool.shape[0], v_pool.shape[1], block_size, -1)[blk, :, off, :]
+    return k, v
+
+
+def _bad_gather_k_token_major(k_pool, v_pool, table_row, length, block_size):
+    _, v = paged.gather(k_pool, v_pool, table_row, length, block_size)
+    k = np.empty_like(v)
+    nb, hkv = k_pool.shape[:2]
+    flat = k_pool.reshape(nb, hkv, block_size, -1)  # ignores the 16-byte chunking
+    for t in range(length):
+        blk, off = paged.slot_of(table_row, t, block_size)
+        k[t] = flat[blk, :, off, :]
     return k, v
 
 
@@ -562,6 +582,7 @@ def _mk_decode(**over):
 MUTANTS = {
     "index-off-by-one": dict(slot_of=_bad_slot_of),
     "v-layout-transposed": dict(gather=_bad_gather_v_layout),
+    "k-layout-token-major": dict(gather=_bad_gather_k_token_major),
     "scale-dropped": dict(attention=_bad_attention_no_scale),
     "gqa-interleaved": dict(attention=_bad_attention_gqa_modulo),
     "score-sign": dict(attention=_bad_attention_sign),

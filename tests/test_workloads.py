@@ -88,7 +88,10 @@ def test_batch_structure(idx):
         assert (batch.ref_counts[batch.block_tables[0, :128]] == 3).all()
     # the slot of the new token is poisoned before the write
     blk, off = divmod(int(batch.slot_mapping[0]), bsz)
-    assert np.isnan(batch.k_pool[blk, :, off, :].float().numpy()).all()
+    assert batch.k_pool.dim() == 5 and batch.k_pool.shape[3] == bsz
+    assert batch.k_pool.shape[2] * batch.k_pool.shape[4] == w.head_dim
+    assert batch.k_pool.shape[4] * batch.k_pool.element_size() == 16
+    assert np.isnan(batch.k_pool[blk, :, :, off, :].float().numpy()).all()
 
 
 def test_batch_is_seeded():
@@ -121,7 +124,7 @@ def test_fp8_batch_codes_and_scales():
     batch = make_batch(w, num_seqs=2, lens=np.array([100, 64]))
     assert batch.k_pool.dtype.itemsize == 1 and batch.k_scale.shape == (8,)
     import torch
-    deq = batch.k_pool.view(torch.float8_e4m3fn).float() * batch.k_scale[None, :, None, None]
+    deq = batch.k_pool.view(torch.float8_e4m3fn).float() * batch.k_scale[None, :, None, None, None]
     assert deq.abs().max() <= 448 * batch.k_scale.max() + 1e-6
     assert math.isclose(float(deq.std()), 1.0, rel_tol=0.05)
 
@@ -134,3 +137,15 @@ def test_relayouts_preserve_tables():
     perm = np.random.default_rng(0).permutation(u.num_blocks)
     p = permute_blocks(u, perm)
     assert (p.k_pool[p.block_tables[1, 5]] == u.k_pool[u.block_tables[1, 5]]).all()
+
+
+def test_chunk_k_pool_keeps_each_token_row():
+    import torch
+    from workloads import chunk_k_pool
+    k = torch.randn(3, 2, 16, 64, dtype=torch.float32)
+    for t in (k, k.to(torch.bfloat16), (k * 10).to(torch.float8_e4m3fn).view(torch.uint8)):
+        c = chunk_k_pool(t)
+        x = 16 // t.element_size()
+        assert tuple(c.shape) == (3, 2, 64 // x, 16, x)
+        for blk, h, off in ((0, 0, 0), (2, 1, 15), (1, 0, 7)):
+            assert torch.equal(c[blk, h, :, off, :].reshape(-1), t[blk, h, off])

@@ -9,6 +9,6 @@ here.
 from .accounting import (ELEMENT_BYTES, decode_bytes, kv_bytes,  # noqa: F401
                          kv_bytes_per_token, write_bytes)
 from .allocator import BlockManager, Sequence  # noqa: F401
-from .batch import (WORKLOADS, Batch, Workload, contiguous_layout,  # noqa: F401
+from .batch import (WORKLOADS, Batch, Workload, chunk_k_pool, contiguous_layout,  # noqa: F401
                     draw_lens, extract_sequences, host_view, make_batch,
                     permute_blocks, unshare)

@@ -111,7 +111,7 @@ class Batch:
     slot_mapping: np.ndarray          # int64 [S], slot of each new token
     ref_counts: np.ndarray            # int32 [num_blocks]
     q: torch.Tensor                   # [S, Hq, d] q dtype
-    k_pool: torch.Tensor              # [nb, Hkv, B, d] cache storage
+    k_pool: torch.Tensor              # [nb, Hkv, d/x, B, x] cache storage, x = 16 B / elt
     v_pool: torch.Tensor              # [nb, Hkv, d, B] cache storage
     k_new: torch.Tensor               # [S, Hkv, d] source dtype
     v_new: torch.Tensor
@@ -163,6 +163,14 @@ def _randn(shape, gen, device):
 
 def _store(x: torch.Tensor, dtype: str) -> torch.Tensor:
     return x.to(TORCH_DTYPE[dtype]) if dtype != "fp8_e4m3" else x
+
+
+def chunk_k_pool(k: torch.Tensor) -> torch.Tensor:
+    """Token-major ``[nb, Hkv, B, d]`` K storage -> the pool's chunked layout
+    ``[nb, Hkv, d/x, B, x]`` (x elements = 16 bytes).  Moves elements only."""
+    nb, hkv, bsz, d = k.shape
+    x = 16 // k.element_size()
+    return k.view(nb, hkv, bsz, d // x, x).permute(0, 1, 3, 2, 4).contiguous()
 
 
 def make_batch(w: Workload, seed: int | None = None, device="cpu",
@@ -260,7 +268,7 @@ def make_batch(w: Workload, seed: int | None = None, device="cpu",
             v_pool.masked_fill_(bad[:, None, None, :], float("nan"))
 
     return Batch(w, seed, lens, tables, slot_mapping, refs, q.contiguous(),
-                 k_pool.contiguous(), v_pool.contiguous(), kn.contiguous(),
+                 chunk_k_pool(k_pool), v_pool.contiguous(), kn.contiguous(),
                  vn.contiguous(), k_scale, v_scale,
                  {"shared_blocks": shared_blocks, "poison": poison})
 
