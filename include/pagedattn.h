@@ -251,6 +251,35 @@ pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_by
                            int partition_size, pa_dtype out_dtype,
                            hipStream_t stream);
 
+/*
+ * pa_copy_blocks -- copy whole blocks inside the pools (copy-on-write).
+ *
+ * When a sequence is about to write a token into a block that other
+ * sequences also reference, the engine gives it a private copy of that one
+ * block first ("AI Inference Serving at Scale", section 3, copy-on-write
+ * sharing; "vLLM & High-Throughput Serving", copy-on-write prefix caching).
+ * The caller's block manager picks the pairs and updates reference counts
+ * and block tables; this call copies the bytes: for each pair i, the K and
+ * V data of every KV head of block src_i is copied to block dst_i.
+ *
+ *   k_cache, v_cache  the pools (layout above), element cache_dtype; a
+ *                  block is num_kv_heads * block_size * head_dim elements
+ *                  of each pool, contiguous
+ *   block_mapping  [num_pairs][2] int64, device: (src_i, dst_i)
+ *   num_blocks     blocks in each pool
+ *
+ * Contract: the dst ids are distinct and none is also a src, so the pairs
+ * are independent and their order does not matter.  Pairs with an id
+ * outside [0, num_blocks) are skipped (no access leaves the pools).
+ * Errors: PA_ERR_INVALID_ARG for null pools, a null mapping with
+ * num_pairs > 0, or negative counts; PA_ERR_UNSUPPORTED for shapes outside
+ * head_dim {64, 128} and block_size {16, 32}; PA_ERR_HIP for a failed
+ * launch.  num_pairs == 0 does nothing.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                         int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                         int64_t num_blocks, pa_dtype cache_dtype, hipStream_t stream);
+
 /* pa_status_string -- static, human-readable name of a status code. */
 const char* pa_status_string(pa_status status);
 

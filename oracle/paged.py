@@ -169,6 +169,34 @@ def write_tokens(k_pool: np.ndarray, v_pool: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# copy-on-write block copy
+# --------------------------------------------------------------------------
+
+def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray,
+                block_mapping: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Copy whole blocks, every KV head, for each (src, dst) pair; return
+    new pools.
+
+    When a sequence is about to write into a block other sequences share,
+    it gets a private copy of that one block ("AI Inference Serving at
+    Scale", section 3, copy-on-write sharing; "vLLM & High-Throughput
+    Serving", copy-on-write prefix caching).  The pairs must be
+    independent: distinct destinations, none of them also a source (else
+    the result would depend on the order); a violation raises.
+    """
+    pairs = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    dst = pairs[:, 1]
+    if len(np.unique(dst)) != len(dst) or np.isin(dst, pairs[:, 0]).any():
+        raise ValueError("copy pairs must have distinct destinations that are not sources")
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    for src, d in pairs:
+        k_out[d] = k_pool[src]
+        v_out[d] = v_pool[src]
+    return k_out, v_out
+
+
+# --------------------------------------------------------------------------
 # attention
 # --------------------------------------------------------------------------
 

@@ -20,7 +20,7 @@ import os
 
 import torch
 
-__all__ = ["PagedAttnError", "load", "kv_cache_write", "decode", "decode_partitions",
+__all__ = ["PagedAttnError", "load", "kv_cache_write", "copy_blocks", "decode", "decode_partitions",
            "decode_reduce", "workspace_size", "new_workspace", "workspace_views", "default_partition_size",
            "PARTITION_AUTO", "LIB_PATH"]
 
@@ -62,6 +62,8 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_reduce.restype = i32
     lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pa_decode_workspace_size.restype = szt
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]
+    lib.pa_copy_blocks.restype = i32
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -166,6 +168,23 @@ def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tens
                                   _dtype_code(k_new), _dtype_code(k_cache),
                                   _ptr(k_scale), _ptr(v_scale), _stream(k_cache))
     _check("pa_kv_cache_write", st)
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                block_mapping: torch.Tensor) -> None:
+    """``pa_copy_blocks``: copy block src to dst in both pools for each row
+    (src, dst) of the int64 device tensor ``block_mapping [n, 2]``."""
+    nb, hkv, bsz, d = _k_pool_shape(k_cache)
+    if tuple(v_cache.shape) != (nb, hkv, d, bsz) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("V pool does not match the K pool")
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be int64 [n, 2]")
+    if not block_mapping.is_contiguous():
+        raise ValueError("block_mapping must be contiguous")
+    st = load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
+                               int(block_mapping.shape[0]), hkv, d, bsz, nb,
+                               _dtype_code(k_cache), _stream(k_cache))
+    _check("pa_copy_blocks", st)
 
 
 def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,

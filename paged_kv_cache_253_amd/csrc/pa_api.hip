@@ -161,6 +161,26 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new, void* k_cache,
   return from_hip(pa::launch_cache_write(a, src, cache, head_dim, block_size, stream));
 }
 
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                         int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                         int64_t num_blocks, pa_dtype cache_dtype, hipStream_t stream) {
+  if (num_pairs < 0 || num_kv_heads < 1 || num_blocks < 1) return PA_ERR_INVALID_ARG;
+  Elem cache;
+  if (!to_elem(cache_dtype, &cache)) return PA_ERR_INVALID_ARG;
+  if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
+  if (!k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;  // an empty mapping may come with a null pointer
+  if (!block_mapping) return PA_ERR_INVALID_ARG;
+  const int elt = cache == Elem::F32 ? 4 : (cache == Elem::BF16 ? 2 : 1);
+  pa::CopyArgs a;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.mapping = block_mapping;
+  a.num_blocks = num_blocks;
+  a.block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elt;
+  a.num_pairs = num_pairs;
+  if (a.block_bytes > (int64_t)65535 * 4096) return PA_ERR_UNSUPPORTED;  // grid z limit
+  return from_hip(pa::launch_copy_blocks(a, stream));
+}
+
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, int max_blocks_per_seq,
                     const int32_t* context_lens, int max_context_len, int num_seqs,

@@ -63,6 +63,15 @@ struct WriteArgs {
   int num_tokens, num_kv_heads;
 };
 
+struct CopyArgs {
+  void* k_cache;
+  void* v_cache;
+  const int64_t* mapping;       // [num_pairs][2] (src, dst) block ids
+  int64_t num_blocks;
+  int64_t block_bytes;          // one block of one pool: Hkv * B * D * elt
+  int num_pairs;
+};
+
 struct ReduceArgs {
   void* out;
   const float* part_out;
@@ -84,5 +93,6 @@ hipError_t launch_cache_write(const WriteArgs& a, Elem src, Elem cache, int head
                               int block_size, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, Elem out, int head_dim, hipStream_t stream);
 hipError_t launch_auto_fixup(const ReduceArgs& a, Elem out, int head_dim, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 
 }  // namespace pa

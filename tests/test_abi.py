@@ -31,8 +31,9 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["pa_decode", "pa_decode_reduce", "pa_decode_workspace_size",
-                                    "pa_kv_cache_write", "pa_status_string"]
+    assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_reduce",
+                                    "pa_decode_workspace_size", "pa_kv_cache_write",
+                                    "pa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -132,6 +133,25 @@ def test_cache_write_rejects(lib):
     assert call(src=FP8, cache=FP8) == UNSUPPORTED
     assert call(cache=FP8) == INVALID          # fp8 cache needs scales
     assert call(n=0) == 0                       # empty append is a no-op
+
+
+def test_copy_blocks_rejects(lib):
+    c = lib.pa_copy_blocks
+    ok = dict(kc=FAKE, vc=FAKE, m=FAKE, n=4, hkv=8, d=128, bs=16, nb=64, dt=BF16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return c(a["kc"], a["vc"], a["m"], a["n"], a["hkv"], a["d"], a["bs"], a["nb"], a["dt"], None)
+    assert call(kc=None) == INVALID
+    assert call(m=None) == INVALID
+    assert call(n=-1) == INVALID
+    assert call(hkv=0) == INVALID
+    assert call(nb=0) == INVALID
+    assert call(dt=7) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(bs=8) == UNSUPPORTED
+    assert call(n=0) == 0                       # no pairs: nothing to do
+    assert call(n=0, m=None) == 0               # (an empty tensor's pointer may be null)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -26,7 +26,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 def _impl(**over):
     """The oracle's functions as a namespace, optionally with replacements."""
-    ns = dict(slot_of=paged.slot_of, gather=paged.gather,
+    ns = dict(slot_of=paged.slot_of, gather=paged.gather, copy_blocks=paged.copy_blocks,
               write_tokens=paged.write_tokens, attention=paged.attention,
               decode=paged.decode, partial=paged.partial, merge=paged.merge,
               e4m3_to_f64=codecs.e4m3_to_f64, e4m3_encode=codecs.e4m3_encode)
@@ -424,6 +424,39 @@ def pin_fp8_write_then_decode(impl):
     assert np.array_equal(out[0], deq[np.arange(4) // 2])
 
 
+def pin_copy_on_write(impl):
+    """Copy-on-write: a sequence that shares a partly filled block forks it
+    before appending.  After the copy and the append, the forked sequence
+    reads the shared tokens plus its new one, every other sequence reads
+    what it read before, and every block outside the copy targets keeps its
+    bits; dependent pairs are refused."""
+    rng = np.random.default_rng(17)
+    bsz, hkv, d, nb = 4, 2, 8, 10
+    k_pool = rng.standard_normal((nb, hkv, d // 4, bsz, 4)).astype(np.float32)
+    v_pool = rng.standard_normal((nb, hkv, d, bsz)).astype(np.float32)
+    shared = [3, 7]                 # prefix of 6 tokens: block 7 holds tokens 4, 5
+    table_a, table_b = list(shared), list(shared)
+    before_b = impl.gather(k_pool, v_pool, np.array(table_b), 6, bsz)
+    table_a[1] = 9                  # a forks block 7 into free block 9
+    k2, v2 = impl.copy_blocks(k_pool, v_pool, np.array([[7, 9]]))
+    kn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    k3, v3 = impl.write_tokens(k2, v2, kn, vn, np.array([9 * bsz + 2]), bsz, "f32", "f32")
+    ka, va = impl.gather(k3, v3, np.array(table_a), 7, bsz)
+    kb, vb = impl.gather(k3, v3, np.array(table_b), 6, bsz)
+    assert np.array_equal(ka[:6], before_b[0]) and np.array_equal(va[:6], before_b[1])
+    assert np.array_equal(ka[6], kn[0]) and np.array_equal(va[6], vn[0])
+    assert np.array_equal(kb, before_b[0]) and np.array_equal(vb, before_b[1])
+    others = [i for i in range(nb) if i != 9]
+    assert np.array_equal(k2[others], k_pool[others]) and np.array_equal(v2[others], v_pool[others])
+    for bad in ([[1, 2], [3, 2]], [[1, 2], [2, 4]]):
+        try:
+            impl.copy_blocks(k_pool, v_pool, np.array(bad))
+        except ValueError:
+            continue
+        raise AssertionError(f"dependent copy pairs accepted: {bad}")
+
+
 # ==========================================================================
 # the pins on the oracle
 # ==========================================================================
@@ -434,7 +467,7 @@ PINS = [pin_golden_index, pin_gather_roundtrip, pin_write_whole_pool,
         pin_library_sdpa, pin_brute_force, pin_brute_force_tiny_workload,
         pin_paged_equals_unpaged, pin_block_permutation, pin_shared_prefix,
         pin_split_merge, pin_e4m3_decode_table, pin_e4m3_encode,
-        pin_fp8_write_then_decode]
+        pin_fp8_write_then_decode, pin_copy_on_write]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -558,6 +591,23 @@ def _bad_write_skip_v(k_pool, v_pool, k_new, v_new, slot_mapping, block_size,
     return k2, v_pool.copy()
 
 
+def _bad_copy_k_only(k_pool, v_pool, block_mapping):
+    k2, _ = paged.copy_blocks(k_pool, v_pool, block_mapping)
+    return k2, v_pool.copy()
+
+
+def _bad_copy_first_head(k_pool, v_pool, block_mapping):
+    k2, v2 = k_pool.copy(), v_pool.copy()
+    for src, dst in np.asarray(block_mapping).reshape(-1, 2):
+        k2[dst, 0] = k_pool[src, 0]
+        v2[dst, 0] = v_pool[src, 0]
+    return k2, v2
+
+
+def _bad_copy_reversed(k_pool, v_pool, block_mapping):
+    return paged.copy_blocks(k_pool, v_pool, np.asarray(block_mapping)[:, ::-1])
+
+
 def _mk_decode(**over):
     """decode() rebuilt on top of possibly broken parts."""
     impl = _impl(**over)
@@ -591,6 +641,9 @@ MUTANTS = {
     "e4m3-exponent-bias": dict(e4m3_to_f64=_bad_e4m3_bias),
     "e4m3-truncating": dict(e4m3_encode=_bad_encode_truncate),
     "write-drops-v": dict(write_tokens=_bad_write_skip_v),
+    "copy-drops-v": dict(copy_blocks=_bad_copy_k_only),
+    "copy-first-head-only": dict(copy_blocks=_bad_copy_first_head),
+    "copy-reversed": dict(copy_blocks=_bad_copy_reversed),
 }
 
 

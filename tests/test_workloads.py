@@ -149,3 +149,22 @@ def test_chunk_k_pool_keeps_each_token_row():
         assert tuple(c.shape) == (3, 2, 64 // x, 16, x)
         for blk, h, off in ((0, 0, 0), (2, 1, 15), (1, 0, 7)):
             assert torch.equal(c[blk, h, :, off, :].reshape(-1), t[blk, h, off])
+
+
+def test_fork_for_append_copies_only_shared_blocks():
+    mgr = BlockManager(6, 16)
+    a, b = Sequence("a"), Sequence("b")
+    assert mgr.allocate_tokens(a, 20)              # blocks 0, 1
+    mgr.share(a, b, 2)
+    assert mgr.ref_count(1) == 2
+    pair = mgr.fork_for_append(b, 20)             # token 20 lives in block 1, shared
+    assert pair == (1, 2) and b.blocks == [0, 2] and a.blocks == [0, 1]
+    assert mgr.ref_count(1) == 1 and mgr.ref_count(2) == 1 and mgr.ref_count(0) == 2
+    assert mgr.fork_for_append(b, 20) is None      # now private: no copy
+    assert mgr.fork_for_append(a, 21) is None      # a holds block 1 alone again
+    c = Sequence("c")
+    mgr.share(a, c, 2)
+    while mgr.free_blocks:
+        assert mgr.allocate(Sequence("filler"))
+    assert mgr.fork_for_append(c, 17) is False     # no free block: nothing changes
+    assert c.blocks == [0, 1] and mgr.ref_count(1) == 2

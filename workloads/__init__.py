@@ -6,7 +6,7 @@ HIP library both consume what this package produces; neither is imported
 here.
 """
 
-from .accounting import (ELEMENT_BYTES, decode_bytes, kv_bytes,  # noqa: F401
+from .accounting import (ELEMENT_BYTES, copy_bytes, decode_bytes, kv_bytes,  # noqa: F401
                          kv_bytes_per_token, write_bytes)
 from .allocator import BlockManager, Sequence  # noqa: F401
 from .batch import (WORKLOADS, Batch, Workload, chunk_k_pool, contiguous_layout,  # noqa: F401

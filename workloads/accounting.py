@@ -59,3 +59,11 @@ def write_bytes(num_tokens: int, num_kv_heads: int, head_dim: int,
     rows = num_tokens * 2 * num_kv_heads * head_dim
     return (rows * ELEMENT_BYTES[src_dtype] + rows * ELEMENT_BYTES[cache_dtype]
             + num_tokens * 8)
+
+
+def copy_bytes(num_pairs: int, num_kv_heads: int, head_dim: int, block_size: int,
+               cache_dtype: str) -> int:
+    """Algorithmic bytes of a block copy: each pair reads and writes one
+    block of the K pool and one of the V pool (every KV head)."""
+    block = num_kv_heads * block_size * head_dim * ELEMENT_BYTES[cache_dtype]
+    return num_pairs * 2 * 2 * block + num_pairs * 16

@@ -10,6 +10,13 @@ list when its count reaches zero.  ``share`` adds the prefix sharing of
 Serving" section 2: a second sequence's table points at the same physical
 blocks, whose reference count goes up.
 
+``fork_for_append`` is the host half of copy-on-write ("AI Inference
+Serving at Scale" section 3; "vLLM & High-Throughput Serving", copy-on-write
+prefix caching): before a sequence writes a token into a block other
+sequences still reference, it gets a fresh block in that table slot, the
+shared block loses one reference, and the (old, new) pair is returned for
+the device copy (``pa_copy_blocks``).
+
 Physical ids come out in the order of the initial free list, so seeding
 that order with a permutation gives the shuffled pools of the workloads.
 """
@@ -78,3 +85,23 @@ class BlockManager:
                 del self._refs[blk]
                 self._free.append(blk)
         seq.blocks = []
+
+    def fork_for_append(self, seq: Sequence, position: int):
+        """Make the block holding token ``position`` of ``seq`` private.
+
+        Returns ``(src, dst)`` when the block was shared (the caller copies
+        src to dst before writing), ``None`` when ``seq`` already owns it
+        alone, and ``False`` when the pool has no free block for the copy
+        (nothing is changed then).
+        """
+        i = int(position) // self.block_size
+        blk = seq.blocks[i]
+        if self._refs[blk] == 1:
+            return None
+        if not self._free:
+            return False
+        new = self._free.pop()
+        self._refs[new] = 1
+        self._refs[blk] -= 1
+        seq.blocks[i] = new
+        return blk, new
