@@ -264,6 +264,54 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
 
 
 # --------------------------------------------------------------------------
+# several query tokens per sequence (chunked prefill, speculative verify)
+# --------------------------------------------------------------------------
+
+def query_positions(context_len: int, num_query: int) -> np.ndarray:
+    """Positions of a sequence's query tokens: they are its last
+    ``num_query`` cached tokens (their K/V were appended before attending),
+    i.e. ``L - Q .. L - 1``."""
+    if num_query > context_len:
+        raise ValueError("a sequence has more query tokens than cached tokens")
+    return np.arange(context_len - num_query, context_len)
+
+
+def prefill_chunk(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                  block_tables: np.ndarray, context_lens: np.ndarray,
+                  query_start: np.ndarray, block_size: int, scale: float,
+                  q_dtype: str, cache_dtype: str, k_scale=None, v_scale=None,
+                  seqs=None) -> np.ndarray:
+    """Attention of several new tokens per sequence over the paged cache.
+
+    Chunked prefill feeds a prompt in chunks of tokens next to the decodes
+    ("vLLM & High-Throughput Serving", section 4); speculative decoding
+    checks K drafted tokens in one pass over the context plus the
+    candidates ("AI Inference Serving at Scale", section 7; "How LLM
+    Inference Engines Work", speculative decoding).  Sequence b owns query
+    rows ``query_start[b] .. query_start[b+1] - 1`` of ``q [T, Hq, d]``;
+    they are its last Q_b cached tokens, and the token at position p
+    attends to cached tokens 0..p -- each token sees the tokens before it
+    and itself ("vLLM & High-Throughput Serving", section 1), never a later
+    one.  Returns float64 ``[T, Hq, d]``.
+    """
+    q64 = to_f64(q, q_dtype)
+    out = np.zeros(q64.shape, dtype=np.float64)
+    scale = float(np.float32(scale))
+    qs = np.asarray(query_start, dtype=np.int64)
+    for b in (range(len(qs) - 1) if seqs is None else seqs):
+        length = int(context_lens[b])
+        r0, r1 = int(qs[b]), int(qs[b + 1])
+        pos = query_positions(length, r1 - r0)
+        if r1 == r0:
+            continue
+        k, v = sequence_kv_f64(k_pool, v_pool, block_tables[b], length,
+                               block_size, cache_dtype, k_scale, v_scale)
+        for i, p in enumerate(pos):
+            out[r0 + i] = attention(q64[r0 + i], k[:p + 1], v[:p + 1], scale)
+    return out
+
+
+# --------------------------------------------------------------------------
 # split context: partial softmax states and their merge
 # --------------------------------------------------------------------------
 

@@ -27,6 +27,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 def _impl(**over):
     """The oracle's functions as a namespace, optionally with replacements."""
     ns = dict(slot_of=paged.slot_of, gather=paged.gather, copy_blocks=paged.copy_blocks,
+              prefill_chunk=paged.prefill_chunk,
               write_tokens=paged.write_tokens, attention=paged.attention,
               decode=paged.decode, partial=paged.partial, merge=paged.merge,
               e4m3_to_f64=codecs.e4m3_to_f64, e4m3_encode=codecs.e4m3_encode)
@@ -457,6 +458,103 @@ def pin_copy_on_write(impl):
         raise AssertionError(f"dependent copy pairs accepted: {bad}")
 
 
+def _prefill_case(rng, lens, qlens, hkv=2, g=2, d=8, bsz=4):
+    """Random paged pools and tables for several sequences (f32)."""
+    nb = sum(-(-L // bsz) for L in lens) + 3
+    perm = rng.permutation(nb)
+    tables, used = [], 0
+    for L in lens:
+        n = -(-L // bsz)
+        tables.append(list(perm[used:used + n]) + [-1] * 0)
+        used += n
+    width = max(len(t) for t in tables)
+    tab = np.full((len(lens), width), -1, np.int64)
+    for b, t in enumerate(tables):
+        tab[b, :len(t)] = t
+    k_pool = rng.standard_normal((nb, hkv, d // 2, bsz, 2)).astype(np.float32)
+    v_pool = rng.standard_normal((nb, hkv, d, bsz)).astype(np.float32)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int64)
+    q = rng.standard_normal((int(qs[-1]), hkv * g, d)).astype(np.float32)
+    return q, k_pool, v_pool, tab, np.array(lens), qs, bsz, g
+
+
+def _brute_prefill(q, k_pool, v_pool, tables, lens, qs, bsz, scale, group):
+    """Pure-Python loops: each query row over the tokens up to its position."""
+    x = len(k_pool[0][0][0][0])
+    out = np.zeros(q.shape)
+    for b in range(len(lens)):
+        nq = int(qs[b + 1] - qs[b])
+        for i in range(nq):
+            p = int(lens[b]) - nq + i
+            for hq in range(q.shape[1]):
+                h = hq // group
+                z, vs = [], []
+                for t in range(p + 1):
+                    blk, off = tables[b][t // bsz], t % bsz
+                    kk = [float(k_pool[blk][h][e // x][off][e % x]) for e in range(q.shape[2])]
+                    z.append(scale * sum(float(q[qs[b] + i][hq][e]) * kk[e] for e in range(q.shape[2])))
+                    vs.append([float(v_pool[blk][h][e][off]) for e in range(q.shape[2])])
+                zm = max(z)
+                w = [math.exp(v_ - zm) for v_ in z]
+                tot = sum(w)
+                out[qs[b] + i, hq] = [sum(w[t] * vs[t][e] for t in range(len(w))) / tot
+                                      for e in range(q.shape[2])]
+    return out
+
+
+def pin_prefill_brute_force(impl):
+    rng = np.random.default_rng(18)
+    q, kp, vp, tab, lens, qs, bsz, g = _prefill_case(rng, [5, 9, 3], [2, 4, 3])
+    got = impl.prefill_chunk(q, kp, vp, tab, lens, qs, bsz, 0.5, "f32", "f32")
+    want = _brute_prefill(q, kp, vp, tab, lens, qs, bsz, 0.5, g)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def pin_prefill_causal(impl):
+    """Row i never sees a token after its position; the last row of a
+    sequence is the single-query decode over the whole context, and a
+    one-token chunk is that decode too."""
+    rng = np.random.default_rng(19)
+    q, kp, vp, tab, lens, qs, bsz, g = _prefill_case(rng, [21, 13], [6, 5], d=16)
+    base = impl.prefill_chunk(q, kp, vp, tab, lens, qs, bsz, 0.7, "f32", "f32")
+    # perturb the token at position L - 2 of sequence 0: rows 0..3 (positions < L - 2) keep their bits
+    L0, Q0 = int(lens[0]), 6
+    t = L0 - 2
+    kp2, vp2 = kp.copy(), vp.copy()
+    blk, off = tab[0][t // bsz], t % bsz
+    kp2[blk, :, :, off, :] += 3.0
+    vp2[blk, :, :, off] -= 2.0
+    pert = impl.prefill_chunk(q, kp2, vp2, tab, lens, qs, bsz, 0.7, "f32", "f32")
+    assert np.array_equal(pert[:Q0 - 2], base[:Q0 - 2])
+    assert not np.allclose(pert[Q0 - 2], base[Q0 - 2])
+    assert np.array_equal(pert[qs[1]:], base[qs[1]:])       # other sequence untouched
+    for b in range(2):
+        last = int(qs[b + 1]) - 1
+        dec = impl.decode(q[last:last + 1], kp, vp, tab[b:b + 1], lens[b:b + 1], bsz, 0.7,
+                          "f32", "f32")
+        np.testing.assert_allclose(base[last], dec[0], rtol=1e-13, atol=1e-14)
+
+
+def pin_prefill_library_sdpa(impl):
+    """One sequence laid out contiguously: the chunk's rows equal torch's
+    float64 scaled-dot-product attention of the last Q positions with an
+    explicit causal mask over the whole context."""
+    rng = np.random.default_rng(20)
+    L, Q, hkv, g, d, bsz = 40, 7, 2, 3, 16, 8
+    q, kp, vp, tab, lens, qs, bsz, g = _prefill_case(rng, [L], [Q], hkv=hkv, g=g, d=d, bsz=bsz)
+    got = impl.prefill_chunk(q, kp, vp, tab, lens, qs, bsz, 0.25, "f32", "f32")
+    kc = np.stack([kp[tab[0][t // bsz], :, :, t % bsz, :].reshape(hkv, d) for t in range(L)])
+    vc = np.stack([vp[tab[0][t // bsz], :, :, t % bsz] for t in range(L)])
+    kt = torch.from_numpy(np.repeat(kc, g, axis=1).astype(np.float64)).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(np.repeat(vc, g, axis=1).astype(np.float64)).permute(1, 0, 2)[None]
+    qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)[None]      # [1, Hq, Q, d]
+    mask = torch.from_numpy(np.arange(L)[None, :] <= (L - Q + np.arange(Q))[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(qt.contiguous(), kt.contiguous(),
+                                                           vt.contiguous(), attn_mask=mask,
+                                                           scale=0.25)
+    np.testing.assert_allclose(got, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
 # ==========================================================================
 # the pins on the oracle
 # ==========================================================================
@@ -467,7 +565,8 @@ PINS = [pin_golden_index, pin_gather_roundtrip, pin_write_whole_pool,
         pin_library_sdpa, pin_brute_force, pin_brute_force_tiny_workload,
         pin_paged_equals_unpaged, pin_block_permutation, pin_shared_prefix,
         pin_split_merge, pin_e4m3_decode_table, pin_e4m3_encode,
-        pin_fp8_write_then_decode, pin_copy_on_write]
+        pin_fp8_write_then_decode, pin_copy_on_write, pin_prefill_brute_force,
+        pin_prefill_causal, pin_prefill_library_sdpa]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -608,6 +707,49 @@ def _bad_copy_reversed(k_pool, v_pool, block_mapping):
     return paged.copy_blocks(k_pool, v_pool, np.asarray(block_mapping)[:, ::-1])
 
 
+def _bad_prefill_excludes_self(q, k_pool, v_pool, block_tables, context_lens, query_start,
+                               block_size, scale, q_dtype, cache_dtype, k_scale=None,
+                               v_scale=None, seqs=None):
+    out = np.zeros(q.shape)
+    for b in range(len(query_start) - 1):
+        r0, r1 = int(query_start[b]), int(query_start[b + 1])
+        L = int(context_lens[b])
+        k, v = paged.sequence_kv_f64(k_pool, v_pool, block_tables[b], L, block_size, cache_dtype)
+        for i in range(r1 - r0):
+            p = L - (r1 - r0) + i
+            out[r0 + i] = paged.attention(paged.to_f64(q[r0 + i], q_dtype), k[:max(p, 1)],
+                                          v[:max(p, 1)], float(np.float32(scale)))
+    return out
+
+
+def _bad_prefill_from_start(q, k_pool, v_pool, block_tables, context_lens, query_start,
+                            block_size, scale, q_dtype, cache_dtype, k_scale=None,
+                            v_scale=None, seqs=None):
+    out = np.zeros(q.shape)
+    for b in range(len(query_start) - 1):
+        r0, r1 = int(query_start[b]), int(query_start[b + 1])
+        L = int(context_lens[b])
+        k, v = paged.sequence_kv_f64(k_pool, v_pool, block_tables[b], L, block_size, cache_dtype)
+        for i in range(r1 - r0):  # positions counted from 0 instead of L - Q
+            out[r0 + i] = paged.attention(paged.to_f64(q[r0 + i], q_dtype), k[:i + 1], v[:i + 1],
+                                          float(np.float32(scale)))
+    return out
+
+
+def _bad_prefill_no_mask(q, k_pool, v_pool, block_tables, context_lens, query_start,
+                         block_size, scale, q_dtype, cache_dtype, k_scale=None,
+                         v_scale=None, seqs=None):
+    out = np.zeros(q.shape)
+    for b in range(len(query_start) - 1):
+        r0, r1 = int(query_start[b]), int(query_start[b + 1])
+        L = int(context_lens[b])
+        k, v = paged.sequence_kv_f64(k_pool, v_pool, block_tables[b], L, block_size, cache_dtype)
+        for i in range(r1 - r0):
+            out[r0 + i] = paged.attention(paged.to_f64(q[r0 + i], q_dtype), k, v,
+                                          float(np.float32(scale)))
+    return out
+
+
 def _mk_decode(**over):
     """decode() rebuilt on top of possibly broken parts."""
     impl = _impl(**over)
@@ -644,6 +786,9 @@ MUTANTS = {
     "copy-drops-v": dict(copy_blocks=_bad_copy_k_only),
     "copy-first-head-only": dict(copy_blocks=_bad_copy_first_head),
     "copy-reversed": dict(copy_blocks=_bad_copy_reversed),
+    "prefill-excludes-self": dict(prefill_chunk=_bad_prefill_excludes_self),
+    "prefill-positions-from-zero": dict(prefill_chunk=_bad_prefill_from_start),
+    "prefill-no-causal-mask": dict(prefill_chunk=_bad_prefill_no_mask),
 }
 
 
