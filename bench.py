@@ -167,6 +167,115 @@ def bench_copy(args) -> int:
     return 0
 
 
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD public spec
+
+
+def bench_prefill(args) -> int:
+    """Several query tokens per sequence: back-to-back pa_prefill_chunk
+    (+ merge) launches on a seeded batch; HBM roofline when the arithmetic
+    intensity is below the bf16 ridge, matrix-core roofline above it."""
+    import torch
+
+    import paged_kv_cache_253_amd as pk
+    from workloads import PREFILL_WORKLOADS, make_batch, prefill_bytes
+
+    w, nq = PREFILL_WORKLOADS[args.case]
+    dev = "cuda"
+    batch = make_batch(w, device=dev)
+    lens = batch.context_lens
+    qlens = np.minimum(lens, nq).astype(np.int32)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    g = torch.Generator(device=dev).manual_seed(w.seed + 1)
+    q = torch.randn((int(qs[-1]), w.num_q_heads, w.head_dim), generator=g,
+                    device=dev).to(torch.bfloat16)
+    bt = torch.from_numpy(batch.block_tables).to(dev)
+    cl = torch.from_numpy(lens).to(dev)
+    qs_d = torch.from_numpy(qs).to(dev)
+    out = torch.empty_like(q)
+    part = args.partition
+    if part is None:  # the binding's own choice, made once and reused
+        hkv = w.num_kv_heads
+        rows = max(1, 16 * (2 if w.head_dim == 128 and w.cache_dtype == "bf16" else 4)
+                   // (w.num_q_heads // hkv))
+        tiles = -(-int(qlens.max()) // rows)
+        part = 0 if len(lens) * hkv * tiles >= 1024 or batch.max_context_len <= 1024 else 512
+    ws = pk.new_workspace(int(qs[-1]), w.num_q_heads, w.num_kv_heads, w.head_dim,
+                          batch.max_context_len, part, dev) if part else None
+
+    def run():
+        pk.prefill_chunk(q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len, qs_d,
+                         int(qlens.max()), batch.scale, batch.k_scale, batch.v_scale,
+                         partition_size=part, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    acc = prefill_bytes(lens, qlens, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                        w.cache_dtype, w.q_dtype)
+    gbs = acc["total"] / (ms * 1e-3) / 1e9
+    tflops = acc["flops"] / (ms * 1e-3) / 1e12
+    mfma_bound = acc["flops"] / acc["total"] > PEAK_MFMA_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    log(f"[bench] prefill {args.case}: {len(lens)} seqs, {int(qs[-1])} query rows, P={part}: "
+        f"{ms * 1e3:.1f} us = {gbs:.0f} GB/s, {tflops:.1f} TFLOP/s "
+        f"({'matrix-core' if mfma_bound else 'HBM'} bound)")
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4),
+                "algorithmic_flops": acc["flops"]}
+        value, unit, metric = tflops, "TFLOP/s", "multi-query paged attention: achieved TFLOP/s"
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": acc["total"]}
+        value, unit, metric = gbs, "GB/s", "multi-query paged attention: achieved HBM GB/s"
+    roof.update({"kernel": "pa_prefill_chunk" + (" + pa_prefill_reduce" if part else ""),
+                 "launch_us": round(ms * 1e3, 2), "traffic": None})
+    result = {
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.cache_dtype,
+        "data": "synthetic",
+        "config": {"workload": args.case, "num_seqs": len(lens), "query_tokens_per_seq": nq,
+                   "context_tokens": acc["tokens"], "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "partition_size": part,
+                   "gbs": round(gbs, 1), "tflops": round(tflops, 2)},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        from oracle import paged
+        from workloads import extract_sequences, host_view
+        b = int(np.argmin(lens))
+        sub = extract_sequences(batch, [b])
+        ns = min(int(qlens[b]), 32)  # the sequence's last ns query rows: a chunk of its own
+        q_h = host_view(q[int(qs[b + 1]) - ns:int(qs[b + 1])])
+        qs_1 = np.array([0, ns], np.int64)
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 8.0) or n == 0:
+            paged.prefill_chunk(q_h, sub["k_pool"], sub["v_pool"], sub["block_tables"],
+                                sub["context_lens"], qs_1, w.block_size, batch.scale, "bf16",
+                                w.cache_dtype, sub["k_scale"], sub["v_scale"])
+            n += 1
+        dt = time.perf_counter() - t0
+        one = prefill_bytes(lens[b:b + 1], [ns], w.num_q_heads, w.num_kv_heads,
+                            w.head_dim, w.block_size, w.cache_dtype, w.q_dtype)
+        result["cpu_baseline"] = {
+            "value": round((one["flops"] / 1e12 if mfma_bound else one["total"] / 1e9) * n / dt, 5),
+            "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{n} oracle runs of the last {ns} query rows of sequence {b} "
+                      f"({int(lens[b])} tokens)"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,9 +291,12 @@ def main() -> int:
                     help="report the eager step time instead of the HIP graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--op", choices=["step", "copy"], default="step",
+    ap.add_argument("--op", choices=["step", "copy", "prefill"], default="step",
                     help="step: append + decode (+ merge); copy: a copy-on-write burst "
-                         "of pa_copy_blocks on the workload's pool")
+                         "of pa_copy_blocks on the workload's pool; prefill: several query "
+                         "tokens per sequence (pa_prefill_chunk), see --case")
+    ap.add_argument("--case", default="spec-verify-8b",
+                    help="prefill shape: spec-verify-8b or chunked-prefill-8b")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -192,6 +304,8 @@ def main() -> int:
         return 2
     if args.op == "copy":
         return bench_copy(args)
+    if args.op == "prefill":
+        return bench_prefill(args)
 
     import torch
 

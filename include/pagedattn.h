@@ -280,6 +280,70 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
                          int num_pairs, int num_kv_heads, int head_dim, int block_size,
                          int64_t num_blocks, pa_dtype cache_dtype, hipStream_t stream);
 
+/*
+ * pa_prefill_chunk -- attention of several new tokens per sequence over the
+ * paged cache: a prompt fed in chunks next to the decodes ("vLLM &
+ * High-Throughput Serving", section 4, chunked prefill) or K drafted tokens
+ * checked in one pass ("AI Inference Serving at Scale", section 7,
+ * speculative decoding).
+ *
+ * Sequence b owns query rows query_start[b] .. query_start[b+1]-1 of q and
+ * out.  They are its last Q_b cached tokens -- their K/V rows were appended
+ * (pa_kv_cache_write) before this call -- and row i, at position
+ * p = L_b - Q_b + i, attends to cached tokens 0 .. p (each token sees the
+ * tokens before it and itself):
+ *
+ *   out[r][hq] = sum_{t <= p} softmax_t(z_t) v_t,  z_t = scale * q[r][hq] . k_t
+ *
+ * with the GQA mapping, FP8 scales and block-table walk of pa_decode.
+ *
+ *   out            [num_query_tokens][num_q_heads][head_dim] bf16; written
+ *                  when partition_size == 0
+ *   q              [num_query_tokens][num_q_heads][head_dim] bf16, device
+ *   query_start    [num_seqs + 1] int32, device: nondecreasing,
+ *                  query_start[0] = 0, query_start[num_seqs] = num_query_tokens
+ *   max_query_len  host upper bound of Q_b (sizes the grid)
+ *   other arguments as pa_decode (cache PA_BF16 or PA_FP8_E4M3)
+ *   partition_size 0: one wavefront per (query tile, KV head, sequence)
+ *                     over its whole prefix, `out` written;
+ *                  P > 0 (a multiple of 32): fixed partitions of the prefix;
+ *                     states to `workspace`, pa_prefill_reduce merges.
+ *   workspace      P > 0: at least pa_decode_workspace_size(num_query_tokens,
+ *                  num_q_heads, num_kv_heads, head_dim, max_context_len, P)
+ *                  bytes, 256-byte aligned; the state of query row r, query
+ *                  head hq, partition p is row (r * num_q_heads + hq) * maxP + p
+ *                  of that layout (maxP = ceil(max_context_len / P)).
+ *
+ * Group sizes: G in {1, 2, 4, 8, 16}.  PA_PARTITION_AUTO is not supported
+ * here (PA_ERR_UNSUPPORTED).  Caller contract: Q_b <= L_b; a row whose
+ * position would be negative attends to nothing and gets zeros.
+ */
+pa_status pa_prefill_chunk(void* out, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int max_context_len,
+                           const int32_t* query_start, int num_query_tokens,
+                           int max_query_len, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size,
+                           int64_t num_blocks, float scale, pa_dtype q_dtype,
+                           pa_dtype cache_dtype, const float* k_scale,
+                           const float* v_scale, int partition_size,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * pa_prefill_reduce -- merge the partition states of a split
+ * pa_prefill_chunk into `out` (the merge of pa_decode_reduce, per query row:
+ * row i of sequence b merges partitions p < ceil((L_b - Q_b + i + 1) / P)).
+ * Arguments as given to pa_prefill_chunk; out_dtype PA_BF16 or PA_F32.
+ */
+pa_status pa_prefill_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                            const int32_t* context_lens, int max_context_len,
+                            const int32_t* query_start, int num_query_tokens,
+                            int max_query_len, int num_seqs, int num_q_heads,
+                            int num_kv_heads, int head_dim, int partition_size,
+                            pa_dtype out_dtype, hipStream_t stream);
+
 /* pa_status_string -- static, human-readable name of a status code. */
 const char* pa_status_string(pa_status status);
 

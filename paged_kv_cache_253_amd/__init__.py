@@ -21,6 +21,7 @@ import os
 import torch
 
 __all__ = ["PagedAttnError", "load", "kv_cache_write", "copy_blocks", "decode", "decode_partitions",
+           "prefill_chunk",
            "decode_reduce", "workspace_size", "new_workspace", "workspace_views", "default_partition_size",
            "PARTITION_AUTO", "LIB_PATH"]
 
@@ -64,6 +65,12 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_workspace_size.restype = szt
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]
     lib.pa_copy_blocks.restype = i32
+    lib.pa_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i32,
+                                     i32, i32, i64, f32, i32, i32, vp, vp, i32, vp, szt, vp]
+    lib.pa_prefill_chunk.restype = i32
+    lib.pa_prefill_reduce.argtypes = [vp, vp, szt, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
+                                      i32, vp]
+    lib.pa_prefill_reduce.restype = i32
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -185,6 +192,52 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
                                int(block_mapping.shape[0]), hkv, d, bsz, nb,
                                _dtype_code(k_cache), _stream(k_cache))
     _check("pa_copy_blocks", st)
+
+
+def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                  query_start: torch.Tensor, max_query_len: int, scale: float | None = None,
+                  k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None,
+                  partition_size: int | None = None, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """``pa_prefill_chunk`` (+ ``pa_prefill_reduce`` when split): attention
+    of each sequence's last Q_b cached tokens (rows ``query_start[b] ..
+    query_start[b+1]-1`` of ``q [T, Hq, D]``) over its prefix; returns out.
+
+    ``partition_size`` None: unsplit when the query tiles alone give the
+    device enough wavefronts, else 512-token partitions."""
+    t, hq, d = q.shape
+    nb, hkv, bsz, _ = _k_pool_shape(k_cache)
+    s = int(query_start.numel()) - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or \
+            query_start.dtype != torch.int32:
+        raise ValueError("block_tables, context_lens and query_start must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    if partition_size is None:
+        g = hq // hkv
+        rows = max(1, 16 * (2 if (q.dtype == k_cache.dtype and d == 128) else 4) // g)
+        tiles = -(-max_query_len // rows) if max_query_len else 0
+        partition_size = 0 if s * hkv * tiles >= 1024 or max_context_len <= 1024 else 512
+    if partition_size and workspace is None:
+        workspace = new_workspace(t, hq, hkv, d, max_context_len, partition_size, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().pa_prefill_chunk(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                 int(max_context_len), _ptr(query_start), t, int(max_query_len),
+                                 s, hq, hkv, d, bsz, nb, float(scale), _dtype_code(q),
+                                 _dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale),
+                                 int(partition_size), _ptr(workspace), ws_bytes, _stream(q))
+    _check("pa_prefill_chunk", st)
+    if partition_size:
+        st = load().pa_prefill_reduce(_ptr(out), _ptr(workspace), ws_bytes, _ptr(context_lens),
+                                      int(max_context_len), _ptr(query_start), t,
+                                      int(max_query_len), s, hq, hkv, d, int(partition_size),
+                                      _dtype_code(out), _stream(out))
+        _check("pa_prefill_reduce", st)
+    return out
 
 
 def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,

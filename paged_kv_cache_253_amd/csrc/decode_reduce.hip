@@ -37,7 +37,10 @@ __device__ __forceinline__ float block_combine(float x, float* scratch) {
   return r;
 }
 
-template <typename OT, int D>
+// MQ: several query tokens per sequence; output row = query token
+// query_start[b] + i (grid z = i), whose context is the tokens up to its
+// position, L_b - Q_b + i.
+template <typename OT, int D, bool MQ>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReduceArgs a) {
   constexpr int TPR = D / 4;                    // threads per partition row
   constexpr int ROWS = kReduceThreads / TPR;    // rows in flight
@@ -48,14 +51,23 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReduceArgs
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int len = clamp_len(a.context_lens[b], a.max_len);
+  int len = clamp_len(a.context_lens[b], a.max_len);
+  size_t qrow = b;
+  if constexpr (MQ) {
+    const int i = blockIdx.z;
+    const int r0 = a.query_start[b];
+    const int nq = a.query_start[b + 1] - r0;
+    if (i >= nq) return;
+    qrow = (size_t)(r0 + i);
+    len = max(min(len - nq + i + 1, len), 0);
+  }
   const int n = (len + a.partition - 1) / a.partition;
-  OT* o = reinterpret_cast<OT*>(a.out) + ((size_t)b * a.num_q_heads + hq) * D;
+  OT* o = reinterpret_cast<OT*>(a.out) + (qrow * a.num_q_heads + hq) * D;
   if (n == 0) {
     if (tid < D) o[tid] = (OT)0.0f;
     return;
   }
-  const size_t base = ((size_t)b * a.num_q_heads + hq) * a.max_parts;
+  const size_t base = (qrow * a.num_q_heads + hq) * a.max_parts;
   float mx = -INFINITY;
   for (int p = tid; p < n; p += kReduceThreads) mx = fmaxf(mx, a.part_max[base + p]);
   mx = block_combine<OpMax>(mx, scratch);
@@ -155,8 +167,14 @@ __global__ __launch_bounds__(kFixupThreads) void auto_fixup_kernel(const ReduceA
 
 template <typename OT, int D>
 hipError_t launch(const ReduceArgs& a, hipStream_t s) {
-  dim3 grid(a.num_q_heads, a.num_seqs);
-  hipLaunchKernelGGL((reduce_kernel<OT, D>), grid, dim3(kReduceThreads), 0, s, a);
+  if (a.query_start) {
+    if (a.max_query_len < 1) return hipSuccess;
+    dim3 grid(a.num_q_heads, a.num_seqs, a.max_query_len);
+    hipLaunchKernelGGL((reduce_kernel<OT, D, true>), grid, dim3(kReduceThreads), 0, s, a);
+  } else {
+    dim3 grid(a.num_q_heads, a.num_seqs);
+    hipLaunchKernelGGL((reduce_kernel<OT, D, false>), grid, dim3(kReduceThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -289,6 +289,7 @@ pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_by
   if (num_seqs == 0) return PA_OK;
   const char* w = static_cast<const char*>(workspace);
   pa::ReduceArgs a;
+  std::memset(&a, 0, sizeof a);
   a.out = out;
   a.header = reinterpret_cast<const int*>(w);
   w += l.head_bytes;
@@ -301,6 +302,110 @@ pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_by
   a.partition = partition_size; a.max_parts = l.max_parts; a.slices_max = l.slices_max;
   if (partition_size == PA_PARTITION_AUTO)
     return from_hip(pa::launch_auto_fixup(a, oe, head_dim, stream));
+  return from_hip(pa::launch_reduce(a, oe, head_dim, stream));
+}
+
+pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int max_context_len,
+                           const int32_t* query_start, int num_query_tokens, int max_query_len,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int block_size, int64_t num_blocks, float scale, pa_dtype q_dtype,
+                           pa_dtype cache_dtype, const float* k_scale, const float* v_scale,
+                           int partition_size, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || num_q_heads < 1 ||
+      num_kv_heads < 1 || max_context_len < 0 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      partition_size < 0)
+    return partition_size == PA_PARTITION_AUTO ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (!(std::isfinite(scale) && scale > 0.0f)) return PA_ERR_INVALID_ARG;
+  Elem qe, ce;
+  if (!to_elem(q_dtype, &qe) || !to_elem(cache_dtype, &ce)) return PA_ERR_INVALID_ARG;
+  if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
+  if (qe != Elem::BF16 || ce == Elem::F32) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  if (group > 16 || (group & (group - 1)) != 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 65535 ||
+      (long long)pa::prefill_query_tiles(group, max_query_len,
+                                         pa::prefill_max_column_tiles(ce, head_dim)) *
+              num_kv_heads > 65535)
+    return PA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_INVALID_ARG;
+  if (partition_size == 0 && !out) return PA_ERR_INVALID_ARG;
+  if (ce == Elem::FP8 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+
+  pa::PrefillArgs p;
+  std::memset(&p, 0, sizeof p);
+  pa::DecodeArgs& a = p.d;
+  a.out = out; a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.block_tables = block_tables; a.context_lens = context_lens;
+  a.k_scale = k_scale; a.v_scale = v_scale;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  const long long cap = (long long)max_blocks_per_seq * block_size;
+  a.cap_len = (int)std::min<long long>(cap, INT32_MAX);
+  a.max_len = (int)std::min<long long>(max_context_len, cap);
+  a.num_seqs = num_seqs; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.partition = partition_size;
+  a.scale = scale;
+  a.max_parts = 1;
+  p.query_start = query_start;
+  p.max_query_len = max_query_len;
+  if (partition_size > 0) {
+    Layout l;
+    if (!workspace_layout(num_query_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          partition_size, &l))
+      return PA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+      return PA_ERR_WORKSPACE;
+    char* w = static_cast<char*>(workspace);
+    a.part_out = reinterpret_cast<float*>(w);
+    a.part_max = reinterpret_cast<float*>(w + l.out_bytes);
+    a.part_sum = reinterpret_cast<float*>(w + l.out_bytes + l.max_bytes);
+    a.max_parts = l.max_parts;
+  }
+  if (num_seqs == 0 || max_query_len == 0 || num_query_tokens == 0) return PA_OK;
+  return from_hip(pa::launch_prefill_mfma(p, ce, head_dim, block_size, stream));
+}
+
+pa_status pa_prefill_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                            const int32_t* context_lens, int max_context_len,
+                            const int32_t* query_start, int num_query_tokens, int max_query_len,
+                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int partition_size, pa_dtype out_dtype, hipStream_t stream) {
+  if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || num_q_heads < 1 ||
+      num_kv_heads < 1 || max_context_len < 0 || partition_size <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  Elem oe;
+  if (!to_elem(out_dtype, &oe)) return PA_ERR_INVALID_ARG;
+  if (oe == Elem::FP8 || !supported_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 65535 || max_query_len > 65535) return PA_ERR_UNSUPPORTED;
+  if (!out || !workspace || !context_lens || !query_start) return PA_ERR_INVALID_ARG;
+  Layout l;
+  if (!workspace_layout(num_query_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                        partition_size, &l))
+    return PA_ERR_INVALID_ARG;
+  if (workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return PA_ERR_WORKSPACE;
+  if (num_seqs == 0 || max_query_len == 0 || num_query_tokens == 0) return PA_OK;
+  const char* w = static_cast<const char*>(workspace);
+  pa::ReduceArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.out = out;
+  a.part_out = reinterpret_cast<const float*>(w);
+  a.part_max = reinterpret_cast<const float*>(w + l.out_bytes);
+  a.part_sum = reinterpret_cast<const float*>(w + l.out_bytes + l.max_bytes);
+  a.context_lens = context_lens;
+  a.max_len = max_context_len;
+  a.num_seqs = num_seqs; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads;
+  a.partition = partition_size; a.max_parts = l.max_parts;
+  a.query_start = query_start;
+  a.max_query_len = max_query_len;
   return from_hip(pa::launch_reduce(a, oe, head_dim, stream));
 }
 

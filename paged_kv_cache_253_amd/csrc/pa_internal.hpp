@@ -51,6 +51,32 @@ struct DecodeArgs {
   float scale;
 };
 
+// Several query tokens per sequence: sequence b's query rows are
+// query_start[b] .. query_start[b+1]-1 of q / out (its last cached tokens).
+// d.num_seqs is the sequence count; d.out, d.q and the partial states are
+// indexed by query row instead of sequence.
+struct PrefillArgs {
+  DecodeArgs d;
+  const int32_t* query_start;   // [S + 1]
+  int max_query_len;
+};
+
+// Column tiles (16 MFMA columns each) of a multi-query wavefront, and the
+// query tiles of a sequence, for group size G and the longest query run.
+// A bf16 cache with head_dim 128 stops at 2 column tiles (4 would spill).
+inline int prefill_max_column_tiles(Elem cache, int head_dim) {
+  return (cache == Elem::BF16 && head_dim == 128) ? 2 : 4;
+}
+inline int prefill_column_tiles(int group, int max_query_len, int max_tiles) {
+  const long long cols = (long long)group * max_query_len;
+  const int nt = cols <= 16 ? 1 : (cols <= 32 ? 2 : 4);
+  return nt < max_tiles ? nt : max_tiles;
+}
+inline int prefill_query_tiles(int group, int max_query_len, int max_tiles) {
+  const int rows_per_tile = 16 * prefill_column_tiles(group, max_query_len, max_tiles) / group;
+  return (max_query_len + rows_per_tile - 1) / rows_per_tile;
+}
+
 struct WriteArgs {
   const void* k_new;
   const void* v_new;
@@ -81,6 +107,8 @@ struct ReduceArgs {
   int max_len, num_seqs, num_q_heads, num_kv_heads, partition, max_parts;
   int slices_max;               // balanced split: upper bound of the decode's wavefront count
   const int* header;            // balanced split: wavefront count recorded by the decode
+  const int32_t* query_start;   // several query tokens per sequence: [S + 1], else null
+  int max_query_len;
 };
 
 // Each launcher returns hipErrorInvalidValue for a shape it has no kernel
@@ -94,5 +122,7 @@ hipError_t launch_cache_write(const WriteArgs& a, Elem src, Elem cache, int head
 hipError_t launch_reduce(const ReduceArgs& a, Elem out, int head_dim, hipStream_t stream);
 hipError_t launch_auto_fixup(const ReduceArgs& a, Elem out, int head_dim, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, Elem cache, int head_dim, int block_size,
+                               hipStream_t stream);
 
 }  // namespace pa

@@ -33,7 +33,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_reduce",
                                     "pa_decode_workspace_size", "pa_kv_cache_write",
-                                    "pa_status_string"]
+                                    "pa_prefill_chunk", "pa_prefill_reduce", "pa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -152,6 +152,35 @@ def test_copy_blocks_rejects(lib):
     assert call(bs=8) == UNSUPPORTED
     assert call(n=0) == 0                       # no pairs: nothing to do
     assert call(n=0, m=None) == 0               # (an empty tensor's pointer may be null)
+
+
+def test_prefill_rejects(lib):
+    f = lib.pa_prefill_chunk
+    ok = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mb=16, cl=FAKE, ml=256, qs=FAKE, t=20,
+              mq=5, s=4, hq=32, hkv=8, d=128, bs=16, nb=64, sc=0.1, qd=BF16, cd=BF16, ks=None,
+              vs=None, p=0, ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mb"], a["cl"], a["ml"], a["qs"],
+                 a["t"], a["mq"], a["s"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["sc"],
+                 a["qd"], a["cd"], a["ks"], a["vs"], a["p"], a["ws"], a["wsb"], None)
+    assert call(qs=None) == INVALID
+    assert call(t=-1) == INVALID
+    assert call(sc=0.0) == INVALID
+    assert call(hq=24) == UNSUPPORTED          # G = 3 is not a power of two
+    assert call(hq=8 * 32) == UNSUPPORTED      # G = 32
+    assert call(qd=F32, cd=F32) == UNSUPPORTED
+    assert call(cd=FP8) == INVALID             # FP8 cache needs scales
+    assert call(p=-1) == UNSUPPORTED           # no balanced split here
+    assert call(p=48) == UNSUPPORTED           # not a multiple of 32
+    assert call(p=64) == WORKSPACE             # split without a workspace
+    assert call(d=96) == UNSUPPORTED
+    assert call(t=0, mq=0) == 0                # nothing to attend
+    r = lib.pa_prefill_reduce
+    assert r(FAKE, FAKE, 1 << 30, FAKE, 256, None, 20, 5, 4, 32, 8, 128, 64, BF16, None) == INVALID
+    assert r(FAKE, FAKE, 16, FAKE, 256, FAKE, 20, 5, 4, 32, 8, 128, 64, BF16, None) == WORKSPACE
+    assert r(FAKE, FAKE, 1 << 30, FAKE, 256, FAKE, 20, 5, 4, 32, 8, 128, 0, BF16, None) == INVALID
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -67,3 +67,26 @@ def copy_bytes(num_pairs: int, num_kv_heads: int, head_dim: int, block_size: int
     block of the K pool and one of the V pool (every KV head)."""
     block = num_kv_heads * block_size * head_dim * ELEMENT_BYTES[cache_dtype]
     return num_pairs * 2 * 2 * block + num_pairs * 16
+
+
+def prefill_bytes(context_lens, query_lens, num_q_heads: int, num_kv_heads: int,
+                  head_dim: int, block_size: int, cache_dtype: str, q_dtype: str) -> dict:
+    """Algorithmic bytes and flops of attention for several query tokens per
+    sequence: every sequence's cached K and V read once, q read and out
+    written once, the used table entries; flops 4 * head_dim per (query
+    row, query head, visible token) -- q.k and the weighted V sum, 2 flops
+    per multiply-add -- with row i of a Q-token chunk seeing L - Q + i + 1
+    tokens."""
+    lens = np.asarray(context_lens, dtype=np.int64)
+    ql = np.asarray(query_lens, dtype=np.int64)
+    elt = ELEMENT_BYTES[cache_dtype]
+    qb = ELEMENT_BYTES[q_dtype]
+    tokens = int(lens.sum())
+    kv = tokens * 2 * num_kv_heads * head_dim * elt
+    rows = int(ql.sum())
+    q_out = 2 * rows * num_q_heads * head_dim * qb
+    tables = int((-(-lens // block_size)).sum()) * 4 + len(lens) * 8
+    visible = int((ql * (lens - ql) + ql * (ql + 1) // 2).sum())  # sum over rows of (p + 1)
+    flops = 4 * head_dim * num_q_heads * visible
+    return {"kv": kv, "q_out": q_out, "tables": tables, "total": kv + q_out + tables,
+            "flops": flops, "query_rows": rows, "tokens": tokens}

@@ -102,6 +102,21 @@ WORKLOADS = {
 }
 
 
+# Several query tokens per sequence (chunked prefill, speculative verify):
+# the batch shape and the query tokens per sequence.  Speculative
+# verification checks the pages' 5 drafted tokens on the 8B-shaped batch;
+# chunked prefill feeds 512-token chunks (the pages' example size) at 8K
+# context for 8 sequences.
+PREFILL_WORKLOADS = {
+    "spec-verify-8b": (WORKLOADS[2], 5),
+    "chunked-prefill-8b": (Workload(6, "chunked-prefill-bf16", 8, 32, 8, 128, 16, "bf16", "bf16",
+                                    ("fixed", 8192), "exact", 0,
+                                    "Chunked prefill: 8 sequences at 8192 cached tokens whose "
+                                    "last 512 are the new chunk; Llama-3-8B heads (32/8, d 128), "
+                                    "bf16 KV, block 16"), 512),
+}
+
+
 @dataclass
 class Batch:
     workload: Workload
