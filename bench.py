@@ -167,6 +167,66 @@ def bench_copy(args) -> int:
     return 0
 
 
+PEAK_HOST_LINK_GBS = 64.0  # PCIe 5.0 x16, one direction (MI355X host interface)
+
+
+def bench_swap(args) -> int:
+    """Preemption swap: pa_swap_blocks moving a quarter of the workload's
+    pool to a pinned host pool and back, each direction timed separately
+    (back-to-back launches, HIP events)."""
+    import torch
+
+    import paged_kv_cache_253_amd as pk
+    from workloads import WORKLOADS, copy_bytes, make_batch
+
+    w = WORKLOADS[args.workload]
+    dev = "cuda"
+    batch = make_batch(w, device=dev)
+    n = batch.num_blocks // 4
+    kh = torch.empty((n,) + tuple(batch.k_pool.shape[1:]), dtype=batch.k_pool.dtype, pin_memory=True)
+    vh = torch.empty((n,) + tuple(batch.v_pool.shape[1:]), dtype=batch.v_pool.dtype, pin_memory=True)
+    rng = np.random.default_rng(w.seed)
+    dev_ids = rng.permutation(batch.num_blocks)[:n]
+    out_map = torch.from_numpy(np.stack([dev_ids, np.arange(n)], 1).astype(np.int64)).to(dev)
+    in_map = torch.from_numpy(np.stack([np.arange(n), dev_ids], 1).astype(np.int64)).to(dev)
+    steps = max(1, min(args.steps, 10))
+
+    def timed(fn):
+        for _ in range(min(args.warmup, 2)):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_out = timed(lambda: pk.swap_blocks(kh, vh, batch.k_pool, batch.v_pool, out_map))
+    ms_in = timed(lambda: pk.swap_blocks(batch.k_pool, batch.v_pool, kh, vh, in_map))
+    moved = copy_bytes(n, w.num_kv_heads, w.head_dim, w.block_size, w.cache_dtype) // 2  # one side
+    gbs_out = moved / (ms_out * 1e-3) / 1e9
+    gbs_in = moved / (ms_in * 1e-3) / 1e9
+    log(f"[bench] swap {n} blocks ({moved / 1e6:.1f} MB each way): out {ms_out * 1e3:.0f} us = "
+        f"{gbs_out:.1f} GB/s, in {ms_in * 1e3:.0f} us = {gbs_in:.1f} GB/s")
+    result = {
+        "metric": "preemption swap over the host link: achieved GB/s (device to host)",
+        "value": round(gbs_out, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": min(args.warmup, 2), "ms_per_step": round(ms_out, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.cache_dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name} pool, swap of {n} blocks", "blocks": n,
+                   "bytes_each_way": moved, "host_to_device_gbs": round(gbs_in, 2),
+                   "host_to_device_ms": round(ms_in, 4)},
+        "roofline": {"bound": "host link", "kernel": "pa_swap_blocks", "achieved": round(gbs_out, 2),
+                     "peak": PEAK_HOST_LINK_GBS, "unit": "GB/s",
+                     "frac": round(gbs_out / PEAK_HOST_LINK_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 PEAK_MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD public spec
 
 
@@ -291,7 +351,7 @@ def main() -> int:
                     help="report the eager step time instead of the HIP graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--op", choices=["step", "copy", "prefill"], default="step",
+    ap.add_argument("--op", choices=["step", "copy", "prefill", "swap"], default="step",
                     help="step: append + decode (+ merge); copy: a copy-on-write burst "
                          "of pa_copy_blocks on the workload's pool; prefill: several query "
                          "tokens per sequence (pa_prefill_chunk), see --case")
@@ -306,6 +366,8 @@ def main() -> int:
         return bench_copy(args)
     if args.op == "prefill":
         return bench_prefill(args)
+    if args.op == "swap":
+        return bench_swap(args)
 
     import torch
 

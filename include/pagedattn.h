@@ -281,6 +281,34 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
                          int64_t num_blocks, pa_dtype cache_dtype, hipStream_t stream);
 
 /*
+ * pa_swap_blocks -- move whole blocks between two pools, e.g. the device
+ * pools and pools in pinned host memory, for preemption ("How LLM Inference
+ * Engines Work", the scheduler swaps a sequence's blocks to CPU memory when
+ * the GPU is full and back when it resumes).
+ *
+ * For each pair i, the K and V data of every KV head of block src_i of the
+ * source pools is copied to block dst_i of the destination pools, in one
+ * launch on `stream`; the GPU reads or writes the host side directly.
+ *
+ *   dst_k, dst_v / src_k, src_v  pools in the layout above, element
+ *                  cache_dtype, device memory or host memory from
+ *                  hipHostMalloc (device-accessible); src_num_blocks /
+ *                  dst_num_blocks blocks each
+ *   block_mapping  [num_pairs][2] int64 (src_i, dst_i), device-accessible
+ *
+ * Contract: distinct dst ids (and, when the pools are the same, no dst is a
+ * src).  Pairs with an id outside its pool are skipped.  Each pool pointer
+ * is checked with hipPointerGetAttributes: memory the GPU cannot address at
+ * that pointer (unpinned host memory, host memory mapped elsewhere) gives
+ * PA_ERR_INVALID_ARG.  Other errors as pa_copy_blocks.  Host memory holds
+ * the GPU's writes once the stream has been synchronised.
+ */
+pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                         const int64_t* block_mapping, int num_pairs, int64_t src_num_blocks,
+                         int64_t dst_num_blocks, int num_kv_heads, int head_dim, int block_size,
+                         pa_dtype cache_dtype, hipStream_t stream);
+
+/*
  * pa_prefill_chunk -- attention of several new tokens per sequence over the
  * paged cache: a prompt fed in chunks next to the decodes ("vLLM &
  * High-Throughput Serving", section 4, chunked prefill) or K drafted tokens

@@ -196,6 +196,30 @@ def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray,
     return k_out, v_out
 
 
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray,
+                dst_v: np.ndarray, block_mapping: np.ndarray
+                ) -> tuple[np.ndarray, np.ndarray]:
+    """Copy whole blocks from one pair of pools to another; return the new
+    destination pools.
+
+    The scheduler preempts a sequence by swapping its blocks out to CPU
+    memory and later back ("How LLM Inference Engines Work", the
+    scheduler).  For each (src, dst) pair, block src of the source pools
+    (every KV head) becomes block dst of the destination pools.
+    Destinations must be distinct (else the result would depend on the
+    order); a violation raises.
+    """
+    pairs = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    if len(np.unique(pairs[:, 1])) != len(pairs):
+        raise ValueError("swap pairs must have distinct destinations")
+    k_out = dst_k.copy()
+    v_out = dst_v.copy()
+    for s_, d in pairs:
+        k_out[d] = src_k[s_]
+        v_out[d] = src_v[s_]
+    return k_out, v_out
+
+
 # --------------------------------------------------------------------------
 # attention
 # --------------------------------------------------------------------------

@@ -20,7 +20,8 @@ import os
 
 import torch
 
-__all__ = ["PagedAttnError", "load", "kv_cache_write", "copy_blocks", "decode", "decode_partitions",
+__all__ = ["PagedAttnError", "load", "kv_cache_write", "copy_blocks", "swap_blocks", "decode",
+           "decode_partitions",
            "prefill_chunk",
            "decode_reduce", "workspace_size", "new_workspace", "workspace_views", "default_partition_size",
            "PARTITION_AUTO", "LIB_PATH"]
@@ -71,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.pa_prefill_reduce.argtypes = [vp, vp, szt, vp, i32, vp, i32, i32, i32, i32, i32, i32, i32,
                                       i32, vp]
     lib.pa_prefill_reduce.restype = i32
+    lib.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, vp]
+    lib.pa_swap_blocks.restype = i32
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -87,11 +90,12 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported element type {t.dtype}")
 
 
-def _ptr(t: torch.Tensor | None):
+def _ptr(t: torch.Tensor | None, pinned_ok: bool = False):
     if t is None:
         return None
-    if not t.is_cuda:
-        raise ValueError("tensors must live in GPU memory")
+    if not (t.is_cuda or (pinned_ok and t.is_pinned())):
+        raise ValueError("tensors must live in GPU memory"
+                         + (" or pinned host memory" if pinned_ok else ""))
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
@@ -192,6 +196,34 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
                                int(block_mapping.shape[0]), hkv, d, bsz, nb,
                                _dtype_code(k_cache), _stream(k_cache))
     _check("pa_copy_blocks", st)
+
+
+def swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor,
+                src_v: torch.Tensor, block_mapping: torch.Tensor) -> None:
+    """``pa_swap_blocks``: copy block src -> dst from the (src_k, src_v) pools
+    to the (dst_k, dst_v) pools for each row of ``block_mapping [n, 2]``
+    (int64, on the GPU).  Either side may be a pinned host pool
+    (``pin_memory=True``); the call runs on the current stream."""
+    snb, hkv, bsz, d = _k_pool_shape(src_k)
+    dnb, hkv2, bsz2, d2 = _k_pool_shape(dst_k)
+    if (hkv2, bsz2, d2) != (hkv, bsz, d) or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination pools differ in shape or type")
+    if tuple(src_v.shape) != (snb, hkv, d, bsz) or tuple(dst_v.shape) != (dnb, hkv, d, bsz):
+        raise ValueError("V pools do not match the K pools")
+    for t in (src_k, src_v, dst_k, dst_v):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError("host pools must be pinned (pin_memory=True)")
+        if not t.is_contiguous():
+            raise ValueError("pools must be contiguous")
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be int64 [n, 2]")
+    if not block_mapping.is_cuda or not block_mapping.is_contiguous():
+        raise ValueError("block_mapping must be a contiguous GPU tensor")
+    st = load().pa_swap_blocks(_ptr(dst_k, True), _ptr(dst_v, True), _ptr(src_k, True),
+                               _ptr(src_v, True),
+                               _ptr(block_mapping), int(block_mapping.shape[0]), snb, dnb, hkv,
+                               d, bsz, _dtype_code(src_k), _stream(block_mapping))
+    _check("pa_swap_blocks", st)
 
 
 def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -9,6 +9,11 @@
 // divergent token).  The host side (reference counts, choosing the new
 // block) decides the (src, dst) pairs; this kernel moves the bytes.
 //
+// The same kernel swaps blocks between the device pools and a pool in
+// pinned host memory that the GPU addresses directly, for preemption ("How
+// LLM Inference Engines Work", the scheduler's swap to CPU memory when the
+// GPU is full): one launch moves any number of blocks over the host link.
+//
 // A block holds every KV head, so in both pools it is one contiguous run of
 // num_kv_heads * block_size * head_dim elements.  Each workgroup copies one
 // 4 KiB chunk of one pair's K or V block with one 16-byte non-temporal load
@@ -29,13 +34,14 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(const CopyArg
   const int64_t chunk = blockIdx.z;     // 4 KiB chunk of the block
   const int64_t src = a.mapping[2 * pair];
   const int64_t dst = a.mapping[2 * pair + 1];
-  // ids outside the pool are skipped; the host validates what it can see
-  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
-  char* base = static_cast<char*>(pool == 0 ? a.k_cache : a.v_cache);
+  // ids outside the pools are skipped; the host validates what it can see
+  if (src < 0 || src >= a.src_blocks || dst < 0 || dst >= a.dst_blocks) return;
+  const char* from = static_cast<const char*>(pool == 0 ? a.src_k : a.src_v);
+  char* to = static_cast<char*>(pool == 0 ? a.dst_k : a.dst_v);
   const int64_t off = chunk * kChunkBytes + (int64_t)threadIdx.x * 16;
   if (off >= a.block_bytes) return;  // a block is a multiple of 1 KiB, not always of 4 KiB
-  const u32x4 v = stream_load<u32x4>(base + src * a.block_bytes + off);
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + dst * a.block_bytes + off));
+  const u32x4 v = stream_load<u32x4>(from + src * a.block_bytes + off);
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(to + dst * a.block_bytes + off));
 }
 
 }  // namespace

@@ -113,6 +113,33 @@ pa_status from_hip(hipError_t e) {
 
 }  // namespace
 
+namespace {
+
+pa_status copy_or_swap(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                       const int64_t* block_mapping, int num_pairs, int64_t src_blocks,
+                       int64_t dst_blocks, int num_kv_heads, int head_dim, int block_size,
+                       pa_dtype cache_dtype, hipStream_t stream) {
+  if (num_pairs < 0 || num_kv_heads < 1 || src_blocks < 1 || dst_blocks < 1)
+    return PA_ERR_INVALID_ARG;
+  Elem cache;
+  if (!to_elem(cache_dtype, &cache)) return PA_ERR_INVALID_ARG;
+  if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
+  if (!src_k || !src_v || !dst_k || !dst_v) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;  // an empty mapping may come with a null pointer
+  if (!block_mapping) return PA_ERR_INVALID_ARG;
+  const int elt = cache == Elem::F32 ? 4 : (cache == Elem::BF16 ? 2 : 1);
+  pa::CopyArgs a;
+  a.src_k = src_k; a.src_v = src_v; a.dst_k = dst_k; a.dst_v = dst_v;
+  a.mapping = block_mapping;
+  a.src_blocks = src_blocks; a.dst_blocks = dst_blocks;
+  a.block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elt;
+  a.num_pairs = num_pairs;
+  if (a.block_bytes > (int64_t)65535 * 4096) return PA_ERR_UNSUPPORTED;  // grid z limit
+  return from_hip(pa::launch_copy_blocks(a, stream));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* pa_status_string(pa_status status) {
@@ -164,21 +191,30 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new, void* k_cache,
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
                          int num_pairs, int num_kv_heads, int head_dim, int block_size,
                          int64_t num_blocks, pa_dtype cache_dtype, hipStream_t stream) {
-  if (num_pairs < 0 || num_kv_heads < 1 || num_blocks < 1) return PA_ERR_INVALID_ARG;
-  Elem cache;
-  if (!to_elem(cache_dtype, &cache)) return PA_ERR_INVALID_ARG;
-  if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
-  if (!k_cache || !v_cache) return PA_ERR_INVALID_ARG;
-  if (num_pairs == 0) return PA_OK;  // an empty mapping may come with a null pointer
-  if (!block_mapping) return PA_ERR_INVALID_ARG;
-  const int elt = cache == Elem::F32 ? 4 : (cache == Elem::BF16 ? 2 : 1);
-  pa::CopyArgs a;
-  a.k_cache = k_cache; a.v_cache = v_cache; a.mapping = block_mapping;
-  a.num_blocks = num_blocks;
-  a.block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elt;
-  a.num_pairs = num_pairs;
-  if (a.block_bytes > (int64_t)65535 * 4096) return PA_ERR_UNSUPPORTED;  // grid z limit
-  return from_hip(pa::launch_copy_blocks(a, stream));
+  return copy_or_swap(k_cache, v_cache, k_cache, v_cache, block_mapping, num_pairs, num_blocks,
+                      num_blocks, num_kv_heads, head_dim, block_size, cache_dtype, stream);
+}
+
+pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                         const int64_t* block_mapping, int num_pairs, int64_t src_num_blocks,
+                         int64_t dst_num_blocks, int num_kv_heads, int head_dim, int block_size,
+                         pa_dtype cache_dtype, hipStream_t stream) {
+  // The kernel dereferences all four pools: each must be memory the GPU
+  // addresses at the same pointer (device memory, or pinned host memory
+  // mapped into the device's address space) -- anything else is refused
+  // here instead of faulting there.
+  for (const void* p : {static_cast<const void*>(dst_k), static_cast<const void*>(dst_v), src_k, src_v}) {
+    if (!p) return PA_ERR_INVALID_ARG;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+      (void)hipGetLastError();  // leave no sticky error behind
+      return PA_ERR_INVALID_ARG;
+    }
+    if (attr.type == hipMemoryTypeUnregistered) return PA_ERR_INVALID_ARG;
+    if (attr.type == hipMemoryTypeHost && attr.devicePointer != p) return PA_ERR_INVALID_ARG;
+  }
+  return copy_or_swap(src_k, src_v, dst_k, dst_v, block_mapping, num_pairs, src_num_blocks,
+                      dst_num_blocks, num_kv_heads, head_dim, block_size, cache_dtype, stream);
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

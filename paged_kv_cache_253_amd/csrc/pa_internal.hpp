@@ -89,11 +89,15 @@ struct WriteArgs {
   int num_tokens, num_kv_heads;
 };
 
+// Whole-block copies from (src_k, src_v) to (dst_k, dst_v): the same pools
+// for copy-on-write, a device pool and a pinned host pool for swapping.
 struct CopyArgs {
-  void* k_cache;
-  void* v_cache;
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
   const int64_t* mapping;       // [num_pairs][2] (src, dst) block ids
-  int64_t num_blocks;
+  int64_t src_blocks, dst_blocks;
   int64_t block_bytes;          // one block of one pool: Hkv * B * D * elt
   int num_pairs;
 };

@@ -33,7 +33,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_reduce",
                                     "pa_decode_workspace_size", "pa_kv_cache_write",
-                                    "pa_prefill_chunk", "pa_prefill_reduce", "pa_status_string"]
+                                    "pa_prefill_chunk", "pa_prefill_reduce", "pa_status_string",
+                                    "pa_swap_blocks"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -152,6 +153,19 @@ def test_copy_blocks_rejects(lib):
     assert call(bs=8) == UNSUPPORTED
     assert call(n=0) == 0                       # no pairs: nothing to do
     assert call(n=0, m=None) == 0               # (an empty tensor's pointer may be null)
+
+
+def test_swap_blocks_rejects(lib):
+    f = lib.pa_swap_blocks
+    ok = dict(dk=FAKE, dv=FAKE, sk=FAKE, sv=FAKE, m=FAKE, n=4, snb=64, dnb=32, hkv=8, d=128,
+              bs=16, dt=BF16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["dk"], a["dv"], a["sk"], a["sv"], a["m"], a["n"], a["snb"], a["dnb"], a["hkv"],
+                 a["d"], a["bs"], a["dt"], None)
+    assert call(dk=None) == INVALID
+    assert call(sv=None) == INVALID
 
 
 def test_prefill_rejects(lib):

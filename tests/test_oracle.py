@@ -27,7 +27,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 def _impl(**over):
     """The oracle's functions as a namespace, optionally with replacements."""
     ns = dict(slot_of=paged.slot_of, gather=paged.gather, copy_blocks=paged.copy_blocks,
-              prefill_chunk=paged.prefill_chunk,
+              prefill_chunk=paged.prefill_chunk, swap_blocks=paged.swap_blocks,
               write_tokens=paged.write_tokens, attention=paged.attention,
               decode=paged.decode, partial=paged.partial, merge=paged.merge,
               e4m3_to_f64=codecs.e4m3_to_f64, e4m3_encode=codecs.e4m3_encode)
@@ -458,6 +458,35 @@ def pin_copy_on_write(impl):
         raise AssertionError(f"dependent copy pairs accepted: {bad}")
 
 
+def pin_swap_round_trip(impl):
+    """Preemption: a sequence's blocks go out to a host pool and come back
+    into different device blocks; through the updated table it reads the
+    same tokens, and nothing else changes."""
+    rng = np.random.default_rng(21)
+    bsz, hkv, d, nb, nh = 4, 2, 8, 12, 6
+    k_dev = rng.standard_normal((nb, hkv, d // 4, bsz, 4)).astype(np.float32)
+    v_dev = rng.standard_normal((nb, hkv, d, bsz)).astype(np.float32)
+    k_host = np.zeros((nh, hkv, d // 4, bsz, 4), np.float32)
+    v_host = np.zeros((nh, hkv, d, bsz), np.float32)
+    table, length = np.array([3, 7, 1]), 10
+    before = impl.gather(k_dev, v_dev, table, length, bsz)
+    k_host, v_host = impl.swap_blocks(k_dev, v_dev, k_host, v_host, np.array([[3, 4], [7, 0], [1, 2]]))
+    k_dev2, v_dev2 = k_dev.copy(), v_dev.copy()
+    k_dev2[[3, 7, 1]] = np.nan                       # the device blocks are reused meanwhile
+    v_dev2[[3, 7, 1]] = np.nan
+    k_dev3, v_dev3 = impl.swap_blocks(k_host, v_host, k_dev2, v_dev2, np.array([[4, 5], [0, 9], [2, 11]]))
+    after = impl.gather(k_dev3, v_dev3, np.array([5, 9, 11]), length, bsz)
+    assert np.array_equal(after[0], before[0]) and np.array_equal(after[1], before[1])
+    keep = [i for i in range(nb) if i not in (5, 9, 11)]
+    assert np.array_equal(k_dev3[keep], k_dev2[keep], equal_nan=True)
+    assert np.array_equal(v_dev3[keep], v_dev2[keep], equal_nan=True)
+    try:
+        impl.swap_blocks(k_dev, v_dev, k_host, v_host, np.array([[1, 2], [3, 2]]))
+    except ValueError:
+        return
+    raise AssertionError("swap pairs with a repeated destination accepted")
+
+
 def _prefill_case(rng, lens, qlens, hkv=2, g=2, d=8, bsz=4):
     """Random paged pools and tables for several sequences (f32)."""
     nb = sum(-(-L // bsz) for L in lens) + 3
@@ -566,7 +595,7 @@ PINS = [pin_golden_index, pin_gather_roundtrip, pin_write_whole_pool,
         pin_paged_equals_unpaged, pin_block_permutation, pin_shared_prefix,
         pin_split_merge, pin_e4m3_decode_table, pin_e4m3_encode,
         pin_fp8_write_then_decode, pin_copy_on_write, pin_prefill_brute_force,
-        pin_prefill_causal, pin_prefill_library_sdpa]
+        pin_prefill_causal, pin_prefill_library_sdpa, pin_swap_round_trip]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -750,6 +779,14 @@ def _bad_prefill_no_mask(q, k_pool, v_pool, block_tables, context_lens, query_st
     return out
 
 
+def _bad_swap_first_token_only(src_k, src_v, dst_k, dst_v, block_mapping):
+    k2, v2 = dst_k.copy(), dst_v.copy()
+    for s_, d in np.asarray(block_mapping).reshape(-1, 2):
+        k2[d, :, :, 0] = src_k[s_, :, :, 0]
+        v2[d, :, :, 0] = src_v[s_, :, :, 0]
+    return k2, v2
+
+
 def _mk_decode(**over):
     """decode() rebuilt on top of possibly broken parts."""
     impl = _impl(**over)
@@ -786,6 +823,7 @@ MUTANTS = {
     "copy-drops-v": dict(copy_blocks=_bad_copy_k_only),
     "copy-first-head-only": dict(copy_blocks=_bad_copy_first_head),
     "copy-reversed": dict(copy_blocks=_bad_copy_reversed),
+    "swap-first-token-only": dict(swap_blocks=_bad_swap_first_token_only),
     "prefill-excludes-self": dict(prefill_chunk=_bad_prefill_excludes_self),
     "prefill-positions-from-zero": dict(prefill_chunk=_bad_prefill_from_start),
     "prefill-no-causal-mask": dict(prefill_chunk=_bad_prefill_no_mask),
