@@ -355,6 +355,8 @@ def main() -> int:
                     help="step: append + decode (+ merge); copy: a copy-on-write burst "
                          "of pa_copy_blocks on the workload's pool; prefill: several query "
                          "tokens per sequence (pa_prefill_chunk), see --case")
+    ap.add_argument("--cache-dtype", choices=["fp8_e4m3", "fp8_e5m2"], default=None,
+                    help="FP8 format of an FP8 workload's cache (default: the workload's)")
     ap.add_argument("--case", default="spec-verify-8b",
                     help="prefill shape: spec-verify-8b or chunked-prefill-8b")
     args = ap.parse_args()
@@ -375,6 +377,13 @@ def main() -> int:
     from workloads import WORKLOADS, decode_bytes, make_batch, write_bytes
 
     w = WORKLOADS[args.workload]
+    if args.cache_dtype:
+        if not w.cache_dtype.startswith("fp8"):
+            print("--cache-dtype applies to FP8 workloads only", file=sys.stderr)
+            return 2
+        import dataclasses
+        w = dataclasses.replace(w, cache_dtype=args.cache_dtype,
+                                name=w.name + ("-e5m2" if args.cache_dtype == "fp8_e5m2" else ""))
     dev = "cuda"
     t_gen = time.perf_counter()
     batch = make_batch(w, device=dev)
@@ -406,13 +415,13 @@ def main() -> int:
         if timed:
             rec("write0")
         pk.kv_cache_write(batch.k_new, batch.v_new, batch.k_pool, batch.v_pool, slots,
-                          batch.k_scale, batch.v_scale)
+                          batch.k_scale, batch.v_scale, cache_dtype=w.cache_dtype)
         if timed:
             rec("write1")
         if part:
             pk.decode_partitions(batch.q, batch.k_pool, batch.v_pool, bt, cl,
                                  batch.max_context_len, part, batch.scale, batch.k_scale,
-                                 batch.v_scale, ws, out=out)
+                                 batch.v_scale, ws, out=out, cache_dtype=w.cache_dtype)
             if timed:
                 rec("decode1")
             pk.decode_reduce(out, ws, cl, batch.max_context_len, part, w.num_kv_heads)
@@ -420,7 +429,8 @@ def main() -> int:
                 rec("reduce1")
         else:
             pk.decode(batch.q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len,
-                      batch.scale, batch.k_scale, batch.v_scale, 0, out=out)
+                      batch.scale, batch.k_scale, batch.v_scale, 0, out=out,
+                      cache_dtype=w.cache_dtype)
             if timed:
                 rec("decode1")
 
@@ -478,10 +488,11 @@ def main() -> int:
         if part:
             pk.decode_partitions(batch.q, batch.k_pool, batch.v_pool, bt, cl,
                                  batch.max_context_len, part, batch.scale, batch.k_scale,
-                                 batch.v_scale, ws, out=out)
+                                 batch.v_scale, ws, out=out, cache_dtype=w.cache_dtype)
         else:
             pk.decode(batch.q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len,
-                      batch.scale, batch.k_scale, batch.v_scale, 0, out=out)
+                      batch.scale, batch.k_scale, batch.v_scale, 0, out=out,
+                      cache_dtype=w.cache_dtype)
 
     reps = max(args.steps, 20)
     for _ in range(3):
@@ -528,7 +539,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8_e4m3", "f32": "f32"}[w.cache_dtype],
+        "dtype": w.cache_dtype,
         "data": "synthetic",
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "context_tokens_per_s": round(dec["tokens"] / (ms_per_step * 1e-3), 1),

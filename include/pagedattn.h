@@ -78,7 +78,8 @@ typedef enum pa_status {
 typedef enum pa_dtype {
   PA_F32 = 0,      /* IEEE binary32 */
   PA_BF16 = 1,     /* bfloat16 (upper half of a binary32) */
-  PA_FP8_E4M3 = 2  /* OCP FP8 E4M3FN code, one byte, with a per-KV-head scale */
+  PA_FP8_E4M3 = 2, /* OCP FP8 E4M3FN code, one byte, with a per-KV-head scale */
+  PA_FP8_E5M2 = 3  /* OCP FP8 E5M2 code, one byte, with a per-KV-head scale */
 } pa_dtype;
 
 /* partition_size value selecting the balanced context split (see pa_decode). */
@@ -103,7 +104,10 @@ typedef enum pa_dtype {
  *   cache_dtype    equal to src_dtype (the bits are copied unchanged), or
  *                  PA_FP8_E4M3: each element x of KV head h is stored as
  *                  round_to_nearest_even_e4m3(fp32(x) / k_scale[h]) (V with
- *                  v_scale), saturated to +-448; NaN stays NaN
+ *                  v_scale), saturated to +-448; NaN stays NaN;
+ *                  PA_FP8_E5M2: the same with E5M2 codes, saturated to
+ *                  +-57344 (the largest finite E5M2 value; no infinities
+ *                  are written)
  *   k_scale, v_scale  [num_kv_heads] float32, device; required for an FP8
  *                  cache, ignored otherwise (may be NULL)
  *
@@ -146,8 +150,9 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
  *                  launch and the workspace without a device sync)
  *   num_blocks     pool size in blocks
  *   scale          softmax scale (typically 1 / sqrt(head_dim))
- *   q_dtype / cache_dtype  (PA_F32, PA_F32), (PA_BF16, PA_BF16) or
- *                  (PA_BF16, PA_FP8_E4M3)
+ *   q_dtype / cache_dtype  (PA_F32, PA_F32), (PA_BF16, PA_BF16),
+ *                  (PA_BF16, PA_FP8_E4M3) or (PA_BF16, PA_FP8_E5M2); FP8
+ *                  codes are widened exactly, times the per-head scales
  *   k_scale, v_scale   [num_kv_heads] float32, device; FP8 cache only
  *   partition_size selects how contexts are cut into ranges, one range per
  *                  wavefront (split-context decoding; a wavefront's softmax
@@ -331,7 +336,7 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void
  *   query_start    [num_seqs + 1] int32, device: nondecreasing,
  *                  query_start[0] = 0, query_start[num_seqs] = num_query_tokens
  *   max_query_len  host upper bound of Q_b (sizes the grid)
- *   other arguments as pa_decode (cache PA_BF16 or PA_FP8_E4M3)
+ *   other arguments as pa_decode (cache PA_BF16, PA_FP8_E4M3 or PA_FP8_E5M2)
  *   partition_size 0: one wavefront per (query tile, KV head, sequence)
  *                     over its whole prefix, `out` written;
  *                  P > 0 (a multiple of 32): fixed partitions of the prefix;

@@ -11,7 +11,13 @@ the bit formats, so these follow the public format definitions:
   single pattern S.1111.111 is NaN; there are no infinities; the largest
   finite magnitude is 1.75 * 2**8 = 448.
 
-Everything returns numpy float64, in which both formats are exact.
+* FP8 E5M2 (OCP): 1 sign bit, 5 exponent bits with bias 15, 2 mantissa
+  bits; exponent field 0 holds subnormals m/4 * 2**-14; exponent field 31
+  is infinity (mantissa 0) or NaN; the largest finite magnitude is
+  1.75 * 2**15 = 57344.  The third page names this format for its FP8 KV
+  cache ("vLLM & High-Throughput Serving", section 5, kv_cache_dtype).
+
+Everything returns numpy float64, in which all three formats are exact.
 """
 
 from __future__ import annotations
@@ -19,6 +25,7 @@ from __future__ import annotations
 import numpy as np
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -74,6 +81,46 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     tie = d_hi == d_lo
     hi_even = (codes[hi] & 1) == 0
     pick_hi = np.where(tie, hi_even, pick_hi)
+    out = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
+    out = np.where(vals[hi] == clipped, codes[hi], out).astype(np.uint8)
+    out = out | np.where(neg, np.uint8(0x80), np.uint8(0)).astype(np.uint8)
+    nan_code = np.where(neg, np.uint8(0xFF), np.uint8(0x7F)).astype(np.uint8)
+    return np.where(np.isnan(x), nan_code, out).astype(np.uint8)
+
+
+def e5m2_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Decode OCP E5M2 codes (uint8) to float64, from the field layout."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    exp = (c >> 2) & 0x1F
+    man = (c & 0x3).astype(np.float64)
+    normal = (1.0 + man / 4.0) * np.exp2(exp.astype(np.float64) - 15.0)
+    subnormal = (man / 4.0) * 2.0 ** -14
+    mag = np.where(exp == 0, subnormal, normal)
+    mag = np.where(exp == 0x1F, np.where((c & 0x3) == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+def e5m2_encode(x: np.ndarray) -> np.ndarray:
+    """Round float values to E5M2 codes: nearest, ties to even, saturating.
+
+    As ``e4m3_encode``: the nearest finite magnitude, an exact tie going to
+    the code with the even last bit; magnitudes above 57344 (infinity
+    included) saturate to 57344 -- the cache never stores an infinity;
+    NaN gives the NaN code 0x7F with the input's sign.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    codes = np.arange(0, 0x7C, dtype=np.uint8)  # 0x7C is +inf
+    vals = e5m2_to_f64(codes)
+    mag = np.abs(x)
+    neg = np.signbit(x)
+    clipped = np.minimum(mag, E5M2_MAX)
+    hi = np.searchsorted(vals, clipped, side="left")
+    hi = np.minimum(hi, len(vals) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = vals[hi] - clipped
+    d_lo = clipped - vals[lo]
+    pick_hi = np.where(d_hi == d_lo, (codes[hi] & 1) == 0, d_hi < d_lo)
     out = np.where(pick_hi, codes[hi], codes[lo]).astype(np.uint8)
     out = np.where(vals[hi] == clipped, codes[hi], out).astype(np.uint8)
     out = out | np.where(neg, np.uint8(0x80), np.uint8(0)).astype(np.uint8)

@@ -15,7 +15,7 @@ definition, not shared with it):
   (block, head) tile, dimension-major rows of ``block_size`` tokens.
 
 Storage is raw: ``"f32"`` arrays are float32, ``"bf16"`` arrays hold
-bfloat16 bit patterns as uint16, ``"fp8_e4m3"`` arrays hold E4M3FN codes as
+bfloat16 bit patterns as uint16, ``"fp8_e4m3"`` / ``"fp8_e5m2"`` arrays hold FP8 codes as
 uint8 with one float32 scale per KV head.
 
 Token t of a sequence lives in physical block ``table[t // B]`` at offset
@@ -30,7 +30,8 @@ import numpy as np
 
 from . import codecs
 
-DTYPES = ("f32", "bf16", "fp8_e4m3")
+DTYPES = ("f32", "bf16", "fp8_e4m3", "fp8_e5m2")
+FP8 = ("fp8_e4m3", "fp8_e5m2")
 
 
 # --------------------------------------------------------------------------
@@ -45,6 +46,8 @@ def to_f64(raw: np.ndarray, dtype: str) -> np.ndarray:
         return codecs.bf16_bits_to_f64(raw)
     if dtype == "fp8_e4m3":
         return codecs.e4m3_to_f64(raw)
+    if dtype == "fp8_e5m2":
+        return codecs.e5m2_to_f64(raw)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -136,10 +139,11 @@ def write_tokens(k_pool: np.ndarray, v_pool: np.ndarray,
     the same slot are a caller error and raise.
 
     Same-type caches store the bits unchanged.  An E4M3 cache stores
-    ``e4m3_encode(float32(x) / float32(scale[h]))`` per KV head h: the
-    quotient rounded once in binary32, then rounded to nearest-even E4M3
-    with saturation at +-448 (the pages give FP8 KV caches without a
-    rounding rule; this is the plain reading).
+    ``e4m3_encode(float32(x) / float32(scale[h]))`` per KV head h (E5M2:
+    ``e5m2_encode``): the quotient rounded once in binary32, then rounded
+    to nearest-even with saturation at the format's largest finite value
+    (the pages give FP8 KV caches without a rounding rule; this is the
+    plain reading).
     """
     slot_mapping = np.asarray(slot_mapping, dtype=np.int64)
     live = slot_mapping[slot_mapping >= 0]
@@ -153,13 +157,14 @@ def write_tokens(k_pool: np.ndarray, v_pool: np.ndarray,
             continue
         blk, off = divmod(int(s), int(block_size))
         for h in range(n_kv):
-            if cache_dtype == "fp8_e4m3":
+            if cache_dtype in FP8:
+                encode = codecs.e4m3_encode if cache_dtype == "fp8_e4m3" else codecs.e5m2_encode
                 kx = source_to_f32(k_new[n, h], src_dtype)
                 vx = source_to_f32(v_new[n, h], src_dtype)
                 kq = kx / np.float32(k_scale[h])
                 vq = vx / np.float32(v_scale[h])
-                set_k_row(k_out, blk, h, off, codecs.e4m3_encode(kq))
-                v_out[blk, h, :, off] = codecs.e4m3_encode(vq)
+                set_k_row(k_out, blk, h, off, encode(kq))
+                v_out[blk, h, :, off] = encode(vq)
             else:
                 if src_dtype != cache_dtype:
                     raise ValueError("non-fp8 caches store the source bits")
@@ -258,7 +263,7 @@ def sequence_kv_f64(k_pool, v_pool, table_row, length, block_size,
     kr, vr = gather(k_pool, v_pool, table_row, length, block_size)
     k = to_f64(kr, cache_dtype)
     v = to_f64(vr, cache_dtype)
-    if cache_dtype == "fp8_e4m3":
+    if cache_dtype in FP8:
         k = k * np.asarray(k_scale, dtype=np.float32).astype(np.float64)[None, :, None]
         v = v * np.asarray(v_scale, dtype=np.float32).astype(np.float64)[None, :, None]
     return k, v

@@ -6,10 +6,13 @@ computation runs in the library's HIP kernels (C ABI in
 ``include/pagedattn.h``).  There is no CPU fallback: when the shared library
 is missing or a call fails, these functions raise.
 
-Pool layout (the library's): K ``[num_blocks, Hkv, B, D]``, V
+Pool layout (the library's): K ``[num_blocks, Hkv, D / X, B, X]`` with X
+elements = 16 bytes (head-dim chunks, token-major per chunk row), V
 ``[num_blocks, Hkv, D, B]``; bf16 / f32 pools hold ``torch.bfloat16`` /
-``torch.float32``, an FP8 pool holds E4M3FN codes as ``torch.uint8`` (or
-``torch.float8_e4m3fn``) with float32 scales per KV head.
+``torch.float32``, an FP8 pool holds its codes as ``torch.uint8`` (E4M3FN
+unless ``cache_dtype="fp8_e5m2"`` says E5M2; ``torch.float8_e4m3fn`` /
+``torch.float8_e5m2`` tensors say it themselves) with float32 scales per KV
+head.
 """
 
 from __future__ import annotations
@@ -28,7 +31,8 @@ __all__ = ["PagedAttnError", "load", "kv_cache_write", "copy_blocks", "swap_bloc
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
-PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_F32, PA_BF16, PA_FP8_E4M3, PA_FP8_E5M2 = 0, 1, 2, 3
+_CACHE_CODES = {"f32": PA_F32, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3, "fp8_e5m2": PA_FP8_E5M2}
 PARTITION_AUTO = -1  # balanced context split (PA_PARTITION_AUTO)
 _STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
            3: "PA_ERR_WORKSPACE", 4: "PA_ERR_HIP"}
@@ -87,7 +91,23 @@ def _dtype_code(t: torch.Tensor) -> int:
         return PA_BF16
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return PA_FP8_E4M3
+    if t.dtype == torch.float8_e5m2:
+        return PA_FP8_E5M2
     raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def _cache_code(k_cache: torch.Tensor, cache_dtype: str | None) -> int:
+    """Element code of a pool: ``cache_dtype`` when given ("f32", "bf16",
+    "fp8_e4m3", "fp8_e5m2"), else from the tensor (uint8 codes are E4M3,
+    a ``torch.float8_e5m2`` tensor is E5M2)."""
+    if cache_dtype is not None:
+        code = _CACHE_CODES[cache_dtype]
+        if (code in (PA_FP8_E4M3, PA_FP8_E5M2)) != (k_cache.element_size() == 1):
+            raise ValueError(f"a {cache_dtype} pool cannot have {k_cache.dtype} elements")
+        return code
+    if k_cache.dtype == torch.float8_e5m2:
+        return PA_FP8_E5M2
+    return _dtype_code(k_cache)
 
 
 def _ptr(t: torch.Tensor | None, pinned_ok: bool = False):
@@ -166,8 +186,10 @@ def _k_pool_shape(k_cache: torch.Tensor) -> tuple[int, int, int, int]:
 def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
                    v_cache: torch.Tensor, slot_mapping: torch.Tensor,
                    k_scale: torch.Tensor | None = None,
-                   v_scale: torch.Tensor | None = None) -> None:
-    """``pa_kv_cache_write``: store row n of k_new/v_new at slot_mapping[n]."""
+                   v_scale: torch.Tensor | None = None, cache_dtype: str | None = None) -> None:
+    """``pa_kv_cache_write``: store row n of k_new/v_new at slot_mapping[n].
+    ``cache_dtype`` names the pool's element format when its tensor type
+    does not ("fp8_e5m2" for a uint8 pool of E5M2 codes)."""
     n, hkv, d = k_new.shape
     nb, hkv2, bsz, d2 = _k_pool_shape(k_cache)
     if (hkv2, d2) != (hkv, d) or tuple(v_cache.shape) != (nb, hkv, d, bsz):
@@ -176,7 +198,7 @@ def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tens
         raise ValueError("slot_mapping must be int64 [num_tokens]")
     st = load().pa_kv_cache_write(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                   _ptr(slot_mapping), n, hkv, d, bsz, nb,
-                                  _dtype_code(k_new), _dtype_code(k_cache),
+                                  _dtype_code(k_new), _cache_code(k_cache, cache_dtype),
                                   _ptr(k_scale), _ptr(v_scale), _stream(k_cache))
     _check("pa_kv_cache_write", st)
 
@@ -194,7 +216,7 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
         raise ValueError("block_mapping must be contiguous")
     st = load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
                                int(block_mapping.shape[0]), hkv, d, bsz, nb,
-                               _dtype_code(k_cache), _stream(k_cache))
+                               _cache_code(k_cache, None), _stream(k_cache))
     _check("pa_copy_blocks", st)
 
 
@@ -222,7 +244,7 @@ def swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor,
     st = load().pa_swap_blocks(_ptr(dst_k, True), _ptr(dst_v, True), _ptr(src_k, True),
                                _ptr(src_v, True),
                                _ptr(block_mapping), int(block_mapping.shape[0]), snb, dnb, hkv,
-                               d, bsz, _dtype_code(src_k), _stream(block_mapping))
+                               d, bsz, _cache_code(src_k, None), _stream(block_mapping))
     _check("pa_swap_blocks", st)
 
 
@@ -231,7 +253,8 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                   query_start: torch.Tensor, max_query_len: int, scale: float | None = None,
                   k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None,
                   partition_size: int | None = None, out: torch.Tensor | None = None,
-                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+                  workspace: torch.Tensor | None = None,
+                  cache_dtype: str | None = None) -> torch.Tensor:
     """``pa_prefill_chunk`` (+ ``pa_prefill_reduce`` when split): attention
     of each sequence's last Q_b cached tokens (rows ``query_start[b] ..
     query_start[b+1]-1`` of ``q [T, Hq, D]``) over its prefix; returns out.
@@ -260,7 +283,7 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                  _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
                                  int(max_context_len), _ptr(query_start), t, int(max_query_len),
                                  s, hq, hkv, d, bsz, nb, float(scale), _dtype_code(q),
-                                 _dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale),
+                                 _cache_code(k_cache, cache_dtype), _ptr(k_scale), _ptr(v_scale),
                                  int(partition_size), _ptr(workspace), ws_bytes, _stream(q))
     _check("pa_prefill_chunk", st)
     if partition_size:
@@ -273,7 +296,7 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
 
 def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
-                 scale, k_scale, v_scale, partition_size, workspace):
+                 scale, k_scale, v_scale, partition_size, workspace, cache_dtype=None):
     s, hq, d = q.shape
     nb, hkv, bsz, _ = _k_pool_shape(k_cache)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
@@ -281,7 +304,8 @@ def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                           block_tables.shape[1], _ptr(context_lens), int(max_context_len), s, hq,
-                          hkv, d, bsz, nb, float(scale), _dtype_code(q), _dtype_code(k_cache),
+                          hkv, d, bsz, nb, float(scale), _dtype_code(q),
+                          _cache_code(k_cache, cache_dtype),
                           _ptr(k_scale), _ptr(v_scale), int(partition_size), _ptr(workspace),
                           ws_bytes, _stream(q))
     _check("pa_decode", st)
@@ -289,7 +313,7 @@ def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
 
 def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                       partition_size, scale=None, k_scale=None, v_scale=None,
-                      workspace=None, out=None) -> torch.Tensor:
+                      workspace=None, out=None, cache_dtype=None) -> torch.Tensor:
     """Split ``pa_decode`` only (fixed partitions, or the balanced split,
     which also writes the rows of ``out`` it finishes); returns the
     workspace."""
@@ -300,7 +324,7 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, max_conte
     if workspace is None:
         workspace = new_workspace(s, hq, hkv, d, max_context_len, partition_size, q.device)
     _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                 k_scale, v_scale, partition_size, workspace)
+                 k_scale, v_scale, partition_size, workspace, cache_dtype)
     return workspace
 
 
@@ -324,8 +348,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
            scale: float | None = None, k_scale: torch.Tensor | None = None,
            v_scale: torch.Tensor | None = None, partition_size: int | None = None,
-           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None
-           ) -> torch.Tensor:
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+           cache_dtype: str | None = None) -> torch.Tensor:
     """Decode attention over the paged cache; returns ``out [S, Hq, D]``.
 
     ``partition_size`` 0 runs unsplit; > 0 (fixed partitions) or
@@ -341,10 +365,10 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         out = torch.empty_like(q)
     if partition_size == 0:
         _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
-                     scale, k_scale, v_scale, 0, None)
+                     scale, k_scale, v_scale, 0, None, cache_dtype)
         return out
     workspace = decode_partitions(q, k_cache, v_cache, block_tables, context_lens,
                                   max_context_len, partition_size, scale, k_scale, v_scale,
-                                  workspace, out=out)
+                                  workspace, out=out, cache_dtype=cache_dtype)
     return decode_reduce(out, workspace, context_lens, max_context_len, partition_size,
                          k_cache.shape[1])

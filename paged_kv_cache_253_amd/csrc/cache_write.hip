@@ -6,7 +6,7 @@
 // tile (element d at chunk d / X, lane d % X of the token, X elements = 16
 // bytes), one element per dimension row in the dimension-major V tile.  Same-type caches copy bits;
 // an FP8 cache stores the E4M3FN code of x / scale[h] (binary32 quotient,
-// then nearest-even E4M3 with saturation).
+// then nearest-even E4M3 or E5M2 with saturation).
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -29,13 +29,17 @@ __global__ __launch_bounds__(64) void cache_write_kernel(const WriteArgs a) {
   auto kidx = [&](int d) { return ((d / X) * BS + off) * X + d % X; };
   const ST* kn = reinterpret_cast<const ST*>(a.k_new) + ((int64_t)n * a.num_kv_heads + h) * D;
   const ST* vn = reinterpret_cast<const ST*>(a.v_new) + ((int64_t)n * a.num_kv_heads + h) * D;
-  if constexpr (CE == Elem::FP8) {
+  if constexpr (CE == Elem::FP8 || CE == Elem::E5M2) {
     const float ks = a.k_scale[h], vs = a.v_scale[h];
     uint8_t* kc = reinterpret_cast<uint8_t*>(a.k_cache) + tile;
     uint8_t* vc = reinterpret_cast<uint8_t*>(a.v_cache) + tile;
+    auto enc = [](float x) -> uint8_t {
+      if constexpr (CE == Elem::E5M2) return (uint8_t)f32_to_e5m2_sat(x);
+      else return (uint8_t)f32_to_e4m3_sat(x);
+    };
     for (int d = threadIdx.x; d < D; d += 64) {
-      kc[kidx(d)] = (uint8_t)f32_to_e4m3_sat(__fdiv_rn(to_f32(kn[d]), ks));
-      vc[d * BS + off] = (uint8_t)f32_to_e4m3_sat(__fdiv_rn(to_f32(vn[d]), vs));
+      kc[kidx(d)] = enc(__fdiv_rn(to_f32(kn[d]), ks));
+      vc[d * BS + off] = enc(__fdiv_rn(to_f32(vn[d]), vs));
     }
   } else {
     ST* kc = reinterpret_cast<ST*>(a.k_cache) + tile;
@@ -71,6 +75,8 @@ hipError_t launch_cache_write(const WriteArgs& a, Elem src, Elem cache, int head
   if (src == Elem::BF16 && cache == Elem::BF16) return by_shape<__bf16, Elem::BF16>(a, head_dim, block_size, stream);
   if (src == Elem::F32 && cache == Elem::FP8) return by_shape<float, Elem::FP8>(a, head_dim, block_size, stream);
   if (src == Elem::BF16 && cache == Elem::FP8) return by_shape<__bf16, Elem::FP8>(a, head_dim, block_size, stream);
+  if (src == Elem::F32 && cache == Elem::E5M2) return by_shape<float, Elem::E5M2>(a, head_dim, block_size, stream);
+  if (src == Elem::BF16 && cache == Elem::E5M2) return by_shape<__bf16, Elem::E5M2>(a, head_dim, block_size, stream);
   return hipErrorInvalidValue;
 }
 

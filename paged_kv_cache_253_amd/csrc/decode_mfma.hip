@@ -54,10 +54,11 @@ struct Target {
 
 // Attention of the G query heads of KV head h of sequence b over tokens
 // [t0, t1) (t0 a multiple of 32).  An empty range writes zeros (final only).
-template <bool FP8, int D, int BS>
+template <int CK, int D, int BS>
 __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const int h, const int t0,
                                        int t1, const Target tgt) {
-  using C = Cfg<FP8, D, BS>;
+  constexpr bool FP8 = one_byte<CK>();
+  using C = Cfg<CK, D, BS>;
   t1 = min(t1, a.cap_len);  // never walk past the table row
   const int lane = threadIdx.x;
   const int col = lane & 15;   // query head within the group (QK/PV column)
@@ -124,7 +125,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
     return (p < 0 || (int64_t)p >= a.num_blocks) ? 0 : (int64_t)p;
   };
 
-  auto issue = [&](StepBuf<FP8, D, BS>& sb, int step) {
+  auto issue = [&](StepBuf<CK, D, BS>& sb, int step) {
     const int lb0 = (t0 + step * kStep) / BS;
     const int lb1 = min(lb0 + C::kBlocksPerStep - 1, lb_last);
     if (lb1 - chunk_base >= 64) {  // slide the table window (long unsplit ranges)
@@ -156,14 +157,14 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
   float m_run = -INFINITY;  // running max of z = c2 * q.k for head `col`
   float l_run = 0.f;        // this lane's share of sum 2^(z - m_run)
 
-  auto compute = [&](StepBuf<FP8, D, BS>& sb, int step) {
+  auto compute = [&](StepBuf<CK, D, BS>& sb, int step) {
     const int base = t0 + step * kStep;
     const bool partial = base + kStep > t1;
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < C::kChunks; ++c) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(sb, 0, c), qop[c], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(sb, 1, c), qop[c], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sb, 0, c), qop[c], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sb, 1, c), qop[c], s1, 0, 0, 0);
     }
     // scores in log2 units: z = s * c2, so exp(scale*q.k - max) = 2^(z - m)
     bool zok[8];  // token of score register i inside the range
@@ -198,10 +199,10 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
     const bf16x8 pop = p_operand(p);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<FP8>(sb.v[dt]), pop, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<CK>(sb.v[dt]), pop, acc[dt], 0, 0, 0);
   };
 
-  StepBuf<FP8, D, BS> bufA, bufB;
+  StepBuf<CK, D, BS> bufA, bufB;
   issue(bufA, 0);
   for (int step = 0; step < nsteps; step += 2) {
     issue(bufB, min(step + 1, nsteps - 1));
@@ -240,19 +241,20 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
 
 // One wavefront per (partition, KV head, sequence); unsplit launches have a
 // single partition covering the whole context.
-template <bool FP8, int D, int BS>
+template <int CK, int D, int BS>
 __global__ __launch_bounds__(64) void decode_mfma_grid(const DecodeArgs a) {
+  constexpr bool FP8 = one_byte<CK>();
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int len = clamp_len(a.context_lens[b], a.max_len);
   if (a.partition == 0) {
-    attend<FP8, D, BS>(a, b, h, 0, len, Target{true, 0, 0});
+    attend<CK, D, BS>(a, b, h, 0, len, Target{true, 0, 0});
     return;
   }
   const int t0 = part * a.partition;
   const int t1 = min(t0 + a.partition, len);
   if (t0 >= t1) return;  // the sequence has no such partition
   const size_t row0 = ((size_t)b * a.num_q_heads + (size_t)h * a.group) * a.max_parts + part;
-  attend<FP8, D, BS>(a, b, h, t0, t1, Target{false, row0, (size_t)a.max_parts});
+  attend<CK, D, BS>(a, b, h, t0, t1, Target{false, row0, (size_t)a.max_parts});
 }
 
 // ---------------------------------------------------------------------------
@@ -282,17 +284,19 @@ constexpr int kFirst = 1, kLast = 2, kFinal = 4;
 #endif
 constexpr int kRing = PA_STREAM_RING;
 
-template <bool FP8, int D>
+template <int CK, int D>
 constexpr int stream_waves_per_cu() {
+  constexpr bool FP8 = one_byte<CK>();
   return kStep * 2 * D * (FP8 ? 1 : 2) >= 16 * 1024 ? 2 : 4;
 }
 
 typedef const __attribute__((address_space(4))) int32_t* const_i32;
 typedef const __attribute__((address_space(4))) float* const_f32;
 
-template <bool FP8, int D, int BS>
+template <int CK, int D, int BS>
 struct Slot {
-  using C = Cfg<FP8, D, BS>;
+  static constexpr bool FP8 = one_byte<CK>();
+  using C = Cfg<CK, D, BS>;
   u32x4 k[2][C::kKLoads];
   VRaw<FP8> v[C::kDTiles];
   bf16x8 q[C::kChunks];
@@ -305,11 +309,12 @@ struct Slot {
   bool real;  // false: a filler step (loads repeated, nothing computed)
 };
 
-template <bool FP8, int D, int BS>
+template <int CK, int D, int BS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_stream(const DecodeArgs a) {
-  using C = Cfg<FP8, D, BS>;
-  using S = Slot<FP8, D, BS>;
+  constexpr bool FP8 = one_byte<CK>();
+  using C = Cfg<CK, D, BS>;
+  using S = Slot<CK, D, BS>;
   const int lane = threadIdx.x;
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -425,8 +430,8 @@ void decode_mfma_stream(const DecodeArgs a) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < C::kChunks; ++c) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(sl, 0, c), sl.q[c], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<FP8>(sl, 1, c), sl.q[c], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sl, 0, c), sl.q[c], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sl, 1, c), sl.q[c], s1, 0, 0, 0);
     }
     const bool partial = sl.base + kStepTokens > sl.t1;
     bool zok[8];
@@ -461,7 +466,7 @@ void decode_mfma_stream(const DecodeArgs a) {
     const bf16x8 pop = p_operand(p);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<FP8>(sl.v[dt]), pop, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<CK>(sl.v[dt]), pop, acc[dt], 0, 0, 0);
 
     if (sl.flags & kLast) {
       const float l_tot = xlane<OpSum, 16, 32>(l_run);
@@ -511,26 +516,28 @@ void decode_mfma_stream(const DecodeArgs a) {
   }
 }
 
-template <bool FP8, int D, int BS>
+template <int CK, int D, int BS>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+  constexpr bool FP8 = one_byte<CK>();
   if (a.partition == kAuto) {
     DecodeArgs b = a;
-    b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : stream_waves_per_cu<FP8, D>());
-    hipLaunchKernelGGL((decode_mfma_stream<FP8, D, BS>), dim3(b.slices), dim3(64), 0, stream, b);
+    b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : stream_waves_per_cu<CK, D>());
+    hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS>), dim3(b.slices), dim3(64), 0, stream, b);
   } else {
     const int parts = a.partition ? a.max_parts : 1;
     dim3 grid(parts, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((decode_mfma_grid<FP8, D, BS>), grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_grid<CK, D, BS>), grid, dim3(64), 0, stream, a);
   }
   return hipGetLastError();
 }
 
-template <bool FP8>
+template <int CK>
 hipError_t dispatch_shape(const DecodeArgs& a, int head_dim, int block_size, hipStream_t s) {
-  if (head_dim == 128 && block_size == 16) return launch<FP8, 128, 16>(a, s);
-  if (head_dim == 128 && block_size == 32) return launch<FP8, 128, 32>(a, s);
-  if (head_dim == 64 && block_size == 16) return launch<FP8, 64, 16>(a, s);
-  if (head_dim == 64 && block_size == 32) return launch<FP8, 64, 32>(a, s);
+  constexpr bool FP8 = one_byte<CK>();
+  if (head_dim == 128 && block_size == 16) return launch<CK, 128, 16>(a, s);
+  if (head_dim == 128 && block_size == 32) return launch<CK, 128, 32>(a, s);
+  if (head_dim == 64 && block_size == 16) return launch<CK, 64, 16>(a, s);
+  if (head_dim == 64 && block_size == 32) return launch<CK, 64, 32>(a, s);
   return hipErrorInvalidValue;
 }
 
@@ -538,8 +545,9 @@ hipError_t dispatch_shape(const DecodeArgs& a, int head_dim, int block_size, hip
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, Elem cache, int head_dim, int block_size,
                               hipStream_t stream) {
-  if (cache == Elem::BF16) return dispatch_shape<false>(a, head_dim, block_size, stream);
-  if (cache == Elem::FP8) return dispatch_shape<true>(a, head_dim, block_size, stream);
+  if (cache == Elem::BF16) return dispatch_shape<kBF16>(a, head_dim, block_size, stream);
+  if (cache == Elem::FP8) return dispatch_shape<kE4M3>(a, head_dim, block_size, stream);
+  if (cache == Elem::E5M2) return dispatch_shape<kE5M2>(a, head_dim, block_size, stream);
   return hipErrorInvalidValue;
 }
 

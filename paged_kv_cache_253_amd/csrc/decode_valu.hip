@@ -29,6 +29,7 @@ template <Elem E> struct ElemBytes;
 template <> struct ElemBytes<Elem::F32> { static constexpr int v = 4; };
 template <> struct ElemBytes<Elem::BF16> { static constexpr int v = 2; };
 template <> struct ElemBytes<Elem::FP8> { static constexpr int v = 1; };
+template <> struct ElemBytes<Elem::E5M2> { static constexpr int v = 1; };
 
 // 16 bytes of cache elements -> floats
 template <Elem E>
@@ -39,6 +40,9 @@ __device__ __forceinline__ void widen16(u32x4 w, float* out) {
   } else if constexpr (E == Elem::BF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) { out[2 * i] = bf16lo_to_f32(w[i]); out[2 * i + 1] = bf16hi_to_f32(w[i]); }
+  } else if constexpr (E == Elem::E5M2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bf8x4_to_f32(w[i], out + 4 * i);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) fp8x4_to_f32(w[i], out + 4 * i);
@@ -106,7 +110,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
   }
 
   float kscale = 1.0f, vscale = 1.0f;
-  if constexpr (E == Elem::FP8) { kscale = a.k_scale[h]; vscale = a.v_scale[h]; }
+  if constexpr (E == Elem::FP8 || E == Elem::E5M2) { kscale = a.k_scale[h]; vscale = a.v_scale[h]; }
   const float c2 = a.scale * kscale * kLog2e;  // q.k -> log2 units
 
   // byte offsets inside the step's tiles: load m*CPL + j reads chunk row
@@ -361,6 +365,7 @@ hipError_t launch_decode_valu(const DecodeArgs& a, Elem q, Elem cache, int head_
   if (q == Elem::F32 && cache == Elem::F32) return launch_shape<float, Elem::F32>(a, head_dim, block_size, stream);
   if (q == Elem::BF16 && cache == Elem::BF16) return launch_shape<__bf16, Elem::BF16>(a, head_dim, block_size, stream);
   if (q == Elem::BF16 && cache == Elem::FP8) return launch_shape<__bf16, Elem::FP8>(a, head_dim, block_size, stream);
+  if (q == Elem::BF16 && cache == Elem::E5M2) return launch_shape<__bf16, Elem::E5M2>(a, head_dim, block_size, stream);
   return hipErrorInvalidValue;
 }
 

@@ -24,6 +24,7 @@ bool to_elem(pa_dtype t, Elem* e) {
     case PA_F32: *e = Elem::F32; return true;
     case PA_BF16: *e = Elem::BF16; return true;
     case PA_FP8_E4M3: *e = Elem::FP8; return true;
+    case PA_FP8_E5M2: *e = Elem::E5M2; return true;
   }
   return false;
 }
@@ -174,11 +175,11 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new, void* k_cache,
   Elem src, cache;
   if (!to_elem(src_dtype, &src) || !to_elem(cache_dtype, &cache)) return PA_ERR_INVALID_ARG;
   if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
-  if (src == Elem::FP8) return PA_ERR_UNSUPPORTED;
-  if (cache != src && cache != Elem::FP8) return PA_ERR_UNSUPPORTED;
+  if (is_fp8(src)) return PA_ERR_UNSUPPORTED;
+  if (cache != src && !is_fp8(cache)) return PA_ERR_UNSUPPORTED;
   if (num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
-  if (cache == Elem::FP8 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  if (is_fp8(cache) && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
   if (num_tokens == 0) return PA_OK;
   pa::WriteArgs a;
   a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
@@ -233,12 +234,12 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (!to_elem(q_dtype, &qe) || !to_elem(cache_dtype, &ce)) return PA_ERR_INVALID_ARG;
   if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
   const bool combo_ok = (qe == Elem::F32 && ce == Elem::F32) || (qe == Elem::BF16 && ce == Elem::BF16) ||
-                        (qe == Elem::BF16 && ce == Elem::FP8);
+                        (qe == Elem::BF16 && is_fp8(ce));
   if (!combo_ok) return PA_ERR_UNSUPPORTED;
   if (partition_size > 0 && partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
   if (partition_size <= 0 && !out) return PA_ERR_INVALID_ARG;
-  if (ce == Elem::FP8 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  if (is_fp8(ce) && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
   if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
 
   const int group = num_q_heads / num_kv_heads;
@@ -312,7 +313,7 @@ pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_by
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   Elem oe;
   if (!to_elem(out_dtype, &oe)) return PA_ERR_INVALID_ARG;
-  if (oe == Elem::FP8 || !supported_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (is_fp8(oe) || !supported_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   if (partition_size > 0 && partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
   if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
   if (num_q_heads / num_kv_heads > 16 && partition_size == PA_PARTITION_AUTO) return PA_ERR_UNSUPPORTED;
@@ -371,7 +372,7 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PA_ERR_INVALID_ARG;
   if (partition_size == 0 && !out) return PA_ERR_INVALID_ARG;
-  if (ce == Elem::FP8 && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
+  if (is_fp8(ce) && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
 
   pa::PrefillArgs p;
   std::memset(&p, 0, sizeof p);
@@ -419,7 +420,7 @@ pa_status pa_prefill_reduce(void* out, const void* workspace, size_t workspace_b
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   Elem oe;
   if (!to_elem(out_dtype, &oe)) return PA_ERR_INVALID_ARG;
-  if (oe == Elem::FP8 || !supported_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (is_fp8(oe) || !supported_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   if (partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
   if (num_seqs > 65535 || max_query_len > 65535) return PA_ERR_UNSUPPORTED;
   if (!out || !workspace || !context_lens || !query_start) return PA_ERR_INVALID_ARG;

@@ -43,6 +43,40 @@ __device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, bf16x2& lo, bf16x2& hi
   hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
 }
 
+// Four E5M2 codes packed in a word -> four floats / four bf16 (exact: every
+// E5M2 value, subnormals and infinities included, is a bf16 and a float).
+// gfx950's "bf8" converters read the OCP E5M2 format (checked on hardware
+// against the format definition for all 256 codes).
+__device__ __forceinline__ void bf8x4_to_f32(uint32_t w, float* out) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_bf8(w, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_bf8(w, true);
+  out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+}
+
+__device__ __forceinline__ void bf8x4_to_bf16(uint32_t w, bf16x2& lo, bf16x2& hi) {
+  lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true);
+}
+
+// Round a float to an E5M2 code: nearest, ties to even, magnitudes that
+// round above 57344 (the largest finite value) saturate to it, NaN stays
+// NaN.  The spacing is 2^-16 below 2^-14 (subnormals) and 2^(e-2) in
+// binade 2^e.
+__device__ __forceinline__ uint32_t f32_to_e5m2_sat(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = __uint_as_float(u & 0x7fffffffu);
+  if (!(a == a)) return sign | 0x7fu;
+  if (a >= 57344.0f) return sign | 0x7bu;
+  if (a < 6.103515625e-05f) {  // below 2^-14: multiples of 2^-16; rint(4) = 4 is code 0x04
+    return sign | (uint32_t)__builtin_rintf(a * 65536.0f);
+  }
+  int e = (int)((u >> 23) & 0xffu) - 127;                 // binade of a, -14..15
+  float q = __builtin_rintf(__builtin_ldexpf(a, 2 - e));  // 4..8
+  uint32_t code = (uint32_t)(((e + 15) << 2) + (int)q - 4);  // q == 8 carries into e
+  return sign | (code > 0x7bu ? 0x7bu : code);             // the carry above 57344 saturates
+}
+
 // Round a float to an E4M3FN code: nearest, ties to even, magnitudes at or
 // above 448 saturate to 448, NaN stays NaN.  Written from the format: the
 // spacing is 2^-9 below 2^-6 (subnormals) and 2^(e-3) in binade 2^e.

@@ -6,7 +6,9 @@
 
 namespace pa {
 
-enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2 };
+// Element types: FP8 is E4M3FN, E5M2 the other FP8 format.
+enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2, E5M2 = 3 };
+inline bool is_fp8(Elem e) { return e == Elem::FP8 || e == Elem::E5M2; }
 
 // Balanced split: most persistent wavefronts per compute unit any decode
 // kernel uses (sizes the workspace and the merge grid), minimum slice length

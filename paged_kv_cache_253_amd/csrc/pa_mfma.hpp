@@ -21,8 +21,15 @@ namespace mfma {
 
 constexpr int kStep = 32;  // tokens per step
 
-template <bool FP8, int D, int BS>
+// Cache element kinds of the matrix-core kernels.  The two FP8 kinds share
+// the 1-byte layout and differ only in how a code widens to bf16.
+constexpr int kBF16 = 0, kE4M3 = 1, kE5M2 = 2;
+template <int CK>
+constexpr bool one_byte() { return CK != kBF16; }
+
+template <int CK, int D, int BS>
 struct Cfg {
+  static constexpr bool FP8 = one_byte<CK>();
   static constexpr int kElt = FP8 ? 1 : 2;
   static constexpr int kChunks = D / 32;            // QK MFMAs per token group
   static constexpr int kDTiles = D / 16;            // PV MFMAs per step
@@ -40,20 +47,26 @@ struct VRaw<false> { u32x4 w; };  // 8 bf16 tokens
 template <>
 struct VRaw<true> { u32x2 w; };   // 8 e4m3 tokens
 
-template <bool FP8, int D, int BS>
+template <int CK, int D, int BS>
 struct StepBuf {
-  using C = Cfg<FP8, D, BS>;
+  using C = Cfg<CK, D, BS>;
   u32x4 k[2][C::kKLoads];
-  VRaw<FP8> v[C::kDTiles];
+  VRaw<C::FP8> v[C::kDTiles];
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
-// 8 e4m3 codes (two words) -> 8 bf16, order kept
+// 8 FP8 codes of kind CK (two words) -> 8 bf16, order kept (exact)
+template <int CK>
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   bf16x2 a, b, c, d;
-  fp8x4_to_bf16(w0, a, b);
-  fp8x4_to_bf16(w1, c, d);
+  if constexpr (CK == kE5M2) {
+    bf8x4_to_bf16(w0, a, b);
+    bf8x4_to_bf16(w1, c, d);
+  } else {
+    fp8x4_to_bf16(w0, a, b);
+    fp8x4_to_bf16(w1, c, d);
+  }
   bf16x8 r;
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
   r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
@@ -61,11 +74,11 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 }
 
 // K operand of QK chunk c for token group m (from a buffer with k[2][..])
-template <bool FP8, class Buf>
+template <int CK, class Buf>
 __device__ __forceinline__ bf16x8 k_operand(const Buf& sb, int m, int c) {
-  if constexpr (FP8) {
+  if constexpr (one_byte<CK>()) {
     const u32x4 w = sb.k[m][c >> 1];
-    return (c & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+    return (c & 1) ? fp8x8_to_bf16x8<CK>(w[2], w[3]) : fp8x8_to_bf16x8<CK>(w[0], w[1]);
   } else {
     return as_bf16x8(sb.k[m][c]);
   }
@@ -97,9 +110,9 @@ __device__ __forceinline__ bf16x8 p_operand(const float* p) {
 // The token of QK result register i (0..7) of lane row grp, within a step.
 __device__ __forceinline__ int qk_token(int grp, int i) { return 4 * grp + (i & 3) + 16 * (i >> 2); }
 
-template <bool FP8>
-__device__ __forceinline__ bf16x8 v_operand(const VRaw<FP8>& r) {
-  if constexpr (FP8) return fp8x8_to_bf16x8(r.w[0], r.w[1]);
+template <int CK>
+__device__ __forceinline__ bf16x8 v_operand(const VRaw<one_byte<CK>()>& r) {
+  if constexpr (one_byte<CK>()) return fp8x8_to_bf16x8<CK>(r.w[0], r.w[1]);
   else return as_bf16x8(r.w);
 }
 

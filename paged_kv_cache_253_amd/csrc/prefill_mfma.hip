@@ -30,9 +30,10 @@ namespace {
 
 using namespace mfma;
 
-template <bool FP8, int D, int BS, int NT>
+template <int CK, int D, int BS, int NT>
 __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
-  using C = Cfg<FP8, D, BS>;
+  constexpr bool FP8 = one_byte<CK>();
+  using C = Cfg<CK, D, BS>;
   const DecodeArgs& a = args.d;
   const int part = blockIdx.x;
   const int tile = blockIdx.y / a.num_kv_heads;
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
       return (p < 0 || (int64_t)p >= a.num_blocks) ? 0 : (int64_t)p;
     };
 
-    auto issue = [&](StepBuf<FP8, D, BS>& sb, int step) {
+    auto issue = [&](StepBuf<CK, D, BS>& sb, int step) {
       const int lb0 = (t0 + step * kStep) / BS;
       const int lb1 = min(lb0 + C::kBlocksPerStep - 1, lb_last);
       if (lb1 - chunk_base >= 64) {  // slide the table window
@@ -151,15 +152,15 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
       }
     };
 
-    auto compute = [&](StepBuf<FP8, D, BS>& sb, int step) {
+    auto compute = [&](StepBuf<CK, D, BS>& sb, int step) {
       const int base = t0 + step * kStep;
       f32x4 s0[NT], s1[NT];
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) { s0[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; s1[ct] = s0[ct]; }
 #pragma unroll
       for (int c = 0; c < C::kChunks; ++c) {
-        const bf16x8 ka = k_operand<FP8>(sb, 0, c);
-        const bf16x8 kb = k_operand<FP8>(sb, 1, c);
+        const bf16x8 ka = k_operand<CK>(sb, 0, c);
+        const bf16x8 kb = k_operand<CK>(sb, 1, c);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
           s0[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[ct][c], s0[ct], 0, 0, 0);
@@ -205,14 +206,14 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
       }
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) {
-        const bf16x8 vop = v_operand<FP8>(sb.v[dt]);
+        const bf16x8 vop = v_operand<CK>(sb.v[dt]);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct)
           acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[ct], acc[ct][dt], 0, 0, 0);
       }
     };
 
-    StepBuf<FP8, D, BS> bufA, bufB;
+    StepBuf<CK, D, BS> bufA, bufB;
     issue(bufA, 0);
     for (int step = 0; step < nsteps; step += 2) {
       issue(bufB, min(step + 1, nsteps - 1));
@@ -253,36 +254,39 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
   }
 }
 
-template <bool FP8, int D, int BS, int NT>
+template <int CK, int D, int BS, int NT>
 hipError_t launch_nt(const PrefillArgs& p, hipStream_t stream) {
+  constexpr bool FP8 = one_byte<CK>();
   const DecodeArgs& a = p.d;
   const int tiles = prefill_query_tiles(a.group, p.max_query_len,
-                                        prefill_max_column_tiles(FP8 ? Elem::FP8 : Elem::BF16, D));
+                                        prefill_max_column_tiles(FP8 ? Elem::FP8 : Elem::BF16, D));  // FP8 kinds alike
   const int parts = a.partition ? a.max_parts : 1;
   if ((long long)tiles * a.num_kv_heads > 65535) return hipErrorInvalidValue;
   dim3 grid(parts, tiles * a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((prefill_mfma<FP8, D, BS, NT>), grid, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((prefill_mfma<CK, D, BS, NT>), grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <bool FP8, int D, int BS>
+template <int CK, int D, int BS>
 hipError_t launch_shape(const PrefillArgs& p, hipStream_t stream) {
+  constexpr bool FP8 = one_byte<CK>();
   constexpr int kMaxNT = (!FP8 && D == 128) ? 2 : 4;
   switch (prefill_column_tiles(p.d.group, p.max_query_len, kMaxNT)) {
-    case 1: return launch_nt<FP8, D, BS, 1>(p, stream);
-    case 2: return launch_nt<FP8, D, BS, 2>(p, stream);
+    case 1: return launch_nt<CK, D, BS, 1>(p, stream);
+    case 2: return launch_nt<CK, D, BS, 2>(p, stream);
     default:
-      if constexpr (kMaxNT >= 4) return launch_nt<FP8, D, BS, 4>(p, stream);
+      if constexpr (kMaxNT >= 4) return launch_nt<CK, D, BS, 4>(p, stream);
       return hipErrorInvalidValue;
   }
 }
 
-template <bool FP8>
+template <int CK>
 hipError_t dispatch(const PrefillArgs& p, int head_dim, int block_size, hipStream_t s) {
-  if (head_dim == 128 && block_size == 16) return launch_shape<FP8, 128, 16>(p, s);
-  if (head_dim == 128 && block_size == 32) return launch_shape<FP8, 128, 32>(p, s);
-  if (head_dim == 64 && block_size == 16) return launch_shape<FP8, 64, 16>(p, s);
-  if (head_dim == 64 && block_size == 32) return launch_shape<FP8, 64, 32>(p, s);
+  constexpr bool FP8 = one_byte<CK>();
+  if (head_dim == 128 && block_size == 16) return launch_shape<CK, 128, 16>(p, s);
+  if (head_dim == 128 && block_size == 32) return launch_shape<CK, 128, 32>(p, s);
+  if (head_dim == 64 && block_size == 16) return launch_shape<CK, 64, 16>(p, s);
+  if (head_dim == 64 && block_size == 32) return launch_shape<CK, 64, 32>(p, s);
   return hipErrorInvalidValue;
 }
 
@@ -290,8 +294,9 @@ hipError_t dispatch(const PrefillArgs& p, int head_dim, int block_size, hipStrea
 
 hipError_t launch_prefill_mfma(const PrefillArgs& p, Elem cache, int head_dim, int block_size,
                                hipStream_t stream) {
-  if (cache == Elem::BF16) return dispatch<false>(p, head_dim, block_size, stream);
-  if (cache == Elem::FP8) return dispatch<true>(p, head_dim, block_size, stream);
+  if (cache == Elem::BF16) return dispatch<kBF16>(p, head_dim, block_size, stream);
+  if (cache == Elem::FP8) return dispatch<kE4M3>(p, head_dim, block_size, stream);
+  if (cache == Elem::E5M2) return dispatch<kE5M2>(p, head_dim, block_size, stream);
   return hipErrorInvalidValue;
 }
 

@@ -131,7 +131,8 @@ def test_repeated_runs_identical(p):
     assert torch.equal(bits(a), bits(b))
 
 
-@pytest.mark.parametrize("cache,group", [("bf16", 4), ("bf16", 1), ("fp8_e4m3", 4), ("f32", 2)])
+@pytest.mark.parametrize("cache,group", [("bf16", 4), ("bf16", 1), ("fp8_e4m3", 4), ("f32", 2),
+                                         ("fp8_e5m2", 4), ("fp8_e5m2", 1)])
 def test_balanced_split_cuts_and_empty_runs(cache, group):
     """Many short and a few long contexts with empty ones between them: the
     balanced slices cut long runs several times and start inside runs."""
@@ -139,7 +140,7 @@ def test_balanced_split_cuts_and_empty_runs(cache, group):
     lens = rng.integers(1, 90, size=40)
     lens[[3, 17]] = 0
     lens[[5, 30]] = [5000, 2500]
-    batch = _custom(cache, 128 if cache != "f32" else 64, 32 if cache == "fp8_e4m3" else 16,
+    batch = _custom(cache, 128 if cache != "f32" else 64, 32 if cache.startswith("fp8") else 16,
                     2 * group, 2, lens)
     k_ref, v_ref = write_and_reference(batch)
     ref = oracle_decode_host(batch, k_ref, v_ref, range(len(lens)))
@@ -153,9 +154,10 @@ def test_balanced_split_cuts_and_empty_runs(cache, group):
 # ---------------------------------------------------------------------------
 
 def _custom(cache, head_dim, block, hq, hkv, lens, seed=11, poison=True):
-    base = WORKLOADS[2] if cache == "bf16" else (WORKLOADS[5] if cache == "fp8_e4m3" else WORKLOADS[1])
+    base = WORKLOADS[2] if cache == "bf16" else (WORKLOADS[5] if cache.startswith("fp8") else WORKLOADS[1])
     w = dataclasses.replace(base, num_q_heads=hq, num_kv_heads=hkv, head_dim=head_dim,
-                            block_size=block, pool="exact")
+                            block_size=block, pool="exact", cache_dtype=base.cache_dtype
+                            if not cache.startswith("fp8") else cache)
     return make_batch(w, seed=seed, device=DEV, lens=np.asarray(lens), poison=poison)
 
 
@@ -165,6 +167,7 @@ EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 511, 512, 513, 1025]
 @pytest.mark.parametrize("cache,head_dim,block", [
     ("bf16", 128, 16), ("bf16", 128, 32), ("bf16", 64, 16), ("bf16", 64, 32),
     ("fp8_e4m3", 128, 32), ("fp8_e4m3", 128, 16), ("fp8_e4m3", 64, 32),
+    ("fp8_e5m2", 128, 32), ("fp8_e5m2", 64, 16),
     ("f32", 64, 16), ("f32", 128, 32),
 ])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
@@ -191,7 +194,7 @@ def test_matrix_core_path_odd_groups(group):
         compare(widen(out), ref, "bf16", f"G={group} P={p}")
 
 
-@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3", "fp8_e5m2"])
 @pytest.mark.parametrize("group", [2, 4, 8])
 def test_forced_paths_agree_with_oracle(monkeypatch, cache, group):
     batch = _custom(cache, 128, 16 if cache == "bf16" else 32, 2 * group, 2, [5, 333, 1500])
@@ -298,9 +301,10 @@ def test_reduce_of_oracle_partitions():
 # the append
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cache,src", [("fp8_e4m3", "bf16"), ("bf16", "bf16"), ("f32", "f32")])
+@pytest.mark.parametrize("cache,src", [("fp8_e4m3", "bf16"), ("fp8_e5m2", "bf16"), ("bf16", "bf16"),
+                                       ("f32", "f32")])
 def test_append_bit_exact_with_padding_and_out_of_range_slots(cache, src):
-    batch = _custom(cache, 128, 32 if cache == "fp8_e4m3" else 16, 8, 2, [40, 90, 3, 200])
+    batch = _custom(cache, 128, 32 if cache.startswith("fp8") else 16, 8, 2, [40, 90, 3, 200])
     slots = batch.slot_mapping.copy()
     slots[1] = -1                                  # padding token
     slots[2] = batch.num_blocks * batch.workload.block_size + 5  # beyond the pool: skipped
@@ -315,15 +319,18 @@ def test_append_bit_exact_with_padding_and_out_of_range_slots(cache, src):
     assert same_bits(host_view(batch.v_pool), v_ref)
 
 
-def test_fp8_append_rounding_matches_oracle_on_many_values():
-    """The E4M3 encoder on the GPU against the oracle's, over a wide spread
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "fp8_e5m2"])
+def test_fp8_append_rounding_matches_oracle_on_many_values(fmt):
+    """The FP8 encoders on the GPU against the oracle's, over a wide spread
     of magnitudes (subnormals, ties, saturation, NaN)."""
     hkv, d, bsz, n = 4, 128, 32, 256
     nb = n
     rng = np.random.default_rng(5)
-    vals = np.concatenate([rng.standard_normal(n * hkv * d // 2) * 100,
-                           rng.standard_normal(n * hkv * d // 2) * 1e-3]).astype(np.float32)
-    vals[:7] = [0.0, -0.0, 448.0, 500.0, -1e9, np.nan, 2.0 ** -10]
+    big = 100 if fmt == "fp8_e4m3" else 20000
+    tiny = 1e-3 if fmt == "fp8_e4m3" else 1e-5
+    vals = np.concatenate([rng.standard_normal(n * hkv * d // 2) * big,
+                           rng.standard_normal(n * hkv * d // 2) * tiny]).astype(np.float32)
+    vals[:10] = [0.0, -0.0, 448.0, 500.0, -1e9, np.nan, 2.0 ** -10, 57344.0, 61440.0, 2.0 ** -17]
     kn = torch.from_numpy(vals.reshape(n, hkv, d)).to(torch.bfloat16)
     vn = torch.from_numpy(vals[::-1].copy().reshape(n, hkv, d)).to(torch.bfloat16)
     ks = torch.tensor([0.5, 1.0, 2.0, 0.01], dtype=torch.float32)
@@ -332,10 +339,10 @@ def test_fp8_append_rounding_matches_oracle_on_many_values():
     v_pool = torch.zeros(nb, hkv, d, bsz, dtype=torch.uint8)
     slots = np.arange(n, dtype=np.int64) * bsz + 7
     k_ref, v_ref = paged.write_tokens(k_pool.numpy(), v_pool.numpy(), host_view(kn), host_view(vn),
-                                      slots, bsz, "bf16", "fp8_e4m3", ks.numpy(), vs.numpy())
+                                      slots, bsz, "bf16", fmt, ks.numpy(), vs.numpy())
     kd, vd = k_pool.to(DEV), v_pool.to(DEV)
     pk.kv_cache_write(kn.to(DEV), vn.to(DEV), kd, vd, torch.from_numpy(slots).to(DEV),
-                      ks.to(DEV), vs.to(DEV))
+                      ks.to(DEV), vs.to(DEV), cache_dtype=fmt)
     _sync()
     assert np.array_equal(kd.cpu().numpy(), k_ref)
     assert np.array_equal(vd.cpu().numpy(), v_ref)

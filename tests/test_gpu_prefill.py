@@ -33,7 +33,8 @@ def _run(w, lens, qlens, partition, seed=0):
     cl = torch.from_numpy(batch.context_lens).to(DEV)
     out = pk.prefill_chunk(q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len,
                            torch.from_numpy(qs).to(DEV), int(max(qlens)), batch.scale,
-                           batch.k_scale, batch.v_scale, partition_size=partition)
+                           batch.k_scale, batch.v_scale, partition_size=partition,
+                           cache_dtype=w.cache_dtype)
     torch.cuda.synchronize()
     sub = extract_sequences(batch, range(len(lens)))
     ref = paged.prefill_chunk(host_view(q), sub["k_pool"], sub["v_pool"], sub["block_tables"],
@@ -49,6 +50,7 @@ W3 = WORKLOADS[3]                     # G = 8
 W4 = WORKLOADS[4]                     # G = 1 (MHA), 64 heads
 W5 = WORKLOADS[5]                     # FP8, B 32
 W_D64 = dataclasses.replace(WORKLOADS[1], cache_dtype="bf16", q_dtype="bf16", name="tiny-mha-bf16")
+W5_E5M2 = dataclasses.replace(W5, cache_dtype="fp8_e5m2", name="long-context-fp8-e5m2")
 
 
 @pytest.mark.parametrize("partition", [0, 64, 512])
@@ -68,6 +70,7 @@ def test_chunks_of_mixed_length(partition):
     (W3, [900, 345, 77], [9, 3, 16]),                      # G = 8
     (W4, [2100, 2060], [17, 3]),                           # G = 1, 64 heads
     (W5, [1500, 800], [33, 8]),                            # FP8 cache, block 32, 4 column tiles
+    (W5_E5M2, [1200, 600], [40, 3]),                       # E5M2 cache
     (W_D64, [150, 33, 90], [20, 7, 33]),                    # head_dim 64, G = 1
 ])
 def test_other_shapes(w, lens, qlens):

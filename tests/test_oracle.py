@@ -30,7 +30,8 @@ def _impl(**over):
               prefill_chunk=paged.prefill_chunk, swap_blocks=paged.swap_blocks,
               write_tokens=paged.write_tokens, attention=paged.attention,
               decode=paged.decode, partial=paged.partial, merge=paged.merge,
-              e4m3_to_f64=codecs.e4m3_to_f64, e4m3_encode=codecs.e4m3_encode)
+              e4m3_to_f64=codecs.e4m3_to_f64, e4m3_encode=codecs.e4m3_encode,
+              e5m2_to_f64=codecs.e5m2_to_f64, e5m2_encode=codecs.e5m2_encode)
     ns.update(over)
     return types.SimpleNamespace(**ns)
 
@@ -393,6 +394,40 @@ def pin_e4m3_encode(impl):
     assert impl.e4m3_encode(np.array([np.nan]))[0] & 0x7F == 0x7F
 
 
+def pin_e5m2_decode_table(impl):
+    """All 256 E5M2 codes against torch's float8_e5m2 dtype (infinities and
+    NaNs included)."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = impl.e5m2_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+    assert mine[0x7B] == 57344.0 and mine[0x01] == 2.0 ** -16 and mine[0x04] == 2.0 ** -14
+    assert mine[0x7C] == np.inf and mine[0xFC] == -np.inf
+
+
+def pin_e5m2_encode(impl):
+    """Round-to-nearest-even against torch's float8_e5m2 cast inside the
+    finite range, every value and every midpoint exactly; saturation at
+    57344 where torch would give infinity."""
+    rng = np.random.default_rng(22)
+    x = np.concatenate([rng.standard_normal(20000) * 3000.0,
+                        rng.uniform(-57344, 57344, 20000),
+                        rng.standard_normal(20000) * 1e-4]).astype(np.float32)
+    mine = impl.e5m2_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+    vals = impl.e5m2_to_f64(np.arange(0x7C, dtype=np.uint8))
+    assert np.array_equal(impl.e5m2_encode(vals), np.arange(0x7C, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    ref_mid = torch.from_numpy(mids).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(impl.e5m2_encode(mids), ref_mid)
+    assert np.all(impl.e5m2_encode(np.array([61440.0, 1e9, -np.inf, np.inf])) == [0x7B, 0x7B, 0xFB, 0x7B])
+    assert impl.e5m2_encode(np.array([np.nan]))[0] & 0x7F == 0x7F
+
+
 def pin_bf16_widen():
     rng = np.random.default_rng(15)
     bits = rng.integers(0, 2**16, 50000).astype(np.uint16)
@@ -405,24 +440,27 @@ def pin_bf16_widen():
 
 def pin_fp8_write_then_decode(impl):
     """An FP8 append stores the codes of x / scale; the decode multiplies the
-    scale back, so a one-token sequence returns the dequantised new row."""
-    rng = np.random.default_rng(16)
-    hkv, d, bsz, nb = 2, 16, 32, 3
-    k_pool = np.zeros((nb, hkv, d // 16, bsz, 16), np.uint8)
-    v_pool = np.zeros((nb, hkv, d, bsz), np.uint8)
-    kn = rng.standard_normal((1, hkv, d)).astype(np.float32)
-    vn = rng.standard_normal((1, hkv, d)).astype(np.float32)
-    ks = np.array([0.01, 0.02], np.float32)
-    vs = np.array([0.015, 0.005], np.float32)
-    k2, v2 = impl.write_tokens(k_pool, v_pool, kn, vn, np.array([2 * bsz]), bsz,
-                               "f32", "fp8_e4m3", ks, vs)
-    ref = torch.from_numpy(vn[0] / vs[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    assert np.array_equal(v2[2, :, :, 0], ref)
-    q = rng.standard_normal((1, 4, d)).astype(np.float32)
-    out = impl.decode(q, k2, v2, np.array([[2]]), np.array([1]), bsz, 0.25,
-                      "f32", "fp8_e4m3", ks, vs)
-    deq = impl.e4m3_to_f64(ref) * vs[:, None].astype(np.float64)
-    assert np.array_equal(out[0], deq[np.arange(4) // 2])
+    scale back, so a one-token sequence returns the dequantised new row
+    (both FP8 formats; codes checked against torch's casts)."""
+    for fmt, tdt, widen in (("fp8_e4m3", torch.float8_e4m3fn, impl.e4m3_to_f64),
+                            ("fp8_e5m2", torch.float8_e5m2, impl.e5m2_to_f64)):
+        rng = np.random.default_rng(16)
+        hkv, d, bsz, nb = 2, 16, 32, 3
+        k_pool = np.zeros((nb, hkv, d // 16, bsz, 16), np.uint8)
+        v_pool = np.zeros((nb, hkv, d, bsz), np.uint8)
+        kn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+        vn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+        ks = np.array([0.01, 0.02], np.float32)
+        vs = np.array([0.015, 0.005], np.float32)
+        k2, v2 = impl.write_tokens(k_pool, v_pool, kn, vn, np.array([2 * bsz]), bsz,
+                                   "f32", fmt, ks, vs)
+        ref = torch.from_numpy(vn[0] / vs[:, None]).to(tdt).view(torch.uint8).numpy()
+        assert np.array_equal(v2[2, :, :, 0], ref)
+        q = rng.standard_normal((1, 4, d)).astype(np.float32)
+        out = impl.decode(q, k2, v2, np.array([[2]]), np.array([1]), bsz, 0.25,
+                          "f32", fmt, ks, vs)
+        deq = widen(ref) * vs[:, None].astype(np.float64)
+        assert np.array_equal(out[0], deq[np.arange(4) // 2])
 
 
 def pin_copy_on_write(impl):
@@ -595,7 +633,8 @@ PINS = [pin_golden_index, pin_gather_roundtrip, pin_write_whole_pool,
         pin_paged_equals_unpaged, pin_block_permutation, pin_shared_prefix,
         pin_split_merge, pin_e4m3_decode_table, pin_e4m3_encode,
         pin_fp8_write_then_decode, pin_copy_on_write, pin_prefill_brute_force,
-        pin_prefill_causal, pin_prefill_library_sdpa, pin_swap_round_trip]
+        pin_prefill_causal, pin_prefill_library_sdpa, pin_swap_round_trip,
+        pin_e5m2_decode_table, pin_e5m2_encode]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -787,6 +826,16 @@ def _bad_swap_first_token_only(src_k, src_v, dst_k, dst_v, block_mapping):
     return k2, v2
 
 
+def _bad_e5m2_bias(codes):
+    return codecs.e5m2_to_f64(codes) * 0.5
+
+
+def _bad_e5m2_overflow_to_inf(x):
+    out = codecs.e5m2_encode(x)
+    big = np.abs(np.asarray(x, np.float64)) > 57344.0
+    return np.where(big, out | 0x7C, out).astype(np.uint8)
+
+
 def _mk_decode(**over):
     """decode() rebuilt on top of possibly broken parts."""
     impl = _impl(**over)
@@ -820,6 +869,8 @@ MUTANTS = {
     "e4m3-exponent-bias": dict(e4m3_to_f64=_bad_e4m3_bias),
     "e4m3-truncating": dict(e4m3_encode=_bad_encode_truncate),
     "write-drops-v": dict(write_tokens=_bad_write_skip_v),
+    "e5m2-exponent-bias": dict(e5m2_to_f64=_bad_e5m2_bias),
+    "e5m2-overflow-to-inf": dict(e5m2_encode=_bad_e5m2_overflow_to_inf),
     "copy-drops-v": dict(copy_blocks=_bad_copy_k_only),
     "copy-first-head-only": dict(copy_blocks=_bad_copy_first_head),
     "copy-reversed": dict(copy_blocks=_bad_copy_reversed),

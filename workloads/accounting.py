@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import numpy as np
 
-ELEMENT_BYTES = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}
+ELEMENT_BYTES = {"f32": 4, "bf16": 2, "fp8_e4m3": 1, "fp8_e5m2": 1}
 
 
 def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int,
@@ -48,7 +48,7 @@ def decode_bytes(context_lens, num_q_heads: int, num_kv_heads: int,
     s = len(lens)
     q_out = 2 * s * num_q_heads * head_dim * qb
     tables = int((-(-lens // block_size)).sum()) * 4 + s * 4
-    scales = 2 * num_kv_heads * 4 if cache_dtype == "fp8_e4m3" else 0
+    scales = 2 * num_kv_heads * 4 if cache_dtype.startswith("fp8") else 0
     return {"kv": kv, "q_out": q_out, "tables": tables, "scales": scales,
             "total": kv + q_out + tables + scales, "tokens": tokens}
 

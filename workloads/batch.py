@@ -18,12 +18,13 @@ Recipe (one batch = one layer's decode step):
   permutation of the pool, so each sequence's blocks are scattered.
 * q, K, V and the new rows are N(0, 1) drawn in float32 from a seeded
   torch generator on the target device, then rounded to the storage type
-  (round-to-nearest-even).  An FP8 cache holds E4M3FN codes of
-  ``x / scale_h`` with ``scale_h = absmax_h / 448`` per KV head (absmax
-  over that head's pool data and new rows), made with torch's float8 cast.
+  (round-to-nearest-even).  An FP8 cache holds E4M3FN (or E5M2) codes of
+  ``x / scale_h`` with ``scale_h = absmax_h / fmax`` per KV head (absmax
+  over that head's pool data and new rows; fmax = 448 for E4M3FN, 57344
+  for E5M2), made with torch's float8 cast.
 * ``poison=True`` fills every slot that holds no valid token -- unused
   blocks, the tail of each last block, and the new token's slot before
-  the write -- with NaN (code 0x7F for E4M3), so a kernel that reads past
+  the write -- with NaN (code 0x7F in both FP8 formats), so a kernel that reads past
   a context length produces NaN.
 * The unused table entries are -1.
 """
@@ -40,7 +41,9 @@ import torch
 from .allocator import BlockManager, Sequence
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16,
-               "fp8_e4m3": torch.uint8}
+               "fp8_e4m3": torch.uint8, "fp8_e5m2": torch.uint8}
+# the largest finite value of each FP8 format (the per-head scale maps absmax there)
+FP8_FORMATS = {"fp8_e4m3": (torch.float8_e4m3fn, 448.0), "fp8_e5m2": (torch.float8_e5m2, 57344.0)}
 
 
 @dataclass(frozen=True)
@@ -177,7 +180,7 @@ def _randn(shape, gen, device):
 
 
 def _store(x: torch.Tensor, dtype: str) -> torch.Tensor:
-    return x.to(TORCH_DTYPE[dtype]) if dtype != "fp8_e4m3" else x
+    return x.to(TORCH_DTYPE[dtype]) if dtype not in FP8_FORMATS else x
 
 
 def chunk_k_pool(k: torch.Tensor) -> torch.Tensor:
@@ -254,15 +257,16 @@ def make_batch(w: Workload, seed: int | None = None, device="cpu",
     kn = kn.to(TORCH_DTYPE[w.src_dtype])
     vn = vn.to(TORCH_DTYPE[w.src_dtype])
     k_scale = v_scale = None
-    if w.cache_dtype == "fp8_e4m3":
+    if w.cache_dtype in FP8_FORMATS:
+        fmt, fmax = FP8_FORMATS[w.cache_dtype]
         kabs = torch.maximum(k32.abs().amax(dim=(0, 2, 3)),
                              kn.float().abs().amax(dim=(0, 2)))
         vabs = torch.maximum(v32.abs().amax(dim=(0, 2, 3)),
                              vn.float().abs().amax(dim=(0, 2)))
-        k_scale = (kabs / 448.0).to(torch.float32)
-        v_scale = (vabs / 448.0).to(torch.float32)
-        k_pool = (k32 / k_scale[None, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
-        v_pool = (v32 / v_scale[None, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        k_scale = (kabs / fmax).to(torch.float32)
+        v_scale = (vabs / fmax).to(torch.float32)
+        k_pool = (k32 / k_scale[None, :, None, None]).to(fmt).view(torch.uint8)
+        v_pool = (v32 / v_scale[None, :, None, None]).to(fmt).view(torch.uint8)
         del k32, v32
     else:
         k_pool = k32.to(TORCH_DTYPE[w.cache_dtype])
@@ -275,7 +279,7 @@ def make_batch(w: Workload, seed: int | None = None, device="cpu",
             pos = np.arange(int(lens[b]) - 1)  # cached tokens, new token excluded
             valid[tables[b, pos // bsz], pos % bsz] = True
         bad = torch.from_numpy(~valid).to(device)
-        if w.cache_dtype == "fp8_e4m3":
+        if w.cache_dtype in FP8_FORMATS:  # 0x7F is NaN in both formats
             k_pool.masked_fill_(bad[:, None, :, None], 0x7F)
             v_pool.masked_fill_(bad[:, None, None, :], 0x7F)
         else:
