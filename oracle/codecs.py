@@ -17,7 +17,17 @@ the bit formats, so these follow the public format definitions:
   1.75 * 2**15 = 57344.  The third page names this format for its FP8 KV
   cache ("vLLM & High-Throughput Serving", section 5, kv_cache_dtype).
 
-Everything returns numpy float64, in which all three formats are exact.
+* INT4: a signed 4-bit integer code c in -8..7, stored as its two's
+  complement nibble, standing for ``c * scale``.  The first page names a
+  4-bit integer KV cache ("AI Inference Serving at Scale", section 6:
+  4-bit keys and values quadruple the requests one GPU holds) without its
+  scheme; the reading here is the plain symmetric one with one float32
+  scale per group, a group being one token's head vector of K (or of V)
+  in one KV head: ``scale = absmax / 7`` and ``c = round(x / scale)``,
+  nearest-even, so the encoder emits -7..7 (the pattern of -8 decodes but
+  is never written).
+
+Everything returns numpy float64, in which all these formats are exact.
 """
 
 from __future__ import annotations
@@ -26,6 +36,7 @@ import numpy as np
 
 E4M3_MAX = 448.0
 E5M2_MAX = 57344.0
+INT4_LEVEL = 7  # largest code magnitude the INT4 encoder emits
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -126,3 +137,41 @@ def e5m2_encode(x: np.ndarray) -> np.ndarray:
     out = out | np.where(neg, np.uint8(0x80), np.uint8(0)).astype(np.uint8)
     nan_code = np.where(neg, np.uint8(0xFF), np.uint8(0x7F)).astype(np.uint8)
     return np.where(np.isnan(x), nan_code, out).astype(np.uint8)
+
+
+def int4_encode(x: np.ndarray) -> tuple[np.ndarray, np.float32]:
+    """Quantize one group (a token's head vector) to INT4 codes and a scale.
+
+    ``scale = float32(absmax) / 7`` (one binary32 division, nearest-even),
+    then each code is ``x / scale`` rounded once in binary32 and then to the
+    nearest integer, ties to even, kept within -7..7.  An all-zero group
+    gets scale 0 and zero codes.  Inputs must be finite.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    absmax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    scale = np.float32(absmax / np.float32(INT4_LEVEL))
+    if scale == 0:
+        return np.zeros(x.shape, dtype=np.int8), np.float32(0.0)
+    quotient = (x / scale).astype(np.float32)
+    codes = np.clip(np.rint(quotient), -INT4_LEVEL, INT4_LEVEL)
+    return codes.astype(np.int8), scale
+
+
+def int4_to_f64(codes: np.ndarray, scale) -> np.ndarray:
+    """Value of INT4 codes (integers -8..7) under their float32 scale."""
+    c = np.asarray(codes, dtype=np.int64).astype(np.float64)
+    return c * np.float64(np.float32(scale))
+
+
+def nibble_to_int4(n: np.ndarray) -> np.ndarray:
+    """Two's complement 4-bit patterns (0..15) -> integers -8..7."""
+    n = np.asarray(n, dtype=np.int64) & 0xF
+    return np.where(n >= 8, n - 16, n)
+
+
+def int4_to_nibble(c: np.ndarray) -> np.ndarray:
+    """Integers -8..7 -> their two's complement 4-bit patterns."""
+    c = np.asarray(c, dtype=np.int64)
+    if np.any((c < -8) | (c > 7)):
+        raise ValueError("INT4 code out of range")
+    return (c & 0xF).astype(np.uint8)

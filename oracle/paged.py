@@ -18,6 +18,16 @@ Storage is raw: ``"f32"`` arrays are float32, ``"bf16"`` arrays hold
 bfloat16 bit patterns as uint16, ``"fp8_e4m3"`` / ``"fp8_e5m2"`` arrays hold FP8 codes as
 uint8 with one float32 scale per KV head.
 
+An ``"int4"`` pool is uint8 ``[num_blocks, num_kv_heads, B * (d/2 + 4)]``:
+each (block, head) tile is its 4-bit codes (``B * d / 2`` bytes) followed
+by ``B`` float32 scales, token j's at byte ``B*d/2 + 4j``.  Codes are
+grouped in octets of 8 consecutive elements in 4 bytes; byte i of an octet
+holds element i in its low nibble and element i + 4 in its high nibble
+(two's complement).  K codes keep the chunked layout with x = 32 elements
+(16 bytes): ``[d/32, B, 16 bytes]``, a token's 32-element chunk being 4
+octets of consecutive dimensions.  V codes are ``[d, B/2 bytes]``: row
+``dim`` holds the block's tokens, in octets of consecutive tokens.
+
 Token t of a sequence lives in physical block ``table[t // B]`` at offset
 ``t % B`` ("vLLM & High-Throughput Serving", section 2, block-table
 equation; "AI Inference Serving at Scale", section 3, logical-to-physical
@@ -30,8 +40,9 @@ import numpy as np
 
 from . import codecs
 
-DTYPES = ("f32", "bf16", "fp8_e4m3", "fp8_e5m2")
+DTYPES = ("f32", "bf16", "fp8_e4m3", "fp8_e5m2", "int4")
 FP8 = ("fp8_e4m3", "fp8_e5m2")
+INT4 = "int4"
 
 
 # --------------------------------------------------------------------------
@@ -76,8 +87,87 @@ def set_k_row(k_pool: np.ndarray, blk: int, h: int, off: int, row: np.ndarray) -
     k_pool[blk, h, :, off, :] = np.asarray(row).reshape(n_chunks, x)
 
 
-def k_head_dim(k_pool: np.ndarray) -> int:
+def k_head_dim(k_pool: np.ndarray, block_size: int | None = None) -> int:
+    if k_pool.ndim == 3:  # INT4 tiles: B * (d/2 + 4) bytes
+        return int_tile_head_dim(k_pool.shape[2], block_size)
     return int(k_pool.shape[2] * k_pool.shape[4])
+
+
+# --------------------------------------------------------------------------
+# INT4 tiles (codes in octets, then one float32 scale per token)
+# --------------------------------------------------------------------------
+
+def int_tile_head_dim(tile_bytes: int, block_size: int) -> int:
+    """head_dim of an INT4 tile of ``tile_bytes`` = B * (d/2 + 4)."""
+    if block_size is None or tile_bytes % block_size:
+        raise ValueError("INT4 tiles need the block size")
+    return 2 * (tile_bytes // block_size - 4)
+
+
+def int4_tile_bytes(head_dim: int, block_size: int) -> int:
+    return block_size * (head_dim // 2 + 4)
+
+
+def unpack_octets(b: np.ndarray) -> np.ndarray:
+    """Bytes ``[..., 4k]`` -> INT4 codes ``[..., 8k]``: byte i of each group
+    of 4 holds element i (low nibble) and element i + 4 (high nibble)."""
+    b = np.asarray(b, dtype=np.uint8)
+    g = b.reshape(b.shape[:-1] + (-1, 4))
+    lo = codecs.nibble_to_int4(g & 0xF)
+    hi = codecs.nibble_to_int4(g >> 4)
+    return np.concatenate([lo, hi], axis=-1).reshape(b.shape[:-1] + (-1,))
+
+
+def pack_octets(c: np.ndarray) -> np.ndarray:
+    """Inverse of ``unpack_octets``: codes ``[..., 8k]`` -> bytes ``[..., 4k]``."""
+    c = np.asarray(c)
+    g = codecs.int4_to_nibble(c).reshape(c.shape[:-1] + (-1, 8))
+    b = g[..., :4] | (g[..., 4:] << 4)
+    return b.astype(np.uint8).reshape(c.shape[:-1] + (-1,))
+
+
+def _int4_scale(tile: np.ndarray, head_dim: int, block_size: int, off: int) -> np.float32:
+    at = block_size * head_dim // 2 + 4 * off
+    return tile[at:at + 4].copy().view(np.float32)[0]
+
+
+def _set_int4_scale(tile: np.ndarray, head_dim: int, block_size: int, off: int, s) -> None:
+    at = block_size * head_dim // 2 + 4 * off
+    tile[at:at + 4] = np.array([s], dtype=np.float32).view(np.uint8)
+
+
+def int4_k_row(k_pool, blk, h, off, block_size):
+    """K codes (``head_dim`` integers) and scale of one token of an INT4 pool."""
+    tile = k_pool[blk, h]
+    d = int_tile_head_dim(tile.shape[0], block_size)
+    chunks = tile[:block_size * d // 2].reshape(d // 32, block_size, 16)
+    return unpack_octets(chunks[:, off, :]).reshape(-1), _int4_scale(tile, d, block_size, off)
+
+
+def int4_v_row(v_pool, blk, h, off, block_size):
+    """V codes (``head_dim`` integers) and scale of one token of an INT4 pool."""
+    tile = v_pool[blk, h]
+    d = int_tile_head_dim(tile.shape[0], block_size)
+    rows = unpack_octets(tile[:block_size * d // 2].reshape(d, block_size // 2))  # [d, B]
+    return rows[:, off].copy(), _int4_scale(tile, d, block_size, off)
+
+
+def set_int4_k_row(k_pool, blk, h, off, block_size, codes, scale) -> None:
+    tile = k_pool[blk, h]
+    d = int_tile_head_dim(tile.shape[0], block_size)
+    chunks = tile[:block_size * d // 2].reshape(d // 32, block_size, 16)
+    chunks[:, off, :] = pack_octets(np.asarray(codes).reshape(d // 32, 32))
+    _set_int4_scale(tile, d, block_size, off, scale)
+
+
+def set_int4_v_row(v_pool, blk, h, off, block_size, codes, scale) -> None:
+    tile = v_pool[blk, h]
+    d = int_tile_head_dim(tile.shape[0], block_size)
+    region = tile[:block_size * d // 2].reshape(d, block_size // 2)
+    rows = unpack_octets(region)
+    rows[:, off] = codes
+    region[:] = pack_octets(rows)
+    _set_int4_scale(tile, d, block_size, off, scale)
 
 
 # --------------------------------------------------------------------------
@@ -106,7 +196,7 @@ def gather(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarray,
     from non-adjacent blocks ("How LLM Inference Engines Work", section on
     PagedAttention); here the gather is one token at a time.
     """
-    n_kv, head_dim = k_pool.shape[1], k_head_dim(k_pool)
+    n_kv, head_dim = k_pool.shape[1], k_head_dim(k_pool, block_size)
     k = np.empty((length, n_kv, head_dim), dtype=k_pool.dtype)
     v = np.empty((length, n_kv, head_dim), dtype=v_pool.dtype)
     for t in range(length):
@@ -143,7 +233,9 @@ def write_tokens(k_pool: np.ndarray, v_pool: np.ndarray,
     ``e5m2_encode``): the quotient rounded once in binary32, then rounded
     to nearest-even with saturation at the format's largest finite value
     (the pages give FP8 KV caches without a rounding rule; this is the
-    plain reading).
+    plain reading).  An INT4 cache stores each row's ``int4_encode``: its
+    codes and its own float32 scale, per token and KV head, for K and V
+    separately (the scales arguments are not used).
     """
     slot_mapping = np.asarray(slot_mapping, dtype=np.int64)
     live = slot_mapping[slot_mapping >= 0]
@@ -157,7 +249,12 @@ def write_tokens(k_pool: np.ndarray, v_pool: np.ndarray,
             continue
         blk, off = divmod(int(s), int(block_size))
         for h in range(n_kv):
-            if cache_dtype in FP8:
+            if cache_dtype == INT4:
+                kc, ks = codecs.int4_encode(source_to_f32(k_new[n, h], src_dtype))
+                vc, vs = codecs.int4_encode(source_to_f32(v_new[n, h], src_dtype))
+                set_int4_k_row(k_out, blk, h, off, block_size, kc, ks)
+                set_int4_v_row(v_out, blk, h, off, block_size, vc, vs)
+            elif cache_dtype in FP8:
                 encode = codecs.e4m3_encode if cache_dtype == "fp8_e4m3" else codecs.e5m2_encode
                 kx = source_to_f32(k_new[n, h], src_dtype)
                 vx = source_to_f32(v_new[n, h], src_dtype)
@@ -257,9 +354,28 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return out
 
 
+def gather_int4_f64(k_pool, v_pool, table_row, length, block_size):
+    """One sequence of an INT4 pool, gathered token by token through its
+    block table and decoded (code times its token's scale) to float64
+    ``[length, num_kv_heads, head_dim]``."""
+    n_kv = k_pool.shape[1]
+    head_dim = int_tile_head_dim(k_pool.shape[2], block_size)
+    k = np.empty((length, n_kv, head_dim))
+    v = np.empty((length, n_kv, head_dim))
+    for t in range(length):
+        blk, off = slot_of(table_row, t, block_size)
+        for h in range(n_kv):
+            k[t, h] = codecs.int4_to_f64(*int4_k_row(k_pool, blk, h, off, block_size))
+            v[t, h] = codecs.int4_to_f64(*int4_v_row(v_pool, blk, h, off, block_size))
+    return k, v
+
+
 def sequence_kv_f64(k_pool, v_pool, table_row, length, block_size,
                     cache_dtype, k_scale=None, v_scale=None):
-    """Gather one sequence and widen it to float64 (times the FP8 scales)."""
+    """Gather one sequence and widen it to float64 (times the FP8 scales;
+    INT4 codes times their per-token scales)."""
+    if cache_dtype == INT4:
+        return gather_int4_f64(k_pool, v_pool, table_row, length, block_size)
     kr, vr = gather(k_pool, v_pool, table_row, length, block_size)
     k = to_f64(kr, cache_dtype)
     v = to_f64(vr, cache_dtype)

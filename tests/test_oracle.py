@@ -31,7 +31,10 @@ def _impl(**over):
               write_tokens=paged.write_tokens, attention=paged.attention,
               decode=paged.decode, partial=paged.partial, merge=paged.merge,
               e4m3_to_f64=codecs.e4m3_to_f64, e4m3_encode=codecs.e4m3_encode,
-              e5m2_to_f64=codecs.e5m2_to_f64, e5m2_encode=codecs.e5m2_encode)
+              e5m2_to_f64=codecs.e5m2_to_f64, e5m2_encode=codecs.e5m2_encode,
+              int4_encode=codecs.int4_encode, unpack_octets=paged.unpack_octets,
+              pack_octets=paged.pack_octets, int4_k_row=paged.int4_k_row,
+              int4_v_row=paged.int4_v_row)
     ns.update(over)
     return types.SimpleNamespace(**ns)
 
@@ -525,6 +528,115 @@ def pin_swap_round_trip(impl):
     raise AssertionError("swap pairs with a repeated destination accepted")
 
 
+def pin_int4_encode(impl):
+    """Symmetric INT4 with one scale per group: closed forms (absmax 7 gives
+    scale 1, so codes are the nearest-even integers), the extremes at +-7,
+    the all-zero group, and a brute-force nearest-level search over -7..7
+    on random groups, with the error bound |x - c*s| <= s/2."""
+    x = np.array([7.0, -3.5, 2.5, 0.5, -0.5, 1.5, -7.0, 6.25, -2.75, 4.5], np.float32)
+    codes, scale = impl.int4_encode(x)
+    assert scale == np.float32(1.0)
+    assert codes.tolist() == [7, -4, 2, 0, 0, 2, -7, 6, -3, 4]
+    codes, scale = impl.int4_encode(np.array([0.3, -0.3, 0.1], np.float32))
+    assert codes.tolist()[:2] == [7, -7] and scale == np.float32(np.float32(0.3) / np.float32(7))
+    codes, scale = impl.int4_encode(np.zeros(16, np.float32))
+    assert scale == 0 and not codes.any()
+    rng = np.random.default_rng(31)
+    levels = np.arange(-7, 8)
+    for mag in (1.0, 1e-3, 40.0):
+        g = (rng.standard_normal((64, 32)) * mag).astype(np.float32)
+        for row in g:
+            codes, scale = impl.int4_encode(row)
+            want_scale = np.float32(np.float32(np.abs(row).max()) / np.float32(7))
+            assert scale == want_scale
+            qv = (row / want_scale).astype(np.float64)
+            dist = np.abs(qv[:, None] - levels[None, :])
+            best = dist.min(axis=1, keepdims=True)
+            cand = np.where(dist == best, levels[None, :], 99)
+            even = np.where(cand % 2 == 0, cand, 99).min(axis=1)
+            want = np.where((cand != 99).sum(axis=1) > 1, even, cand.min(axis=1))
+            assert np.array_equal(codes, want)
+            err = np.abs(row.astype(np.float64) - codes * np.float64(scale))
+            assert np.all(err <= 0.5 * np.float64(scale) * (1 + 1e-6))
+            assert np.abs(codes).max() == 7
+
+
+def pin_int4_octets(impl):
+    """Nibble layout, from literal bytes: byte i of an octet holds element i
+    (low nibble) and element i + 4 (high nibble), two's complement."""
+    b = np.array([0x51, 0x62, 0x73, 0xF4, 0x88, 0x0F, 0xF0, 0x00], np.uint8)
+    want = [1, 2, 3, 4, 5, 6, 7, -1, -8, -1, 0, 0, -8, 0, -1, 0]
+    assert impl.unpack_octets(b).tolist() == want
+    assert impl.pack_octets(np.array(want)).tolist() == b.tolist()
+
+
+def pin_int4_tile_index(impl):
+    """INT4 tiles built byte by byte from the layout's index arithmetic
+    (written here, not taken from the oracle) read back token by token:
+    K element i of token j at byte (i // 32 * B + j) * 16 + (i % 32) // 8 * 4
+    + i % 4, high nibble iff i % 8 >= 4; V element of dimension i, token j at
+    byte i * B / 2 + j // 8 * 4 + j % 4, high nibble iff j % 8 >= 4; token
+    j's scale at byte B * d / 2 + 4 j."""
+    rng = np.random.default_rng(32)
+    for d, bsz in ((64, 16), (128, 32)):
+        kc = rng.integers(-8, 8, (bsz, d))
+        vc = rng.integers(-8, 8, (bsz, d))
+        ks = rng.uniform(0.1, 1.0, bsz).astype(np.float32)
+        vs = rng.uniform(0.1, 1.0, bsz).astype(np.float32)
+        tiles = np.zeros((2, 1, 1, bsz * (d // 2 + 4)), np.uint8)
+        for j in range(bsz):
+            for i in range(d):
+                kb = (i // 32 * bsz + j) * 16 + (i % 32) // 8 * 4 + i % 4
+                vb = i * bsz // 2 + j // 8 * 4 + j % 4
+                tiles[0, 0, 0, kb] |= (int(kc[j, i]) & 15) << (4 if i % 8 >= 4 else 0)
+                tiles[1, 0, 0, vb] |= (int(vc[j, i]) & 15) << (4 if j % 8 >= 4 else 0)
+        at = bsz * d // 2
+        tiles[0, 0, 0, at:] = ks.view(np.uint8)
+        tiles[1, 0, 0, at:] = vs.view(np.uint8)
+        kpool, vpool = tiles[0], tiles[1]
+        for j in range(bsz):
+            c, s_ = impl.int4_k_row(kpool, 0, 0, j, bsz)
+            assert np.array_equal(c, kc[j]) and s_ == ks[j]
+            c, s_ = impl.int4_v_row(vpool, 0, 0, j, bsz)
+            assert np.array_equal(c, vc[j]) and s_ == vs[j]
+
+
+def pin_int4_write_then_decode(impl):
+    """An INT4 append stores each row's codes and scale; a one-token
+    sequence decodes to its dequantised V row exactly, and the decode of an
+    INT4 cache equals the (pinned) f32 decode of the same values placed in
+    an f32 cache, up to the f32 rounding of code * scale."""
+    rng = np.random.default_rng(33)
+    hkv, g, d, bsz, nb = 2, 3, 64, 16, 6
+    tile = bsz * (d // 2 + 4)
+    k_pool = np.zeros((nb, hkv, tile), np.uint8)
+    v_pool = np.zeros((nb, hkv, tile), np.uint8)
+    lens = np.array([1, 21, 40])
+    tables = np.array([[4, -1, -1], [0, 5, -1], [1, 2, 3]])
+    slots = [tables[b, t // bsz] * bsz + t % bsz for b in range(3) for t in range(lens[b])]
+    n = len(slots)
+    kn = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    k2, v2 = impl.write_tokens(k_pool, v_pool, kn, vn, np.array(slots), bsz, "f32", "int4")
+    q = rng.standard_normal((3, hkv * g, d)).astype(np.float32)
+    out = impl.decode(q, k2, v2, tables, lens, bsz, 0.125, "f32", "int4")
+    vc, vsc = impl.int4_encode(vn[0, 1])
+    assert np.array_equal(out[0, g:2 * g], np.tile(vc * np.float64(vsc), (g, 1)))
+    kf = np.zeros((nb, hkv, d // 4, bsz, 4), np.float32)
+    vf = np.zeros((nb, hkv, d, bsz), np.float32)
+    for idx, sl in enumerate(slots):
+        blk, off = divmod(sl, bsz)
+        for h in range(hkv):
+            kcode, kscale = impl.int4_encode(kn[idx, h])
+            vcode, vscale = impl.int4_encode(vn[idx, h])
+            assert np.array_equal(impl.int4_k_row(k2, blk, h, off, bsz)[0], kcode)
+            kf[blk, h, :, off, :] = (kcode * kscale).astype(np.float32).reshape(d // 4, 4)
+            vf[blk, h, :, off] = (vcode * vscale).astype(np.float32)
+    ref = impl.decode(q, kf, vf, tables, lens, bsz, 0.125, "f32", "f32")
+    # code * scale needs up to 27 significant bits: the f32 cache rounds it
+    np.testing.assert_allclose(out, ref, rtol=2e-6, atol=2e-7)
+
+
 def _prefill_case(rng, lens, qlens, hkv=2, g=2, d=8, bsz=4):
     """Random paged pools and tables for several sequences (f32)."""
     nb = sum(-(-L // bsz) for L in lens) + 3
@@ -634,7 +746,8 @@ PINS = [pin_golden_index, pin_gather_roundtrip, pin_write_whole_pool,
         pin_split_merge, pin_e4m3_decode_table, pin_e4m3_encode,
         pin_fp8_write_then_decode, pin_copy_on_write, pin_prefill_brute_force,
         pin_prefill_causal, pin_prefill_library_sdpa, pin_swap_round_trip,
-        pin_e5m2_decode_table, pin_e5m2_encode]
+        pin_e5m2_decode_table, pin_e5m2_encode, pin_int4_encode, pin_int4_octets,
+        pin_int4_tile_index, pin_int4_write_then_decode]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -836,6 +949,44 @@ def _bad_e5m2_overflow_to_inf(x):
     return np.where(big, out | 0x7C, out).astype(np.uint8)
 
 
+def _bad_int4_truncate(x):
+    codes, scale = codecs.int4_encode(x)
+    if scale == 0:
+        return codes, scale
+    q = (np.asarray(x, np.float32) / scale).astype(np.float32)
+    return np.clip(np.trunc(q), -7, 7).astype(np.int8), scale
+
+
+def _bad_int4_scale_8(x):
+    x = np.asarray(x, np.float32)
+    scale = np.float32(np.float32(np.abs(x).max()) / np.float32(8))
+    if scale == 0:
+        return np.zeros(x.shape, np.int8), scale
+    return np.clip(np.rint(x / scale), -8, 7).astype(np.int8), scale
+
+
+def _bad_unpack_swapped(b):
+    b = np.asarray(b, np.uint8)
+    return paged.unpack_octets(((b & 0xF) << 4) | (b >> 4))
+
+
+def _bad_unpack_ones_complement(b):
+    c = paged.unpack_octets(b)
+    return np.where(c < 0, c + 1, c)
+
+
+def _bad_int4_v_token_major(v_pool, blk, h, off, block_size):
+    tile = v_pool[blk, h]
+    d = paged.int_tile_head_dim(tile.shape[0], block_size)
+    rows = paged.unpack_octets(tile[:block_size * d // 2].reshape(block_size, d // 2))
+    return rows[off].copy(), paged._int4_scale(tile, d, block_size, off)
+
+
+def _bad_int4_k_dims_interleaved(k_pool, blk, h, off, block_size):
+    codes, scale = paged.int4_k_row(k_pool, blk, h, off, block_size)
+    return codes.reshape(-1, 2)[:, ::-1].reshape(-1), scale
+
+
 def _mk_decode(**over):
     """decode() rebuilt on top of possibly broken parts."""
     impl = _impl(**over)
@@ -846,6 +997,11 @@ def _mk_decode(**over):
         out = np.zeros(q64.shape)
         scale = float(np.float32(scale))
         for b in range(q64.shape[0]):
+            if cache_dtype == "int4":  # tiles of codes and scales: no raw-row gather
+                k, v = paged.gather_int4_f64(k_pool, v_pool, block_tables[b],
+                                             int(context_lens[b]), block_size)
+                out[b] = impl.attention(q64[b], k, v, scale)
+                continue
             kr, vr = impl.gather(k_pool, v_pool, block_tables[b], int(context_lens[b]), block_size)
             k = paged.to_f64(kr, cache_dtype)
             v = paged.to_f64(vr, cache_dtype)
@@ -878,6 +1034,12 @@ MUTANTS = {
     "prefill-excludes-self": dict(prefill_chunk=_bad_prefill_excludes_self),
     "prefill-positions-from-zero": dict(prefill_chunk=_bad_prefill_from_start),
     "prefill-no-causal-mask": dict(prefill_chunk=_bad_prefill_no_mask),
+    "int4-truncating": dict(int4_encode=_bad_int4_truncate),
+    "int4-scale-absmax-over-8": dict(int4_encode=_bad_int4_scale_8),
+    "int4-nibbles-swapped": dict(unpack_octets=_bad_unpack_swapped),
+    "int4-ones-complement": dict(unpack_octets=_bad_unpack_ones_complement),
+    "int4-v-token-major": dict(int4_v_row=_bad_int4_v_token_major),
+    "int4-k-dims-interleaved": dict(int4_k_row=_bad_int4_k_dims_interleaved),
 }
 
 

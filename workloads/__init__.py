@@ -8,7 +8,7 @@ here.
 
 from .accounting import (ELEMENT_BYTES, copy_bytes, decode_bytes, kv_bytes,  # noqa: F401
                          prefill_bytes,
-                         kv_bytes_per_token, write_bytes)
+                         kv_bytes_per_token, row_bytes, write_bytes)
 from .allocator import BlockManager, Sequence  # noqa: F401
 from .batch import (PREFILL_WORKLOADS, WORKLOADS, Batch, Workload,  # noqa: F401
                     chunk_k_pool, contiguous_layout,

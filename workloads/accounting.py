@@ -19,6 +19,14 @@ import numpy as np
 ELEMENT_BYTES = {"f32": 4, "bf16": 2, "fp8_e4m3": 1, "fp8_e5m2": 1}
 
 
+def row_bytes(cache_dtype: str, head_dim: int) -> int:
+    """Bytes of one token's K (or V) row of one KV head in the cache.  An
+    INT4 row is head_dim 4-bit codes plus its own float32 scale."""
+    if cache_dtype == "int4":
+        return head_dim // 2 + 4
+    return head_dim * ELEMENT_BYTES[cache_dtype]
+
+
 def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int,
                        bytes_per_element: int) -> int:
     """K and V bytes one token occupies across all layers."""
@@ -38,13 +46,13 @@ def decode_bytes(context_lens, num_q_heads: int, num_kv_heads: int,
 
     K and V of every valid token, each read once; q read and out written
     once; the used block-table entries and the lengths read once; one
-    float32 scale per KV head for K and for V when the cache is FP8.
+    float32 scale per KV head for K and for V when the cache is FP8 (an
+    INT4 cache's per-token scales are part of its rows).
     """
     lens = np.asarray(context_lens, dtype=np.int64)
-    elt = ELEMENT_BYTES[cache_dtype]
     qb = ELEMENT_BYTES[q_dtype]
     tokens = int(lens.sum())
-    kv = tokens * 2 * num_kv_heads * head_dim * elt
+    kv = tokens * 2 * num_kv_heads * row_bytes(cache_dtype, head_dim)
     s = len(lens)
     q_out = 2 * s * num_q_heads * head_dim * qb
     tables = int((-(-lens // block_size)).sum()) * 4 + s * 4
@@ -56,8 +64,8 @@ def decode_bytes(context_lens, num_q_heads: int, num_kv_heads: int,
 def write_bytes(num_tokens: int, num_kv_heads: int, head_dim: int,
                 src_dtype: str, cache_dtype: str) -> int:
     """Algorithmic bytes of one cache append: read new rows, write slots."""
-    rows = num_tokens * 2 * num_kv_heads * head_dim
-    return (rows * ELEMENT_BYTES[src_dtype] + rows * ELEMENT_BYTES[cache_dtype]
+    rows = num_tokens * 2 * num_kv_heads
+    return (rows * head_dim * ELEMENT_BYTES[src_dtype] + rows * row_bytes(cache_dtype, head_dim)
             + num_tokens * 8)
 
 
@@ -65,7 +73,7 @@ def copy_bytes(num_pairs: int, num_kv_heads: int, head_dim: int, block_size: int
                cache_dtype: str) -> int:
     """Algorithmic bytes of a block copy: each pair reads and writes one
     block of the K pool and one of the V pool (every KV head)."""
-    block = num_kv_heads * block_size * head_dim * ELEMENT_BYTES[cache_dtype]
+    block = num_kv_heads * block_size * row_bytes(cache_dtype, head_dim)
     return num_pairs * 2 * 2 * block + num_pairs * 16
 
 
@@ -79,10 +87,9 @@ def prefill_bytes(context_lens, query_lens, num_q_heads: int, num_kv_heads: int,
     tokens."""
     lens = np.asarray(context_lens, dtype=np.int64)
     ql = np.asarray(query_lens, dtype=np.int64)
-    elt = ELEMENT_BYTES[cache_dtype]
     qb = ELEMENT_BYTES[q_dtype]
     tokens = int(lens.sum())
-    kv = tokens * 2 * num_kv_heads * head_dim * elt
+    kv = tokens * 2 * num_kv_heads * row_bytes(cache_dtype, head_dim)
     rows = int(ql.sum())
     q_out = 2 * rows * num_q_heads * head_dim * qb
     tables = int((-(-lens // block_size)).sum()) * 4 + len(lens) * 8

@@ -22,10 +22,14 @@ Recipe (one batch = one layer's decode step):
   ``x / scale_h`` with ``scale_h = absmax_h / fmax`` per KV head (absmax
   over that head's pool data and new rows; fmax = 448 for E4M3FN, 57344
   for E5M2), made with torch's float8 cast.
+* An INT4 cache is drawn directly in its storage: every code byte uniform
+  over 0..255 (so every 4-bit pattern, -8..7, occurs) and one float32 scale
+  per (block, KV head, token) for K and for V, uniform in [0.25, 0.5); no
+  quantisation happens here.  New rows are N(0, 1) bf16 like the others.
 * ``poison=True`` fills every slot that holds no valid token -- unused
   blocks, the tail of each last block, and the new token's slot before
-  the write -- with NaN (code 0x7F in both FP8 formats), so a kernel that reads past
-  a context length produces NaN.
+  the write -- with NaN (code 0x7F in both FP8 formats; a NaN scale for
+  INT4), so a kernel that reads past a context length produces NaN.
 * The unused table entries are -1.
 """
 
@@ -41,7 +45,7 @@ import torch
 from .allocator import BlockManager, Sequence
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16,
-               "fp8_e4m3": torch.uint8, "fp8_e5m2": torch.uint8}
+               "fp8_e4m3": torch.uint8, "fp8_e5m2": torch.uint8, "int4": torch.uint8}
 # the largest finite value of each FP8 format (the per-head scale maps absmax there)
 FP8_FORMATS = {"fp8_e4m3": (torch.float8_e4m3fn, 448.0), "fp8_e5m2": (torch.float8_e5m2, 57344.0)}
 
@@ -131,6 +135,7 @@ class Batch:
     q: torch.Tensor                   # [S, Hq, d] q dtype
     k_pool: torch.Tensor              # [nb, Hkv, d/x, B, x] cache storage, x = 16 B / elt
     v_pool: torch.Tensor              # [nb, Hkv, d, B] cache storage
+                                      # (INT4: both uint8 [nb, Hkv, B * (d/2 + 4)] tiles)
     k_new: torch.Tensor               # [S, Hkv, d] source dtype
     v_new: torch.Tensor
     k_scale: torch.Tensor | None      # float32 [Hkv] (FP8 cache only)
@@ -249,6 +254,9 @@ def make_batch(w: Workload, seed: int | None = None, device="cpu",
     gen.manual_seed(seed)
     hkv, hq, d = w.num_kv_heads, w.num_q_heads, w.head_dim
     q = _randn((s_count, hq, d), gen, device)
+    if w.cache_dtype == "int4":
+        return _int4_batch(w, seed, lens, tables, slot_mapping, refs, q, gen, device,
+                           num_blocks, poison)
     k32 = _randn((num_blocks, hkv, bsz, d), gen, device)
     v32 = _randn((num_blocks, hkv, d, bsz), gen, device)
     kn = _randn((s_count, hkv, d), gen, device)
@@ -274,11 +282,7 @@ def make_batch(w: Workload, seed: int | None = None, device="cpu",
         del k32, v32
 
     if poison:
-        valid = np.zeros((num_blocks, bsz), dtype=bool)
-        for b in range(s_count):
-            pos = np.arange(int(lens[b]) - 1)  # cached tokens, new token excluded
-            valid[tables[b, pos // bsz], pos % bsz] = True
-        bad = torch.from_numpy(~valid).to(device)
+        bad = _invalid_slots(lens, tables, num_blocks, bsz, device)
         if w.cache_dtype in FP8_FORMATS:  # 0x7F is NaN in both formats
             k_pool.masked_fill_(bad[:, None, :, None], 0x7F)
             v_pool.masked_fill_(bad[:, None, None, :], 0x7F)
@@ -290,6 +294,39 @@ def make_batch(w: Workload, seed: int | None = None, device="cpu",
                  chunk_k_pool(k_pool), v_pool.contiguous(), kn.contiguous(),
                  vn.contiguous(), k_scale, v_scale,
                  {"shared_blocks": shared_blocks, "poison": poison})
+
+
+def _invalid_slots(lens, tables, num_blocks, bsz, device) -> torch.Tensor:
+    """[num_blocks, B] bool: slots that hold no cached token of any sequence
+    (the new token's slot counts as empty before the write)."""
+    valid = np.zeros((num_blocks, bsz), dtype=bool)
+    for b in range(len(lens)):
+        pos = np.arange(int(lens[b]) - 1)  # cached tokens, new token excluded
+        valid[tables[b, pos // bsz], pos % bsz] = True
+    return torch.from_numpy(~valid).to(device)
+
+
+def _int4_batch(w, seed, lens, tables, slot_mapping, refs, q, gen, device, num_blocks,
+                poison) -> Batch:
+    """INT4 pools drawn in storage form: random code bytes, then per-token
+    float32 scales at the end of each (block, head) tile."""
+    hkv, d, bsz = w.num_kv_heads, w.head_dim, w.block_size
+    pools = []
+    for _ in range(2):  # K, then V
+        codes = torch.randint(0, 256, (num_blocks, hkv, bsz * d // 2), generator=gen,
+                              device=device, dtype=torch.uint8)
+        scales = 0.25 + 0.25 * torch.rand((num_blocks, hkv, bsz), generator=gen,
+                                          device=device, dtype=torch.float32)
+        if poison:
+            bad = _invalid_slots(lens, tables, num_blocks, bsz, device)
+            scales.masked_fill_(bad[:, None, :], float("nan"))
+        pools.append(torch.cat([codes, scales.view(torch.uint8)], dim=2).contiguous())
+    kn = _randn((len(lens), hkv, d), gen, device).to(TORCH_DTYPE[w.src_dtype])
+    vn = _randn((len(lens), hkv, d), gen, device).to(TORCH_DTYPE[w.src_dtype])
+    return Batch(w, seed, lens, tables, slot_mapping, refs,
+                 q.to(TORCH_DTYPE[w.q_dtype]).contiguous(), pools[0], pools[1],
+                 kn.contiguous(), vn.contiguous(), None, None,
+                 {"shared_blocks": 0, "poison": poison})
 
 
 # --------------------------------------------------------------------------
