@@ -22,6 +22,10 @@
  *   - An FP8 KV cache ("AI Inference Serving at Scale", section 6) stores
  *     OCP E4M3FN codes with one float32 scale per KV head: value = code *
  *     scale.
+ *   - An INT4 KV cache (same section: 4-bit keys and values) stores, for
+ *     every token and KV head, its K row (and its V row) as signed 4-bit
+ *     codes plus one float32 scale of its own: value = code * scale, with
+ *     scale = absmax(row) / 7 and codes in -7..7 written by the append.
  *
  * Conventions for every entry point:
  *
@@ -52,6 +56,16 @@
  *            (inside a (block, head) tile: one row of block_size tokens per
  *            dimension)
  *
+ * PA_INT4 pools are bytes [num_blocks][num_kv_heads][T] with tile size
+ * T = block_size * (head_dim / 2 + 4): the tile's codes (block_size *
+ * head_dim / 2 bytes) in the layout above with 4-bit elements -- K chunk
+ * rows of X = 32 elements (16 bytes per token), V rows of block_size / 2
+ * bytes -- followed by block_size float32 scales, token j's at byte
+ * block_size * head_dim / 2 + 4 * j.  Codes are two's complement nibbles
+ * grouped in octets of 8 consecutive elements of a row (8 dimensions of a K
+ * row, 8 tokens of a V row) in 4 bytes: byte i of an octet holds element i
+ * in its low nibble and element i + 4 in its high nibble.
+ *
  * Supported shapes: head_dim 64 or 128; block_size 16 or 32; element types
  * as listed per call.
  */
@@ -79,7 +93,8 @@ typedef enum pa_dtype {
   PA_F32 = 0,      /* IEEE binary32 */
   PA_BF16 = 1,     /* bfloat16 (upper half of a binary32) */
   PA_FP8_E4M3 = 2, /* OCP FP8 E4M3FN code, one byte, with a per-KV-head scale */
-  PA_FP8_E5M2 = 3  /* OCP FP8 E5M2 code, one byte, with a per-KV-head scale */
+  PA_FP8_E5M2 = 3, /* OCP FP8 E5M2 code, one byte, with a per-KV-head scale */
+  PA_INT4 = 4      /* signed 4-bit code, with a float32 scale per (token, KV head) */
 } pa_dtype;
 
 /* partition_size value selecting the balanced context split (see pa_decode). */
@@ -107,7 +122,12 @@ typedef enum pa_dtype {
  *                  v_scale), saturated to +-448; NaN stays NaN;
  *                  PA_FP8_E5M2: the same with E5M2 codes, saturated to
  *                  +-57344 (the largest finite E5M2 value; no infinities
- *                  are written)
+ *                  are written);
+ *                  PA_INT4: each token's K row of KV head h gets its own
+ *                  scale s = fp32(absmax of the row) / 7 and codes
+ *                  round_to_nearest_even(fp32(x) / s) within -7..7 (all
+ *                  zero when s == 0); V rows likewise.  Rows must be finite
+ *                  (a row with NaN or infinity stores unspecified codes)
  *   k_scale, v_scale  [num_kv_heads] float32, device; required for an FP8
  *                  cache, ignored otherwise (may be NULL)
  *
@@ -136,6 +156,8 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
  *   z_t = scale * dot(q[b][hq], k_t)              (FP8: k_t = code * k_scale[h])
  *   out[b][hq] = sum_t softmax(z)_t * v_t          (FP8: v_t = code * v_scale[h])
  *
+ * (INT4: k_t and v_t are codes times token t's own K and V scales.)
+ *
  * accumulated in float32.  L == 0 gives zeros.
  *
  *   out            [num_seqs][num_q_heads][head_dim], element q_dtype; see
@@ -151,8 +173,10 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
  *   num_blocks     pool size in blocks
  *   scale          softmax scale (typically 1 / sqrt(head_dim))
  *   q_dtype / cache_dtype  (PA_F32, PA_F32), (PA_BF16, PA_BF16),
- *                  (PA_BF16, PA_FP8_E4M3) or (PA_BF16, PA_FP8_E5M2); FP8
- *                  codes are widened exactly, times the per-head scales
+ *                  (PA_BF16, PA_FP8_E4M3), (PA_BF16, PA_FP8_E5M2) or
+ *                  (PA_BF16, PA_INT4); FP8 codes are widened exactly,
+ *                  times the per-head scales; INT4 scales are applied in
+ *                  float32 to the scores and to the softmax weights
  *   k_scale, v_scale   [num_kv_heads] float32, device; FP8 cache only
  *   partition_size selects how contexts are cut into ranges, one range per
  *                  wavefront (split-context decoding; a wavefront's softmax
@@ -177,8 +201,8 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
  *                  ignored when partition_size == 0.  Concurrent calls must
  *                  not share a workspace.
  *
- * Group sizes: any G <= 16 for a bf16 or FP8 cache; G in {1, 2, 4, 8} for
- * an f32 cache.
+ * Group sizes: any G <= 16 for a bf16, FP8 or INT4 cache; G in {1, 2, 4, 8}
+ * for an f32 cache.
  *
  * Caller contract: context_lens[b] <= max_context_len and <=
  * max_blocks_per_seq * block_size, and the table entries read are in
@@ -269,7 +293,8 @@ pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_by
  *
  *   k_cache, v_cache  the pools (layout above), element cache_dtype; a
  *                  block is num_kv_heads * block_size * head_dim elements
- *                  of each pool, contiguous
+ *                  of each pool, contiguous (PA_INT4: num_kv_heads tiles of
+ *                  block_size * (head_dim / 2 + 4) bytes, scales included)
  *   block_mapping  [num_pairs][2] int64, device: (src_i, dst_i)
  *   num_blocks     blocks in each pool
  *
@@ -328,7 +353,7 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void
  *
  *   out[r][hq] = sum_{t <= p} softmax_t(z_t) v_t,  z_t = scale * q[r][hq] . k_t
  *
- * with the GQA mapping, FP8 scales and block-table walk of pa_decode.
+ * with the GQA mapping, FP8 / INT4 scales and block-table walk of pa_decode.
  *
  *   out            [num_query_tokens][num_q_heads][head_dim] bf16; written
  *                  when partition_size == 0
@@ -336,7 +361,8 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void
  *   query_start    [num_seqs + 1] int32, device: nondecreasing,
  *                  query_start[0] = 0, query_start[num_seqs] = num_query_tokens
  *   max_query_len  host upper bound of Q_b (sizes the grid)
- *   other arguments as pa_decode (cache PA_BF16, PA_FP8_E4M3 or PA_FP8_E5M2)
+ *   other arguments as pa_decode (cache PA_BF16, PA_FP8_E4M3, PA_FP8_E5M2
+ *                  or PA_INT4)
  *   partition_size 0: one wavefront per (query tile, KV head, sequence)
  *                     over its whole prefix, `out` written;
  *                  P > 0 (a multiple of 32): fixed partitions of the prefix;

@@ -354,20 +354,41 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return out
 
 
+def int4_block_values(tiles: np.ndarray, block_size: int, which: str) -> np.ndarray:
+    """Values of every token of one block of an INT4 pool, all KV heads:
+    ``tiles`` is ``pool[blk]`` (``[Hkv, T]`` bytes); returns float64
+    ``[B, Hkv, head_dim]``, code times its token's scale.  ``which`` is
+    "k" (chunked K codes) or "v" (dimension-major V codes)."""
+    n_kv, tile = tiles.shape
+    d = int_tile_head_dim(tile, block_size)
+    code_bytes = block_size * d // 2
+    scales = tiles[:, code_bytes:].copy().view(np.float32).astype(np.float64)  # [Hkv, B]
+    region = tiles[:, :code_bytes]
+    if which == "k":
+        c = unpack_octets(region.reshape(n_kv, d // 32, block_size, 16))  # [Hkv, d/32, B, 32]
+        c = c.transpose(2, 0, 1, 3).reshape(block_size, n_kv, d)
+    else:
+        c = unpack_octets(region.reshape(n_kv, d, block_size // 2))         # [Hkv, d, B]
+        c = c.transpose(2, 0, 1)
+    return c.astype(np.float64) * scales.T[:, :, None]
+
+
 def gather_int4_f64(k_pool, v_pool, table_row, length, block_size):
-    """One sequence of an INT4 pool, gathered token by token through its
-    block table and decoded (code times its token's scale) to float64
-    ``[length, num_kv_heads, head_dim]``."""
-    n_kv = k_pool.shape[1]
-    head_dim = int_tile_head_dim(k_pool.shape[2], block_size)
-    k = np.empty((length, n_kv, head_dim))
-    v = np.empty((length, n_kv, head_dim))
-    for t in range(length):
-        blk, off = slot_of(table_row, t, block_size)
-        for h in range(n_kv):
-            k[t, h] = codecs.int4_to_f64(*int4_k_row(k_pool, blk, h, off, block_size))
-            v[t, h] = codecs.int4_to_f64(*int4_v_row(v_pool, blk, h, off, block_size))
-    return k, v
+    """One sequence of an INT4 pool, gathered through its block table and
+    decoded (code times its token's scale) to float64 ``[length,
+    num_kv_heads, head_dim]``: logical block i is physical block
+    ``table_row[i]``, token t its offset ``t mod B``."""
+    n_blocks = -(-int(length) // int(block_size))
+    ks, vs = [], []
+    for i in range(n_blocks):
+        blk = int(table_row[i])
+        ks.append(int4_block_values(k_pool[blk], block_size, "k"))
+        vs.append(int4_block_values(v_pool[blk], block_size, "v"))
+    if not ks:
+        n_kv = k_pool.shape[1]
+        d = int_tile_head_dim(k_pool.shape[2], block_size)
+        return np.zeros((0, n_kv, d)), np.zeros((0, n_kv, d))
+    return np.concatenate(ks)[:length], np.concatenate(vs)[:length]
 
 
 def sequence_kv_f64(k_pool, v_pool, table_row, length, block_size,

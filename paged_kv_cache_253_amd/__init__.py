@@ -12,7 +12,9 @@ elements = 16 bytes (head-dim chunks, token-major per chunk row), V
 ``torch.float32``, an FP8 pool holds its codes as ``torch.uint8`` (E4M3FN
 unless ``cache_dtype="fp8_e5m2"`` says E5M2; ``torch.float8_e4m3fn`` /
 ``torch.float8_e5m2`` tensors say it themselves) with float32 scales per KV
-head.
+head.  An INT4 pool (``cache_dtype="int4"``) is ``torch.uint8 [num_blocks,
+Hkv, B * (D/2 + 4)]``: per (block, head) tile the 4-bit codes, then one
+float32 scale per token.
 """
 
 from __future__ import annotations
@@ -31,8 +33,9 @@ __all__ = ["PagedAttnError", "load", "kv_cache_write", "copy_blocks", "swap_bloc
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
-PA_F32, PA_BF16, PA_FP8_E4M3, PA_FP8_E5M2 = 0, 1, 2, 3
-_CACHE_CODES = {"f32": PA_F32, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3, "fp8_e5m2": PA_FP8_E5M2}
+PA_F32, PA_BF16, PA_FP8_E4M3, PA_FP8_E5M2, PA_INT4 = 0, 1, 2, 3, 4
+_CACHE_CODES = {"f32": PA_F32, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3, "fp8_e5m2": PA_FP8_E5M2,
+                "int4": PA_INT4}
 PARTITION_AUTO = -1  # balanced context split (PA_PARTITION_AUTO)
 _STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
            3: "PA_ERR_WORKSPACE", 4: "PA_ERR_HIP"}
@@ -102,6 +105,10 @@ def _cache_code(k_cache: torch.Tensor, cache_dtype: str | None) -> int:
     a ``torch.float8_e5m2`` tensor is E5M2)."""
     if cache_dtype is not None:
         code = _CACHE_CODES[cache_dtype]
+        if code == PA_INT4:
+            if k_cache.dtype != torch.uint8:
+                raise ValueError("an int4 pool holds uint8 bytes")
+            return code
         if (code in (PA_FP8_E4M3, PA_FP8_E5M2)) != (k_cache.element_size() == 1):
             raise ValueError(f"a {cache_dtype} pool cannot have {k_cache.dtype} elements")
         return code
@@ -173,6 +180,37 @@ def default_partition_size(max_context_len: int) -> int:
     return PARTITION_AUTO
 
 
+def _pool_dims(k_cache: torch.Tensor, v_cache: torch.Tensor | None, cache_dtype: str | None,
+               head_dim: int | None = None,
+               block_size: int | None = None) -> tuple[int, int, int, int]:
+    """(num_blocks, num_kv_heads, block_size, head_dim) of a K/V pool pair,
+    checking the V pool against the K pool.  An INT4 pool's tiles give
+    block_size * (head_dim/2 + 4), so one of the two must be known."""
+    if cache_dtype == "int4":
+        if k_cache.dim() != 3 or k_cache.dtype != torch.uint8:
+            raise ValueError("an int4 pool is uint8 [num_blocks, num_kv_heads, B * (D/2 + 4)]")
+        nb, hkv, tile = (int(x) for x in k_cache.shape)
+        if head_dim is not None:
+            bsz, rem = divmod(tile, head_dim // 2 + 4)
+        elif block_size is not None:
+            bsz = int(block_size)
+            per_token, rem = divmod(tile, bsz)
+            head_dim = 2 * (per_token - 4)
+        else:
+            raise ValueError("an int4 pool needs head_dim or block_size")
+        if rem or bsz < 1 or head_dim < 1:
+            raise ValueError("int4 tile size does not match the head_dim / block_size")
+        if v_cache is not None and (tuple(v_cache.shape) != tuple(k_cache.shape)
+                                    or v_cache.dtype != k_cache.dtype):
+            raise ValueError("V pool does not match the K pool")
+        return nb, hkv, bsz, int(head_dim)
+    nb, hkv, bsz, d = _k_pool_shape(k_cache)
+    if v_cache is not None and (tuple(v_cache.shape) != (nb, hkv, d, bsz)
+                                or v_cache.dtype != k_cache.dtype):
+        raise ValueError("V pool does not match the K pool")
+    return nb, hkv, bsz, d
+
+
 def _k_pool_shape(k_cache: torch.Tensor) -> tuple[int, int, int, int]:
     """(num_blocks, num_kv_heads, block_size, head_dim) of a K pool laid out
     ``[nb, Hkv, head_dim / X, block_size, X]`` with X elements = 16 bytes."""
@@ -191,8 +229,8 @@ def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tens
     ``cache_dtype`` names the pool's element format when its tensor type
     does not ("fp8_e5m2" for a uint8 pool of E5M2 codes)."""
     n, hkv, d = k_new.shape
-    nb, hkv2, bsz, d2 = _k_pool_shape(k_cache)
-    if (hkv2, d2) != (hkv, d) or tuple(v_cache.shape) != (nb, hkv, d, bsz):
+    nb, hkv2, bsz, d2 = _pool_dims(k_cache, v_cache, cache_dtype, head_dim=d)
+    if (hkv2, d2) != (hkv, d):
         raise ValueError("cache shapes do not match the new rows")
     if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != n:
         raise ValueError("slot_mapping must be int64 [num_tokens]")
@@ -204,34 +242,34 @@ def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tens
 
 
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
-                block_mapping: torch.Tensor) -> None:
+                block_mapping: torch.Tensor, cache_dtype: str | None = None,
+                block_size: int | None = None) -> None:
     """``pa_copy_blocks``: copy block src to dst in both pools for each row
-    (src, dst) of the int64 device tensor ``block_mapping [n, 2]``."""
-    nb, hkv, bsz, d = _k_pool_shape(k_cache)
-    if tuple(v_cache.shape) != (nb, hkv, d, bsz) or v_cache.dtype != k_cache.dtype:
-        raise ValueError("V pool does not match the K pool")
+    (src, dst) of the int64 device tensor ``block_mapping [n, 2]``.  INT4
+    pools need ``cache_dtype="int4"`` and their ``block_size``."""
+    nb, hkv, bsz, d = _pool_dims(k_cache, v_cache, cache_dtype, block_size=block_size)
     if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be int64 [n, 2]")
     if not block_mapping.is_contiguous():
         raise ValueError("block_mapping must be contiguous")
     st = load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
                                int(block_mapping.shape[0]), hkv, d, bsz, nb,
-                               _cache_code(k_cache, None), _stream(k_cache))
+                               _cache_code(k_cache, cache_dtype), _stream(k_cache))
     _check("pa_copy_blocks", st)
 
 
 def swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor,
-                src_v: torch.Tensor, block_mapping: torch.Tensor) -> None:
+                src_v: torch.Tensor, block_mapping: torch.Tensor, cache_dtype: str | None = None,
+                block_size: int | None = None) -> None:
     """``pa_swap_blocks``: copy block src -> dst from the (src_k, src_v) pools
     to the (dst_k, dst_v) pools for each row of ``block_mapping [n, 2]``
     (int64, on the GPU).  Either side may be a pinned host pool
-    (``pin_memory=True``); the call runs on the current stream."""
-    snb, hkv, bsz, d = _k_pool_shape(src_k)
-    dnb, hkv2, bsz2, d2 = _k_pool_shape(dst_k)
+    (``pin_memory=True``); the call runs on the current stream.  INT4 pools
+    need ``cache_dtype="int4"`` and their ``block_size``."""
+    snb, hkv, bsz, d = _pool_dims(src_k, src_v, cache_dtype, block_size=block_size)
+    dnb, hkv2, bsz2, d2 = _pool_dims(dst_k, dst_v, cache_dtype, block_size=block_size)
     if (hkv2, bsz2, d2) != (hkv, bsz, d) or src_k.dtype != dst_k.dtype:
         raise ValueError("source and destination pools differ in shape or type")
-    if tuple(src_v.shape) != (snb, hkv, d, bsz) or tuple(dst_v.shape) != (dnb, hkv, d, bsz):
-        raise ValueError("V pools do not match the K pools")
     for t in (src_k, src_v, dst_k, dst_v):
         if not (t.is_cuda or t.is_pinned()):
             raise ValueError("host pools must be pinned (pin_memory=True)")
@@ -244,7 +282,7 @@ def swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor,
     st = load().pa_swap_blocks(_ptr(dst_k, True), _ptr(dst_v, True), _ptr(src_k, True),
                                _ptr(src_v, True),
                                _ptr(block_mapping), int(block_mapping.shape[0]), snb, dnb, hkv,
-                               d, bsz, _cache_code(src_k, None), _stream(block_mapping))
+                               d, bsz, _cache_code(src_k, cache_dtype), _stream(block_mapping))
     _check("pa_swap_blocks", st)
 
 
@@ -262,7 +300,7 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     ``partition_size`` None: unsplit when the query tiles alone give the
     device enough wavefronts, else 512-token partitions."""
     t, hq, d = q.shape
-    nb, hkv, bsz, _ = _k_pool_shape(k_cache)
+    nb, hkv, bsz, _ = _pool_dims(k_cache, v_cache, cache_dtype, head_dim=d)
     s = int(query_start.numel()) - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -273,7 +311,8 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         out = torch.empty_like(q)
     if partition_size is None:
         g = hq // hkv
-        rows = max(1, 16 * (2 if (q.dtype == k_cache.dtype and d == 128) else 4) // g)
+        two_tiles = d == 128 and (q.dtype == k_cache.dtype or cache_dtype == "int4")
+        rows = max(1, 16 * (2 if two_tiles else 4) // g)
         tiles = -(-max_query_len // rows) if max_query_len else 0
         partition_size = 0 if s * hkv * tiles >= 1024 or max_context_len <= 1024 else 512
     if partition_size and workspace is None:
@@ -298,7 +337,7 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                  scale, k_scale, v_scale, partition_size, workspace, cache_dtype=None):
     s, hq, d = q.shape
-    nb, hkv, bsz, _ = _k_pool_shape(k_cache)
+    nb, hkv, bsz, _ = _pool_dims(k_cache, v_cache, cache_dtype, head_dim=d)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise ValueError("block_tables and context_lens must be int32")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -1,4 +1,4 @@
-// Paged decode attention on the matrix cores (bf16 or FP8-E4M3 KV cache).
+// Paged decode attention on the matrix cores (bf16, FP8 or INT4 KV cache).
 //
 // One wavefront owns one (sequence, KV head, context partition).  It walks
 // the partition in steps of 32 tokens (two 16-token blocks or one 32-token
@@ -85,7 +85,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
 #pragma unroll
     for (int c = 0; c < C::kChunks; ++c) {
       // dims of chunk c held by this lane; K rows use the same map
-      const int d0 = FP8 ? (c >> 1) * 64 + grp * 16 + (c & 1) * 8 : c * 32 + grp * 8;
+      const int d0 = q_dim<CK, D>(grp, c);
       if (head_ok) {
         qop[c] = *reinterpret_cast<const bf16x8*>(qrow + d0);
       } else {
@@ -98,16 +98,14 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
   float kscale = 1.0f, vscale = 1.0f;
   if constexpr (FP8) { kscale = a.k_scale[h]; vscale = a.v_scale[h]; }
   const float c2 = a.scale * kscale * kLog2e;  // q.k -> log2 units
+  float qbias = 0.f;
+  if constexpr (C::I4) qbias = q_bias<C::kChunks>(qop);
 
   // ---- per-lane byte offsets inside the step's tiles ----------------------
-  // K: QK row i = col of group m is token 8*(col/4) + 4*m + col%4 of the step.
   // K: QK row col of group m is token 16*m + col of the step; load j of the
-  // group reads chunk row 4*j + grp.
-  const uint32_t koff = ((uint32_t)grp * BS + (uint32_t)col) * 16;
-  // V: dimension dt*16 + col, tokens 8*grp .. +7 of the step.
-  const int vblk = (BS == 16) ? (grp >> 1) : 0;
-  const uint32_t vtok = (BS == 16) ? (uint32_t)(8 * (grp & 1)) : (uint32_t)(8 * grp);
-  const uint32_t voff = (uint32_t)col * C::kRowV + vtok * C::kElt;
+  // group reads chunk row 4*j + grp (INT4: the chunk row and half holding
+  // dimensions D/4*grp ..).  V: dimension dt*16 + col, tokens 8*grp .. +7.
+  const LaneOffsets<CK, D, BS> lo(grp, col);
 
   const char* kc = reinterpret_cast<const char*>(a.k_cache);
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
@@ -136,24 +134,13 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
     const int64_t p1 = (C::kBlocksPerStep == 2) ? phys_of(lb1) : p0;
     const int64_t tile0 = (p0 * a.num_kv_heads + h) * C::kTile;
     const int64_t tile1 = (p1 * a.num_kv_heads + h) * C::kTile;
-    const char* kp0 = kc + tile0 + koff;
-    const char* kp1 = (BS == 16) ? kc + tile1 + koff : kp0 + 16 * 16;
-    const char* vp = vc + (vblk ? tile1 : tile0) + voff;
-#pragma unroll
-    for (int j = 0; j < C::kKLoads; ++j) {
-      sb.k[0][j] = stream_load<u32x4>(kp0 + j * 4 * C::kChunkRow);
-      sb.k[1][j] = stream_load<u32x4>(kp1 + j * 4 * C::kChunkRow);
-    }
-#pragma unroll
-    for (int dt = 0; dt < C::kDTiles; ++dt) {
-      if constexpr (FP8) sb.v[dt].w = stream_load<u32x2>(vp + dt * 16 * C::kRowV);
-      else sb.v[dt].w = stream_load<u32x4>(vp + dt * 16 * C::kRowV);
-    }
+    load_step(sb, kc, vc, tile0, tile1, lo, grp);
   };
 
   f32x4 acc[C::kDTiles];
 #pragma unroll
   for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accb = {0.f, 0.f, 0.f, 0.f};  // INT4: column sums of the PV weights
   float m_run = -INFINITY;  // running max of z = c2 * q.k for head `col`
   float l_run = 0.f;        // this lane's share of sum 2^(z - m_run)
 
@@ -171,12 +158,11 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
 #pragma unroll
     for (int i = 0; i < 8; ++i) zok[i] = !partial || base + qk_token(grp, i) < t1;
     float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = zok[i] ? __fmul_rn(z[i], c2) : -INFINITY;
+    qk_to_log2<CK>(z, sb, zok, c2, qbias);
     if (partial) {  // PV k-slots of this lane: tokens 8*grp .. +7
       const int vvalid = min(max(t1 - (base + 8 * grp), 0), 8);
 #pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<FP8>(sb.v[dt], vvalid);
+      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sb.v[dt], vvalid);
     }
     float mx = z[0];
 #pragma unroll
@@ -188,6 +174,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] *= alpha;
+      if constexpr (C::I4) accb *= alpha;
       m_run = m_new;
     }
     float p[8];
@@ -196,10 +183,11 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
       p[i] = zok[i] ? exp2f(z[i] - m_run) : 0.f;
       l_run += p[i];
     }
-    const bf16x8 pop = p_operand(p);
+    const bf16x8 pop = pv_operand<CK>(p, sb, zok);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<CK>(sb.v[dt]), pop, acc[dt], 0, 0, 0);
+    if constexpr (C::I4) accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop, accb, 0, 0, 0);
   };
 
   StepBuf<CK, D, BS> bufA, bufB;
@@ -215,6 +203,12 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
   // ---- epilogue -------------------------------------------------------------
   const float l_tot = xlane<OpSum, 16, 32>(l_run);
   const float inv = vscale / l_tot;
+  if constexpr (C::I4) {  // remove the operand bias: 136 * sum_t p(t) s_v(t)
+#pragma unroll
+    for (int dt = 0; dt < C::kDTiles; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[dt][r] = fmaf(-kI4Bias, accb[0], acc[dt][r]);
+  }
   if (!head_ok) return;
   if (tgt.final_out) {
     __bf16* o = reinterpret_cast<__bf16*>(a.out) + ((size_t)b * a.num_q_heads + hq) * D;
@@ -243,7 +237,6 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
 // single partition covering the whole context.
 template <int CK, int D, int BS>
 __global__ __launch_bounds__(64) void decode_mfma_grid(const DecodeArgs a) {
-  constexpr bool FP8 = one_byte<CK>();
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int len = clamp_len(a.context_lens[b], a.max_len);
   if (a.partition == 0) {
@@ -286,19 +279,15 @@ constexpr int kRing = PA_STREAM_RING;
 
 template <int CK, int D>
 constexpr int stream_waves_per_cu() {
-  constexpr bool FP8 = one_byte<CK>();
-  return kStep * 2 * D * (FP8 ? 1 : 2) >= 16 * 1024 ? 2 : 4;
+  return kStep * 2 * D * (CK == kBF16 ? 2 : 1) >= 16 * 1024 ? 2 : 4;
 }
 
 typedef const __attribute__((address_space(4))) int32_t* const_i32;
 typedef const __attribute__((address_space(4))) float* const_f32;
 
 template <int CK, int D, int BS>
-struct Slot {
-  static constexpr bool FP8 = one_byte<CK>();
+struct Slot : StepBuf<CK, D, BS> {
   using C = Cfg<CK, D, BS>;
-  u32x4 k[2][C::kKLoads];
-  VRaw<FP8> v[C::kDTiles];
   bf16x8 q[C::kChunks];
   // segment descriptor (wave-uniform)
   int base;   // first token of the step
@@ -344,18 +333,13 @@ void decode_mfma_stream(const DecodeArgs a) {
   int pending = 0;        // real steps issued and not yet computed
 
   // per-lane offsets inside a step's tiles (see attend)
-  const uint32_t koff = ((uint32_t)grp * BS + (uint32_t)col) * 16;
-  const int vblk = (BS == 16) ? (grp >> 1) : 0;
-  const uint32_t vtok = (BS == 16) ? (uint32_t)(8 * (grp & 1)) : (uint32_t)(8 * grp);
-  const uint32_t voff = (uint32_t)col * C::kRowV + vtok * C::kElt;
+  const LaneOffsets<CK, D, BS> lo(grp, col);
   const int qhead = min(col, G - 1);        // lanes past the group read a real row; unused
   const char* kc = reinterpret_cast<const char*>(a.k_cache);
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
   const __bf16* qbase = reinterpret_cast<const __bf16*>(a.q);
 
-  const char* kp = kc;
-  const char* kp1 = kc;
-  const char* vp = vc;
+  int64_t tile0 = 0, tile1 = 0;  // the last real step's tiles (filler steps reload them)
   const __bf16* qp = qbase;
 
   auto issue = [&](S& sl) {
@@ -386,46 +370,35 @@ void decode_mfma_stream(const DecodeArgs a) {
       int p1 = (C::kBlocksPerStep == 2 && lb0 + 1 <= lb_last) ? tables[row + lb0 + 1] : p0;
       p0 = (p0 < 0 || (int64_t)p0 >= a.num_blocks) ? 0 : p0;
       p1 = (p1 < 0 || (int64_t)p1 >= a.num_blocks) ? 0 : p1;
-      const int64_t tile0 = ((int64_t)p0 * a.num_kv_heads + ch) * C::kTile;
-      const int64_t tile1 = ((int64_t)p1 * a.num_kv_heads + ch) * C::kTile;
-      kp = kc + tile0 + koff;
-      kp1 = (BS == 16) ? kc + tile1 + koff : kp + 16 * 16;
-      vp = vc + (vblk ? tile1 : tile0) + voff;
+      tile0 = ((int64_t)p0 * a.num_kv_heads + ch) * C::kTile;
+      tile1 = ((int64_t)p1 * a.num_kv_heads + ch) * C::kTile;
       qp = qbase + ((size_t)cb * a.num_q_heads + (size_t)ch * G + qhead) * D;
       ++ci;
       --left;
       ++pending;
     }
+    load_step(sl, kc, vc, tile0, tile1, lo, grp);
 #pragma unroll
-    for (int j = 0; j < C::kKLoads; ++j) {
-      sl.k[0][j] = stream_load<u32x4>(kp + j * 4 * C::kChunkRow);
-      sl.k[1][j] = stream_load<u32x4>(kp1 + j * 4 * C::kChunkRow);
-    }
-#pragma unroll
-    for (int dt = 0; dt < C::kDTiles; ++dt) {
-      if constexpr (FP8) sl.v[dt].w = stream_load<u32x2>(vp + dt * 16 * C::kRowV);
-      else sl.v[dt].w = stream_load<u32x4>(vp + dt * 16 * C::kRowV);
-    }
-#pragma unroll
-    for (int c = 0; c < C::kChunks; ++c) {
-      const int d0 = FP8 ? (c >> 1) * 64 + grp * 16 + (c & 1) * 8 : c * 32 + grp * 8;
-      sl.q[c] = *reinterpret_cast<const bf16x8*>(qp + d0);
-    }
+    for (int c = 0; c < C::kChunks; ++c)
+      sl.q[c] = *reinterpret_cast<const bf16x8*>(qp + q_dim<CK, D>(grp, c));
   };
 
   // ---- compute side ---------------------------------------------------------
   f32x4 acc[C::kDTiles];
-  float m_run = -INFINITY, l_run = 0.f, c2 = 0.f;
+  f32x4 accb = {0.f, 0.f, 0.f, 0.f};  // INT4: column sums of the PV weights
+  float m_run = -INFINITY, l_run = 0.f, c2 = 0.f, qbias = 0.f;
 
   auto compute = [&](S& sl) {
     if (sl.flags & kFirst) {
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accb = f32x4{0.f, 0.f, 0.f, 0.f};
       m_run = -INFINITY;
       l_run = 0.f;
       float kscale = 1.0f;
       if constexpr (FP8) kscale = ((const_f32)a.k_scale)[sl.h];
       c2 = a.scale * kscale * kLog2e;
+      if constexpr (C::I4) qbias = q_bias<C::kChunks>(sl.q);
     }
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -438,12 +411,11 @@ void decode_mfma_stream(const DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) zok[i] = !partial || sl.base + qk_token(grp, i) < sl.t1;
     float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = zok[i] ? __fmul_rn(z[i], c2) : -INFINITY;
+    qk_to_log2<CK>(z, sl, zok, c2, qbias);
     if (partial) {
       const int vvalid = min(max(sl.t1 - (sl.base + 8 * grp), 0), 8);
 #pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<FP8>(sl.v[dt], vvalid);
+      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sl.v[dt], vvalid);
     }
     float mx = z[0];
 #pragma unroll
@@ -455,6 +427,7 @@ void decode_mfma_stream(const DecodeArgs a) {
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] *= alpha;
+      if constexpr (C::I4) accb *= alpha;
       m_run = m_new;
     }
     float p[8];
@@ -463,16 +436,23 @@ void decode_mfma_stream(const DecodeArgs a) {
       p[i] = zok[i] ? exp2f(z[i] - m_run) : 0.f;
       l_run += p[i];
     }
-    const bf16x8 pop = p_operand(p);
+    const bf16x8 pop = pv_operand<CK>(p, sl, zok);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<CK>(sl.v[dt]), pop, acc[dt], 0, 0, 0);
+    if constexpr (C::I4) accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop, accb, 0, 0, 0);
 
     if (sl.flags & kLast) {
       const float l_tot = xlane<OpSum, 16, 32>(l_run);
       float vscale = 1.0f;
       if constexpr (FP8) vscale = ((const_f32)a.v_scale)[sl.h];
       const float inv = l_tot > 0.f ? vscale / l_tot : 0.f;  // an empty run writes zeros
+      if constexpr (C::I4) {  // remove the operand bias: 136 * sum_t p(t) s_v(t)
+#pragma unroll
+        for (int dt = 0; dt < C::kDTiles; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[dt][r] = fmaf(-kI4Bias, accb[0], acc[dt][r]);
+      }
       if (col < G) {
         if (sl.flags & kFinal) {
           __bf16* o = reinterpret_cast<__bf16*>(a.out) +
@@ -518,7 +498,6 @@ void decode_mfma_stream(const DecodeArgs a) {
 
 template <int CK, int D, int BS>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-  constexpr bool FP8 = one_byte<CK>();
   if (a.partition == kAuto) {
     DecodeArgs b = a;
     b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : stream_waves_per_cu<CK, D>());
@@ -533,7 +512,6 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
 
 template <int CK>
 hipError_t dispatch_shape(const DecodeArgs& a, int head_dim, int block_size, hipStream_t s) {
-  constexpr bool FP8 = one_byte<CK>();
   if (head_dim == 128 && block_size == 16) return launch<CK, 128, 16>(a, s);
   if (head_dim == 128 && block_size == 32) return launch<CK, 128, 32>(a, s);
   if (head_dim == 64 && block_size == 16) return launch<CK, 64, 16>(a, s);
@@ -548,6 +526,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, Elem cache, int head_dim, int
   if (cache == Elem::BF16) return dispatch_shape<kBF16>(a, head_dim, block_size, stream);
   if (cache == Elem::FP8) return dispatch_shape<kE4M3>(a, head_dim, block_size, stream);
   if (cache == Elem::E5M2) return dispatch_shape<kE5M2>(a, head_dim, block_size, stream);
+  if (cache == Elem::I4) return dispatch_shape<kI4>(a, head_dim, block_size, stream);
   return hipErrorInvalidValue;
 }
 

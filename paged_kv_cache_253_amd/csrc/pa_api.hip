@@ -25,6 +25,7 @@ bool to_elem(pa_dtype t, Elem* e) {
     case PA_BF16: *e = Elem::BF16; return true;
     case PA_FP8_E4M3: *e = Elem::FP8; return true;
     case PA_FP8_E5M2: *e = Elem::E5M2; return true;
+    case PA_INT4: *e = Elem::I4; return true;
   }
   return false;
 }
@@ -128,12 +129,11 @@ pa_status copy_or_swap(const void* src_k, const void* src_v, void* dst_k, void* 
   if (!src_k || !src_v || !dst_k || !dst_v) return PA_ERR_INVALID_ARG;
   if (num_pairs == 0) return PA_OK;  // an empty mapping may come with a null pointer
   if (!block_mapping) return PA_ERR_INVALID_ARG;
-  const int elt = cache == Elem::F32 ? 4 : (cache == Elem::BF16 ? 2 : 1);
   pa::CopyArgs a;
   a.src_k = src_k; a.src_v = src_v; a.dst_k = dst_k; a.dst_v = dst_v;
   a.mapping = block_mapping;
   a.src_blocks = src_blocks; a.dst_blocks = dst_blocks;
-  a.block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elt;
+  a.block_bytes = (int64_t)num_kv_heads * pa::tile_bytes(cache, head_dim, block_size);
   a.num_pairs = num_pairs;
   if (a.block_bytes > (int64_t)65535 * 4096) return PA_ERR_UNSUPPORTED;  // grid z limit
   return from_hip(pa::launch_copy_blocks(a, stream));
@@ -175,8 +175,8 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new, void* k_cache,
   Elem src, cache;
   if (!to_elem(src_dtype, &src) || !to_elem(cache_dtype, &cache)) return PA_ERR_INVALID_ARG;
   if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
-  if (is_fp8(src)) return PA_ERR_UNSUPPORTED;
-  if (cache != src && !is_fp8(cache)) return PA_ERR_UNSUPPORTED;
+  if (src != Elem::F32 && src != Elem::BF16) return PA_ERR_UNSUPPORTED;
+  if (cache != src && !is_fp8(cache) && cache != Elem::I4) return PA_ERR_UNSUPPORTED;
   if (num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
   if (is_fp8(cache) && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
@@ -234,7 +234,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (!to_elem(q_dtype, &qe) || !to_elem(cache_dtype, &ce)) return PA_ERR_INVALID_ARG;
   if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
   const bool combo_ok = (qe == Elem::F32 && ce == Elem::F32) || (qe == Elem::BF16 && ce == Elem::BF16) ||
-                        (qe == Elem::BF16 && is_fp8(ce));
+                        (qe == Elem::BF16 && (is_fp8(ce) || ce == Elem::I4));
   if (!combo_ok) return PA_ERR_UNSUPPORTED;
   if (partition_size > 0 && partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
@@ -249,6 +249,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (ce == Elem::F32) {
     if (force == 2 || !valu_group) return PA_ERR_UNSUPPORTED;
     use_mfma = false;
+  } else if (ce == Elem::I4) {  // matrix-core kernels only, any G <= 16
+    if (force == 1 || group > 16) return PA_ERR_UNSUPPORTED;
+    use_mfma = true;
   } else if (force == 1) {
     if (!valu_group) return PA_ERR_UNSUPPORTED;
     use_mfma = false;

@@ -95,6 +95,37 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// INT4 codes
+// ---------------------------------------------------------------------------
+
+// Bias of the widened INT4 operands: a code c becomes the bf16 136 + c.
+constexpr float kI4Bias = 136.0f;
+
+// One octet word of INT4 codes (byte i: element i in the low nibble,
+// element i + 4 in the high nibble, two's complement) -> eight bf16 holding
+// 136 + code, in element order.  XOR with 8 turns each nibble into c + 8
+// (0..15); a bf16 with high byte 0x43 and low byte u is exactly 128 + u for
+// u < 128, so one byte permute per pair builds the bit patterns.  Exact; the
+// consumer subtracts the bias in float32.
+__device__ __forceinline__ u32x4 i4x8_biased_words(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu;         // elements 0..3, one per byte
+  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // elements 4..7
+  constexpr uint32_t k43 = 0x43434343u;
+  // v_perm_b32: selector byte 0..3 picks a byte of the second operand, 4..7
+  // of the first; {b0, 0x43, b1, 0x43} and {b2, 0x43, b3, 0x43}
+  return u32x4{__builtin_amdgcn_perm(k43, lo, 0x04010400u), __builtin_amdgcn_perm(k43, lo, 0x04030402u),
+               __builtin_amdgcn_perm(k43, hi, 0x04010400u), __builtin_amdgcn_perm(k43, hi, 0x04030402u)};
+}
+
+// INT4 code of x under scale s (s > 0): x / s rounded once in binary32,
+// then to the nearest integer, ties to even, kept within -7..7.
+__device__ __forceinline__ int i4_code(float x, float s) {
+  const float q = __builtin_rintf(__fdiv_rn(x, s));
+  return (int)fminf(fmaxf(q, -7.0f), 7.0f);
+}
+
+// ---------------------------------------------------------------------------
 // cross-lane combine.  DPP row controls (within 16-lane rows):
 //   0xB1 quad_perm[1,0,3,2]  (partner = lane ^ 1)
 //   0x4E quad_perm[2,3,0,1]  (partner = lane ^ 2)

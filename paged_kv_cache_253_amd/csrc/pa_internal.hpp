@@ -6,9 +6,17 @@
 
 namespace pa {
 
-// Element types: FP8 is E4M3FN, E5M2 the other FP8 format.
-enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2, E5M2 = 3 };
+// Element types: FP8 is E4M3FN, E5M2 the other FP8 format, I4 the 4-bit
+// integer codes with a float32 scale per (token, KV head) in each tile.
+enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2, E5M2 = 3, I4 = 4 };
 inline bool is_fp8(Elem e) { return e == Elem::FP8 || e == Elem::E5M2; }
+
+// Bytes of one (block, KV head) tile of a pool.
+inline int64_t tile_bytes(Elem e, int head_dim, int block_size) {
+  if (e == Elem::I4) return (int64_t)block_size * (head_dim / 2 + 4);
+  const int elt = e == Elem::F32 ? 4 : (e == Elem::BF16 ? 2 : 1);
+  return (int64_t)block_size * head_dim * elt;
+}
 
 // Balanced split: most persistent wavefronts per compute unit any decode
 // kernel uses (sizes the workspace and the merge grid), minimum slice length
@@ -67,7 +75,7 @@ struct PrefillArgs {
 // query tiles of a sequence, for group size G and the longest query run.
 // A bf16 cache with head_dim 128 stops at 2 column tiles (4 would spill).
 inline int prefill_max_column_tiles(Elem cache, int head_dim) {
-  return (cache == Elem::BF16 && head_dim == 128) ? 2 : 4;
+  return ((cache == Elem::BF16 || cache == Elem::I4) && head_dim == 128) ? 2 : 4;
 }
 inline int prefill_column_tiles(int group, int max_query_len, int max_tiles) {
   const long long cols = (long long)group * max_query_len;
@@ -100,7 +108,7 @@ struct CopyArgs {
   void* dst_v;
   const int64_t* mapping;       // [num_pairs][2] (src, dst) block ids
   int64_t src_blocks, dst_blocks;
-  int64_t block_bytes;          // one block of one pool: Hkv * B * D * elt
+  int64_t block_bytes;          // one block of one pool: Hkv tiles
   int num_pairs;
 };
 

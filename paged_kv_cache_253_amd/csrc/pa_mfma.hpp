@@ -11,6 +11,17 @@
 // then holds the scores of tokens 4*(l/16) + r and 16 + 4*(l/16) + r (r =
 // 0..3), while its PV k-slots need tokens 8*(l/16) .. +7: p_operand moves
 // them there with two lane swaps.
+//
+// The k-slots of QK chunk c map to head dimensions per cache kind (q_dim):
+// any map works as long as q and K use the same one, so each kind takes the
+// one its K loads deliver.
+//
+// INT4 caches: K and V codes widen to bf16 136 + code (exact; see
+// i4x8_biased_words) and the bias is removed in float32: a score is
+// s_k(t) * (S - 136 * sum_d q_d) with S the MFMA result, and the PV
+// operand carries p(t) * s_v(t), whose own sum (one extra MFMA against a
+// row of ones) gives the 136 * sum_t p(t) s_v(t) to subtract from the
+// output.  Every token's two scales sit at the end of its tile.
 #pragma once
 
 #include "pa_device.hpp"
@@ -23,36 +34,119 @@ constexpr int kStep = 32;  // tokens per step
 
 // Cache element kinds of the matrix-core kernels.  The two FP8 kinds share
 // the 1-byte layout and differ only in how a code widens to bf16.
-constexpr int kBF16 = 0, kE4M3 = 1, kE5M2 = 2;
+constexpr int kBF16 = 0, kE4M3 = 1, kE5M2 = 2, kI4 = 3;
 template <int CK>
-constexpr bool one_byte() { return CK != kBF16; }
+constexpr bool one_byte() { return CK == kE4M3 || CK == kE5M2; }
 
 template <int CK, int D, int BS>
 struct Cfg {
   static constexpr bool FP8 = one_byte<CK>();
-  static constexpr int kElt = FP8 ? 1 : 2;
+  static constexpr bool I4 = CK == kI4;
+  static constexpr int kElt = FP8 ? 1 : 2;          // bytes per element (bf16 / FP8)
   static constexpr int kChunks = D / 32;            // QK MFMAs per token group
   static constexpr int kDTiles = D / 16;            // PV MFMAs per step
-  static constexpr int kKLoads = FP8 ? D / 64 : D / 32;  // 16-byte K loads per token group
+  // K loads per token group and lane: 16 bytes each (INT4: D/8 bytes, one load)
+  static constexpr int kKLoads = I4 ? 1 : (FP8 ? D / 64 : D / 32);
   static constexpr int kChunkRow = BS * 16;         // bytes of one K chunk row (16 B per token)
-  static constexpr int kRowV = BS * kElt;           // bytes of one V row (dimension)
-  static constexpr int kTile = BS * D * kElt;       // bytes of one (block, head) tile
+  static constexpr int kRowV = I4 ? BS / 2 : BS * kElt;  // bytes of one V row (dimension)
+  static constexpr int kCodeBytes = I4 ? BS * D / 2 : BS * D * kElt;
+  static constexpr int kTile = I4 ? BS * (D / 2 + 4) : kCodeBytes;  // one (block, head) tile
   static constexpr int kBlocksPerStep = kStep / BS;
 };
 
-template <bool FP8>
-struct VRaw;
+// Raw K words of one token group (per lane).
+template <int CK, int D>
+struct KWord { using T = u32x4; };
 template <>
-struct VRaw<false> { u32x4 w; };  // 8 bf16 tokens
+struct KWord<kI4, 64> { using T = u32x2; };
+
+// Raw V words of one PV tile (per lane: 8 tokens of one dimension).
+template <int CK>
+struct VRaw { u32x4 w; };     // 8 bf16
 template <>
-struct VRaw<true> { u32x2 w; };   // 8 e4m3 tokens
+struct VRaw<kE4M3> { u32x2 w; };
+template <>
+struct VRaw<kE5M2> { u32x2 w; };
+template <>
+struct VRaw<kI4> { uint32_t w; };
+
+// Per-token scales of an INT4 step, in QK register order: k[0] / v[0] for
+// tokens 4*grp + r, k[1] / v[1] for tokens 16 + 4*grp + r.
+template <int CK>
+struct TokScales {};
+template <>
+struct TokScales<kI4> { f32x4 k[2], v[2]; };
 
 template <int CK, int D, int BS>
 struct StepBuf {
   using C = Cfg<CK, D, BS>;
-  u32x4 k[2][C::kKLoads];
-  VRaw<C::FP8> v[C::kDTiles];
+  typename KWord<CK, D>::T k[2][C::kKLoads];
+  VRaw<CK> v[C::kDTiles];
+  TokScales<CK> ts;
 };
+
+// Head dimension of k-slot 0 of QK chunk c for lane group grp (8 contiguous
+// dimensions follow it).
+template <int CK, int D>
+__device__ __forceinline__ int q_dim(int grp, int c) {
+  if constexpr (CK == kI4) return (D / 4) * grp + 8 * c;                  // one D/8-byte load
+  else if constexpr (one_byte<CK>()) return (c >> 1) * 64 + grp * 16 + (c & 1) * 8;
+  else return c * 32 + grp * 8;
+}
+
+// Byte offsets of a lane's data inside the step's tiles: K (token col of
+// group 0, its k-slot dimensions) and V (dimension col of PV tile 0, tokens
+// 8*grp .. +7 of the step, in tile vblk of the step).
+template <int CK, int D, int BS>
+struct LaneOffsets {
+  uint32_t koff, voff;
+  int vblk;
+  __device__ __forceinline__ LaneOffsets(int grp, int col) {
+    using C = Cfg<CK, D, BS>;
+    if constexpr (CK == kI4) {
+      const int dim0 = (D / 4) * grp;
+      koff = (uint32_t)(((dim0 / 32) * BS + col) * 16 + (dim0 % 32) / 2);
+    } else {
+      koff = (uint32_t)((grp * BS + col) * 16);
+    }
+    vblk = (BS == 16) ? (grp >> 1) : 0;
+    const int vtok = (BS == 16) ? 8 * (grp & 1) : 8 * grp;
+    voff = (uint32_t)(col * C::kRowV) + (CK == kI4 ? (uint32_t)(vtok / 2) : (uint32_t)(vtok * C::kElt));
+  }
+};
+
+// Issue one step's tile loads.  tile0 / tile1: byte offsets of the (block,
+// head) tiles of the step's first and second 16 tokens (equal at block size
+// 32).  Every call issues the same number of loads.
+template <int CK, int D, int BS>
+__device__ __forceinline__ void load_step(StepBuf<CK, D, BS>& sb, const char* kc, const char* vc,
+                                          int64_t tile0, int64_t tile1, const LaneOffsets<CK, D, BS>& lo,
+                                          int grp) {
+  using C = Cfg<CK, D, BS>;
+  using KW = typename KWord<CK, D>::T;
+  const char* kp0 = kc + tile0 + lo.koff;
+  const char* kp1 = (BS == 16) ? kc + tile1 + lo.koff : kp0 + 16 * 16;
+  const char* vp = vc + (lo.vblk ? tile1 : tile0) + lo.voff;
+#pragma unroll
+  for (int j = 0; j < C::kKLoads; ++j) {
+    sb.k[0][j] = stream_load<KW>(kp0 + j * 4 * C::kChunkRow);
+    sb.k[1][j] = stream_load<KW>(kp1 + j * 4 * C::kChunkRow);
+  }
+#pragma unroll
+  for (int dt = 0; dt < C::kDTiles; ++dt) {
+    if constexpr (CK == kI4) sb.v[dt].w = stream_load<uint32_t>(vp + dt * 16 * C::kRowV);
+    else if constexpr (C::FP8) sb.v[dt].w = stream_load<u32x2>(vp + dt * 16 * C::kRowV);
+    else sb.v[dt].w = stream_load<u32x4>(vp + dt * 16 * C::kRowV);
+  }
+  if constexpr (CK == kI4) {
+    const int64_t s0 = tile0 + C::kCodeBytes + 16 * grp;
+    const int64_t s1 = (BS == 16) ? tile1 + C::kCodeBytes + 16 * grp : s0 + 64;
+    sb.ts.k[0] = stream_load<f32x4>(kc + s0);
+    sb.ts.k[1] = stream_load<f32x4>(kc + s1);
+    sb.ts.v[0] = stream_load<f32x4>(vc + s0);
+    sb.ts.v[1] = stream_load<f32x4>(vc + s1);
+  }
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
@@ -76,7 +170,9 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 // K operand of QK chunk c for token group m (from a buffer with k[2][..])
 template <int CK, class Buf>
 __device__ __forceinline__ bf16x8 k_operand(const Buf& sb, int m, int c) {
-  if constexpr (one_byte<CK>()) {
+  if constexpr (CK == kI4) {
+    return as_bf16x8(i4x8_biased_words(sb.k[m][0][c]));
+  } else if constexpr (one_byte<CK>()) {
     const u32x4 w = sb.k[m][c >> 1];
     return (c & 1) ? fp8x8_to_bf16x8<CK>(w[2], w[3]) : fp8x8_to_bf16x8<CK>(w[0], w[1]);
   } else {
@@ -111,22 +207,24 @@ __device__ __forceinline__ bf16x8 p_operand(const float* p) {
 __device__ __forceinline__ int qk_token(int grp, int i) { return 4 * grp + (i & 3) + 16 * (i >> 2); }
 
 template <int CK>
-__device__ __forceinline__ bf16x8 v_operand(const VRaw<one_byte<CK>()>& r) {
-  if constexpr (one_byte<CK>()) return fp8x8_to_bf16x8<CK>(r.w[0], r.w[1]);
+__device__ __forceinline__ bf16x8 v_operand(const VRaw<CK>& r) {
+  if constexpr (CK == kI4) return as_bf16x8(i4x8_biased_words(r.w));
+  else if constexpr (one_byte<CK>()) return fp8x8_to_bf16x8<CK>(r.w[0], r.w[1]);
   else return as_bf16x8(r.w);
 }
 
-// Zero the V elements of k-slots whose token is past the range end.
-template <bool FP8>
-__device__ __forceinline__ void mask_v(VRaw<FP8>& r, int valid) {  // valid = tokens kept, 0..8
-  if constexpr (FP8) {
+// Zero the V elements of k-slots whose token is past the range end.  INT4
+// needs none: its codes are finite and those tokens' weights are zero.
+template <int CK>
+__device__ __forceinline__ void mask_v(VRaw<CK>& r, int valid) {  // valid = tokens kept, 0..8
+  if constexpr (one_byte<CK>()) {
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       int n = valid - 4 * w;
       uint32_t keep = n >= 4 ? 0xffffffffu : (n <= 0 ? 0u : (0xffffffffu >> (32 - 8 * n)));
       r.w[w] &= keep;
     }
-  } else {
+  } else if constexpr (CK == kBF16) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       int n = valid - 2 * w;
@@ -134,6 +232,58 @@ __device__ __forceinline__ void mask_v(VRaw<FP8>& r, int valid) {  // valid = to
       r.w[w] &= keep;
     }
   }
+}
+
+// Raw QK results (QK register order) -> scores in log2 units, -inf where
+// the token is outside the range.  c2 = softmax scale * log2(e) (times the
+// FP8 K scale); INT4: qbias = 136 * sum of the lane column's q, and each
+// token's own K scale.
+template <int CK, class Buf>
+__device__ __forceinline__ void qk_to_log2(float* z, const Buf& sb, const bool* ok, float c2,
+                                           float qbias) {
+  if constexpr (CK == kI4) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float ks = sb.ts.k[i >> 2][i & 3];
+      z[i] = ok[i] ? (z[i] - qbias) * (ks * c2) : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = ok[i] ? __fmul_rn(z[i], c2) : -INFINITY;
+  }
+}
+
+// PV weights: the softmax weights, times each token's V scale for INT4
+// (selected to 0 outside the range, where a scale may be anything).
+template <int CK, class Buf>
+__device__ __forceinline__ bf16x8 pv_operand(const float* p, const Buf& sb, const bool* ok) {
+  if constexpr (CK == kI4) {
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = ok[i] ? p[i] * sb.ts.v[i >> 2][i & 3] : 0.f;
+    return p_operand(pv);
+  } else {
+    return p_operand(p);
+  }
+}
+
+// bf16 1.0 in every k-slot: the A operand whose product with the PV weights
+// is their column sums.
+__device__ __forceinline__ bf16x8 ones_operand() {
+  const u32x4 w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  return as_bf16x8(w);
+}
+
+// 136 * sum of this lane column's q over all head dimensions (the lanes of
+// one column hold disjoint dimension sets; all lanes must call).
+template <int NC>
+__device__ __forceinline__ float q_bias(const bf16x8* q) {
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += (float)q[c][e];
+  return kI4Bias * xlane<OpSum, 16, 32>(s);
 }
 
 }  // namespace mfma

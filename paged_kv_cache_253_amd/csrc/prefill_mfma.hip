@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
     for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
       for (int c = 0; c < C::kChunks; ++c) {
-        const int d0 = FP8 ? (c >> 1) * 64 + grp * 16 + (c & 1) * 8 : c * 32 + grp * 8;
+        const int d0 = q_dim<CK, D>(grp, c);
         if (cvalid[ct]) {
           qop[ct][c] = *reinterpret_cast<const bf16x8*>(qbase + qrow[ct] * D + d0);
         } else {
@@ -98,21 +98,22 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
   const float c2 = a.scale * kscale * kLog2e;  // q.k -> log2 units
 
   f32x4 acc[NT][C::kDTiles];
-  float m_run[NT], l_run[NT];
+  f32x4 accb[NT];  // INT4: column sums of the PV weights
+  float m_run[NT], l_run[NT], qbias[NT];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
     m_run[ct] = -INFINITY;
     l_run[ct] = 0.f;
+    accb[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    qbias[ct] = 0.f;
+    if constexpr (C::I4) qbias[ct] = q_bias<C::kChunks>(qop[ct]);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt) acc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   if (t0 < t1) {
     // ---- per-lane byte offsets inside a step's tiles (as the decode) -------
-    const uint32_t koff = ((uint32_t)grp * BS + (uint32_t)col) * 16;
-    const int vblk = (BS == 16) ? (grp >> 1) : 0;
-    const uint32_t vtok = (BS == 16) ? (uint32_t)(8 * (grp & 1)) : (uint32_t)(8 * grp);
-    const uint32_t voff = (uint32_t)col * C::kRowV + vtok * C::kElt;
+    const LaneOffsets<CK, D, BS> lo(grp, col);
     const char* kc = reinterpret_cast<const char*>(a.k_cache);
     const char* vc = reinterpret_cast<const char*>(a.v_cache);
     const int32_t* table = a.block_tables + (size_t)b * a.max_blocks;
@@ -137,19 +138,7 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
       const int64_t p1 = (C::kBlocksPerStep == 2) ? phys_of(lb1) : p0;
       const int64_t tile0 = (p0 * a.num_kv_heads + h) * C::kTile;
       const int64_t tile1 = (p1 * a.num_kv_heads + h) * C::kTile;
-      const char* kp0 = kc + tile0 + koff;
-      const char* kp1 = (BS == 16) ? kc + tile1 + koff : kp0 + 16 * 16;
-      const char* vp = vc + (vblk ? tile1 : tile0) + voff;
-#pragma unroll
-      for (int j = 0; j < C::kKLoads; ++j) {
-        sb.k[0][j] = stream_load<u32x4>(kp0 + j * 4 * C::kChunkRow);
-        sb.k[1][j] = stream_load<u32x4>(kp1 + j * 4 * C::kChunkRow);
-      }
-#pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt) {
-        if constexpr (FP8) sb.v[dt].w = stream_load<u32x2>(vp + dt * 16 * C::kRowV);
-        else sb.v[dt].w = stream_load<u32x4>(vp + dt * 16 * C::kRowV);
-      }
+      load_step(sb, kc, vc, tile0, tile1, lo, grp);
     };
 
     auto compute = [&](StepBuf<CK, D, BS>& sb, int step) {
@@ -170,7 +159,7 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
       if (base + kStep > t1) {  // PV k-slots of this lane: tokens 8*grp .. +7
         const int vvalid = min(max(t1 - (base + 8 * grp), 0), 8);
 #pragma unroll
-        for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<FP8>(sb.v[dt], vvalid);
+        for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sb.v[dt], vvalid);
       }
       bf16x8 pop[NT];
 #pragma unroll
@@ -180,10 +169,8 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
         float z[8] = {s0[ct][0], s0[ct][1], s0[ct][2], s0[ct][3],
                       s1[ct][0], s1[ct][1], s1[ct][2], s1[ct][3]};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ok[i] = cvalid[ct] && base + qk_token(grp, i) <= lim;
-          z[i] = ok[i] ? __fmul_rn(z[i], c2) : -INFINITY;
-        }
+        for (int i = 0; i < 8; ++i) ok[i] = cvalid[ct] && base + qk_token(grp, i) <= lim;
+        qk_to_log2<CK>(z, sb, ok, c2, qbias[ct]);
         float mx = z[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
@@ -194,6 +181,7 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
           l_run[ct] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < C::kDTiles; ++dt) acc[ct][dt] *= alpha;
+          if constexpr (C::I4) accb[ct] *= alpha;
           m_run[ct] = m_new;
         }
         float p[8];
@@ -202,7 +190,7 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
           p[i] = ok[i] ? exp2f(z[i] - m_run[ct]) : 0.f;
           l_run[ct] += p[i];
         }
-        pop[ct] = p_operand(p);
+        pop[ct] = pv_operand<CK>(p, sb, ok);
       }
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) {
@@ -210,6 +198,11 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct)
           acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[ct], acc[ct][dt], 0, 0, 0);
+      }
+      if constexpr (C::I4) {
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+          accb[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop[ct], accb[ct], 0, 0, 0);
       }
     };
 
@@ -230,6 +223,12 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
     const float l_tot = xlane<OpSum, 16, 32>(l_run[ct]);
     if (!cvalid[ct]) continue;
     const float inv = l_tot > 0.f ? vscale / l_tot : 0.f;  // a row with no token writes zeros
+    if constexpr (C::I4) {  // remove the operand bias: 136 * sum_t p(t) s_v(t)
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ct][dt][r] = fmaf(-kI4Bias, accb[ct][0], acc[ct][dt][r]);
+    }
     if (a.partition == 0) {
       __bf16* o = reinterpret_cast<__bf16*>(a.out) + qrow[ct] * D;
 #pragma unroll
@@ -258,8 +257,8 @@ template <int CK, int D, int BS, int NT>
 hipError_t launch_nt(const PrefillArgs& p, hipStream_t stream) {
   constexpr bool FP8 = one_byte<CK>();
   const DecodeArgs& a = p.d;
-  const int tiles = prefill_query_tiles(a.group, p.max_query_len,
-                                        prefill_max_column_tiles(FP8 ? Elem::FP8 : Elem::BF16, D));  // FP8 kinds alike
+  const Elem e = CK == kI4 ? Elem::I4 : (FP8 ? Elem::FP8 : Elem::BF16);  // FP8 kinds alike
+  const int tiles = prefill_query_tiles(a.group, p.max_query_len, prefill_max_column_tiles(e, D));
   const int parts = a.partition ? a.max_parts : 1;
   if ((long long)tiles * a.num_kv_heads > 65535) return hipErrorInvalidValue;
   dim3 grid(parts, tiles * a.num_kv_heads, a.num_seqs);
@@ -269,8 +268,7 @@ hipError_t launch_nt(const PrefillArgs& p, hipStream_t stream) {
 
 template <int CK, int D, int BS>
 hipError_t launch_shape(const PrefillArgs& p, hipStream_t stream) {
-  constexpr bool FP8 = one_byte<CK>();
-  constexpr int kMaxNT = (!FP8 && D == 128) ? 2 : 4;
+  constexpr int kMaxNT = (!one_byte<CK>() && D == 128) ? 2 : 4;  // as prefill_max_column_tiles
   switch (prefill_column_tiles(p.d.group, p.max_query_len, kMaxNT)) {
     case 1: return launch_nt<CK, D, BS, 1>(p, stream);
     case 2: return launch_nt<CK, D, BS, 2>(p, stream);
@@ -282,7 +280,6 @@ hipError_t launch_shape(const PrefillArgs& p, hipStream_t stream) {
 
 template <int CK>
 hipError_t dispatch(const PrefillArgs& p, int head_dim, int block_size, hipStream_t s) {
-  constexpr bool FP8 = one_byte<CK>();
   if (head_dim == 128 && block_size == 16) return launch_shape<CK, 128, 16>(p, s);
   if (head_dim == 128 && block_size == 32) return launch_shape<CK, 128, 32>(p, s);
   if (head_dim == 64 && block_size == 16) return launch_shape<CK, 64, 16>(p, s);
@@ -297,6 +294,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& p, Elem cache, int head_dim, i
   if (cache == Elem::BF16) return dispatch<kBF16>(p, head_dim, block_size, stream);
   if (cache == Elem::FP8) return dispatch<kE4M3>(p, head_dim, block_size, stream);
   if (cache == Elem::E5M2) return dispatch<kE5M2>(p, head_dim, block_size, stream);
+  if (cache == Elem::I4) return dispatch<kI4>(p, head_dim, block_size, stream);
   return hipErrorInvalidValue;
 }
 

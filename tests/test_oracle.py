@@ -34,7 +34,7 @@ def _impl(**over):
               e5m2_to_f64=codecs.e5m2_to_f64, e5m2_encode=codecs.e5m2_encode,
               int4_encode=codecs.int4_encode, unpack_octets=paged.unpack_octets,
               pack_octets=paged.pack_octets, int4_k_row=paged.int4_k_row,
-              int4_v_row=paged.int4_v_row)
+              int4_v_row=paged.int4_v_row, int4_block_values=paged.int4_block_values)
     ns.update(over)
     return types.SimpleNamespace(**ns)
 
@@ -572,11 +572,12 @@ def pin_int4_octets(impl):
 
 def pin_int4_tile_index(impl):
     """INT4 tiles built byte by byte from the layout's index arithmetic
-    (written here, not taken from the oracle) read back token by token:
-    K element i of token j at byte (i // 32 * B + j) * 16 + (i % 32) // 8 * 4
-    + i % 4, high nibble iff i % 8 >= 4; V element of dimension i, token j at
-    byte i * B / 2 + j // 8 * 4 + j % 4, high nibble iff j % 8 >= 4; token
-    j's scale at byte B * d / 2 + 4 j."""
+    (written here, not taken from the oracle) read back token by token and
+    block by block: K element i of token j at byte (i // 32 * B + j) * 16 +
+    (i % 32) // 8 * 4 + i % 4, high nibble iff i % 8 >= 4; V element of
+    dimension i, token j at byte i * B / 2 + j // 8 * 4 + j % 4, high nibble
+    iff j % 8 >= 4; token j's scale at byte B * d / 2 + 4 j.  An append of
+    rows with absmax 7 (scale 1, codes = the values) writes those bytes."""
     rng = np.random.default_rng(32)
     for d, bsz in ((64, 16), (128, 32)):
         kc = rng.integers(-8, 8, (bsz, d))
@@ -599,6 +600,26 @@ def pin_int4_tile_index(impl):
             assert np.array_equal(c, kc[j]) and s_ == ks[j]
             c, s_ = impl.int4_v_row(vpool, 0, 0, j, bsz)
             assert np.array_equal(c, vc[j]) and s_ == vs[j]
+        assert np.array_equal(impl.int4_block_values(kpool[0], bsz, "k")[:, 0],
+                              kc * ks[:, None].astype(np.float64))
+        assert np.array_equal(impl.int4_block_values(vpool[0], bsz, "v")[:, 0],
+                              vc * vs[:, None].astype(np.float64))
+        # append: rows reaching +-7 get scale 1 and store their own values
+        rows_k = np.clip(kc, -7, 7).astype(np.float32)
+        rows_v = np.clip(vc, -7, 7).astype(np.float32)
+        rows_k[:, 0], rows_v[:, 0] = 7.0, -7.0
+        empty = np.zeros((1, 1, bsz * (d // 2 + 4)), np.uint8)
+        kw, vw = impl.write_tokens(empty, empty.copy(), rows_k[:, None, :], rows_v[:, None, :],
+                                   np.arange(bsz), bsz, "f32", "int4")
+        want = np.zeros((2, bsz * (d // 2 + 4)), np.uint8)
+        for j in range(bsz):
+            for i in range(d):
+                kb = (i // 32 * bsz + j) * 16 + (i % 32) // 8 * 4 + i % 4
+                vb = i * bsz // 2 + j // 8 * 4 + j % 4
+                want[0, kb] |= (int(rows_k[j, i]) & 15) << (4 if i % 8 >= 4 else 0)
+                want[1, vb] |= (int(rows_v[j, i]) & 15) << (4 if j % 8 >= 4 else 0)
+        want[:, bsz * d // 2:] = np.ones(bsz, np.float32).view(np.uint8)
+        assert np.array_equal(kw[0, 0], want[0]) and np.array_equal(vw[0, 0], want[1])
 
 
 def pin_int4_write_then_decode(impl):
@@ -982,6 +1003,16 @@ def _bad_int4_v_token_major(v_pool, blk, h, off, block_size):
     return rows[off].copy(), paged._int4_scale(tile, d, block_size, off)
 
 
+def _bad_int4_block_v_token_major(tiles, block_size, which):
+    if which == "k":
+        return paged.int4_block_values(tiles, block_size, which)
+    n_kv, tile = tiles.shape
+    d = paged.int_tile_head_dim(tile, block_size)
+    c = paged.unpack_octets(tiles[:, :block_size * d // 2].reshape(n_kv, block_size, d // 2))
+    s_ = tiles[:, block_size * d // 2:].copy().view(np.float32).astype(np.float64)
+    return c.transpose(1, 0, 2) * s_.T[:, :, None]
+
+
 def _bad_int4_k_dims_interleaved(k_pool, blk, h, off, block_size):
     codes, scale = paged.int4_k_row(k_pool, blk, h, off, block_size)
     return codes.reshape(-1, 2)[:, ::-1].reshape(-1), scale
@@ -1040,6 +1071,7 @@ MUTANTS = {
     "int4-ones-complement": dict(unpack_octets=_bad_unpack_ones_complement),
     "int4-v-token-major": dict(int4_v_row=_bad_int4_v_token_major),
     "int4-k-dims-interleaved": dict(int4_k_row=_bad_int4_k_dims_interleaved),
+    "int4-block-v-token-major": dict(int4_block_values=_bad_int4_block_v_token_major),
 }
 
 
