@@ -105,7 +105,10 @@ def bench_copy(args) -> int:
     from oracle import paged
     from workloads import WORKLOADS, copy_bytes, host_view, make_batch
 
-    w = WORKLOADS[args.workload]
+    w = with_cache_dtype(WORKLOADS[args.workload], args.cache_dtype)
+    if w is None:
+        return 2
+    kw = dict(cache_dtype=w.cache_dtype, block_size=w.block_size)
     dev = "cuda"
     batch = make_batch(w, device=dev)
     nb = batch.num_blocks
@@ -114,13 +117,13 @@ def bench_copy(args) -> int:
     pairs_np = np.stack([ids[:npairs], ids[npairs:]], axis=1).astype(np.int64)
     pairs = torch.from_numpy(pairs_np).to(dev)
     for _ in range(args.warmup):
-        pk.copy_blocks(batch.k_pool, batch.v_pool, pairs)
+        pk.copy_blocks(batch.k_pool, batch.v_pool, pairs, **kw)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        pk.copy_blocks(batch.k_pool, batch.v_pool, pairs)
+        pk.copy_blocks(batch.k_pool, batch.v_pool, pairs, **kw)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -179,7 +182,10 @@ def bench_swap(args) -> int:
     import paged_kv_cache_253_amd as pk
     from workloads import WORKLOADS, copy_bytes, make_batch
 
-    w = WORKLOADS[args.workload]
+    w = with_cache_dtype(WORKLOADS[args.workload], args.cache_dtype)
+    if w is None:
+        return 2
+    kw = dict(cache_dtype=w.cache_dtype, block_size=w.block_size)
     dev = "cuda"
     batch = make_batch(w, device=dev)
     n = batch.num_blocks // 4
@@ -204,8 +210,8 @@ def bench_swap(args) -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    ms_out = timed(lambda: pk.swap_blocks(kh, vh, batch.k_pool, batch.v_pool, out_map))
-    ms_in = timed(lambda: pk.swap_blocks(batch.k_pool, batch.v_pool, kh, vh, in_map))
+    ms_out = timed(lambda: pk.swap_blocks(kh, vh, batch.k_pool, batch.v_pool, out_map, **kw))
+    ms_in = timed(lambda: pk.swap_blocks(batch.k_pool, batch.v_pool, kh, vh, in_map, **kw))
     moved = copy_bytes(n, w.num_kv_heads, w.head_dim, w.block_size, w.cache_dtype) // 2  # one side
     gbs_out = moved / (ms_out * 1e-3) / 1e9
     gbs_in = moved / (ms_in * 1e-3) / 1e9
@@ -240,6 +246,9 @@ def bench_prefill(args) -> int:
     from workloads import PREFILL_WORKLOADS, make_batch, prefill_bytes
 
     w, nq = PREFILL_WORKLOADS[args.case]
+    w = with_cache_dtype(w, args.cache_dtype)
+    if w is None:
+        return 2
     dev = "cuda"
     batch = make_batch(w, device=dev)
     lens = batch.context_lens
@@ -255,7 +264,7 @@ def bench_prefill(args) -> int:
     part = args.partition
     if part is None:  # the binding's own choice, made once and reused
         hkv = w.num_kv_heads
-        rows = max(1, 16 * (2 if w.head_dim == 128 and w.cache_dtype == "bf16" else 4)
+        rows = max(1, 16 * (2 if w.head_dim == 128 and w.cache_dtype in ("bf16", "int4") else 4)
                    // (w.num_q_heads // hkv))
         tiles = -(-int(qlens.max()) // rows)
         part = 0 if len(lens) * hkv * tiles >= 1024 or batch.max_context_len <= 1024 else 512
@@ -265,7 +274,7 @@ def bench_prefill(args) -> int:
     def run():
         pk.prefill_chunk(q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len, qs_d,
                          int(qlens.max()), batch.scale, batch.k_scale, batch.v_scale,
-                         partition_size=part, out=out, workspace=ws)
+                         partition_size=part, out=out, workspace=ws, cache_dtype=w.cache_dtype)
 
     for _ in range(args.warmup):
         run()
@@ -336,6 +345,25 @@ def bench_prefill(args) -> int:
     return 0
 
 
+def with_cache_dtype(w, cache_dtype):
+    """The workload with another KV cache format, or None (message printed)
+    when the swap makes no sense."""
+    if not cache_dtype or cache_dtype == w.cache_dtype:
+        return w
+    import dataclasses
+    if cache_dtype == "int4":
+        if w.cache_dtype == "f32":
+            print("--cache-dtype int4 needs a bf16 or FP8 workload (bf16 queries)", file=sys.stderr)
+            return None
+        return dataclasses.replace(w, cache_dtype="int4", q_dtype="bf16",
+                                   name=w.name.rsplit("-", 1)[0] + "-int4")
+    if not w.cache_dtype.startswith("fp8"):
+        print("--cache-dtype fp8_* applies to FP8 workloads only", file=sys.stderr)
+        return None
+    return dataclasses.replace(w, cache_dtype=cache_dtype,
+                               name=w.name + ("-e5m2" if cache_dtype == "fp8_e5m2" else ""))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,8 +383,10 @@ def main() -> int:
                     help="step: append + decode (+ merge); copy: a copy-on-write burst "
                          "of pa_copy_blocks on the workload's pool; prefill: several query "
                          "tokens per sequence (pa_prefill_chunk), see --case")
-    ap.add_argument("--cache-dtype", choices=["fp8_e4m3", "fp8_e5m2"], default=None,
-                    help="FP8 format of an FP8 workload's cache (default: the workload's)")
+    ap.add_argument("--cache-dtype", choices=["fp8_e4m3", "fp8_e5m2", "int4"], default=None,
+                    help="KV cache format in place of the workload's: the other FP8 format "
+                         "for an FP8 workload, or INT4 (per-token scales, bf16 queries) for "
+                         "any bf16 or FP8 workload")
     ap.add_argument("--case", default="spec-verify-8b",
                     help="prefill shape: spec-verify-8b or chunked-prefill-8b")
     args = ap.parse_args()
@@ -376,14 +406,9 @@ def main() -> int:
     import paged_kv_cache_253_amd as pk
     from workloads import WORKLOADS, decode_bytes, make_batch, write_bytes
 
-    w = WORKLOADS[args.workload]
-    if args.cache_dtype:
-        if not w.cache_dtype.startswith("fp8"):
-            print("--cache-dtype applies to FP8 workloads only", file=sys.stderr)
-            return 2
-        import dataclasses
-        w = dataclasses.replace(w, cache_dtype=args.cache_dtype,
-                                name=w.name + ("-e5m2" if args.cache_dtype == "fp8_e5m2" else ""))
+    w = with_cache_dtype(WORKLOADS[args.workload], args.cache_dtype)
+    if w is None:
+        return 2
     dev = "cuda"
     t_gen = time.perf_counter()
     batch = make_batch(w, device=dev)

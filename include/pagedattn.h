@@ -191,7 +191,7 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
  *                     is a run of ceil(L / 32) 32-token steps (one step for
  *                     L == 0); the runs of the batch, KV head major, are cut
  *                     into W equal slices, one per persistent wavefront
- *                     (W = 2 to 4 per compute unit of the current device, by
+ *                     (W = 2 to 8 per compute unit of the current device, by
  *                     kernel variant).  Runs one slice covers whole are
  *                     written to `out` here; the state of each run cut by a
  *                     slice boundary goes to `workspace`, and pa_decode_reduce
@@ -237,9 +237,9 @@ pa_status pa_decode(void* out, const void* q,
  * partition p of sequence b, query head hq is row (b * num_q_heads + hq) *
  * maxP + p; rows of partitions a sequence does not have are unused.
  * PA_PARTITION_AUTO: H = 256 (pa_decode stores W there, as an int32 at
- * offset 0, for pa_decode_reduce), R = 4 * CUs * 2 * G (CUs = compute
+ * offset 0, for pa_decode_reduce), R = 8 * CUs * 2 * G (CUs = compute
  * units of the current device, G = num_q_heads / num_kv_heads; a decode
- * uses at most 4 * CUs slices); slice s keeps the state of its first run in
+ * uses at most 8 * CUs slices); slice s keeps the state of its first run in
  * rows (2s) * G + g and of its last run in rows (2s + 1) * G + g, for the
  * group's query heads g, when those runs are cut.
  *

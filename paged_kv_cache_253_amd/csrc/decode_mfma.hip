@@ -141,8 +141,8 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
 #pragma unroll
   for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 accb = {0.f, 0.f, 0.f, 0.f};  // INT4: column sums of the PV weights
-  float m_run = -INFINITY;  // running max of z = c2 * q.k for head `col`
-  float l_run = 0.f;        // this lane's share of sum 2^(z - m_run)
+  float m_run = -INFINITY;  // running max of the scores (q.k units) of head `col`
+  float l_run = 0.f;        // this lane's share of sum 2^((z - m_run) * c2)
 
   auto compute = [&](StepBuf<CK, D, BS>& sb, int step) {
     const int base = t0 + step * kStep;
@@ -153,37 +153,17 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sb, 0, c), qop[c], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sb, 1, c), qop[c], s1, 0, 0, 0);
     }
-    // scores in log2 units: z = s * c2, so exp(scale*q.k - max) = 2^(z - m)
-    bool zok[8];  // token of score register i inside the range
-#pragma unroll
-    for (int i = 0; i < 8; ++i) zok[i] = !partial || base + qk_token(grp, i) < t1;
     float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    qk_to_log2<CK>(z, sb, zok, c2, qbias);
-    if (partial) {  // PV k-slots of this lane: tokens 8*grp .. +7
-      const int vvalid = min(max(t1 - (base + 8 * grp), 0), 8);
+    qk_scores<CK>(z, sb, qbias);
+    bool zok[8];  // partial step: token of score register i inside the range
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zok[i] = qk_token(grp, i) < t1 - base;
+      const int vvalid = min(max(t1 - (base + 8 * grp), 0), 8);  // PV k-slots: tokens 8*grp .. +7
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sb.v[dt], vvalid);
     }
-    float mx = z[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-    mx = xlane<OpMax, 16, 32>(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (wave_any(m_new > m_run)) {
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] *= alpha;
-      if constexpr (C::I4) accb *= alpha;
-      m_run = m_new;
-    }
-    float p[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = zok[i] ? exp2f(z[i] - m_run) : 0.f;
-      l_run += p[i];
-    }
-    const bf16x8 pop = pv_operand<CK>(p, sb, zok);
+    const bf16x8 pop = softmax_step<CK, C::kDTiles>(z, partial, zok, sb, c2, m_run, l_run, acc, accb);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<CK>(sb.v[dt]), pop, acc[dt], 0, 0, 0);
@@ -227,7 +207,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
     for (int dt = 0; dt < C::kDTiles; ++dt)
       *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = acc[dt] * inv;
     if (grp == 0) {
-      a.part_max[row] = m_run * kLn2;  // back to natural units
+      a.part_max[row] = m_run * (c2 * kLn2);  // natural units: scale * q.k
       a.part_sum[row] = l_tot;
     }
   }
@@ -277,10 +257,17 @@ constexpr int kFirst = 1, kLast = 2, kFinal = 4;
 #endif
 constexpr int kRing = PA_STREAM_RING;
 
+// INT4 steps (4.25 KiB at head_dim 128) are the smallest and carry the most
+// VALU work per byte: two wavefronts per SIMD (8 per CU, 240 VGPRs each)
+// let one wavefront's widening and softmax overlap the other's loads.
 template <int CK, int D>
 constexpr int stream_waves_per_cu() {
+  if (CK == kI4) return 8;
   return kStep * 2 * D * (CK == kBF16 ? 2 : 1) >= 16 * 1024 ? 2 : 4;
 }
+template <int CK>
+constexpr int stream_waves_per_simd() { return CK == kI4 ? 2 : 1; }
+static_assert(stream_waves_per_cu<kI4, 128>() <= kAutoMaxWavesPerCU, "workspace bound");
 
 typedef const __attribute__((address_space(4))) int32_t* const_i32;
 typedef const __attribute__((address_space(4))) float* const_f32;
@@ -299,7 +286,8 @@ struct Slot : StepBuf<CK, D, BS> {
 };
 
 template <int CK, int D, int BS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<CK>(), stream_waves_per_simd<CK>())))
 void decode_mfma_stream(const DecodeArgs a) {
   constexpr bool FP8 = one_byte<CK>();
   using C = Cfg<CK, D, BS>;
@@ -407,36 +395,18 @@ void decode_mfma_stream(const DecodeArgs a) {
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sl, 1, c), sl.q[c], s1, 0, 0, 0);
     }
     const bool partial = sl.base + kStepTokens > sl.t1;
-    bool zok[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) zok[i] = !partial || sl.base + qk_token(grp, i) < sl.t1;
     float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    qk_to_log2<CK>(z, sl, zok, c2, qbias);
+    qk_scores<CK>(z, sl, qbias);
+    bool zok[8];  // partial step: token of score register i inside the range
     if (partial) {
-      const int vvalid = min(max(sl.t1 - (sl.base + 8 * grp), 0), 8);
+      const int n = sl.t1 - sl.base;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zok[i] = qk_token(grp, i) < n;
+      const int vvalid = min(max(n - 8 * grp, 0), 8);
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sl.v[dt], vvalid);
     }
-    float mx = z[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-    mx = xlane<OpMax, 16, 32>(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (wave_any(m_new > m_run)) {
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] *= alpha;
-      if constexpr (C::I4) accb *= alpha;
-      m_run = m_new;
-    }
-    float p[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = zok[i] ? exp2f(z[i] - m_run) : 0.f;
-      l_run += p[i];
-    }
-    const bf16x8 pop = pv_operand<CK>(p, sl, zok);
+    const bf16x8 pop = softmax_step<CK, C::kDTiles>(z, partial, zok, sl, c2, m_run, l_run, acc, accb);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<CK>(sl.v[dt]), pop, acc[dt], 0, 0, 0);
@@ -472,7 +442,7 @@ void decode_mfma_stream(const DecodeArgs a) {
           for (int dt = 0; dt < C::kDTiles; ++dt)
             *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = acc[dt] * inv;
           if (grp == 0) {
-            a.part_max[row] = m_run * kLn2;
+            a.part_max[row] = m_run * (c2 * kLn2);  // natural units: scale * q.k
             a.part_sum[row] = l_tot;
           }
         }

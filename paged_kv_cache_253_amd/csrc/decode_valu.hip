@@ -24,6 +24,7 @@ namespace pa {
 namespace {
 
 constexpr int kStep = kStepTokens;
+constexpr int kValuWavesPerCU = 4;  // balanced split: persistent wavefronts per CU
 
 template <Elem E> struct ElemBytes;
 template <> struct ElemBytes<Elem::F32> { static constexpr int v = 4; };
@@ -328,7 +329,7 @@ template <typename QT, Elem E, int D, int BS, int G>
 hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
   if (a.partition == kAuto) {
     DecodeArgs b = a;
-    b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : kAutoMaxWavesPerCU);
+    b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : kValuWavesPerCU);
     hipLaunchKernelGGL((decode_valu_auto<QT, E, D, BS, G>), dim3(b.slices), dim3(64), 0, stream, b);
   } else {
     const int parts = a.partition ? a.max_parts : 1;

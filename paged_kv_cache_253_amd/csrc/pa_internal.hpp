@@ -22,7 +22,7 @@ inline int64_t tile_bytes(Elem e, int head_dim, int block_size) {
 // kernel uses (sizes the workspace and the merge grid), minimum slice length
 // in 32-token steps, the XCD count used to group slices, and the size of the
 // workspace header (the decode kernel records its slice count there).
-constexpr int kAutoMaxWavesPerCU = 4;
+constexpr int kAutoMaxWavesPerCU = 8;
 constexpr int kAutoMinSteps = 4;
 constexpr int kXcds = 8;
 constexpr int kWorkspaceHeader = 256;

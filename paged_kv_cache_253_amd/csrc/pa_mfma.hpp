@@ -234,33 +234,67 @@ __device__ __forceinline__ void mask_v(VRaw<CK>& r, int valid) {  // valid = tok
   }
 }
 
-// Raw QK results (QK register order) -> scores in log2 units, -inf where
-// the token is outside the range.  c2 = softmax scale * log2(e) (times the
-// FP8 K scale); INT4: qbias = 136 * sum of the lane column's q, and each
-// token's own K scale.
+// 2^x on the transcendental unit (v_exp_f32) without the library's range
+// reduction: results below 2^-126 may flush to zero, far below what any
+// softmax weight here can contribute (the largest weight of a row is 1).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw QK results (QK register order) -> scores in q.k units.  INT4: remove
+// the operand bias (qbias = 136 * sum of the lane column's q) and apply each
+// token's own K scale.  Other kinds: unchanged (an FP8 K scale is folded
+// into the log2 factor).
 template <int CK, class Buf>
-__device__ __forceinline__ void qk_to_log2(float* z, const Buf& sb, const bool* ok, float c2,
-                                           float qbias) {
+__device__ __forceinline__ void qk_scores(float* z, const Buf& sb, float qbias) {
   if constexpr (CK == kI4) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float ks = sb.ts.k[i >> 2][i & 3];
-      z[i] = ok[i] ? (z[i] - qbias) * (ks * c2) : -INFINITY;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = ok[i] ? __fmul_rn(z[i], c2) : -INFINITY;
+    for (int i = 0; i < 8; ++i) z[i] = (z[i] - qbias) * sb.ts.k[i >> 2][i & 3];
   }
 }
 
-// PV weights: the softmax weights, times each token's V scale for INT4
-// (selected to 0 outside the range, where a scale may be anything).
-template <int CK, class Buf>
-__device__ __forceinline__ bf16x8 pv_operand(const float* p, const Buf& sb, const bool* ok) {
+// One online-softmax step over the 8 scores a lane holds (QK register
+// order, q.k units): update the running max m and sum l of the lane's
+// column, rescale the accumulators when the max grows, and return the PV
+// weights operand.  c2 = softmax scale * log2(e) (times an FP8 K scale), so
+// a weight is 2^(z*c2 - m*c2).  Only a partial step (one holding tokens
+// outside the range) reads ok[]; every token of a full step is in range.
+// INT4: the weights carry each token's V scale, and accb their column sums.
+template <int CK, int NDT, class Buf>
+__device__ __forceinline__ bf16x8 softmax_step(float* z, bool partial, const bool* ok, const Buf& sb,
+                                               float c2, float& m_run, float& l_run, f32x4* acc,
+                                               f32x4& accb) {
+  if (partial) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = ok[i] ? z[i] : -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+  mx = xlane<OpMax, 16, 32>(mx);
+  const float m_new = fmaxf(m_run, mx);
+  if (wave_any(m_new > m_run)) {
+    const float alpha = exp2_fast((m_run - m_new) * c2);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+    if constexpr (CK == kI4) accb *= alpha;
+    m_run = m_new;
+  }
+  const float mc = m_run * c2;
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(z[i], c2, -mc));
+  if (partial) {  // all-masked rows have m = -inf: select, not rely on exp2(-inf)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = ok[i] ? p[i] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) l_run += p[i];
   if constexpr (CK == kI4) {
     float pv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pv[i] = ok[i] ? p[i] * sb.ts.v[i >> 2][i & 3] : 0.f;
+    for (int i = 0; i < 8; ++i) pv[i] = p[i] * sb.ts.v[i >> 2][i & 3];
+    if (partial) {  // a scale outside the range may be anything, NaN included
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv[i] = ok[i] ? pv[i] : 0.f;
+    }
     return p_operand(pv);
   } else {
     return p_operand(p);

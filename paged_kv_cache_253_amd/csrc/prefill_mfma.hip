@@ -165,32 +165,18 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
         const int lim = min(t1 - 1, pos[ct]);  // last token this column may see here
-        bool ok[8];
         float z[8] = {s0[ct][0], s0[ct][1], s0[ct][2], s0[ct][3],
                       s1[ct][0], s1[ct][1], s1[ct][2], s1[ct][3]};
+        qk_scores<CK>(z, sb, qbias[ct]);
+        // the step is full for every real column unless one stops inside it
+        const bool partial = wave_any(cvalid[ct] && base + kStep - 1 > lim);
+        bool ok[8];
+        if (partial) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ok[i] = cvalid[ct] && base + qk_token(grp, i) <= lim;
-        qk_to_log2<CK>(z, sb, ok, c2, qbias[ct]);
-        float mx = z[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-        mx = xlane<OpMax, 16, 32>(mx);
-        const float m_new = fmaxf(m_run[ct], mx);
-        if (wave_any(m_new > m_run[ct])) {
-          const float alpha = exp2f(m_run[ct] - m_new);
-          l_run[ct] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < C::kDTiles; ++dt) acc[ct][dt] *= alpha;
-          if constexpr (C::I4) accb[ct] *= alpha;
-          m_run[ct] = m_new;
+          for (int i = 0; i < 8; ++i) ok[i] = cvalid[ct] && base + qk_token(grp, i) <= lim;
         }
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = ok[i] ? exp2f(z[i] - m_run[ct]) : 0.f;
-          l_run[ct] += p[i];
-        }
-        pop[ct] = pv_operand<CK>(p, sb, ok);
+        pop[ct] = softmax_step<CK, C::kDTiles>(z, partial, ok, sb, c2, m_run[ct], l_run[ct], acc[ct],
+                                               accb[ct]);
       }
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) {
@@ -246,7 +232,7 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
       for (int dt = 0; dt < C::kDTiles; ++dt)
         *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = acc[ct][dt] * inv;
       if (grp == 0) {
-        a.part_max[row] = m_run[ct] * kLn2;  // back to natural units
+        a.part_max[row] = m_run[ct] * (c2 * kLn2);  // natural units: scale * q.k
         a.part_sum[row] = l_tot;
       }
     }

@@ -346,3 +346,15 @@ def test_fp8_append_rounding_matches_oracle_on_many_values(fmt):
     _sync()
     assert np.array_equal(kd.cpu().numpy(), k_ref)
     assert np.array_equal(vd.cpu().numpy(), v_ref)
+
+
+def test_balanced_workspace_size_follows_documented_layout():
+    """PA_PARTITION_AUTO: a 256-byte header, then R = 8 * CUs * 2 * G rows of
+    partial state (the documented bound on the decode's wavefronts)."""
+    def align(x):
+        return (x + 255) // 256 * 256
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for s, hq, hkv, d in [(64, 32, 8, 128), (3, 16, 16, 64), (8, 64, 4, 128)]:
+        rows = 8 * cus * 2 * (hq // hkv)
+        want = 256 + align(rows * d * 4) + 2 * align(rows * 4)
+        assert pk.workspace_size(s, hq, hkv, d, 4096, -1) == want
