@@ -33,6 +33,14 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  The multi-query kernels keep their accumulators in
+# VGPRs (VGPR-form MFMA): with the default AGPR form the compiler copied all
+# accumulators to VGPRs and back on every 32-token step for the (rare) softmax
+# rescale, a third of the kernel's VALU work; in VGPR form they fit with no
+# spills.
+EXTRA_FLAGS = {"prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -56,7 +64,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        out = _run([cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        out = _run([cc, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out)
         return obj

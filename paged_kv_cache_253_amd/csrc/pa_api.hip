@@ -367,11 +367,14 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
   if (partition_size > 0 && partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
   const int group = num_q_heads / num_kv_heads;
   if (group > 16 || (group & (group - 1)) != 0) return PA_ERR_UNSUPPORTED;
-  if (num_seqs > 65535 ||
-      (long long)pa::prefill_query_tiles(group, max_query_len,
-                                         pa::prefill_max_column_tiles(ce, head_dim)) *
-              num_kv_heads > 65535)
-    return PA_ERR_UNSUPPORTED;
+  {  // one workgroup per (partition, query tile, KV head, sequence), padded to whole XCD rounds
+    const long long tiles = pa::prefill_query_tiles(group, max_query_len,
+                                                    pa::prefill_max_column_tiles(ce, head_dim));
+    const long long parts = partition_size > 0
+        ? std::max(1LL, ((long long)max_context_len + partition_size - 1) / partition_size) : 1;
+    const long long pairs = ((long long)num_seqs * num_kv_heads + pa::kXcds - 1) / pa::kXcds * pa::kXcds;
+    if (num_seqs > 65535 || pairs * parts * tiles > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  }
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PA_ERR_INVALID_ARG;
   if (partition_size == 0 && !out) return PA_ERR_INVALID_ARG;

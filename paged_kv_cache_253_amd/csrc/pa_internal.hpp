@@ -69,6 +69,7 @@ struct PrefillArgs {
   DecodeArgs d;
   const int32_t* query_start;   // [S + 1]
   int max_query_len;
+  int tiles;                    // query tiles per (sequence, KV head) (set by the launcher)
 };
 
 // Column tiles (16 MFMA columns each) of a multi-query wavefront, and the

@@ -103,3 +103,24 @@ def test_single_query_matches_decode():
     err = (a.float() - b.float()).abs().max().item()
     print(f"[prefill] single query vs decode max diff {err:.3e}", flush=True)
     assert err <= 1e-2
+
+
+W_D64_B32 = dataclasses.replace(WORKLOADS[2], head_dim=64, block_size=32, name="d64-b32-bf16")
+W5_D64 = dataclasses.replace(W5, head_dim=64, name="fp8-d64")
+
+
+@pytest.mark.parametrize("w,lens,qlens", [
+    (W2, [900, 1300, 64, 700], [200, 0, 64, 31]),        # whole context, no queries, ragged
+    (W5, [2000, 1500], [150, 77]),                        # FP8, block 32, 4 column tiles
+    (W5_E5M2, [1200, 600], [96, 130]),
+    (W5_D64, [1024, 333], [64, 65]),                       # FP8 d64
+    (W_D64_B32, [800, 1100, 95], [120, 64, 95]),           # bf16 d64 B32
+    (dataclasses.replace(W2, num_q_heads=128, name="g16"), [700, 300], [33, 40]),  # G = 16
+])
+@pytest.mark.parametrize("partition", [0, 64, 256])
+def test_long_query_runs(w, lens, qlens, partition):
+    """Long query runs: many query tiles per sequence and KV head, each
+    ending at its own position, with every cache kind, d 64 / 128, B 16 / 32,
+    G up to 16, a sequence without queries and one whose whole context is
+    new."""
+    _run(w, lens, qlens, partition, seed=7)
