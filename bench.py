@@ -28,7 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD public spec
-KERNEL_SOURCES = ["decode_mfma.hip", "decode_valu.hip", "pa_device.hpp", "pa_split.hpp", "pa_internal.hpp"]
+KERNEL_SOURCES = ["decode_mfma.hip", "decode_valu.hip", "pa_device.hpp", "pa_mfma.hpp", "pa_split.hpp",
+                  "pa_internal.hpp"]
 
 
 def log(*a):
