@@ -371,6 +371,58 @@ void decode_mfma_stream(const DecodeArgs a) {
       sl.q[c] = *reinterpret_cast<const bf16x8*>(qp + q_dim<CK, D>(grp, c));
   };
 
+  // ---- finished segments ----------------------------------------------------
+  // A finished segment's G output rows (and, for a cut run, its maxima and
+  // sums) wait in LDS and are written after the ring has drained, or when
+  // the buffer is full.  A wavefront's memory operations retire in order, so
+  // a global store issued while the ring's loads are in flight holds up
+  // every younger load until the write completes: a bubble of about one
+  // memory latency per finished segment (measured on MI355X: ~4 us each,
+  // 17 us of 284 on the 70B-shaped batch).  The G rows are contiguous in
+  // out and in the workspace, so they leave as 16-byte stores over all
+  // lanes.  Rows are padded by 4 floats so the G writing lanes hit
+  // different banks.
+  constexpr int kStageRow = D + 4;
+  constexpr int kOutFloats = (stream_waves_per_cu<CK, D>() >= 8 ? 16384 : 32768) / 4;
+  constexpr int kOutSlotsMax = 32;
+  __shared__ __attribute__((aligned(16))) float outbuf[kOutFloats];
+  __shared__ int outtag[kOutSlotsMax];  // out row of the group's head 0 (final), or -1 - row0 (state)
+  const int slot_floats = (G * kStageRow + 2 * G + 3) & ~3;
+  const int out_cap = min(kOutSlotsMax, kOutFloats / slot_floats);
+  int nout = 0;
+
+  auto flush = [&]() {
+    __builtin_amdgcn_wave_barrier();  // the slots were written by other lanes of this wavefront
+    for (int sidx = 0; sidx < nout; ++sidx) {
+      const int tag = __builtin_amdgcn_readfirstlane(outtag[sidx]);
+      const float* src = outbuf + sidx * slot_floats;
+      if (tag >= 0) {
+        __bf16* o = reinterpret_cast<__bf16*>(a.out) + (size_t)tag * D;
+        for (int q = lane; q < G * (D / 8); q += 64) {  // 8 outputs per 16-byte store
+          const float* e = src + (q / (D / 8)) * kStageRow + (q % (D / 8)) * 8;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(e);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(e + 4);
+          bf16x8 y;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { y[i] = (__bf16)x0[i]; y[4 + i] = (__bf16)x1[i]; }
+          *reinterpret_cast<bf16x8*>(o + (size_t)q * 8) = y;
+        }
+      } else {
+        const int row0 = -1 - tag;
+        float* o = a.part_out + (size_t)row0 * D;
+        for (int q = lane; q < G * (D / 4); q += 64)
+          *reinterpret_cast<f32x4*>(o + (size_t)q * 4) =
+              *reinterpret_cast<const f32x4*>(src + (q / (D / 4)) * kStageRow + (q % (D / 4)) * 4);
+        if (lane < G) {
+          a.part_max[row0 + lane] = src[G * kStageRow + lane];
+          a.part_sum[row0 + lane] = src[G * kStageRow + G + lane];
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // reads done before the slots are reused
+    nout = 0;
+  };
+
   // ---- compute side ---------------------------------------------------------
   f32x4 acc[C::kDTiles];
   f32x4 accb = {0.f, 0.f, 0.f, 0.f};  // INT4: column sums of the PV weights
@@ -423,30 +475,21 @@ void decode_mfma_stream(const DecodeArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[dt][r] = fmaf(-kI4Bias, accb[0], acc[dt][r]);
       }
+      if (nout == out_cap) flush();  // rare: many short runs in one slice
+      float* dst = outbuf + nout * slot_floats;
       if (col < G) {
-        if (sl.flags & kFinal) {
-          __bf16* o = reinterpret_cast<__bf16*>(a.out) +
-                      ((size_t)sl.b * a.num_q_heads + (size_t)sl.h * G + col) * D;
+        float* row = dst + col * kStageRow;
 #pragma unroll
-          for (int dt = 0; dt < C::kDTiles; ++dt) {
-            bf16x2 lo, hi;
-            lo[0] = (__bf16)(acc[dt][0] * inv); lo[1] = (__bf16)(acc[dt][1] * inv);
-            hi[0] = (__bf16)(acc[dt][2] * inv); hi[1] = (__bf16)(acc[dt][3] * inv);
-            u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-            *reinterpret_cast<u32x2*>(o + dt * 16 + grp * 4) = w;
-          }
-        } else {
-          const size_t row = (size_t)sl.row0 + col;
-          float* o = a.part_out + row * D;
-#pragma unroll
-          for (int dt = 0; dt < C::kDTiles; ++dt)
-            *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = acc[dt] * inv;
-          if (grp == 0) {
-            a.part_max[row] = m_run * (c2 * kLn2);  // natural units: scale * q.k
-            a.part_sum[row] = l_tot;
-          }
+        for (int dt = 0; dt < C::kDTiles; ++dt)
+          *reinterpret_cast<f32x4*>(row + dt * 16 + grp * 4) = acc[dt] * inv;
+        if (!(sl.flags & kFinal) && grp == 0) {
+          dst[G * kStageRow + col] = m_run * (c2 * kLn2);  // natural units: scale * q.k
+          dst[G * kStageRow + G + col] = l_tot;
         }
       }
+      if (lane == 0)
+        outtag[nout] = (sl.flags & kFinal) ? sl.b * a.num_q_heads + sl.h * G : -1 - sl.row0;
+      ++nout;
     }
   };
 
@@ -464,6 +507,7 @@ void decode_mfma_stream(const DecodeArgs a) {
       }
     }
   }
+  flush();
 }
 
 template <int CK, int D, int BS>
