@@ -236,12 +236,15 @@ pa_status pa_decode(void* out, const void* q,
  * maxP = max(1, ceil(max_context_len / partition_size)); the state of
  * partition p of sequence b, query head hq is row (b * num_q_heads + hq) *
  * maxP + p; rows of partitions a sequence does not have are unused.
- * PA_PARTITION_AUTO: H = 256 (pa_decode stores W there, as an int32 at
- * offset 0, for pa_decode_reduce), R = 8 * CUs * 2 * G (CUs = compute
- * units of the current device, G = num_q_heads / num_kv_heads; a decode
- * uses at most 8 * CUs slices); slice s keeps the state of its first run in
- * rows (2s) * G + g and of its last run in rows (2s + 1) * G + g, for the
- * group's query heads g, when those runs are cut.
+ * PA_PARTITION_AUTO: H = 256 + align(16 * 8 * CUs), R = 8 * CUs * 2 * G
+ * (CUs = compute units of the current device, G = num_q_heads /
+ * num_kv_heads; a decode uses at most W = 8 * CUs slices).  pa_decode
+ * stores W as an int32 at offset 0 and, at offset 256 + 16 s, four int32
+ * naming the cut run whose first piece slice s holds (sequence, KV head,
+ * number of slices holding a piece, state slot of the first piece; a piece
+ * count of 0 = none), for pa_decode_reduce.  Slice s keeps the state of its
+ * first run in rows (2s) * G + g and of its last run in rows (2s + 1) * G +
+ * g, for the group's query heads g, when those runs are cut.
  *
  * A state over tokens T of a query head, with z_t as in pa_decode:
  * part_max = max_{t in T} z_t, part_sum = sum_t exp(z_t - part_max),

@@ -302,7 +302,10 @@ void decode_mfma_stream(const DecodeArgs a) {
   const int r = slice_of_wave(blockIdx.x, W);
   int64_t g0, g_end;
   slice_bounds(sp, r, g0, g_end);
-  if (g0 >= g_end) return;
+  if (g0 >= g_end) {
+    if (lane == 0) store_merge_rec(a.header, r, MergeRec{0, 0, 0, 0});
+    return;
+  }
 
   const const_i32 lens = (const_i32)a.context_lens;
   const const_i32 tables = (const_i32)a.block_tables;
@@ -319,6 +322,9 @@ void decode_mfma_stream(const DecodeArgs a) {
   int cflags_run = (ci == 0 && cseg_end == cn) ? kFinal : 0;
   int crow0 = r * 2 * G;  // the slice's first run -> rows (2r)*G..
   int pending = 0;        // real steps issued and not yet computed
+  // merge record: only the slice's last run can be cut by the next boundary
+  MergeRec rec{0, 0, 0, 0};
+  if (ci == 0 && cseg_end < cn) rec = merge_rec_of(sp, r, g0, cn, cb, ch, 0);
 
   // per-lane offsets inside a step's tiles (see attend)
   const LaneOffsets<CK, D, BS> lo(grp, col);
@@ -343,6 +349,7 @@ void decode_mfma_stream(const DecodeArgs a) {
         cseg_end = (int)min((int64_t)cn, left);
         cflags_run = (cseg_end == cn) ? kFinal : 0;
         crow0 = (r * 2 + 1) * G;
+        if (cseg_end < cn) rec = merge_rec_of(sp, r, g_end - left, cn, cb, ch, 1);
       }
       sl.base = ci * kStepTokens;
       sl.t1 = min(min(cseg_end * kStepTokens, clen), a.cap_len);
@@ -508,6 +515,7 @@ void decode_mfma_stream(const DecodeArgs a) {
     }
   }
   flush();
+  if (lane == 0) store_merge_rec(a.header, r, rec);
 }
 
 template <int CK, int D, int BS>

@@ -10,9 +10,10 @@
 //  * reduce_kernel: fixed partitions.  One 256-thread workgroup per
 //    (sequence, query head); 16-byte loads, D/4 threads per partition row,
 //    256/(D/4) rows in flight; the row groups are summed in order at the end.
-//  * auto_fixup_kernel: balanced slices.  One workgroup per slice boundary;
-//    the first boundary that cuts a (sequence, KV head) run merges all of the
-//    run's slice states (see pa_split.hpp), one query head per wavefront,
+//  * auto_fixup_kernel: balanced slices.  One workgroup per slice; the
+//    slice's merge record (written by the decode, see pa_split.hpp) names
+//    the cut run whose first piece it holds, if any, and the workgroup
+//    merges all of that run's slice states, one query head per wavefront,
 //    the pieces' maxima and weights taken by the lanes in parallel.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
@@ -106,55 +107,81 @@ constexpr int kFixupThreads = 256;
 template <typename OT, int D>
 __global__ __launch_bounds__(kFixupThreads) void auto_fixup_kernel(const ReduceArgs a) {
   constexpr int PER = D / 64;
-  const int r = blockIdx.x + 1;  // boundary between slices r-1 and r
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const int r_first = blockIdx.x;  // slice holding the run's first piece
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int slices = a.header[kHdrSlices];  // as launched by the decode
-  if (r >= slices) return;
-  // every wavefront of the workgroup derives the same plan
-  const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, slices);
-  int64_t g, g_unused;
-  slice_bounds(sp, r, g, g_unused);
-  if (g >= sp.total) return;
-  const int h = (int)(g / sp.per_head);
-  int b, i;
-  locate_step(a.context_lens, a.num_seqs, a.max_len, g - (int64_t)h * sp.per_head, b, i);
-  if (i == 0) return;                 // the boundary does not cut a run
-  const int64_t gs = g - i;           // first step of the run
-  const int r_first = slice_of_step(sp, gs);
-  if (r != r_first + 1) return;       // an earlier boundary cuts the same run
-  const int n = steps_of_len(clamp_len(a.context_lens[b], a.max_len));
-  const int64_t ge = gs + n;          // one past its last step
-  int64_t first_start;
-  slice_bounds(sp, r_first, first_start, g_unused);
-  const int k_first = (gs == first_start) ? 0 : 1;
-  const int nparts = slice_of_step(sp, ge - 1) - r_first + 1;  // slices holding a piece
+  const i32x4 rec = *reinterpret_cast<const i32x4*>(reinterpret_cast<const char*>(a.header) +
+                                                     kHdrRecordsBytes + (size_t)r_first * kMergeRecordBytes);
+  if (r_first >= slices || slices > a.slices_max) return;
+  const int b = rec[0], h = rec[1], nparts = rec[2], k_first = rec[3];
+  if (nparts < 2) return;  // slice r_first's last run is not cut
+  // a workspace no decode has filled must not send the merge out of bounds
+  if (nparts > slices - r_first || (unsigned)b >= (unsigned)a.num_seqs ||
+      (unsigned)h >= (unsigned)a.num_kv_heads || (unsigned)k_first > 1u)
+    return;
   const int G = a.num_q_heads / a.num_kv_heads;
   auto row_of = [&](int j, int gq) -> size_t {  // piece j of the run, in slice order
     const int rr = r_first + j;
     return ((size_t)rr * 2 + (j == 0 ? k_first : 0)) * G + gq;
   };
   for (int gq = wave; gq < G; gq += kFixupThreads / 64) {
-    // lanes take the pieces' maxima and exp-sums in parallel
-    float mx = -INFINITY;
-    for (int j = lane; j < nparts; j += 64) mx = fmaxf(mx, a.part_max[row_of(j, gq)]);
-    mx = xlane<OpMax, 1, 32>(mx);
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    float wsum = 0.f;
-    for (int j0 = 0; j0 < nparts; j0 += 64) {
-      const int j = j0 + lane;
-      const size_t row = row_of(j < nparts ? j : j0, gq);
-      const float w = j < nparts ? a.part_sum[row] * __expf(a.part_max[row] - mx) : 0.f;
-      wsum += w;
-      const int cnt = min(64, nparts - j0);
-#pragma unroll 4
-      for (int jj = 0; jj < cnt; ++jj) {
-        const float wj = __int_as_float(readlane(__float_as_int(w), jj));
-        const float* src = a.part_out + row_of(j0 + jj, gq) * D + lane;
+    float mx, wsum;
+    if (nparts <= 64) {
+      // Lane j takes piece j's maximum and exp-sum; the rows of the first
+      // kBatch pieces are loaded with them, later batches one load round
+      // each.  Same arithmetic, in the same order, as the general loop below.
+      const bool mine = lane < nparts;
+      const size_t rl = row_of(mine ? lane : 0, gq);
+      const float pm = a.part_max[rl], ps = a.part_sum[rl];
+      constexpr int kBatch = 8;
+      float rows[kBatch][PER];
+      auto load_batch = [&](int j0) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, src[64 * e], acc[e]);
+        for (int jj = 0; jj < kBatch; ++jj) {
+          const float* src = a.part_out + row_of(min(j0 + jj, nparts - 1), gq) * D + lane;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) rows[jj][e] = src[64 * e];
+        }
+      };
+      load_batch(0);
+      mx = xlane<OpMax, 1, 32>(mine ? pm : -INFINITY);
+      const float w = mine ? ps * __expf(pm - mx) : 0.f;
+      wsum = w;
+      for (int j0 = 0; j0 < nparts; j0 += kBatch) {
+        if (j0 > 0) load_batch(j0);
+#pragma unroll
+        for (int jj = 0; jj < kBatch; ++jj) {
+          if (j0 + jj < nparts) {
+            const float wj = __int_as_float(readlane(__float_as_int(w), j0 + jj));
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, rows[jj][e], acc[e]);
+          }
+        }
+      }
+    } else {
+      // lanes take the pieces' maxima and exp-sums in parallel
+      mx = -INFINITY;
+      for (int j = lane; j < nparts; j += 64) mx = fmaxf(mx, a.part_max[row_of(j, gq)]);
+      mx = xlane<OpMax, 1, 32>(mx);
+      wsum = 0.f;
+      for (int j0 = 0; j0 < nparts; j0 += 64) {
+        const int j = j0 + lane;
+        const size_t row = row_of(j < nparts ? j : j0, gq);
+        const float w = j < nparts ? a.part_sum[row] * __expf(a.part_max[row] - mx) : 0.f;
+        wsum += w;
+        const int cnt = min(64, nparts - j0);
+#pragma unroll 4
+        for (int jj = 0; jj < cnt; ++jj) {
+          const float wj = __int_as_float(readlane(__float_as_int(w), jj));
+          const float* src = a.part_out + row_of(j0 + jj, gq) * D + lane;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, src[64 * e], acc[e]);
+        }
       }
     }
     const float total = xlane<OpSum, 1, 32>(wsum);
@@ -181,7 +208,7 @@ hipError_t launch(const ReduceArgs& a, hipStream_t s) {
 template <typename OT, int D>
 hipError_t launch_fixup(const ReduceArgs& a, hipStream_t s) {
   if (a.slices_max < 2) return hipSuccess;
-  hipLaunchKernelGGL((auto_fixup_kernel<OT, D>), dim3(a.slices_max - 1), dim3(kFixupThreads), 0, s, a);
+  hipLaunchKernelGGL((auto_fixup_kernel<OT, D>), dim3(a.slices_max), dim3(kFixupThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -301,7 +301,11 @@ __global__ __launch_bounds__(64) void decode_valu_auto(const DecodeArgs a) {
   const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, a.slices);
   int64_t g, g_end;
   slice_bounds(sp, r, g, g_end);
-  if (g >= g_end) return;
+  MergeRec rec{0, 0, 0, 0};
+  if (g >= g_end) {
+    if (threadIdx.x == 0) store_merge_rec(a.header, r, rec);
+    return;
+  }
   int h = (int)(g / sp.per_head);
   int b, i0;
   locate_step(a.context_lens, a.num_seqs, a.max_len, g - (int64_t)h * sp.per_head, b, i0);
@@ -317,12 +321,14 @@ __global__ __launch_bounds__(64) void decode_valu_auto(const DecodeArgs a) {
     } else {
       const size_t row0 = ((size_t)r * 2 + (first ? 0 : 1)) * G;
       attend<QT, E, D, BS, G>(a, b, h, t0, t1, Target{false, row0, 1});
+      if (i0 == 0) rec = merge_rec_of(sp, r, g, n, b, h, first ? 0 : 1);
     }
     g += seg;
     first = false;
     i0 = 0;
     if (++b == a.num_seqs) { b = 0; ++h; }
   }
+  if (threadIdx.x == 0) store_merge_rec(a.header, r, rec);
 }
 
 template <typename QT, Elem E, int D, int BS, int G>

@@ -78,7 +78,7 @@ bool workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_
     l->cus = device_cus();
     if (l->cus <= 0) return false;
     l->slices_max = l->cus * pa::kAutoMaxWavesPerCU;
-    l->head_bytes = pa::kWorkspaceHeader;
+    l->head_bytes = pa::kHdrRecordsBytes + align256((size_t)l->slices_max * pa::kMergeRecordBytes);
     rows = (size_t)l->slices_max * 2 * (size_t)(num_q_heads / num_kv_heads);
   } else if (partition_size > 0) {
     const long long parts = std::max(1LL, ((long long)max_context_len + partition_size - 1) / partition_size);

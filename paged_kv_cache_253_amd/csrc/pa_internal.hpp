@@ -20,15 +20,16 @@ inline int64_t tile_bytes(Elem e, int head_dim, int block_size) {
 
 // Balanced split: most persistent wavefronts per compute unit any decode
 // kernel uses (sizes the workspace and the merge grid), minimum slice length
-// in 32-token steps, the XCD count used to group slices, and the size of the
-// workspace header (the decode kernel records its slice count there).
+// in 32-token steps, and the XCD count used to group slices.
 constexpr int kAutoMaxWavesPerCU = 8;
 constexpr int kAutoMinSteps = 4;
 constexpr int kXcds = 8;
-constexpr int kWorkspaceHeader = 256;
-// Workspace header word (int32 index) where the decode records its
-// wavefront count W for the merge.
+// Balanced-split workspace header: the decode's wavefront count W as the
+// int32 at word kHdrSlices, then from byte kHdrRecordsBytes one 16-byte
+// merge record per slice (see pa_split.hpp).
 constexpr int kHdrSlices = 0;
+constexpr int kHdrRecordsBytes = 256;
+constexpr int kMergeRecordBytes = 16;
 
 // Split modes (DecodeArgs::partition): > 0 fixed partitions of that many
 // tokens, 0 unsplit, kAuto balanced slices.
@@ -57,7 +58,7 @@ struct DecodeArgs {
   int slices;                   // balanced split: persistent wavefronts (set by the launcher)
   int cus;                      // balanced split: compute units of the device
   int waves_per_cu;             // balanced split: 0 = the kernel's own choice
-  int* header;                  // balanced split: workspace header (kHdrSlices)
+  int* header;                  // balanced split: workspace header (W, merge records)
   float scale;
 };
 
@@ -121,7 +122,7 @@ struct ReduceArgs {
   const int32_t* context_lens;
   int max_len, num_seqs, num_q_heads, num_kv_heads, partition, max_parts;
   int slices_max;               // balanced split: upper bound of the decode's wavefront count
-  const int* header;            // balanced split: wavefront count recorded by the decode
+  const int* header;            // balanced split: W and merge records written by the decode
   const int32_t* query_start;   // several query tokens per sequence: [S + 1], else null
   int max_query_len;
 };

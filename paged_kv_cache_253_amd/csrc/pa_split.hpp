@@ -11,7 +11,9 @@
 //    (b, h) that one slice covers whole is finished by that wavefront; one
 //    that straddles a slice boundary leaves a partial softmax state per
 //    slice, merged afterwards.  Each slice has at most two such states: its
-//    first run ("head", slot 0) and its last run ("tail", slot 1).
+//    first run ("head", slot 0) and its last run ("tail", slot 1).  The
+//    wavefront that holds a cut run's first piece leaves a merge record
+//    for it, so the merge needs neither the plan nor a search.
 #pragma once
 
 #include "pa_device.hpp"
@@ -100,6 +102,33 @@ __device__ __forceinline__ void locate_step(const int32_t* lens, int num_seqs, i
   }
   b_out = num_seqs - 1;  // not reached for rem < per_head
   i_out = 0;
+}
+
+// Merge record of slice r: the run whose first piece is slice r's last
+// segment, when a later slice boundary cuts it -- sequence, KV head, the
+// number of slices holding a piece (pieces j >= 1 are the first runs of
+// slices r + j), and the state slot of piece 0 in slice r (0 when the run
+// is also the slice's first run, else 1).  nparts = 0: no such run.  Every
+// wavefront of a balanced launch writes its record, so none survives from
+// an earlier launch.
+struct MergeRec {
+  int b, h, nparts, slot;
+};
+
+__device__ __forceinline__ void store_merge_rec(int* header, int r, const MergeRec& m) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 v = {m.b, m.h, m.nparts, m.slot};
+  *reinterpret_cast<i32x4*>(reinterpret_cast<char*>(header) + kHdrRecordsBytes +
+                            (size_t)r * kMergeRecordBytes) = v;
+}
+
+// Record of the run that starts at step gs (its first piece in slice r,
+// state slot `slot`) and has n steps, if it runs past slice r.
+__device__ __forceinline__ MergeRec merge_rec_of(const Split& s, int r, int64_t gs, int n, int b,
+                                                 int h, int slot) {
+  const int last = slice_of_step(s, gs + n - 1);
+  if (last == r) return MergeRec{0, 0, 0, 0};
+  return MergeRec{b, h, last - r + 1, slot};
 }
 
 // Slice of wavefront w: slices handled by one XCD (workgroups are dealt to

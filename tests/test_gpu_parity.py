@@ -149,6 +149,48 @@ def test_balanced_split_cuts_and_empty_runs(cache, group):
     compare(widen(out), ref, cache, f"balanced {cache} G={group}")
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3"])
+def test_balanced_split_run_over_many_slices(cache):
+    """One KV head and a 20,000-token context next to short ones: the long
+    run is cut into well over 64 pieces (a slice is at least 4 steps), which
+    the merge takes through its general loop rather than the one-batch
+    path."""
+    lens = np.array([20000, 37, 1, 300])
+    batch = _custom(cache, 128, 32 if cache.startswith("fp8") else 16, 4, 1, lens)
+    k_ref, v_ref = write_and_reference(batch)
+    ref = oracle_decode_host(batch, k_ref, v_ref, range(len(lens)))
+    out = gpu_decode(batch, -1)
+    _sync()
+    compare(widen(out), ref, cache, f"balanced, long run, {cache}")
+
+
+def test_balanced_merge_records_written_every_launch():
+    """The merge of the balanced split reads one record per slice that the
+    decode writes on every launch, empty slices included.  Records planted in
+    the workspace (each naming a real run as cut across two slices) must not
+    reach the output: a long batch, then a short one whose slices are mostly
+    empty, on the same workspace, both match the oracle."""
+    rng = np.random.default_rng(5)
+    long_lens = rng.integers(1, 90, size=40)
+    long_lens[[5, 30]] = [5000, 2500]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ws = None
+    for lens in (long_lens, np.array([3, 40, 0, 7])):
+        batch = _custom("bf16", 128, 16, 8, 2, lens)
+        k_ref, v_ref = write_and_reference(batch)
+        ref = oracle_decode_host(batch, k_ref, v_ref, range(len(lens)))
+        if ws is None:
+            ws = pk.new_workspace(len(long_lens), 8, 2, 128, int(long_lens.max()), -1, DEV)
+        recs = ws[256:256 + 16 * 8 * cus].view(torch.int32).view(-1, 4)
+        recs.copy_(torch.tensor([0, 1, 2, 0], dtype=torch.int32, device=DEV).expand_as(recs))
+        bt, cl = device_tables(batch)
+        out = pk.decode(batch.q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len,
+                        batch.scale, batch.k_scale, batch.v_scale, -1, workspace=ws,
+                        cache_dtype=batch.workload.cache_dtype)
+        _sync()
+        compare(widen(out), ref, "bf16", f"planted records, {len(lens)} seqs")
+
+
 # ---------------------------------------------------------------------------
 # shapes, groups, paths and edge cases on small batches
 # ---------------------------------------------------------------------------
@@ -349,12 +391,13 @@ def test_fp8_append_rounding_matches_oracle_on_many_values(fmt):
 
 
 def test_balanced_workspace_size_follows_documented_layout():
-    """PA_PARTITION_AUTO: a 256-byte header, then R = 8 * CUs * 2 * G rows of
-    partial state (the documented bound on the decode's wavefronts)."""
+    """PA_PARTITION_AUTO: a header of 256 bytes plus a 16-byte merge record
+    per possible slice, then R = 8 * CUs * 2 * G rows of partial state (the
+    documented bound on the decode's wavefronts)."""
     def align(x):
         return (x + 255) // 256 * 256
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for s, hq, hkv, d in [(64, 32, 8, 128), (3, 16, 16, 64), (8, 64, 4, 128)]:
         rows = 8 * cus * 2 * (hq // hkv)
-        want = 256 + align(rows * d * 4) + 2 * align(rows * 4)
+        want = 256 + align(16 * 8 * cus) + align(rows * d * 4) + 2 * align(rows * 4)
         assert pk.workspace_size(s, hq, hkv, d, 4096, -1) == want
