@@ -1,9 +1,11 @@
 """Benchmark of the paged decode hot path on one MI355X.
 
 One step = the whole hot path over one synthetic batch already resident in
-HBM: append each sequence's new K/V token (``pa_kv_cache_write``), then
-decode attention over the paged cache (``pa_decode``, plus
-``pa_decode_reduce`` when the context is split).  Default workload: the
+HBM: append each sequence's new K/V token, then decode attention over the
+paged cache -- by default one ``pa_decode_append`` call (slots from the
+block tables), ``--separate-append`` for ``pa_kv_cache_write`` with the
+slot mapping then ``pa_decode`` -- plus ``pa_decode_reduce`` when the
+context is split.  Default workload: the
 Llama-3-8B-shaped decode batch (64 sequences, 32 query / 8 KV heads, head
 dim 128, 16-token blocks, bf16 KV, lengths U[512, 4096]).
 
@@ -388,6 +390,9 @@ def main() -> int:
                     help="KV cache format in place of the workload's: the other FP8 format "
                          "for an FP8 workload, or INT4 (per-token scales, bf16 queries) for "
                          "any bf16 or FP8 workload")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="step as pa_kv_cache_write + pa_decode (two launches) instead of "
+                         "pa_decode_append")
     ap.add_argument("--case", default="spec-verify-8b",
                     help="prefill shape: spec-verify-8b or chunked-prefill-8b")
     args = ap.parse_args()
@@ -437,28 +442,35 @@ def main() -> int:
         e.record()
         ev.setdefault(name, []).append(e)
 
-    def step(timed: bool):
-        if timed:
-            rec("write0")
-        pk.kv_cache_write(batch.k_new, batch.v_new, batch.k_pool, batch.v_pool, slots,
-                          batch.k_scale, batch.v_scale, cache_dtype=w.cache_dtype)
-        if timed:
-            rec("write1")
+    one_call = not args.separate_append  # the step calls pa_decode_append
+
+    def attend(new_rows):
+        """pa_decode_append (new_rows given) or pa_decode, without the merge."""
         if part:
             pk.decode_partitions(batch.q, batch.k_pool, batch.v_pool, bt, cl,
                                  batch.max_context_len, part, batch.scale, batch.k_scale,
-                                 batch.v_scale, ws, out=out, cache_dtype=w.cache_dtype)
-            if timed:
-                rec("decode1")
-            pk.decode_reduce(out, ws, cl, batch.max_context_len, part, w.num_kv_heads)
-            if timed:
-                rec("reduce1")
+                                 batch.v_scale, ws, out=out, cache_dtype=w.cache_dtype,
+                                 **new_rows)
         else:
             pk.decode(batch.q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len,
                       batch.scale, batch.k_scale, batch.v_scale, 0, out=out,
-                      cache_dtype=w.cache_dtype)
+                      cache_dtype=w.cache_dtype, **new_rows)
+
+    def step(timed: bool):
+        if timed:
+            rec("write0")
+        if not one_call:
+            pk.kv_cache_write(batch.k_new, batch.v_new, batch.k_pool, batch.v_pool, slots,
+                              batch.k_scale, batch.v_scale, cache_dtype=w.cache_dtype)
+        if timed:
+            rec("write1")
+        attend(dict(k_new=batch.k_new, v_new=batch.v_new) if one_call else {})
+        if timed:
+            rec("decode1")
+        if part:
+            pk.decode_reduce(out, ws, cl, batch.max_context_len, part, w.num_kv_heads)
             if timed:
-                rec("decode1")
+                rec("reduce1")
 
     for _ in range(args.warmup):
         step(False)
@@ -511,14 +523,7 @@ def main() -> int:
     # The decode kernel alone: back-to-back launches on the stream it runs on,
     # one event pair around them, so per-launch event overhead is amortised.
     def decode_only():
-        if part:
-            pk.decode_partitions(batch.q, batch.k_pool, batch.v_pool, bt, cl,
-                                 batch.max_context_len, part, batch.scale, batch.k_scale,
-                                 batch.v_scale, ws, out=out, cache_dtype=w.cache_dtype)
-        else:
-            pk.decode(batch.q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len,
-                      batch.scale, batch.k_scale, batch.v_scale, 0, out=out,
-                      cache_dtype=w.cache_dtype)
+        attend({})
 
     reps = max(args.steps, 20)
     for _ in range(3):
@@ -539,8 +544,10 @@ def main() -> int:
     step_bytes = dec["total"] + wr
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dec["total"] / (decode_ms * 1e-3) / 1e9
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us (write {write_ms * 1e3:.1f}, decode "
-        f"{decode_ms_in_step * 1e3:.1f}, reduce {reduce_ms * 1e3:.1f}); decode alone "
+    first = (f"append+decode {decode_ms_in_step * 1e3:.1f}" if one_call else
+             f"write {write_ms * 1e3:.1f}, decode {decode_ms_in_step * 1e3:.1f}")
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us ({first}, reduce {reduce_ms * 1e3:.1f}); "
+        f"decode alone "
         f"{decode_ms * 1e3:.1f} us = {achieved:.0f} GB/s = {100 * achieved / PEAK_HBM_GBS:.1f}% "
         f"of peak")
 
@@ -573,12 +580,13 @@ def main() -> int:
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size,
                    "kv_dtype": w.cache_dtype, "context_tokens": dec["tokens"],
-                   "partition_size": part, "split": split, "step": "kv_cache_write + decode"
+                   "partition_size": part, "split": split,
+                   "step": ("decode_append" if one_call else "kv_cache_write + decode")
                    + (" + reduce" if part else ""),
                    "launch": "eager" if args.eager else "hip graph replay",
                    "eager_ms_per_step": round(eager_ms_per_step, 4)},
-        "kernels_us": {"kv_cache_write": round(write_ms * 1e3, 2),
-                       "decode": round(decode_ms_in_step * 1e3, 2),
+        "kernels_us": {"kv_cache_write": round(write_ms * 1e3, 2) if not one_call else None,
+                       "decode_append" if one_call else "decode": round(decode_ms_in_step * 1e3, 2),
                        "decode_reduce": round(reduce_ms * 1e3, 2),
                        "decode_back_to_back": round(decode_ms * 1e3, 2)},
         "roofline": {"bound": "hbm", "kernel": "pa_decode", "achieved": round(achieved, 1),

@@ -221,6 +221,46 @@ pa_status pa_decode(void* out, const void* q,
                     hipStream_t stream);
 
 /*
+ * pa_decode_append -- one decode step's append and attention in one call:
+ * the effect of pa_kv_cache_write of every sequence's newest token followed
+ * by pa_decode ("AI Inference Serving at Scale", section 3: the token just
+ * generated joins its sequence's current block, and the next query attends
+ * over the context including it).
+ *
+ * Sequence b's newest token is position L - 1, L = context_lens[b] clamped
+ * to [0, max_context_len]; its slot is block_tables[b][(L - 1) / block_size]
+ * * block_size + (L - 1) % block_size.  Rows k_new[b], v_new[b] are written
+ * there exactly as pa_kv_cache_write writes a token with that slot; nothing
+ * is written for b when L == 0, when (L - 1) / block_size >=
+ * max_blocks_per_seq, or when that table entry is outside [0, num_blocks).
+ * Then the attention is pa_decode with the same arguments: out, workspace
+ * and pa_decode_reduce behave as there, and the results (pool contents and
+ * out, bit for bit) are those of the two calls in sequence.
+ *
+ *   k_new, v_new   [num_seqs][num_kv_heads][head_dim], element src_dtype
+ *                  (PA_F32 or PA_BF16; cache_dtype equal to it, FP8 or INT4)
+ *   other arguments as pa_decode
+ *
+ * The append is a launch of its own on `stream`, before the decode's, so
+ * the caller needs no slot mapping for a decode step.
+ *
+ * Caller contract: that of pa_decode and of pa_kv_cache_write (two
+ * sequences' newest tokens must not share a slot).
+ */
+pa_status pa_decode_append(void* out, const void* q,
+                           const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int max_context_len,
+                           int num_seqs, int num_q_heads, int num_kv_heads,
+                           int head_dim, int block_size, int64_t num_blocks,
+                           float scale, pa_dtype q_dtype, pa_dtype src_dtype,
+                           pa_dtype cache_dtype,
+                           const float* k_scale, const float* v_scale,
+                           int partition_size, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * pa_decode_workspace_size -- bytes of workspace a split pa_decode needs
  * (0 when partition_size == 0; SIZE_MAX for invalid arguments, or for
  * PA_PARTITION_AUTO when the current HIP device cannot be queried).

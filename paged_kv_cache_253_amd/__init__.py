@@ -26,7 +26,7 @@ import os
 import torch
 
 __all__ = ["PagedAttnError", "load", "kv_cache_write", "copy_blocks", "swap_blocks", "decode",
-           "decode_partitions",
+           "decode_append", "decode_partitions",
            "prefill_chunk",
            "decode_reduce", "workspace_size", "new_workspace", "workspace_views", "default_partition_size",
            "PARTITION_AUTO", "LIB_PATH"]
@@ -67,6 +67,9 @@ def load() -> ctypes.CDLL:
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, i64,
                               f32, i32, i32, vp, vp, i32, vp, szt, vp]
     lib.pa_decode.restype = i32
+    lib.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
+                                     i32, i64, f32, i32, i32, i32, vp, vp, i32, vp, szt, vp]
+    lib.pa_decode_append.restype = i32
     lib.pa_decode_reduce.argtypes = [vp, vp, szt, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_decode_reduce.restype = i32
     lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -335,12 +338,27 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
 
 def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
-                 scale, k_scale, v_scale, partition_size, workspace, cache_dtype=None):
+                 scale, k_scale, v_scale, partition_size, workspace, cache_dtype=None,
+                 k_new=None, v_new=None):
     s, hq, d = q.shape
     nb, hkv, bsz, _ = _pool_dims(k_cache, v_cache, cache_dtype, head_dim=d)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise ValueError("block_tables and context_lens must be int32")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if k_new is not None:
+        if (k_new.shape != (s, hkv, d) or v_new is None or v_new.shape != k_new.shape
+                or v_new.dtype != k_new.dtype or not k_new.is_contiguous()
+                or not v_new.is_contiguous()):
+            raise ValueError("k_new and v_new must be contiguous [num_seqs, num_kv_heads, "
+                             "head_dim] tensors of one dtype")
+        st = load().pa_decode_append(
+            _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len),
+            s, hq, hkv, d, bsz, nb, float(scale), _dtype_code(q), _dtype_code(k_new),
+            _cache_code(k_cache, cache_dtype), _ptr(k_scale), _ptr(v_scale), int(partition_size),
+            _ptr(workspace), ws_bytes, _stream(q))
+        _check("pa_decode_append", st)
+        return
     st = load().pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                           block_tables.shape[1], _ptr(context_lens), int(max_context_len), s, hq,
                           hkv, d, bsz, nb, float(scale), _dtype_code(q),
@@ -352,9 +370,11 @@ def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
 
 def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                       partition_size, scale=None, k_scale=None, v_scale=None,
-                      workspace=None, out=None, cache_dtype=None) -> torch.Tensor:
+                      workspace=None, out=None, cache_dtype=None, k_new=None,
+                      v_new=None) -> torch.Tensor:
     """Split ``pa_decode`` only (fixed partitions, or the balanced split,
-    which also writes the rows of ``out`` it finishes); returns the
+    which also writes the rows of ``out`` it finishes), or
+    ``pa_decode_append`` when ``k_new``/``v_new`` are given; returns the
     workspace."""
     s, hq, d = q.shape
     hkv = k_cache.shape[1]
@@ -363,7 +383,7 @@ def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, max_conte
     if workspace is None:
         workspace = new_workspace(s, hq, hkv, d, max_context_len, partition_size, q.device)
     _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                 k_scale, v_scale, partition_size, workspace, cache_dtype)
+                 k_scale, v_scale, partition_size, workspace, cache_dtype, k_new, v_new)
     return workspace
 
 
@@ -388,12 +408,17 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            scale: float | None = None, k_scale: torch.Tensor | None = None,
            v_scale: torch.Tensor | None = None, partition_size: int | None = None,
            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-           cache_dtype: str | None = None) -> torch.Tensor:
+           cache_dtype: str | None = None, k_new: torch.Tensor | None = None,
+           v_new: torch.Tensor | None = None) -> torch.Tensor:
     """Decode attention over the paged cache; returns ``out [S, Hq, D]``.
 
     ``partition_size`` 0 runs unsplit; > 0 (fixed partitions) or
     ``PARTITION_AUTO`` (balanced split) runs the split decode followed by
     the merge; None picks ``default_partition_size(max_context_len)``.
+    With ``k_new``/``v_new`` ([S, Hkv, D]) each sequence's newest token
+    (position ``context_lens[b] - 1``, slot from its block table) is
+    appended first, in the same launch where the kernels allow
+    (``pa_decode_append``).
     """
     s, hq, d = q.shape
     if scale is None:
@@ -404,10 +429,21 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         out = torch.empty_like(q)
     if partition_size == 0:
         _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
-                     scale, k_scale, v_scale, 0, None, cache_dtype)
+                     scale, k_scale, v_scale, 0, None, cache_dtype, k_new, v_new)
         return out
     workspace = decode_partitions(q, k_cache, v_cache, block_tables, context_lens,
                                   max_context_len, partition_size, scale, k_scale, v_scale,
-                                  workspace, out=out, cache_dtype=cache_dtype)
+                                  workspace, out=out, cache_dtype=cache_dtype, k_new=k_new,
+                                  v_new=v_new)
     return decode_reduce(out, workspace, context_lens, max_context_len, partition_size,
                          k_cache.shape[1])
+
+
+def decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                  k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, max_context_len: int, **kw) -> torch.Tensor:
+    """One decode step: append every sequence's newest K/V row (its slot
+    taken from the block table) and attend (``pa_decode_append``, then the
+    merge of a split).  Keyword arguments as ``decode``."""
+    return decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                  k_new=k_new, v_new=v_new, **kw)

@@ -182,6 +182,7 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new, void* k_cache,
   if (is_fp8(cache) && (!k_scale || !v_scale)) return PA_ERR_INVALID_ARG;
   if (num_tokens == 0) return PA_OK;
   pa::WriteArgs a;
+  std::memset(&a, 0, sizeof a);
   a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
   a.slots = slot_mapping; a.k_scale = k_scale; a.v_scale = v_scale;
   a.num_slots = num_blocks * block_size;
@@ -218,13 +219,17 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void
                       dst_num_blocks, num_kv_heads, head_dim, block_size, cache_dtype, stream);
 }
 
-pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, int max_blocks_per_seq,
-                    const int32_t* context_lens, int max_context_len, int num_seqs,
-                    int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                    int64_t num_blocks, float scale, pa_dtype q_dtype, pa_dtype cache_dtype,
-                    const float* k_scale, const float* v_scale, int partition_size,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// pa_decode, and pa_decode_append when k_new is not null.
+pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
+                      const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int64_t num_blocks, float scale, pa_dtype q_dtype, pa_dtype src_dtype,
+                      pa_dtype cache_dtype, const float* k_scale, const float* v_scale,
+                      int partition_size, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0 ||
       max_blocks_per_seq < 1 || num_blocks < 1 || partition_size < PA_PARTITION_AUTO)
     return PA_ERR_INVALID_ARG;
@@ -263,6 +268,19 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     use_mfma = group > 1;
   }
 
+  const bool append = k_new != nullptr;
+  Elem se = Elem::BF16;
+  if (append) {
+    if (!v_new || !to_elem(src_dtype, &se)) return PA_ERR_INVALID_ARG;
+    if (se != Elem::F32 && se != Elem::BF16) return PA_ERR_UNSUPPORTED;
+    if (ce != se && !is_fp8(ce) && ce != Elem::I4) return PA_ERR_UNSUPPORTED;
+  }
+  // The append is a launch of its own, before the decode's.  Writing the
+  // rows inside the decode kernel (the wavefront that reads a newest
+  // token's tile appends it first) was measured on MI355X and gained
+  // nothing: the partial-line stores, issued ahead of the streaming loads,
+  // held up each wavefront's in-order memory queue by as long as the
+  // separate launch takes.
   pa::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
   a.out = out; a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
@@ -298,12 +316,56 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   }
   if (num_seqs == 0) return PA_OK;
   if (log_enabled())
-    std::fprintf(stderr, "[pagedattn] decode path=%s S=%d Hq=%d Hkv=%d G=%d D=%d B=%d P=%d parts=%d cus=%d\n",
+    std::fprintf(stderr, "[pagedattn] decode path=%s S=%d Hq=%d Hkv=%d G=%d D=%d B=%d P=%d parts=%d cus=%d append=%s\n",
                  use_mfma ? "mfma" : "valu", num_seqs, num_q_heads, num_kv_heads, group, head_dim,
-                 block_size, partition_size, a.max_parts, a.cus);
+                 block_size, partition_size, a.max_parts, a.cus,
+                 append ? "yes" : "no");
+  if (append) {
+    pa::WriteArgs w;
+    std::memset(&w, 0, sizeof w);
+    w.k_new = k_new; w.v_new = v_new;
+    w.k_cache = const_cast<void*>(k_cache); w.v_cache = const_cast<void*>(v_cache);
+    w.tables = block_tables; w.lens = context_lens;
+    w.k_scale = k_scale; w.v_scale = v_scale;
+    w.num_slots = num_blocks * block_size;
+    w.num_tokens = num_seqs; w.num_kv_heads = num_kv_heads;
+    w.max_blocks = max_blocks_per_seq; w.max_len = max_context_len;
+    const hipError_t e = pa::launch_cache_write(w, se, ce, head_dim, block_size, stream);
+    if (e != hipSuccess) return from_hip(e);
+  }
   hipError_t e = use_mfma ? pa::launch_decode_mfma(a, ce, head_dim, block_size, stream)
                           : pa::launch_decode_valu(a, qe, ce, head_dim, block_size, stream);
   return from_hip(e);
+}
+
+}  // namespace
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, int max_context_len, int num_seqs,
+                    int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                    int64_t num_blocks, float scale, pa_dtype q_dtype, pa_dtype cache_dtype,
+                    const float* k_scale, const float* v_scale, int partition_size,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     block_size, num_blocks, scale, q_dtype, PA_BF16, cache_dtype, k_scale, v_scale,
+                     partition_size, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, const int32_t* block_tables,
+                           int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int block_size, int64_t num_blocks, float scale, pa_dtype q_dtype,
+                           pa_dtype src_dtype, pa_dtype cache_dtype, const float* k_scale,
+                           const float* v_scale, int partition_size, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (!k_new || !v_new) return PA_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_new, v_new, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     block_size, num_blocks, scale, q_dtype, src_dtype, cache_dtype, k_scale, v_scale,
+                     partition_size, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,

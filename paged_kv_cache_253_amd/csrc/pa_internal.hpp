@@ -12,7 +12,7 @@ enum class Elem : int { F32 = 0, BF16 = 1, FP8 = 2, E5M2 = 3, I4 = 4 };
 inline bool is_fp8(Elem e) { return e == Elem::FP8 || e == Elem::E5M2; }
 
 // Bytes of one (block, KV head) tile of a pool.
-inline int64_t tile_bytes(Elem e, int head_dim, int block_size) {
+__host__ __device__ constexpr int64_t tile_bytes(Elem e, int head_dim, int block_size) {
   if (e == Elem::I4) return (int64_t)block_size * (head_dim / 2 + 4);
   const int elt = e == Elem::F32 ? 4 : (e == Elem::BF16 ? 2 : 1);
   return (int64_t)block_size * head_dim * elt;
@@ -94,11 +94,14 @@ struct WriteArgs {
   const void* v_new;
   void* k_cache;
   void* v_cache;
-  const int64_t* slots;
+  const int64_t* slots;         // per token, or null: token n is sequence n's newest token
+  const int32_t* tables;        // with slots null: [num_tokens][max_blocks] block tables
+  const int32_t* lens;          // with slots null: [num_tokens] context lengths (incl. the new token)
   const float* k_scale;
   const float* v_scale;
   int64_t num_slots;            // num_blocks * block_size
   int num_tokens, num_kv_heads;
+  int max_blocks, max_len;      // with slots null: table row length, clamp for lens
 };
 
 // Whole-block copies from (src_k, src_v) to (dst_k, dst_v): the same pools

@@ -31,7 +31,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_reduce",
+    assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_append",
+                                    "pa_decode_reduce",
                                     "pa_decode_workspace_size", "pa_kv_cache_write",
                                     "pa_prefill_chunk", "pa_prefill_reduce", "pa_status_string",
                                     "pa_swap_blocks"]
@@ -107,6 +108,36 @@ def _decode(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
+
+
+def _decode_append(lib, **kw):
+    args = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, bt=FAKE, maxb=8, cl=FAKE,
+                maxlen=128, s=2, hq=8, hkv=2, d=128, bs=16, nb=64, scale=0.088, qdt=BF16,
+                sdt=BF16, cdt=BF16, ks=None, vs=None, p=-1, ws=None, wsb=0)
+    args.update(kw)
+    a = args
+    return lib.pa_decode_append(a["out"], a["q"], a["kn"], a["vn"], a["k"], a["v"], a["bt"],
+                                a["maxb"], a["cl"], a["maxlen"], a["s"], a["hq"], a["hkv"],
+                                a["d"], a["bs"], a["nb"], a["scale"], a["qdt"], a["sdt"],
+                                a["cdt"], a["ks"], a["vs"], a["p"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), INVALID),
+    (dict(vn=None), INVALID),
+    (dict(sdt=7), INVALID),
+    (dict(sdt=F32), UNSUPPORTED),               # rows must match a same-type cache
+    (dict(sdt=FP8, cdt=FP8, ks=FAKE, vs=FAKE), UNSUPPORTED),  # rows are f32 or bf16
+    (dict(sdt=INT4, cdt=INT4), UNSUPPORTED),
+    (dict(cdt=FP8), INVALID),                   # fp8 cache without scales
+    (dict(q=None), INVALID),                    # the decode's own checks apply
+    (dict(d=96), UNSUPPORTED),
+    (dict(p=64, ws=None), WORKSPACE),
+    (dict(p=0, out=None), INVALID),
+    (dict(hq=64, hkv=2), UNSUPPORTED),
+])
+def test_decode_append_rejects(lib, kw, code):
+    assert _decode_append(lib, **kw) == code
 
 
 def test_int4_decode_has_no_vector_only_path(lib, monkeypatch):
