@@ -5,7 +5,8 @@ HBM: append each sequence's new K/V token, then decode attention over the
 paged cache -- by default one ``pa_decode_append`` call (slots from the
 block tables), ``--separate-append`` for ``pa_kv_cache_write`` with the
 slot mapping then ``pa_decode`` -- plus ``pa_decode_reduce`` when the
-context is split.  Default workload: the
+context is split and not merged inside the decode launch (``--partition
+-2``, ``PA_PARTITION_AUTO_MERGED``).  Default workload: the
 Llama-3-8B-shaped decode batch (64 sequences, 32 query / 8 KV heads, head
 dim 128, 16-token blocks, bf16 KV, lengths U[512, 4096]).
 
@@ -31,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD public spec
 KERNEL_SOURCES = ["decode_mfma.hip", "decode_valu.hip", "pa_device.hpp", "pa_mfma.hpp", "pa_split.hpp",
-                  "pa_internal.hpp"]
+                  "pa_internal.hpp", "pa_merge.hpp"]
 
 
 def log(*a):
@@ -374,8 +375,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--partition", type=int, default=None,
-                    help="context split: tokens per partition, 0 unsplit, -1 balanced "
-                         "(default: the workload's own, else the library default)")
+                    help="context split: tokens per partition, 0 unsplit, -1 balanced with "
+                         "a separate merge launch, -2 balanced merged in the decode launch "
+                         "(default: the workload's own, else the library default, -1)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -443,6 +445,7 @@ def main() -> int:
         ev.setdefault(name, []).append(e)
 
     one_call = not args.separate_append  # the step calls pa_decode_append
+    merge_launch = part not in (0, pk.PARTITION_AUTO_MERGED)  # a pa_decode_reduce per step
 
     def attend(new_rows):
         """pa_decode_append (new_rows given) or pa_decode, without the merge."""
@@ -467,7 +470,7 @@ def main() -> int:
         attend(dict(k_new=batch.k_new, v_new=batch.v_new) if one_call else {})
         if timed:
             rec("decode1")
-        if part:
+        if merge_launch:
             pk.decode_reduce(out, ws, cl, batch.max_context_len, part, w.num_kv_heads)
             if timed:
                 rec("reduce1")
@@ -518,7 +521,7 @@ def main() -> int:
     write_ms = float(np.mean(span("write0", "write1")))
     decode_ms_list = span("write1", "decode1")
     decode_ms_in_step = float(np.mean(decode_ms_list))
-    reduce_ms = float(np.mean(span("decode1", "reduce1"))) if part else 0.0
+    reduce_ms = float(np.mean(span("decode1", "reduce1"))) if merge_launch else 0.0
 
     # The decode kernel alone: back-to-back launches on the stream it runs on,
     # one event pair around them, so per-launch event overhead is amortised.
@@ -560,7 +563,8 @@ def main() -> int:
         log("[bench] copy calibration: 3 x 1 GiB device copies done")
 
     traffic = measured_traffic(w.name, part, 1)
-    split = {0: "unsplit", -1: "balanced"}.get(part, f"{part}-token partitions")
+    split = {0: "unsplit", -1: "balanced", -2: "balanced, merged in the decode launch"}.get(
+        part, f"{part}-token partitions")
     result = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) and context tokens/s",
         "value": round(gbs, 1),
@@ -582,12 +586,12 @@ def main() -> int:
                    "kv_dtype": w.cache_dtype, "context_tokens": dec["tokens"],
                    "partition_size": part, "split": split,
                    "step": ("decode_append" if one_call else "kv_cache_write + decode")
-                   + (" + reduce" if part else ""),
+                   + (" + reduce" if merge_launch else ""),
                    "launch": "eager" if args.eager else "hip graph replay",
                    "eager_ms_per_step": round(eager_ms_per_step, 4)},
         "kernels_us": {"kv_cache_write": round(write_ms * 1e3, 2) if not one_call else None,
                        "decode_append" if one_call else "decode": round(decode_ms_in_step * 1e3, 2),
-                       "decode_reduce": round(reduce_ms * 1e3, 2),
+                       "decode_reduce": round(reduce_ms * 1e3, 2) if merge_launch else None,
                        "decode_back_to_back": round(decode_ms * 1e3, 2)},
         "roofline": {"bound": "hbm", "kernel": "pa_decode", "achieved": round(achieved, 1),
                      "launch_us": round(decode_ms * 1e3, 2),

@@ -97,8 +97,10 @@ typedef enum pa_dtype {
   PA_INT4 = 4      /* signed 4-bit code, with a float32 scale per (token, KV head) */
 } pa_dtype;
 
-/* partition_size value selecting the balanced context split (see pa_decode). */
+/* partition_size values selecting the balanced context split (see pa_decode):
+ * merged by pa_decode_reduce, or merged inside the decode launch itself. */
 #define PA_PARTITION_AUTO (-1)
+#define PA_PARTITION_AUTO_MERGED (-2)
 
 /*
  * pa_kv_cache_write -- append new tokens' K and V rows into the pool.
@@ -196,6 +198,16 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
  *                     written to `out` here; the state of each run cut by a
  *                     slice boundary goes to `workspace`, and pa_decode_reduce
  *                     (same arguments) writes those runs' output.
+ *                  PA_PARTITION_AUTO_MERGED: the same split, with every cut
+ *                     run merged inside this launch by the wavefront that
+ *                     finishes its last piece (an arrival counter per cut
+ *                     run in the workspace header), so `out` is complete when
+ *                     the call's work ends and pa_decode_reduce has nothing
+ *                     to do.  Same output bits as PA_PARTITION_AUTO followed
+ *                     by pa_decode_reduce.  The workspace's counters must be
+ *                     zero on entry -- as in a zero-filled new workspace --
+ *                     and every call leaves them zero (pa_decode_append
+ *                     clears them itself before its decode).
  *   workspace, workspace_bytes  device scratch for the split modes; at least
  *                  pa_decode_workspace_size(...) bytes, 256-byte aligned;
  *                  ignored when partition_size == 0.  Concurrent calls must
@@ -242,7 +254,9 @@ pa_status pa_decode(void* out, const void* q,
  *   other arguments as pa_decode
  *
  * The append is a launch of its own on `stream`, before the decode's, so
- * the caller needs no slot mapping for a decode step.
+ * the caller needs no slot mapping for a decode step.  With
+ * PA_PARTITION_AUTO_MERGED it also clears the workspace's merge counters,
+ * so a step is two launches and needs no pa_decode_reduce.
  *
  * Caller contract: that of pa_decode and of pa_kv_cache_write (two
  * sequences' newest tokens must not share a slot).
@@ -276,15 +290,19 @@ pa_status pa_decode_append(void* out, const void* q,
  * maxP = max(1, ceil(max_context_len / partition_size)); the state of
  * partition p of sequence b, query head hq is row (b * num_q_heads + hq) *
  * maxP + p; rows of partitions a sequence does not have are unused.
- * PA_PARTITION_AUTO: H = 256 + align(16 * 8 * CUs), R = 8 * CUs * 2 * G
- * (CUs = compute units of the current device, G = num_q_heads /
- * num_kv_heads; a decode uses at most W = 8 * CUs slices).  pa_decode
- * stores W as an int32 at offset 0 and, at offset 256 + 16 s, four int32
- * naming the cut run whose first piece slice s holds (sequence, KV head,
- * number of slices holding a piece, state slot of the first piece; a piece
- * count of 0 = none), for pa_decode_reduce.  Slice s keeps the state of its
- * first run in rows (2s) * G + g and of its last run in rows (2s + 1) * G +
- * g, for the group's query heads g, when those runs are cut.
+ * PA_PARTITION_AUTO and PA_PARTITION_AUTO_MERGED: H = 256 + align(16 * 8 *
+ * CUs) + align(4 * 8 * CUs), R = 8 * CUs * 2 * G (CUs = compute units of
+ * the current device, G = num_q_heads / num_kv_heads; a decode uses at most
+ * W = 8 * CUs slices).  pa_decode stores W as an int32 at offset 0 and, at
+ * offset 256 + 16 s, four int32 naming the cut run whose first piece slice
+ * s holds (sequence, KV head, number of slices holding a piece, state slot
+ * of the first piece; a piece count of 0 = none), for pa_decode_reduce.
+ * Then, at offset 256 + align(16 * 8 * CUs), 8 * CUs int32 arrival
+ * counters for PA_PARTITION_AUTO_MERGED (counter s counts the finished
+ * pieces of the cut run whose first piece slice s holds).  Slice s keeps
+ * the state of its first run in rows (2s) * G + g and of its last run in
+ * rows (2s + 1) * G + g, for the group's query heads g, when those runs are
+ * cut.
  *
  * A state over tokens T of a query head, with z_t as in pa_decode:
  * part_max = max_{t in T} z_t, part_sum = sum_t exp(z_t - part_max),
@@ -307,7 +325,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
  * in float32, ranges added in a fixed order (identical bits on every call).
  * Fixed partitions: every row of `out` is written (L == 0 gives zeros).
  * PA_PARTITION_AUTO: only the rows of runs that pa_decode left cut are
- * written; pa_decode wrote the others.
+ * written; pa_decode wrote the others.  PA_PARTITION_AUTO_MERGED: nothing
+ * to merge (the decode launch did); returns PA_OK after the argument checks.
  *
  *   out            [num_seqs][num_q_heads][head_dim], element out_dtype
  *                  (PA_F32 or PA_BF16, rounded to nearest even)

@@ -29,7 +29,7 @@ __all__ = ["PagedAttnError", "load", "kv_cache_write", "copy_blocks", "swap_bloc
            "decode_append", "decode_partitions",
            "prefill_chunk",
            "decode_reduce", "workspace_size", "new_workspace", "workspace_views", "default_partition_size",
-           "PARTITION_AUTO", "LIB_PATH"]
+           "PARTITION_AUTO", "PARTITION_AUTO_MERGED", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 
@@ -37,6 +37,7 @@ PA_F32, PA_BF16, PA_FP8_E4M3, PA_FP8_E5M2, PA_INT4 = 0, 1, 2, 3, 4
 _CACHE_CODES = {"f32": PA_F32, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3, "fp8_e5m2": PA_FP8_E5M2,
                 "int4": PA_INT4}
 PARTITION_AUTO = -1  # balanced context split (PA_PARTITION_AUTO)
+PARTITION_AUTO_MERGED = -2  # the same, merged inside the decode launch (PA_PARTITION_AUTO_MERGED)
 _STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
            3: "PA_ERR_WORKSPACE", 4: "PA_ERR_HIP"}
 
@@ -179,7 +180,10 @@ def workspace_views(workspace: torch.Tensor, num_seqs: int, num_q_heads: int, he
 
 
 def default_partition_size(max_context_len: int) -> int:
-    """Context split used when the caller gives none: the balanced split."""
+    """Context split used when the caller gives none: the balanced split
+    with a separate merge launch (the merge inside the decode launch,
+    ``PARTITION_AUTO_MERGED``, measured no faster on MI355X: its last
+    wavefront's store, count and reload take about as long as that launch)."""
     return PARTITION_AUTO
 
 
@@ -414,11 +418,13 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
     ``partition_size`` 0 runs unsplit; > 0 (fixed partitions) or
     ``PARTITION_AUTO`` (balanced split) runs the split decode followed by
-    the merge; None picks ``default_partition_size(max_context_len)``.
+    the merge; ``PARTITION_AUTO_MERGED`` is the balanced split merged in the
+    decode launch (a given ``workspace`` must then hold zero merge counters,
+    as a new one and every merged call leave it; ``pa_decode_append``
+    clears them itself).  None picks ``default_partition_size(max_context_len)``.
     With ``k_new``/``v_new`` ([S, Hkv, D]) each sequence's newest token
     (position ``context_lens[b] - 1``, slot from its block table) is
-    appended first, in the same launch where the kernels allow
-    (``pa_decode_append``).
+    appended first (``pa_decode_append``).
     """
     s, hq, d = q.shape
     if scale is None:
@@ -435,6 +441,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                   max_context_len, partition_size, scale, k_scale, v_scale,
                                   workspace, out=out, cache_dtype=cache_dtype, k_new=k_new,
                                   v_new=v_new)
+    if partition_size == PARTITION_AUTO_MERGED:
+        return out
     return decode_reduce(out, workspace, context_lens, max_context_len, partition_size,
                          k_cache.shape[1])
 
@@ -444,6 +452,7 @@ def decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                   context_lens: torch.Tensor, max_context_len: int, **kw) -> torch.Tensor:
     """One decode step: append every sequence's newest K/V row (its slot
     taken from the block table) and attend (``pa_decode_append``, then the
-    merge of a split).  Keyword arguments as ``decode``."""
+    merge of a split unless it is ``PARTITION_AUTO_MERGED``).  Keyword
+    arguments as ``decode``."""
     return decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                   k_new=k_new, v_new=v_new, **kw)

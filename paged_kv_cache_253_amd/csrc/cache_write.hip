@@ -25,6 +25,10 @@ __global__ __launch_bounds__(64) void cache_write_kernel(const WriteArgs a) {
   const int n = blockIdx.x;
   const int h = blockIdx.y;
   const int lane = threadIdx.x;
+  if (a.zero_counters) {  // the following decode launch's merge counters
+    const int stride = gridDim.x * gridDim.y * 64;
+    for (int i = (h * gridDim.x + n) * 64 + lane; i < a.num_counters; i += stride) a.zero_counters[i] = 0;
+  }
   const ST* kn = reinterpret_cast<const ST*>(a.k_new) + ((int64_t)n * a.num_kv_heads + h) * D;
   const ST* vn = reinterpret_cast<const ST*>(a.v_new) + ((int64_t)n * a.num_kv_heads + h) * D;
   NewRow<ST> row;

@@ -35,6 +35,7 @@
 // slices of the whole batch (see pa_split.hpp).
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
+#include "pa_merge.hpp"
 #include "pa_mfma.hpp"
 #include "pa_split.hpp"
 
@@ -240,7 +241,9 @@ __global__ __launch_bounds__(64) void decode_mfma_grid(const DecodeArgs a) {
 // slot's compute is exact.  Block-table entries and lengths are read with
 // scalar loads (separate wait counter from the tile loads).  A run the slice
 // covers whole is finished here; the slice's first and last runs, when cut
-// by a slice boundary, leave partial states in rows (2r)*G.. and (2r+1)*G..
+// by a slice boundary, leave partial states in rows (2r)*G.. and (2r+1)*G..,
+// merged by a separate launch or, when the launch has merge counters, by the
+// wavefront that finishes a cut run's last piece (pa_merge.hpp).
 // ---------------------------------------------------------------------------
 
 constexpr int kFirst = 1, kLast = 2, kFinal = 4;
@@ -325,6 +328,9 @@ void decode_mfma_stream(const DecodeArgs a) {
   // merge record: only the slice's last run can be cut by the next boundary
   MergeRec rec{0, 0, 0, 0};
   if (ci == 0 && cseg_end < cn) rec = merge_rec_of(sp, r, g0, cn, cb, ch, 0);
+  // the slice's first and last runs (first step, steps, sequence, KV head):
+  // the pieces this wavefront may hold of cut runs, for a merge in the launch
+  CutPiece pieces[2] = {{g0 - ci, cn, cb, ch, true}, {0, 0, 0, 0, false}};
 
   // per-lane offsets inside a step's tiles (see attend)
   const LaneOffsets<CK, D, BS> lo(grp, col);
@@ -350,6 +356,7 @@ void decode_mfma_stream(const DecodeArgs a) {
         cflags_run = (cseg_end == cn) ? kFinal : 0;
         crow0 = (r * 2 + 1) * G;
         if (cseg_end < cn) rec = merge_rec_of(sp, r, g_end - left, cn, cb, ch, 1);
+        pieces[1] = CutPiece{g_end - left, cn, cb, ch, true};
       }
       sl.base = ci * kStepTokens;
       sl.t1 = min(min(cseg_end * kStepTokens, clen), a.cap_len);
@@ -417,12 +424,17 @@ void decode_mfma_stream(const DecodeArgs a) {
       } else {
         const int row0 = -1 - tag;
         float* o = a.part_out + (size_t)row0 * D;
-        for (int q = lane; q < G * (D / 4); q += 64)
-          *reinterpret_cast<f32x4*>(o + (size_t)q * 4) =
-              *reinterpret_cast<const f32x4*>(src + (q / (D / 4)) * kStageRow + (q % (D / 4)) * 4);
+        if (a.counters) {  // merged in this launch, maybe on another XCD: device-scope stores
+          for (int q = lane; q < G * D; q += 64)
+            state_store(o + q, src[(q / D) * kStageRow + q % D], true);
+        } else {
+          for (int q = lane; q < G * (D / 4); q += 64)
+            *reinterpret_cast<f32x4*>(o + (size_t)q * 4) =
+                *reinterpret_cast<const f32x4*>(src + (q / (D / 4)) * kStageRow + (q % (D / 4)) * 4);
+        }
         if (lane < G) {
-          a.part_max[row0 + lane] = src[G * kStageRow + lane];
-          a.part_sum[row0 + lane] = src[G * kStageRow + G + lane];
+          state_store(a.part_max + row0 + lane, src[G * kStageRow + lane], a.counters != nullptr);
+          state_store(a.part_sum + row0 + lane, src[G * kStageRow + G + lane], a.counters != nullptr);
         }
       }
     }
@@ -516,6 +528,10 @@ void decode_mfma_stream(const DecodeArgs a) {
   }
   flush();
   if (lane == 0) store_merge_rec(a.header, r, rec);
+  if (a.counters) {  // cut runs merged in this launch by the wavefront finishing last
+    const MergeView v{a.out, a.part_out, a.part_max, a.part_sum, a.num_q_heads, G};
+    arrive_and_merge<__bf16, D>(v, a.counters, sp, pieces);
+  }
 }
 
 template <int CK, int D, int BS>

@@ -13,10 +13,12 @@
 //  * auto_fixup_kernel: balanced slices.  One workgroup per slice; the
 //    slice's merge record (written by the decode, see pa_split.hpp) names
 //    the cut run whose first piece it holds, if any, and the workgroup
-//    merges all of that run's slice states, one query head per wavefront,
-//    the pieces' maxima and weights taken by the lanes in parallel.
+//    merges all of that run's slice states (merge_cut_run in pa_merge.hpp,
+//    the routine the decode kernels use when they merge in their own
+//    launch), query heads dealt to the wavefronts in turn.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
+#include "pa_merge.hpp"
 #include "pa_split.hpp"
 
 namespace pa {
@@ -106,10 +108,8 @@ constexpr int kFixupThreads = 256;
 
 template <typename OT, int D>
 __global__ __launch_bounds__(kFixupThreads) void auto_fixup_kernel(const ReduceArgs a) {
-  constexpr int PER = D / 64;
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   const int r_first = blockIdx.x;  // slice holding the run's first piece
-  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int slices = a.header[kHdrSlices];  // as launched by the decode
   const i32x4 rec = *reinterpret_cast<const i32x4*>(reinterpret_cast<const char*>(a.header) +
@@ -121,75 +121,9 @@ __global__ __launch_bounds__(kFixupThreads) void auto_fixup_kernel(const ReduceA
   if (nparts > slices - r_first || (unsigned)b >= (unsigned)a.num_seqs ||
       (unsigned)h >= (unsigned)a.num_kv_heads || (unsigned)k_first > 1u)
     return;
-  const int G = a.num_q_heads / a.num_kv_heads;
-  auto row_of = [&](int j, int gq) -> size_t {  // piece j of the run, in slice order
-    const int rr = r_first + j;
-    return ((size_t)rr * 2 + (j == 0 ? k_first : 0)) * G + gq;
-  };
-  for (int gq = wave; gq < G; gq += kFixupThreads / 64) {
-    float acc[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    float mx, wsum;
-    if (nparts <= 64) {
-      // Lane j takes piece j's maximum and exp-sum; the rows of the first
-      // kBatch pieces are loaded with them, later batches one load round
-      // each.  Same arithmetic, in the same order, as the general loop below.
-      const bool mine = lane < nparts;
-      const size_t rl = row_of(mine ? lane : 0, gq);
-      const float pm = a.part_max[rl], ps = a.part_sum[rl];
-      constexpr int kBatch = 8;
-      float rows[kBatch][PER];
-      auto load_batch = [&](int j0) {
-#pragma unroll
-        for (int jj = 0; jj < kBatch; ++jj) {
-          const float* src = a.part_out + row_of(min(j0 + jj, nparts - 1), gq) * D + lane;
-#pragma unroll
-          for (int e = 0; e < PER; ++e) rows[jj][e] = src[64 * e];
-        }
-      };
-      load_batch(0);
-      mx = xlane<OpMax, 1, 32>(mine ? pm : -INFINITY);
-      const float w = mine ? ps * __expf(pm - mx) : 0.f;
-      wsum = w;
-      for (int j0 = 0; j0 < nparts; j0 += kBatch) {
-        if (j0 > 0) load_batch(j0);
-#pragma unroll
-        for (int jj = 0; jj < kBatch; ++jj) {
-          if (j0 + jj < nparts) {
-            const float wj = __int_as_float(readlane(__float_as_int(w), j0 + jj));
-#pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, rows[jj][e], acc[e]);
-          }
-        }
-      }
-    } else {
-      // lanes take the pieces' maxima and exp-sums in parallel
-      mx = -INFINITY;
-      for (int j = lane; j < nparts; j += 64) mx = fmaxf(mx, a.part_max[row_of(j, gq)]);
-      mx = xlane<OpMax, 1, 32>(mx);
-      wsum = 0.f;
-      for (int j0 = 0; j0 < nparts; j0 += 64) {
-        const int j = j0 + lane;
-        const size_t row = row_of(j < nparts ? j : j0, gq);
-        const float w = j < nparts ? a.part_sum[row] * __expf(a.part_max[row] - mx) : 0.f;
-        wsum += w;
-        const int cnt = min(64, nparts - j0);
-#pragma unroll 4
-        for (int jj = 0; jj < cnt; ++jj) {
-          const float wj = __int_as_float(readlane(__float_as_int(w), jj));
-          const float* src = a.part_out + row_of(j0 + jj, gq) * D + lane;
-#pragma unroll
-          for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, src[64 * e], acc[e]);
-        }
-      }
-    }
-    const float total = xlane<OpSum, 1, 32>(wsum);
-    OT* o = reinterpret_cast<OT*>(a.out) + ((size_t)b * a.num_q_heads + (size_t)h * G + gq) * D;
-    const float inv = 1.0f / total;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[lane + 64 * e] = (OT)(acc[e] * inv);
-  }
+  const MergeView v{a.out, a.part_out, a.part_max, a.part_sum, a.num_q_heads,
+                    a.num_q_heads / a.num_kv_heads};
+  merge_cut_run<OT, D, false>(v, b, h, r_first, k_first, nparts, wave, kFixupThreads / 64);
 }
 
 template <typename OT, int D>

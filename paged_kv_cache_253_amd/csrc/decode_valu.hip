@@ -18,6 +18,7 @@
 // Lanes sharing a dimension are summed once at the end.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
+#include "pa_merge.hpp"
 #include "pa_split.hpp"
 
 namespace pa {
@@ -269,12 +270,12 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
       if (tc == 0) {
         const int d = i * DSTRIDE + lane / CPR;
         if (tgt.final_out) out[((size_t)b * a.num_q_heads + hq) * D + d] = (QT)v;
-        else a.part_out[row * D + d] = v;
+        else state_store(a.part_out + row * D + d, v, a.counters != nullptr);
       }
     }
     if (!tgt.final_out && lane == 0) {
-      a.part_max[row] = m_run[g] * kLn2;  // back to natural units
-      a.part_sum[row] = l_tot;
+      state_store(a.part_max + row, m_run[g] * kLn2, a.counters != nullptr);  // natural units
+      state_store(a.part_sum + row, l_tot, a.counters != nullptr);
     }
   }
 }
@@ -310,9 +311,11 @@ __global__ __launch_bounds__(64) void decode_valu_auto(const DecodeArgs a) {
   int b, i0;
   locate_step(a.context_lens, a.num_seqs, a.max_len, g - (int64_t)h * sp.per_head, b, i0);
   bool first = true;
+  CutPiece pieces[2] = {{0, 0, 0, 0, false}, {0, 0, 0, 0, false}};  // first and last runs
   while (g < g_end) {
     const int len = clamp_len(a.context_lens[b], a.max_len);
     const int n = steps_of_len(len);
+    pieces[first ? 0 : 1] = CutPiece{g - i0, n, b, h, true};
     const int seg = (int)min((int64_t)(n - i0), g_end - g);
     const int t0 = i0 * kStep;
     const int t1 = min((i0 + seg) * kStep, len);
@@ -329,6 +332,10 @@ __global__ __launch_bounds__(64) void decode_valu_auto(const DecodeArgs a) {
     if (++b == a.num_seqs) { b = 0; ++h; }
   }
   if (threadIdx.x == 0) store_merge_rec(a.header, r, rec);
+  if (a.counters) {  // cut runs merged in this launch by the wavefront finishing last
+    const MergeView v{a.out, a.part_out, a.part_max, a.part_sum, a.num_q_heads, G};
+    arrive_and_merge<QT, D>(v, a.counters, sp, pieces);
+  }
 }
 
 template <typename QT, Elem E, int D, int BS, int G>

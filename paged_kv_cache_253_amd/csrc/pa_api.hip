@@ -12,6 +12,9 @@
 
 using pa::Elem;
 
+static_assert(pa::kAuto == PA_PARTITION_AUTO && pa::kAutoMerged == PA_PARTITION_AUTO_MERGED,
+              "split-mode values of the ABI");
+
 namespace {
 
 constexpr int kStepTokens = 32;  // kernels walk the context in 32-token steps
@@ -34,6 +37,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   size_t head_bytes, out_bytes, max_bytes, total;
+  size_t counters_off;  // balanced split: offset of the merge counters in the header
   int max_parts;   // fixed partitions: partitions per (sequence, query head)
   int slices_max;  // balanced split: most persistent wavefronts
   int cus;         // balanced split: compute units
@@ -74,11 +78,13 @@ bool workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_
   l->slices_max = 0;
   l->cus = 0;
   l->head_bytes = 0;
-  if (partition_size == pa::kAuto) {
+  l->counters_off = 0;
+  if (partition_size == pa::kAuto || partition_size == pa::kAutoMerged) {
     l->cus = device_cus();
     if (l->cus <= 0) return false;
     l->slices_max = l->cus * pa::kAutoMaxWavesPerCU;
-    l->head_bytes = pa::kHdrRecordsBytes + align256((size_t)l->slices_max * pa::kMergeRecordBytes);
+    l->counters_off = pa::kHdrRecordsBytes + align256((size_t)l->slices_max * pa::kMergeRecordBytes);
+    l->head_bytes = l->counters_off + align256((size_t)l->slices_max * sizeof(int));
     rows = (size_t)l->slices_max * 2 * (size_t)(num_q_heads / num_kv_heads);
   } else if (partition_size > 0) {
     const long long parts = std::max(1LL, ((long long)max_context_len + partition_size - 1) / partition_size);
@@ -231,8 +237,10 @@ pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v
                       int partition_size, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0 ||
-      max_blocks_per_seq < 1 || num_blocks < 1 || partition_size < PA_PARTITION_AUTO)
+      max_blocks_per_seq < 1 || num_blocks < 1 || partition_size < PA_PARTITION_AUTO_MERGED)
     return PA_ERR_INVALID_ARG;
+  const bool merged = partition_size == PA_PARTITION_AUTO_MERGED;
+  const bool balanced = merged || partition_size == PA_PARTITION_AUTO;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (!(std::isfinite(scale) && scale > 0.0f)) return PA_ERR_INVALID_ARG;
   Elem qe, ce;
@@ -290,22 +298,26 @@ pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v
   a.max_blocks = max_blocks_per_seq;
   const long long cap = (long long)max_blocks_per_seq * block_size;
   a.cap_len = (int)std::min<long long>(cap, INT32_MAX);
-  a.max_len = partition_size == PA_PARTITION_AUTO ? max_context_len
-                                                  : (int)std::min<long long>(max_context_len, cap);
+  a.max_len = balanced ? max_context_len : (int)std::min<long long>(max_context_len, cap);
   a.num_seqs = num_seqs; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads;
   a.group = group;
-  a.partition = partition_size;
+  a.partition = balanced ? pa::kAuto : partition_size;
   a.scale = scale;
   a.max_parts = 1;
+  int num_counters = 0;
   if (partition_size != 0) {
     Layout l;
     if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                           partition_size, &l))
-      return partition_size == PA_PARTITION_AUTO ? PA_ERR_HIP : PA_ERR_INVALID_ARG;
+      return balanced ? PA_ERR_HIP : PA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
       return PA_ERR_WORKSPACE;
     char* w = static_cast<char*>(workspace);
     a.header = reinterpret_cast<int*>(w);
+    if (merged) {
+      a.counters = reinterpret_cast<int*>(w + l.counters_off);
+      num_counters = l.slices_max;
+    }
     w += l.head_bytes;
     a.part_out = reinterpret_cast<float*>(w);
     a.part_max = reinterpret_cast<float*>(w + l.out_bytes);
@@ -330,6 +342,8 @@ pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v
     w.num_slots = num_blocks * block_size;
     w.num_tokens = num_seqs; w.num_kv_heads = num_kv_heads;
     w.max_blocks = max_blocks_per_seq; w.max_len = max_context_len;
+    w.zero_counters = a.counters;  // the decode below counts arrivals from zero
+    w.num_counters = num_counters;
     const hipError_t e = pa::launch_cache_write(w, se, ce, head_dim, block_size, stream);
     if (e != hipSuccess) return from_hip(e);
   }
@@ -373,7 +387,8 @@ pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_by
                            int num_q_heads, int num_kv_heads, int head_dim, int partition_size,
                            pa_dtype out_dtype, hipStream_t stream) {
   if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0 ||
-      (partition_size <= 0 && partition_size != PA_PARTITION_AUTO))
+      (partition_size <= 0 && partition_size != PA_PARTITION_AUTO &&
+       partition_size != PA_PARTITION_AUTO_MERGED))
     return PA_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   Elem oe;
@@ -381,14 +396,14 @@ pa_status pa_decode_reduce(void* out, const void* workspace, size_t workspace_by
   if (is_fp8(oe) || !supported_dim(head_dim)) return PA_ERR_UNSUPPORTED;
   if (partition_size > 0 && partition_size % kStepTokens != 0) return PA_ERR_UNSUPPORTED;
   if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
-  if (num_q_heads / num_kv_heads > 16 && partition_size == PA_PARTITION_AUTO) return PA_ERR_UNSUPPORTED;
+  if (num_q_heads / num_kv_heads > 16 && partition_size < 0) return PA_ERR_UNSUPPORTED;
   if (!out || !workspace || !context_lens) return PA_ERR_INVALID_ARG;
   Layout l;
   if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                         partition_size, &l))
-    return partition_size == PA_PARTITION_AUTO ? PA_ERR_HIP : PA_ERR_INVALID_ARG;
+    return partition_size < 0 ? PA_ERR_HIP : PA_ERR_INVALID_ARG;
   if (workspace_bytes < l.total || (reinterpret_cast<uintptr_t>(workspace) & 255)) return PA_ERR_WORKSPACE;
-  if (num_seqs == 0) return PA_OK;
+  if (num_seqs == 0 || partition_size == PA_PARTITION_AUTO_MERGED) return PA_OK;  // merged by the decode
   const char* w = static_cast<const char*>(workspace);
   pa::ReduceArgs a;
   std::memset(&a, 0, sizeof a);
@@ -419,7 +434,8 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
   if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || num_q_heads < 1 ||
       num_kv_heads < 1 || max_context_len < 0 || max_blocks_per_seq < 1 || num_blocks < 1 ||
       partition_size < 0)
-    return partition_size == PA_PARTITION_AUTO ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
+    return (partition_size == PA_PARTITION_AUTO || partition_size == PA_PARTITION_AUTO_MERGED)
+               ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (!(std::isfinite(scale) && scale > 0.0f)) return PA_ERR_INVALID_ARG;
   Elem qe, ce;

@@ -26,14 +26,18 @@ constexpr int kAutoMinSteps = 4;
 constexpr int kXcds = 8;
 // Balanced-split workspace header: the decode's wavefront count W as the
 // int32 at word kHdrSlices, then from byte kHdrRecordsBytes one 16-byte
-// merge record per slice (see pa_split.hpp).
+// merge record per slice (see pa_split.hpp), then (256-byte aligned) one
+// int32 arrival counter per slice for the merge inside the decode launch
+// (see pa_merge.hpp).
 constexpr int kHdrSlices = 0;
 constexpr int kHdrRecordsBytes = 256;
 constexpr int kMergeRecordBytes = 16;
 
 // Split modes (DecodeArgs::partition): > 0 fixed partitions of that many
-// tokens, 0 unsplit, kAuto balanced slices.
+// tokens, 0 unsplit, kAuto balanced slices (the merge inside the decode
+// launch when DecodeArgs::counters is set).
 constexpr int kAuto = -1;
+constexpr int kAutoMerged = -2;  // ABI value of the balanced split merged in the decode launch
 
 // Everything a decode launch needs; passed by value as the kernel argument.
 struct DecodeArgs {
@@ -59,6 +63,8 @@ struct DecodeArgs {
   int cus;                      // balanced split: compute units of the device
   int waves_per_cu;             // balanced split: 0 = the kernel's own choice
   int* header;                  // balanced split: workspace header (W, merge records)
+  int* counters;                // balanced split merged in the decode launch: [slices_max]
+                                // arrival counters, zero on entry and on exit; else null
   float scale;
 };
 
@@ -102,6 +108,8 @@ struct WriteArgs {
   int64_t num_slots;            // num_blocks * block_size
   int num_tokens, num_kv_heads;
   int max_blocks, max_len;      // with slots null: table row length, clamp for lens
+  int* zero_counters;           // if set: [num_counters] ints cleared by this launch (the
+  int num_counters;             // merge counters of the decode launch that follows)
 };
 
 // Whole-block copies from (src_k, src_v) to (dst_k, dst_v): the same pools

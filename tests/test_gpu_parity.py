@@ -68,7 +68,8 @@ def test_workload_write_and_decode(idx):
     seqs = _sample(batch, SAMPLE[idx])
     ref = oracle_decode_host(batch, k_ref, v_ref, seqs)
     del k_ref, v_ref
-    splits = [w.partition_size, -1] if w.partition_size else [-1, 0, 512]
+    # -2: the balanced split merged inside the decode launch (the bench's step)
+    splits = [w.partition_size, -1, -2] if w.partition_size else [-1, -2, 0, 512]
     for p in splits:
         out = gpu_decode(batch, p)
         _sync()
@@ -391,13 +392,16 @@ def test_fp8_append_rounding_matches_oracle_on_many_values(fmt):
 
 
 def test_balanced_workspace_size_follows_documented_layout():
-    """PA_PARTITION_AUTO: a header of 256 bytes plus a 16-byte merge record
-    per possible slice, then R = 8 * CUs * 2 * G rows of partial state (the
-    documented bound on the decode's wavefronts)."""
+    """PA_PARTITION_AUTO (and _MERGED, same layout): a header of 256 bytes,
+    a 16-byte merge record and a 4-byte merge counter per possible slice,
+    then R = 8 * CUs * 2 * G rows of partial state (the documented bound on
+    the decode's wavefronts)."""
     def align(x):
         return (x + 255) // 256 * 256
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for s, hq, hkv, d in [(64, 32, 8, 128), (3, 16, 16, 64), (8, 64, 4, 128)]:
         rows = 8 * cus * 2 * (hq // hkv)
-        want = 256 + align(16 * 8 * cus) + align(rows * d * 4) + 2 * align(rows * 4)
+        want = (256 + align(16 * 8 * cus) + align(4 * 8 * cus) + align(rows * d * 4)
+                + 2 * align(rows * 4))
         assert pk.workspace_size(s, hq, hkv, d, 4096, -1) == want
+        assert pk.workspace_size(s, hq, hkv, d, 4096, -2) == want
