@@ -300,13 +300,17 @@ void decode_mfma_stream(const DecodeArgs a) {
   const int grp = lane >> 4;
   const int G = a.group;
   const int W = a.slices;
-  if (blockIdx.x == 0 && lane == 0) a.header[kHdrSlices] = W;  // for the merge
-  const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, W);
+  // fixed partitions: steps per partition, and the workspace row stride of
+  // a group's query heads (their rows are max_parts apart); 0 / 1 balanced
+  const int pst = a.partition > 0 ? a.partition / kStepTokens : 0;
+  const int rstride = pst ? a.max_parts : 1;
+  if (blockIdx.x == 0 && lane == 0 && !pst) a.header[kHdrSlices] = W;  // for the merge
+  const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, W, pst);
   const int r = slice_of_wave(blockIdx.x, W);
   int64_t g0, g_end;
   slice_bounds(sp, r, g0, g_end);
   if (g0 >= g_end) {
-    if (lane == 0) store_merge_rec(a.header, r, MergeRec{0, 0, 0, 0});
+    if (lane == 0 && !pst) store_merge_rec(a.header, r, MergeRec{0, 0, 0, 0});
     return;
   }
 
@@ -314,20 +318,36 @@ void decode_mfma_stream(const DecodeArgs a) {
   const const_i32 tables = (const_i32)a.block_tables;
 
   // ---- issue-side cursor over the slice's runs ----------------------------
-  int64_t left = g_end - g0;  // slice steps not yet issued
+  // Balanced: `left` counts the slice's steps not yet issued.  Fixed
+  // partitions: the slice is whole partitions; `left` counts those not yet
+  // started, and each partition is one segment of its run.
+  int64_t left = g_end - g0;
   int cb, ci;                 // run (sequence cb, KV head ch) and its step index
   int ch = (int)(g0 / sp.per_head);
-  locate_step(a.context_lens, a.num_seqs, a.max_len, g0 - (int64_t)ch * sp.per_head, cb, ci);
+  locate_step(a.context_lens, a.num_seqs, a.max_len, g0 - (int64_t)ch * sp.per_head, cb, ci, pst);
   int clen = clamp_len(lens[cb], a.max_len);
   int cn = steps_of_len(clen);
-  int cseg_start = ci;                                     // the segment (run part inside the
-  int cseg_end = (int)min((int64_t)cn, (int64_t)ci + left);  // slice), in run steps
-  int cflags_run = (ci == 0 && cseg_end == cn) ? kFinal : 0;
-  int crow0 = r * 2 * G;  // the slice's first run -> rows (2r)*G..
+  int cpart = 0;              // fixed partitions: the current partition of the run
+  int cseg_start, cseg_end;   // the segment (run part inside the slice), in run steps
+  int cflags_run, crow0;
+  if (pst) {
+    cpart = ci;
+    ci = cpart * pst;
+    cseg_start = ci;
+    cseg_end = min(ci + pst, cn);
+    cflags_run = 0;
+    crow0 = (cb * a.num_q_heads + ch * G) * a.max_parts + cpart;
+    --left;
+  } else {
+    cseg_start = ci;
+    cseg_end = (int)min((int64_t)cn, (int64_t)ci + left);
+    cflags_run = (ci == 0 && cseg_end == cn) ? kFinal : 0;
+    crow0 = r * 2 * G;  // the slice's first run -> rows (2r)*G..
+  }
   int pending = 0;        // real steps issued and not yet computed
   // merge record: only the slice's last run can be cut by the next boundary
   MergeRec rec{0, 0, 0, 0};
-  if (ci == 0 && cseg_end < cn) rec = merge_rec_of(sp, r, g0, cn, cb, ch, 0);
+  if (!pst && ci == 0 && cseg_end < cn) rec = merge_rec_of(sp, r, g0, cn, cb, ch, 0);
   // the slice's first and last runs (first step, steps, sequence, KV head):
   // the pieces this wavefront may hold of cut runs, for a merge in the launch
   CutPiece pieces[2] = {{g0 - ci, cn, cb, ch, true}, {0, 0, 0, 0, false}};
@@ -343,10 +363,24 @@ void decode_mfma_stream(const DecodeArgs a) {
   const __bf16* qp = qbase;
 
   auto issue = [&](S& sl) {
-    const bool real = left > 0;
+    const bool real = pst ? (ci < cseg_end || left > 0) : left > 0;
     sl.real = real;
     if (real) {
-      if (ci == cseg_end) {  // next run of the slice
+      if (pst && ci == cseg_end) {  // next partition of the slice
+        --left;
+        if (++cpart * pst >= cn) {  // next run that has a partition
+          do {
+            if (++cb == a.num_seqs) { cb = 0; ++ch; }
+            clen = clamp_len(lens[cb], a.max_len);
+          } while (clen == 0);
+          cn = steps_of_len(clen);
+          cpart = 0;
+        }
+        ci = cpart * pst;
+        cseg_start = ci;
+        cseg_end = min(ci + pst, cn);
+        crow0 = (cb * a.num_q_heads + ch * G) * a.max_parts + cpart;
+      } else if (ci == cseg_end) {  // next run of the slice
         if (++cb == a.num_seqs) { cb = 0; ++ch; }
         clen = clamp_len(lens[cb], a.max_len);
         cn = steps_of_len(clen);
@@ -376,7 +410,7 @@ void decode_mfma_stream(const DecodeArgs a) {
       tile1 = ((int64_t)p1 * a.num_kv_heads + ch) * C::kTile;
       qp = qbase + ((size_t)cb * a.num_q_heads + (size_t)ch * G + qhead) * D;
       ++ci;
-      --left;
+      if (!pst) --left;
       ++pending;
     }
     load_step(sl, kc, vc, tile0, tile1, lo, grp);
@@ -422,19 +456,23 @@ void decode_mfma_stream(const DecodeArgs a) {
           *reinterpret_cast<bf16x8*>(o + (size_t)q * 8) = y;
         }
       } else {
-        const int row0 = -1 - tag;
-        float* o = a.part_out + (size_t)row0 * D;
+        const int row0 = -1 - tag;  // head g of the group at row row0 + g * rstride
         if (a.counters) {  // merged in this launch, maybe on another XCD: device-scope stores
+          float* o = a.part_out + (size_t)row0 * D;
           for (int q = lane; q < G * D; q += 64)
             state_store(o + q, src[(q / D) * kStageRow + q % D], true);
         } else {
-          for (int q = lane; q < G * (D / 4); q += 64)
-            *reinterpret_cast<f32x4*>(o + (size_t)q * 4) =
-                *reinterpret_cast<const f32x4*>(src + (q / (D / 4)) * kStageRow + (q % (D / 4)) * 4);
+          for (int q = lane; q < G * (D / 4); q += 64) {
+            const int g = q / (D / 4);
+            *reinterpret_cast<f32x4*>(a.part_out + ((size_t)row0 + (size_t)g * rstride) * D +
+                                      (q % (D / 4)) * 4) =
+                *reinterpret_cast<const f32x4*>(src + g * kStageRow + (q % (D / 4)) * 4);
+          }
         }
         if (lane < G) {
-          state_store(a.part_max + row0 + lane, src[G * kStageRow + lane], a.counters != nullptr);
-          state_store(a.part_sum + row0 + lane, src[G * kStageRow + G + lane], a.counters != nullptr);
+          const size_t rl = (size_t)row0 + (size_t)lane * rstride;
+          state_store(a.part_max + rl, src[G * kStageRow + lane], a.counters != nullptr);
+          state_store(a.part_sum + rl, src[G * kStageRow + G + lane], a.counters != nullptr);
         }
       }
     }
@@ -527,6 +565,7 @@ void decode_mfma_stream(const DecodeArgs a) {
     }
   }
   flush();
+  if (pst) return;
   if (lane == 0) store_merge_rec(a.header, r, rec);
   if (a.counters) {  // cut runs merged in this launch by the wavefront finishing last
     const MergeView v{a.out, a.part_out, a.part_max, a.part_sum, a.num_q_heads, G};
@@ -536,7 +575,7 @@ void decode_mfma_stream(const DecodeArgs a) {
 
 template <int CK, int D, int BS>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-  if (a.partition == kAuto) {
+  if (a.partition == kAuto || (a.partition > 0 && a.stream_fixed)) {
     DecodeArgs b = a;
     b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : stream_waves_per_cu<CK, D>());
     hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS>), dim3(b.slices), dim3(64), 0, stream, b);

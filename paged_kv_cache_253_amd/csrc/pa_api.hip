@@ -99,6 +99,13 @@ bool workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_
   return true;
 }
 
+// PA_FIXED_GRID=1 runs fixed partitions one wavefront per partition
+// instead of on the persistent streaming grid (cross-checks and timing).
+bool fixed_grid_forced() {
+  const char* e = std::getenv("PA_FIXED_GRID");
+  return e && e[0] == '1';
+}
+
 // "valu" / "mfma" forces a decode kernel family (tuning and cross-checks).
 int forced_path() {
   const char* e = std::getenv("PA_FORCE_PATH");
@@ -323,8 +330,11 @@ pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v
     a.part_max = reinterpret_cast<float*>(w + l.out_bytes);
     a.part_sum = reinterpret_cast<float*>(w + l.out_bytes + l.max_bytes);
     a.max_parts = l.max_parts;
-    a.cus = l.cus;
+    a.cus = balanced ? l.cus : device_cus();
     a.waves_per_cu = auto_waves_override();
+    // fixed partitions stream when their state rows fit the kernel's int row index
+    a.stream_fixed = !balanced && a.cus > 0 && !fixed_grid_forced() &&
+                     (long long)num_seqs * num_q_heads * l.max_parts < INT32_MAX;
   }
   if (num_seqs == 0) return PA_OK;
   if (log_enabled())

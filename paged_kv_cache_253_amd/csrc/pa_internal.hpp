@@ -62,6 +62,8 @@ struct DecodeArgs {
   int slices;                   // balanced split: persistent wavefronts (set by the launcher)
   int cus;                      // balanced split: compute units of the device
   int waves_per_cu;             // balanced split: 0 = the kernel's own choice
+  int stream_fixed;             // fixed partitions on the persistent streaming grid (matrix-core
+                                // kernels; else one wavefront per partition)
   int* header;                  // balanced split: workspace header (W, merge records)
   int* counters;                // balanced split merged in the decode launch: [slices_max]
                                 // arrival counters, zero on entry and on exit; else null

@@ -14,6 +14,10 @@
 //    first run ("head", slot 0) and its last run ("tail", slot 1).  The
 //    wavefront that holds a cut run's first piece leaves a merge record
 //    for it, so the merge needs neither the plan nor a search.
+//  * Fixed partitions on the persistent grid: the same plan counted in
+//    whole partitions instead of steps (a run of L tokens has ceil(L / P)
+//    of them, none when L = 0), so no partition is cut and every one
+//    leaves its state in its own workspace row.
 #pragma once
 
 #include "pa_device.hpp"
@@ -31,6 +35,14 @@ __device__ __forceinline__ int steps_of_len(int len) {
   return len <= 0 ? 1 : (len + kStepTokens - 1) / kStepTokens;
 }
 
+// Work units of a run of len tokens: 32-token steps (pst == 0, balanced
+// split) or partitions of pst steps.
+__device__ __forceinline__ int units_of_len(int len, int pst) {
+  if (pst == 0) return steps_of_len(len);
+  const int part = pst * kStepTokens;
+  return len <= 0 ? 0 : (len + part - 1) / part;
+}
+
 // Inclusive prefix sum over the 64 lanes of the wavefront.
 __device__ __forceinline__ int wave_scan_incl(int x) {
   const int lane = threadIdx.x & 63;
@@ -43,22 +55,22 @@ __device__ __forceinline__ int wave_scan_incl(int x) {
 }
 
 struct Split {
-  int64_t per_head;  // steps of one KV head over the whole batch
-  int64_t total;     // steps of the batch (all KV heads)
-  int64_t per;       // steps per slice
+  int64_t per_head;  // units (steps, or partitions) of one KV head over the whole batch
+  int64_t total;     // units of the batch (all KV heads)
+  int64_t per;       // units per slice
   int slices;        // persistent wavefronts W
 };
 
 // Every wavefront computes the same plan from the lengths (no device-wide
-// communication).  A slice is at least kAutoMinSteps steps, so small
-// batches use fewer wavefronts instead of many tiny slices.
+// communication).  A balanced slice is at least kAutoMinSteps steps, so
+// small batches use fewer wavefronts instead of many tiny slices.
 __device__ __forceinline__ Split plan_split(const int32_t* lens, int num_seqs, int max_len,
-                                            int num_kv_heads, int slices) {
+                                            int num_kv_heads, int slices, int pst = 0) {
   const int lane = threadIdx.x & 63;
   int64_t tot = 0;
   for (int c = 0; c < num_seqs; c += 64) {
     const int b = c + lane;
-    const int n = b < num_seqs ? steps_of_len(clamp_len(lens[b], max_len)) : 0;
+    const int n = b < num_seqs ? units_of_len(clamp_len(lens[b], max_len), pst) : 0;
     tot += readlane(wave_scan_incl(n), 63);
   }
   Split s;
@@ -66,7 +78,8 @@ __device__ __forceinline__ Split plan_split(const int32_t* lens, int num_seqs, i
   s.total = tot * num_kv_heads;
   s.slices = slices;
   const int64_t even = (s.total + slices - 1) / slices;
-  s.per = even > kAutoMinSteps ? even : kAutoMinSteps;
+  const int64_t least = pst ? 1 : kAutoMinSteps;
+  s.per = even > least ? even : least;
   return s;
 }
 
@@ -81,14 +94,14 @@ __device__ __forceinline__ void slice_bounds(const Split& s, int c, int64_t& g0,
 // Slice holding step g (0 <= g < total).
 __device__ __forceinline__ int slice_of_step(const Split& s, int64_t g) { return (int)(g / s.per); }
 
-// Sequence b and step offset i of step `rem` (0 <= rem < per_head) of a head.
+// Sequence b and unit offset i of unit `rem` (0 <= rem < per_head) of a head.
 __device__ __forceinline__ void locate_step(const int32_t* lens, int num_seqs, int max_len,
-                                            int64_t rem, int& b_out, int& i_out) {
+                                            int64_t rem, int& b_out, int& i_out, int pst = 0) {
   const int lane = threadIdx.x & 63;
   int64_t base = 0;
   for (int c = 0; c < num_seqs; c += 64) {
     const int b = c + lane;
-    const int n = b < num_seqs ? steps_of_len(clamp_len(lens[b], max_len)) : 0;
+    const int n = b < num_seqs ? units_of_len(clamp_len(lens[b], max_len), pst) : 0;
     const int incl = wave_scan_incl(n);
     const int chunk = readlane(incl, 63);
     if (rem < base + chunk) {
