@@ -253,8 +253,13 @@ pa_status pa_decode(void* out, const void* q,
  *                  (PA_F32 or PA_BF16; cache_dtype equal to it, FP8 or INT4)
  *   other arguments as pa_decode
  *
- * The append is a launch of its own on `stream`, before the decode's, so
- * the caller needs no slot mapping for a decode step.  With
+ * The caller needs no slot mapping for a decode step.  With a bf16 cache
+ * and bf16 rows, PA_PARTITION_AUTO and G >= 2, the decode launch appends
+ * the rows itself: the wavefront that reads a newest token's step takes
+ * its rows from k_new / v_new and writes them to the pool after its last
+ * read, so that block must not be read by any other sequence of the call
+ * (copy-on-write first, as for any append into a shared block).  Otherwise
+ * the append is a launch of its own on `stream`, before the decode's; with
  * PA_PARTITION_AUTO_MERGED it also clears the workspace's merge counters,
  * so a step is two launches and needs no pa_decode_reduce.
  *

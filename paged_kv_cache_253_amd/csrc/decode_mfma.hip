@@ -275,9 +275,25 @@ static_assert(stream_waves_per_cu<kI4, 128>() <= kAutoMaxWavesPerCU, "workspace 
 typedef const __attribute__((address_space(4))) int32_t* const_i32;
 typedef const __attribute__((address_space(4))) float* const_f32;
 
-template <int CK, int D, int BS>
+// The newest token of a run (position L - 1) when a decode step appends it
+// itself (bf16 cache): this lane's share of its K and V rows -- the k-slot
+// dimensions of each QK chunk, as q, and dimension 16 * dt + col of V --
+// its place in the step, and where it is written.
+template <int D, bool ON>
+struct NewRows {};
+template <int D>
+struct NewRows<D, true> {
+  u32x4 k[D / 32];
+  uint32_t v[D / 16];
+  int pos;       // token of the step, -1 if the step holds no newest token
+  int off;       // offset in its block
+  int64_t tile;  // byte offset of its (block, KV head) tile in either pool
+};
+
+template <int CK, int D, int BS, bool APPEND>
 struct Slot : StepBuf<CK, D, BS> {
   using C = Cfg<CK, D, BS>;
+  NewRows<D, APPEND> nw;
   bf16x8 q[C::kChunks];
   // segment descriptor (wave-uniform)
   int base;   // first token of the step
@@ -288,13 +304,22 @@ struct Slot : StepBuf<CK, D, BS> {
   bool real;  // false: a filler step (loads repeated, nothing computed)
 };
 
-template <int CK, int D, int BS>
+// APPEND (bf16 cache, balanced split): the launch also appends every
+// sequence's newest token, at the slot its block table gives (pa_decode_append).
+// The wavefront that computes a run's last step loads that token's K and V
+// rows with the step, puts them into the step's operand registers in place
+// of the pool's bytes, and writes them to the pool after its ring has
+// drained: no other step reads that block, so the result is bit for bit that
+// of an append launch before the decode, without its launch and without
+// partial-line stores in the middle of the stream.
+template <int CK, int D, int BS, bool APPEND>
 __global__ __launch_bounds__(64)
 __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<CK>(), stream_waves_per_simd<CK>())))
 void decode_mfma_stream(const DecodeArgs a) {
   constexpr bool FP8 = one_byte<CK>();
   using C = Cfg<CK, D, BS>;
-  using S = Slot<CK, D, BS>;
+  using S = Slot<CK, D, BS, APPEND>;
+  static_assert(!APPEND || CK == kBF16, "the decode appends only into bf16 caches");
   const int lane = threadIdx.x;
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -365,6 +390,7 @@ void decode_mfma_stream(const DecodeArgs a) {
   auto issue = [&](S& sl) {
     const bool real = pst ? (ci < cseg_end || left > 0) : left > 0;
     sl.real = real;
+    if constexpr (APPEND) sl.nw.pos = -1;
     if (real) {
       if (pst && ci == cseg_end) {  // next partition of the slice
         --left;
@@ -404,10 +430,32 @@ void decode_mfma_stream(const DecodeArgs a) {
       const int64_t row = (int64_t)cb * a.max_blocks;
       int p0 = sl.t1 > sl.base ? tables[row + lb0] : 0;
       int p1 = (C::kBlocksPerStep == 2 && lb0 + 1 <= lb_last) ? tables[row + lb0 + 1] : p0;
+      // the run's newest token (position clen - 1) in this step, in a block
+      // the table names (else the append writes nothing, as a slot outside
+      // the pool)
+      const int np = clen - 1;
+      const int pn = (np / BS == lb0) ? p0 : p1;
+      const bool newest = APPEND && ci + 1 == cn && clen > 0 && np < a.cap_len && pn >= 0 &&
+                          (int64_t)pn < a.num_blocks;
       p0 = (p0 < 0 || (int64_t)p0 >= a.num_blocks) ? 0 : p0;
       p1 = (p1 < 0 || (int64_t)p1 >= a.num_blocks) ? 0 : p1;
       tile0 = ((int64_t)p0 * a.num_kv_heads + ch) * C::kTile;
       tile1 = ((int64_t)p1 * a.num_kv_heads + ch) * C::kTile;
+      if constexpr (APPEND) {
+        if (newest) {
+          sl.nw.pos = np - sl.base;
+          sl.nw.off = np % BS;
+          sl.nw.tile = ((int64_t)pn * a.num_kv_heads + ch) * C::kTile;
+          const size_t nrow = ((size_t)cb * a.num_kv_heads + ch) * D;
+          const __bf16* kn = reinterpret_cast<const __bf16*>(a.k_new) + nrow;
+          const uint16_t* vn = reinterpret_cast<const uint16_t*>(a.v_new) + nrow;
+#pragma unroll
+          for (int c = 0; c < C::kChunks; ++c)
+            sl.nw.k[c] = *reinterpret_cast<const u32x4*>(kn + q_dim<CK, D>(grp, c));
+#pragma unroll
+          for (int dt = 0; dt < C::kDTiles; ++dt) sl.nw.v[dt] = vn[dt * 16 + col];
+        }
+      }
       qp = qbase + ((size_t)cb * a.num_q_heads + (size_t)ch * G + qhead) * D;
       ++ci;
       if (!pst) --left;
@@ -480,12 +528,84 @@ void decode_mfma_stream(const DecodeArgs a) {
     nout = 0;
   };
 
+  // ---- appended rows --------------------------------------------------------
+  // A newest token's K and V rows wait in LDS, with their tile and offset,
+  // and are written after the ring has drained (or when the buffer fills).
+  constexpr int kAppMax = APPEND ? 8 : 1;
+  __shared__ __attribute__((aligned(16))) uint32_t appk[kAppMax][D / 2];  // K row, bf16 pairs
+  __shared__ uint16_t appv[kAppMax][D];                                    // V row
+  __shared__ int64_t apptile[kAppMax];
+  __shared__ int appoff[kAppMax];
+  int napp = 0;
+  char* const kw = const_cast<char*>(kc);
+  char* const vw = const_cast<char*>(vc);
+
+  auto flush_app = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_wave_barrier();  // the rows were staged by other lanes of this wavefront
+    for (int i = 0; i < napp; ++i) {
+      const int64_t tile = apptile[i];
+      const int off = appoff[i];
+      // K: D/8 pieces of 16 bytes, piece r (dimensions 8r .. 8r + 7) in chunk row r
+      if (lane < D / 8)
+        *reinterpret_cast<u32x4*>(kw + tile + ((int64_t)lane * BS + off) * 16) =
+            *reinterpret_cast<const u32x4*>(&appk[i][lane * 4]);
+      // V: dimension d in row d of the dimension-major tile
+      for (int d = lane; d < D; d += 64)
+        *reinterpret_cast<uint16_t*>(vw + tile + ((int64_t)d * BS + off) * 2) = appv[i][d];
+    }
+    __builtin_amdgcn_wave_barrier();  // reads done before the rows are reused
+    napp = 0;
+  };
+
   // ---- compute side ---------------------------------------------------------
   f32x4 acc[C::kDTiles];
   f32x4 accb = {0.f, 0.f, 0.f, 0.f};  // INT4: column sums of the PV weights
   float m_run = -INFINITY, l_run = 0.f, c2 = 0.f, qbias = 0.f;
 
   auto compute = [&](S& sl) {
+    if constexpr (APPEND) {
+      // The newest token's rows replace the pool's bytes in the step's
+      // registers (K: lanes of its QK row; V: element pos % 8 of the lanes
+      // of its k-slot group) and are staged for the write.
+      const int tn = sl.nw.pos;
+      if (tn >= 0) {
+        // value selects on both token groups: a store through a chosen
+        // group index would put the ring in scratch memory
+        const bool row0 = col == (tn & 15) && tn < 16;
+        const bool row1 = col == (tn & 15) && tn >= 16;
+#pragma unroll
+        for (int c = 0; c < C::kChunks; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sl.k[0][c][e] = row0 ? sl.nw.k[c][e] : sl.k[0][c][e];
+            sl.k[1][c][e] = row1 ? sl.nw.k[c][e] : sl.k[1][c][e];
+          }
+        if (grp == (tn >> 3)) {
+          const int wi = (tn & 7) >> 1;
+          const int sh = (tn & 1) * 16;
+#pragma unroll
+          for (int dt = 0; dt < C::kDTiles; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (i == wi) sl.v[dt].w[i] = (sl.v[dt].w[i] & ~(0xffffu << sh)) | (sl.nw.v[dt] << sh);
+        }
+        if (napp == kAppMax) flush_app();  // rare: many runs end in one slice
+        if (col == 0) {
+#pragma unroll
+          for (int c = 0; c < C::kChunks; ++c)
+            *reinterpret_cast<u32x4*>(&appk[napp][q_dim<CK, D>(grp, c) / 2]) = sl.nw.k[c];
+        }
+        if (grp == 0) {
+#pragma unroll
+          for (int dt = 0; dt < C::kDTiles; ++dt) appv[napp][dt * 16 + col] = (uint16_t)sl.nw.v[dt];
+        }
+        if (lane == 0) {
+          apptile[napp] = sl.nw.tile;
+          appoff[napp] = sl.nw.off;
+        }
+        ++napp;
+      }
+    }
     if (sl.flags & kFirst) {
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -565,6 +685,7 @@ void decode_mfma_stream(const DecodeArgs a) {
     }
   }
   flush();
+  if constexpr (APPEND) flush_app();
   if (pst) return;
   if (lane == 0) store_merge_rec(a.header, r, rec);
   if (a.counters) {  // cut runs merged in this launch by the wavefront finishing last
@@ -575,10 +696,20 @@ void decode_mfma_stream(const DecodeArgs a) {
 
 template <int CK, int D, int BS>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+  if (a.k_new) {  // the decode appends the newest tokens itself (bf16, balanced split)
+    if constexpr (CK == kBF16) {
+      if (a.partition != kAuto || a.counters) return hipErrorInvalidValue;
+      DecodeArgs b = a;
+      b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : stream_waves_per_cu<CK, D>());
+      hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, true>), dim3(b.slices), dim3(64), 0, stream, b);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.partition == kAuto || (a.partition > 0 && a.stream_fixed)) {
     DecodeArgs b = a;
     b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : stream_waves_per_cu<CK, D>());
-    hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS>), dim3(b.slices), dim3(64), 0, stream, b);
+    hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, false>), dim3(b.slices), dim3(64), 0, stream, b);
   } else {
     const int parts = a.partition ? a.max_parts : 1;
     dim3 grid(parts, a.num_kv_heads, a.num_seqs);

@@ -99,6 +99,13 @@ bool workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_
   return true;
 }
 
+// PA_SEPARATE_APPEND=1 makes pa_decode_append launch its append separately
+// even where the decode kernel can append (cross-checks and timing).
+bool separate_append_forced() {
+  const char* e = std::getenv("PA_SEPARATE_APPEND");
+  return e && e[0] == '1';
+}
+
 // PA_FIXED_GRID=1 runs fixed partitions one wavefront per partition
 // instead of on the persistent streaming grid (cross-checks and timing).
 bool fixed_grid_forced() {
@@ -290,12 +297,14 @@ pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v
     if (se != Elem::F32 && se != Elem::BF16) return PA_ERR_UNSUPPORTED;
     if (ce != se && !is_fp8(ce) && ce != Elem::I4) return PA_ERR_UNSUPPORTED;
   }
-  // The append is a launch of its own, before the decode's.  Writing the
-  // rows inside the decode kernel (the wavefront that reads a newest
-  // token's tile appends it first) was measured on MI355X and gained
-  // nothing: the partial-line stores, issued ahead of the streaming loads,
-  // held up each wavefront's in-order memory queue by as long as the
-  // separate launch takes.
+  // bf16 cache, balanced split, matrix-core kernels: the decode launch
+  // appends the newest tokens itself (their rows go into the operand
+  // registers of the step that reads them and into the pool after the
+  // wavefront's ring has drained).  Otherwise the append is a launch of its
+  // own, before the decode's.  PA_SEPARATE_APPEND=1 forces the two launches
+  // (cross-checks and timing).
+  const bool fuse_append = append && use_mfma && ce == Elem::BF16 && se == Elem::BF16 &&
+                           partition_size == PA_PARTITION_AUTO && !separate_append_forced();
   pa::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
   a.out = out; a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
@@ -341,8 +350,11 @@ pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v
     std::fprintf(stderr, "[pagedattn] decode path=%s S=%d Hq=%d Hkv=%d G=%d D=%d B=%d P=%d parts=%d cus=%d append=%s\n",
                  use_mfma ? "mfma" : "valu", num_seqs, num_q_heads, num_kv_heads, group, head_dim,
                  block_size, partition_size, a.max_parts, a.cus,
-                 append ? "yes" : "no");
-  if (append) {
+                 fuse_append ? "in the decode launch" : (append ? "separate launch" : "no"));
+  if (fuse_append) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+  } else if (append) {
     pa::WriteArgs w;
     std::memset(&w, 0, sizeof w);
     w.k_new = k_new; w.v_new = v_new;

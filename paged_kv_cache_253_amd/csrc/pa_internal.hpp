@@ -65,6 +65,8 @@ struct DecodeArgs {
   int stream_fixed;             // fixed partitions on the persistent streaming grid (matrix-core
                                 // kernels; else one wavefront per partition)
   int* header;                  // balanced split: workspace header (W, merge records)
+  const void* k_new;            // [S][Hkv][D] bf16: the decode launch appends each sequence's
+  const void* v_new;            // newest token itself (bf16 cache, balanced split); else null
   int* counters;                // balanced split merged in the decode launch: [slices_max]
                                 // arrival counters, zero on entry and on exit; else null
   float scale;
