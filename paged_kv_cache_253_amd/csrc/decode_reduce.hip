@@ -15,7 +15,7 @@
 //    the cut run whose first piece it holds, if any, and the workgroup
 //    merges all of that run's slice states (merge_cut_run in pa_merge.hpp,
 //    the routine the decode kernels use when they merge in their own
-//    launch), query heads dealt to the wavefronts in turn.
+//    launch), all of its query heads by one wavefront.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 #include "pa_merge.hpp"
@@ -104,13 +104,15 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const ReduceArgs
   }
 }
 
-constexpr int kFixupThreads = 256;
+// One wavefront per slice: merge_cut_run loads up to eight heads' states
+// per round, and most slices have no cut run to merge (the grid covers the
+// most slices a decode can use).
+constexpr int kFixupThreads = 64;
 
 template <typename OT, int D>
 __global__ __launch_bounds__(kFixupThreads) void auto_fixup_kernel(const ReduceArgs a) {
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   const int r_first = blockIdx.x;  // slice holding the run's first piece
-  const int wave = threadIdx.x >> 6;
   const int slices = a.header[kHdrSlices];  // as launched by the decode
   const i32x4 rec = *reinterpret_cast<const i32x4*>(reinterpret_cast<const char*>(a.header) +
                                                      kHdrRecordsBytes + (size_t)r_first * kMergeRecordBytes);
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kFixupThreads) void auto_fixup_kernel(const ReduceA
     return;
   const MergeView v{a.out, a.part_out, a.part_max, a.part_sum, a.num_q_heads,
                     a.num_q_heads / a.num_kv_heads};
-  merge_cut_run<OT, D, false>(v, b, h, r_first, k_first, nparts, wave, kFixupThreads / 64);
+  merge_cut_run<OT, D, false>(v, b, h, r_first, k_first, nparts, 0, 1);
 }
 
 template <typename OT, int D>

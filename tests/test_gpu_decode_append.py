@@ -148,3 +148,20 @@ def test_repeated_step_is_idempotent():
     b = _one_call(batch, batch.k_pool, batch.v_pool, pk.PARTITION_AUTO)
     _sync()
     _assert_same((k1, v1, a), (batch.k_pool, batch.v_pool, b), "replay")
+
+
+def test_many_runs_end_in_one_slice():
+    """4096 one-step sequences over two KV heads: each slice of the balanced
+    split holds 16 whole runs, more than the decode kernel stages at once
+    (appended rows and held outputs are then written in the middle of the
+    stream) -- pools and outputs still equal the separate launches', and the
+    output matches the oracle."""
+    lens = np.random.default_rng(9).integers(1, 33, size=4096)
+    batch = _batch("bf16", 128, 16, 8, 2, lens)
+    k_ref, v_ref = oracle_write(batch, host_view(batch.k_pool), host_view(batch.v_pool))
+    sep, one = _both(batch, pk.PARTITION_AUTO)
+    _assert_same(sep, one, "many short runs")
+    assert same_bits(host_view(one[0]), k_ref) and same_bits(host_view(one[1]), v_ref)
+    seqs = list(range(0, 4096, 97))
+    ref = oracle_decode_host(batch, k_ref, v_ref, seqs)
+    compare(widen(one[2])[seqs], ref, "bf16", "many short runs")
