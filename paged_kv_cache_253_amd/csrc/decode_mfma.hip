@@ -537,8 +537,8 @@ void decode_mfma_stream(const DecodeArgs a) {
   __shared__ int64_t apptile[kAppMax];
   __shared__ int appoff[kAppMax];
   int napp = 0;
-  char* const kw = const_cast<char*>(kc);
-  char* const vw = const_cast<char*>(vc);
+  char* const kw = reinterpret_cast<char*>(a.k_pool_w);  // set when APPEND
+  char* const vw = reinterpret_cast<char*>(a.v_pool_w);
 
   auto flush_app = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_wave_barrier();  // the rows were staged by other lanes of this wavefront

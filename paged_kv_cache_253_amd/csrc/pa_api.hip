@@ -241,8 +241,10 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void
 
 namespace {
 
-// pa_decode, and pa_decode_append when k_new is not null.
+// pa_decode, and pa_decode_append when k_new is not null (k_pool_w /
+// v_pool_w: the same pools as k_cache / v_cache, writable; null for pa_decode).
 pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
+                      void* k_pool_w, void* v_pool_w,
                       const void* k_cache, const void* v_cache, const int32_t* block_tables,
                       int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
@@ -354,11 +356,13 @@ pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v
   if (fuse_append) {
     a.k_new = k_new;
     a.v_new = v_new;
+    a.k_pool_w = k_pool_w;
+    a.v_pool_w = v_pool_w;
   } else if (append) {
     pa::WriteArgs w;
     std::memset(&w, 0, sizeof w);
     w.k_new = k_new; w.v_new = v_new;
-    w.k_cache = const_cast<void*>(k_cache); w.v_cache = const_cast<void*>(v_cache);
+    w.k_cache = k_pool_w; w.v_cache = v_pool_w;
     w.tables = block_tables; w.lens = context_lens;
     w.k_scale = k_scale; w.v_scale = v_scale;
     w.num_slots = num_blocks * block_size;
@@ -383,7 +387,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int64_t num_blocks, float scale, pa_dtype q_dtype, pa_dtype cache_dtype,
                     const float* k_scale, const float* v_scale, int partition_size,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, max_blocks_per_seq,
+  return decode_impl(out, q, nullptr, nullptr, nullptr, nullptr, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq,
                      context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
                      block_size, num_blocks, scale, q_dtype, PA_BF16, cache_dtype, k_scale, v_scale,
                      partition_size, workspace, workspace_bytes, stream);
@@ -398,7 +403,8 @@ pa_status pa_decode_append(void* out, const void* q, const void* k_new, const vo
                            const float* v_scale, int partition_size, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
   if (!k_new || !v_new) return PA_ERR_INVALID_ARG;
-  return decode_impl(out, q, k_new, v_new, k_cache, v_cache, block_tables, max_blocks_per_seq,
+  return decode_impl(out, q, k_new, v_new, k_cache, v_cache, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq,
                      context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
                      block_size, num_blocks, scale, q_dtype, src_dtype, cache_dtype, k_scale, v_scale,
                      partition_size, workspace, workspace_bytes, stream);

@@ -67,6 +67,8 @@ struct DecodeArgs {
   int* header;                  // balanced split: workspace header (W, merge records)
   const void* k_new;            // [S][Hkv][D] bf16: the decode launch appends each sequence's
   const void* v_new;            // newest token itself (bf16 cache, balanced split); else null
+  void* k_pool_w;               // with k_new: the pools the rows go to (k_cache, v_cache)
+  void* v_pool_w;
   int* counters;                // balanced split merged in the decode launch: [slices_max]
                                 // arrival counters, zero on entry and on exit; else null
   float scale;
