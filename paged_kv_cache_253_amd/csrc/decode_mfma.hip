@@ -312,7 +312,12 @@ struct Slot : StepBuf<CK, D, BS> {
 // drained: no other step reads that block, so the result is bit for bit that
 // of an append launch before the decode, without its launch and without
 // partial-line stores in the middle of the stream.
-template <int CK, int D, int BS, bool APPEND>
+//
+// MERGE (PA_PARTITION_AUTO_MERGED): cut runs are merged in this launch by
+// the wavefront that finishes a run's last piece (pa_merge.hpp).  FIXED:
+// fixed partitions (slices of whole partitions).  Template parameters so
+// that each launch carries only its own mode's code.
+template <int CK, int D, int BS, bool APPEND, bool MERGE, bool FIXED>
 __global__ __launch_bounds__(64)
 __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<CK>(), stream_waves_per_simd<CK>())))
 void decode_mfma_stream(const DecodeArgs a) {
@@ -320,6 +325,8 @@ void decode_mfma_stream(const DecodeArgs a) {
   using C = Cfg<CK, D, BS>;
   using S = Slot<CK, D, BS, APPEND>;
   static_assert(!APPEND || CK == kBF16, "the decode appends only into bf16 caches");
+  static_assert(!(APPEND && MERGE), "the appending decode uses the separate merge");
+  static_assert(!(FIXED && (APPEND || MERGE)), "fixed partitions neither append nor merge");
   const int lane = threadIdx.x;
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -327,8 +334,8 @@ void decode_mfma_stream(const DecodeArgs a) {
   const int W = a.slices;
   // fixed partitions: steps per partition, and the workspace row stride of
   // a group's query heads (their rows are max_parts apart); 0 / 1 balanced
-  const int pst = a.partition > 0 ? a.partition / kStepTokens : 0;
-  const int rstride = pst ? a.max_parts : 1;
+  const int pst = FIXED ? a.partition / kStepTokens : 0;
+  const int rstride = FIXED ? a.max_parts : 1;
   if (blockIdx.x == 0 && lane == 0 && !pst) a.header[kHdrSlices] = W;  // for the merge
   const Split sp = plan_split(a.context_lens, a.num_seqs, a.max_len, a.num_kv_heads, W, pst);
   const int r = slice_of_wave(blockIdx.x, W);
@@ -416,7 +423,7 @@ void decode_mfma_stream(const DecodeArgs a) {
         cflags_run = (cseg_end == cn) ? kFinal : 0;
         crow0 = (r * 2 + 1) * G;
         if (cseg_end < cn) rec = merge_rec_of(sp, r, g_end - left, cn, cb, ch, 1);
-        pieces[1] = CutPiece{g_end - left, cn, cb, ch, true};
+        if constexpr (MERGE) pieces[1] = CutPiece{g_end - left, cn, cb, ch, true};
       }
       sl.base = ci * kStepTokens;
       sl.t1 = min(min(cseg_end * kStepTokens, clen), a.cap_len);
@@ -505,7 +512,7 @@ void decode_mfma_stream(const DecodeArgs a) {
         }
       } else {
         const int row0 = -1 - tag;  // head g of the group at row row0 + g * rstride
-        if (a.counters) {  // merged in this launch, maybe on another XCD: device-scope stores
+        if constexpr (MERGE) {  // merged in this launch, maybe on another XCD: device-scope stores
           float* o = a.part_out + (size_t)row0 * D;
           for (int q = lane; q < G * D; q += 64)
             state_store(o + q, src[(q / D) * kStageRow + q % D], true);
@@ -519,8 +526,8 @@ void decode_mfma_stream(const DecodeArgs a) {
         }
         if (lane < G) {
           const size_t rl = (size_t)row0 + (size_t)lane * rstride;
-          state_store(a.part_max + rl, src[G * kStageRow + lane], a.counters != nullptr);
-          state_store(a.part_sum + rl, src[G * kStageRow + G + lane], a.counters != nullptr);
+          state_store(a.part_max + rl, src[G * kStageRow + lane], MERGE);
+          state_store(a.part_sum + rl, src[G * kStageRow + G + lane], MERGE);
         }
       }
     }
@@ -688,7 +695,7 @@ void decode_mfma_stream(const DecodeArgs a) {
   if constexpr (APPEND) flush_app();
   if (pst) return;
   if (lane == 0) store_merge_rec(a.header, r, rec);
-  if (a.counters) {  // cut runs merged in this launch by the wavefront finishing last
+  if constexpr (MERGE) {  // cut runs merged in this launch by the wavefront finishing last
     const MergeView v{a.out, a.part_out, a.part_max, a.part_sum, a.num_q_heads, G};
     arrive_and_merge<__bf16, D>(v, a.counters, sp, pieces);
   }
@@ -701,7 +708,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
       if (a.partition != kAuto || a.counters) return hipErrorInvalidValue;
       DecodeArgs b = a;
       b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : stream_waves_per_cu<CK, D>());
-      hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, true>), dim3(b.slices), dim3(64), 0, stream, b);
+      hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, true, false, false>), dim3(b.slices), dim3(64), 0, stream, b);
       return hipGetLastError();
     }
     return hipErrorInvalidValue;
@@ -709,7 +716,15 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   if (a.partition == kAuto || (a.partition > 0 && a.stream_fixed)) {
     DecodeArgs b = a;
     b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : stream_waves_per_cu<CK, D>());
-    hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, false>), dim3(b.slices), dim3(64), 0, stream, b);
+    if (a.partition > 0) {
+      if constexpr (CK != kI4)  // INT4 fixed partitions take the grid (host side)
+        hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, false, false, true>), dim3(b.slices), dim3(64), 0, stream, b);
+      else
+        return hipErrorInvalidValue;
+    } else if (a.counters)
+      hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, false, true, false>), dim3(b.slices), dim3(64), 0, stream, b);
+    else
+      hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, false, false, false>), dim3(b.slices), dim3(64), 0, stream, b);
   } else {
     const int parts = a.partition ? a.max_parts : 1;
     dim3 grid(parts, a.num_kv_heads, a.num_seqs);

@@ -295,7 +295,9 @@ __global__ __launch_bounds__(64) void decode_valu_grid(const DecodeArgs a) {
   attend<QT, E, D, BS, G>(a, b, h, t0, t1, Target{false, row0, (size_t)a.max_parts});
 }
 
-template <typename QT, Elem E, int D, int BS, int G>
+// MERGE: cut runs merged in this launch (a template parameter so that the
+// other launches carry none of its code).
+template <typename QT, Elem E, int D, int BS, int G, bool MERGE>
 __global__ __launch_bounds__(64) void decode_valu_auto(const DecodeArgs a) {
   if (blockIdx.x == 0 && threadIdx.x == 0) a.header[kHdrSlices] = a.slices;  // for the merge
   const int r = slice_of_wave(blockIdx.x, a.slices);
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(64) void decode_valu_auto(const DecodeArgs a) {
     if (++b == a.num_seqs) { b = 0; ++h; }
   }
   if (threadIdx.x == 0) store_merge_rec(a.header, r, rec);
-  if (a.counters) {  // cut runs merged in this launch by the wavefront finishing last
+  if constexpr (MERGE) {  // cut runs merged in this launch by the wavefront finishing last
     const MergeView v{a.out, a.part_out, a.part_max, a.part_sum, a.num_q_heads, G};
     arrive_and_merge<QT, D>(v, a.counters, sp, pieces);
   }
@@ -343,7 +345,10 @@ hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
   if (a.partition == kAuto) {
     DecodeArgs b = a;
     b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : kValuWavesPerCU);
-    hipLaunchKernelGGL((decode_valu_auto<QT, E, D, BS, G>), dim3(b.slices), dim3(64), 0, stream, b);
+    if (a.counters)
+      hipLaunchKernelGGL((decode_valu_auto<QT, E, D, BS, G, true>), dim3(b.slices), dim3(64), 0, stream, b);
+    else
+      hipLaunchKernelGGL((decode_valu_auto<QT, E, D, BS, G, false>), dim3(b.slices), dim3(64), 0, stream, b);
   } else {
     const int parts = a.partition ? a.max_parts : 1;
     dim3 grid(parts, a.num_kv_heads, a.num_seqs);

@@ -343,8 +343,11 @@ pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v
     a.max_parts = l.max_parts;
     a.cus = balanced ? l.cus : device_cus();
     a.waves_per_cu = auto_waves_override();
-    // fixed partitions stream when their state rows fit the kernel's int row index
-    a.stream_fixed = !balanced && a.cus > 0 && !fixed_grid_forced() &&
+    // fixed partitions stream when their state rows fit the kernel's int row
+    // index -- except INT4, whose streaming variant spills registers and
+    // measured slower than one wavefront per partition (269 vs 261 us on
+    // the 131K-token batch)
+    a.stream_fixed = !balanced && a.cus > 0 && !fixed_grid_forced() && ce != Elem::I4 &&
                      (long long)num_seqs * num_q_heads * l.max_parts < INT32_MAX;
   }
   if (num_seqs == 0) return PA_OK;

@@ -2,7 +2,8 @@
 
 Fixed-partition decodes run on the matrix-core kernels' persistent grid
 (slices of whole partitions) unless PA_FIXED_GRID=1 asks for one wavefront
-per partition.  Both compute each partition's softmax state with the same
+per partition (INT4 caches always take the latter; their case here checks
+that both settings agree).  Both compute each partition's softmax state with the same
 per-step arithmetic over the same tokens, so the workspace (every
 partition's row) and the merged output must be identical bit for bit, for
 every cache kind, shape and group size, partition sizes from one step up,
