@@ -68,6 +68,22 @@
  *
  * Supported shapes: head_dim 64 or 128; block_size 16 or 32; element types
  * as listed per call.
+ *
+ * Environment switches (read by the host side; none changes a result's
+ * definition, only which kernel computes it):
+ *
+ *   PA_FORCE_PATH=valu|mfma   decode kernel family (vector units or matrix
+ *                             cores) where both support the arguments
+ *   PA_AUTO_WAVES_PER_CU=n    persistent wavefronts per compute unit for the
+ *                             balanced split (1..8; default per kernel)
+ *   PA_FIXED_GRID=1           fixed partitions one wavefront per partition
+ *                             instead of on the persistent streaming grid
+ *                             (same bits)
+ *   PA_SEPARATE_APPEND=1      pa_decode_append launches its append on its
+ *                             own even where the decode kernel can append
+ *                             (same bits)
+ *   PA_LOG=1                  one line per decode call on stderr (kernel
+ *                             path, shape, split) and HIP error strings
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
