@@ -486,7 +486,12 @@ void decode_mfma_stream(const DecodeArgs a) {
   // lanes.  Rows are padded by 4 floats so the G writing lanes hit
   // different banks.
   constexpr int kStageRow = D + 4;
-  constexpr int kOutFloats = (stream_waves_per_cu<CK, D>() >= 8 ? 16384 : 32768) / 4;
+  // LDS per wavefront: 16 KiB at eight per CU, 37 KiB at four (four such
+  // workgroups, tags and appended-row staging included, stay within the
+  // CU's 160 KiB; a slice of 16 fixed partitions at G = 4, head_dim 128,
+  // then never flushes mid-stream), 32 KiB at two.
+  constexpr int kWaves = stream_waves_per_cu<CK, D>();
+  constexpr int kOutFloats = (kWaves >= 8 ? 16384 : (kWaves >= 4 ? 37888 : 32768)) / 4;
   constexpr int kOutSlotsMax = 32;
   __shared__ __attribute__((aligned(16))) float outbuf[kOutFloats];
   __shared__ int outtag[kOutSlotsMax];  // out row of the group's head 0 (final), or -1 - row0 (state)
