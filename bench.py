@@ -547,6 +547,8 @@ def main() -> int:
     step_bytes = dec["total"] + wr
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = dec["total"] / (decode_ms * 1e-3) / 1e9
+    in_step_bytes = dec["total"] + (wr if one_call else 0)
+    in_step_gbs = in_step_bytes / (decode_ms_in_step * 1e-3) / 1e9
     first = (f"append+decode {decode_ms_in_step * 1e3:.1f}" if one_call else
              f"write {write_ms * 1e3:.1f}, decode {decode_ms_in_step * 1e3:.1f}")
     log(f"[bench] step {ms_per_step * 1e3:.1f} us ({first}, reduce {reduce_ms * 1e3:.1f}); "
@@ -598,7 +600,16 @@ def main() -> int:
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "algorithmic_bytes": dec["total"],
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     # the same figure for the launch the timed steps make (eager
+                     # steps' HIP events): pa_decode_append's decode with the
+                     # append inside where the kernels allow, else the append
+                     # launch plus the decode
+                     "in_step": {"kernel": "pa_decode_append" if one_call else "pa_decode",
+                                 "launch_us": round(decode_ms_in_step * 1e3, 2),
+                                 "achieved": round(in_step_gbs, 1),
+                                 "frac": round(in_step_gbs / PEAK_HBM_GBS, 4),
+                                 "algorithmic_bytes": in_step_bytes}},
     }
     if not args.no_cpu:
         log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f}s")
