@@ -162,3 +162,23 @@ def test_full_size_step_merged_equals_separate(idx):
     assert _bits_equal(got, ref)
     assert torch.equal(k2.view(torch.int16), batch.k_pool.view(torch.int16))
     assert torch.equal(v2.view(torch.int16), batch.v_pool.view(torch.int16))
+
+
+def test_many_launches_on_one_workspace_identical():
+    """Twenty merged launches back to back on the full 8B-shaped batch (about
+    500 cut runs, pieces on every XCD), one workspace: every output equals
+    the separate merge's bit for bit, so no merge read a piece's state before
+    it was visible."""
+    w = WORKLOADS[2]
+    batch = make_batch(w, device=DEV)
+    ref = _decode(batch, AUTO).clone()
+    s, hq, d = batch.q.shape
+    ws = pk.new_workspace(s, hq, w.num_kv_heads, d, batch.max_context_len, MERGED, DEV)
+    bt, cl = device_tables(batch)
+    outs = [torch.empty_like(batch.q) for _ in range(20)]
+    for o in outs:
+        pk.decode(batch.q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len, batch.scale,
+                  partition_size=MERGED, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    bad = [i for i, o in enumerate(outs) if not _bits_equal(o, ref)]
+    assert not bad, f"launches {bad} differ from the separate merge"
