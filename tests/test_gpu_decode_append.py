@@ -188,3 +188,17 @@ def test_full_size_step_as_the_bench_runs_it(idx):
     seqs = sorted(seqs)
     ref = oracle_decode_host(batch, k_ref, v_ref, seqs)
     compare(widen(one[2])[seqs], ref, w.cache_dtype, f"full-size step {w.name}")
+
+
+def test_context_past_the_table_row():
+    """A sequence whose length exceeds what its (truncated) table row can
+    address: its newest position is past the row, so nothing is appended
+    for it (as pa_kv_cache_write with a padding slot) and the decode clamps
+    its context to the row; the others append and decode as usual."""
+    batch = _batch("bf16", 128, 16, 8, 2, [40, 300, 17, 208])
+    tables = np.ascontiguousarray(batch.block_tables[:, :13])  # rows address 208 tokens
+    slots = batch.slot_mapping.copy()
+    slots[1] = -1  # token 299 is past the row
+    batch = batch.replace(block_tables=tables, slot_mapping=slots)
+    sep, one = _both(batch, pk.PARTITION_AUTO)
+    _assert_same(sep, one, "context past the table row")
