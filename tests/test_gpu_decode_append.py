@@ -202,3 +202,21 @@ def test_context_past_the_table_row():
     batch = batch.replace(block_tables=tables, slot_mapping=slots)
     sep, one = _both(batch, pk.PARTITION_AUTO)
     _assert_same(sep, one, "context past the table row")
+
+
+def test_maximum_sequence_count():
+    """65,535 sequences (the largest count the library accepts) of 1 to 3
+    tokens: every wavefront's plan walks all lengths, and each slice ends
+    about 256 runs, so appended rows and held outputs are written many
+    times in the middle of the stream.  Pools and outputs equal the separate
+    launches' bit for bit and the oracle's append; sampled outputs match
+    the oracle's decode."""
+    lens = np.random.default_rng(21).integers(1, 4, size=65535)
+    batch = _batch("bf16", 64, 16, 4, 2, lens)
+    k_ref, v_ref = oracle_write(batch, host_view(batch.k_pool), host_view(batch.v_pool))
+    sep, one = _both(batch, pk.PARTITION_AUTO)
+    _assert_same(sep, one, "65535 sequences")
+    assert same_bits(host_view(one[0]), k_ref) and same_bits(host_view(one[1]), v_ref)
+    seqs = list(range(0, 65535, 1311))
+    ref = oracle_decode_host(batch, k_ref, v_ref, seqs)
+    compare(widen(one[2])[seqs], ref, "bf16", "65535 sequences")
