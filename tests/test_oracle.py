@@ -459,11 +459,59 @@ def pin_fp8_write_then_decode(impl):
                                    "f32", fmt, ks, vs)
         ref = torch.from_numpy(vn[0] / vs[:, None]).to(tdt).view(torch.uint8).numpy()
         assert np.array_equal(v2[2, :, :, 0], ref)
+        # K codes: chunk c of the token's row sits at [blk, h, c, off, :]
+        kref = torch.from_numpy(kn[0] / ks[:, None]).to(tdt).view(torch.uint8).numpy()
+        assert np.array_equal(k2[2, :, :, 0, :].reshape(hkv, d), kref)
         q = rng.standard_normal((1, 4, d)).astype(np.float32)
         out = impl.decode(q, k2, v2, np.array([[2]]), np.array([1]), bsz, 0.25,
                           "f32", fmt, ks, vs)
         deq = widen(ref) * vs[:, None].astype(np.float64)
         assert np.array_equal(out[0], deq[np.arange(4) // 2])
+
+
+def pin_fp8_multi_token_decode(impl):
+    """FP8 caches over several tokens, where the K scale no longer cancels
+    out of the softmax: sequences of 1, 21 and 40 tokens appended into
+    E4M3 / E5M2 pools (K and V codes each checked against torch's cast of
+    x / scale) decode to the pinned f32 decode of the dequantised values,
+    code * scale per KV head ("AI Inference Serving at Scale", section 6,
+    FP8 KV cache), placed in an f32 cache."""
+    for fmt, tdt in (("fp8_e4m3", torch.float8_e4m3fn), ("fp8_e5m2", torch.float8_e5m2)):
+        rng = np.random.default_rng(41)
+        hkv, g, d, bsz, nb = 2, 3, 32, 16, 6
+        lens = np.array([1, 21, 40])
+        tables = np.array([[4, -1, -1], [0, 5, -1], [1, 2, 3]])
+        slots = [int(tables[b, t // bsz]) * bsz + t % bsz
+                 for b in range(3) for t in range(lens[b])]
+        n = len(slots)
+        kn = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        vn = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        # scales far from 1, unequal between K and V and between heads, and
+        # large enough that no |x| / scale passes 448 (torch does not saturate)
+        ks = np.array([0.011, 0.031], np.float32)
+        vs = np.array([0.023, 0.013], np.float32)
+        k_pool = _k_pool(nb, hkv, bsz, d, 16, 0, np.uint8)
+        v_pool = np.zeros((nb, hkv, d, bsz), np.uint8)
+        k2, v2 = impl.write_tokens(k_pool, v_pool, kn, vn, np.array(slots), bsz,
+                                   "f32", fmt, ks, vs)
+        kcodes = torch.from_numpy(kn / ks[None, :, None]).to(tdt)
+        vcodes = torch.from_numpy(vn / vs[None, :, None]).to(tdt)
+        kf = _k_pool(nb, hkv, bsz, d, 4, 0, np.float32)
+        vf = np.zeros((nb, hkv, d, bsz), np.float32)
+        for idx, sl in enumerate(slots):
+            blk, off = divmod(sl, bsz)
+            assert np.array_equal(k2[blk, :, :, off, :].reshape(hkv, d),
+                                  kcodes[idx].view(torch.uint8).numpy())
+            assert np.array_equal(v2[blk, :, :, off], vcodes[idx].view(torch.uint8).numpy())
+            kval = kcodes[idx].to(torch.float64).numpy() * ks[:, None].astype(np.float64)
+            vval = vcodes[idx].to(torch.float64).numpy() * vs[:, None].astype(np.float64)
+            kf[blk, :, :, off, :] = kval.astype(np.float32).reshape(hkv, d // 4, 4)
+            vf[blk, :, :, off] = vval.astype(np.float32)
+        q = rng.standard_normal((3, hkv * g, d)).astype(np.float32)
+        out = impl.decode(q, k2, v2, tables, lens, bsz, 0.5, "f32", fmt, ks, vs)
+        ref = impl.decode(q, kf, vf, tables, lens, bsz, 0.5, "f32", "f32")
+        # code * scale has up to 28 significant bits: the f32 cache rounds it
+        np.testing.assert_allclose(out, ref, rtol=2e-6, atol=2e-7)
 
 
 def pin_copy_on_write(impl):
@@ -765,7 +813,7 @@ PINS = [pin_golden_index, pin_gather_roundtrip, pin_write_whole_pool,
         pin_library_sdpa, pin_brute_force, pin_brute_force_tiny_workload,
         pin_paged_equals_unpaged, pin_block_permutation, pin_shared_prefix,
         pin_split_merge, pin_e4m3_decode_table, pin_e4m3_encode,
-        pin_fp8_write_then_decode, pin_copy_on_write, pin_prefill_brute_force,
+        pin_fp8_write_then_decode, pin_fp8_multi_token_decode, pin_copy_on_write, pin_prefill_brute_force,
         pin_prefill_causal, pin_prefill_library_sdpa, pin_swap_round_trip,
         pin_e5m2_decode_table, pin_e5m2_encode, pin_int4_encode, pin_int4_octets,
         pin_int4_tile_index, pin_int4_write_then_decode]
@@ -1018,6 +1066,21 @@ def _bad_int4_k_dims_interleaved(k_pool, blk, h, off, block_size):
     return codes.reshape(-1, 2)[:, ::-1].reshape(-1), scale
 
 
+def _bad_fp8_decode_drops_k_scale(q, k_pool, v_pool, block_tables, context_lens, block_size,
+                                  scale, q_dtype, cache_dtype, k_scale=None, v_scale=None,
+                                  seqs=None):
+    if cache_dtype in ("fp8_e4m3", "fp8_e5m2"):
+        k_scale = np.ones_like(np.asarray(k_scale, np.float32))
+    return paged.decode(q, k_pool, v_pool, block_tables, context_lens, block_size, scale,
+                        q_dtype, cache_dtype, k_scale, v_scale, seqs)
+
+
+def _bad_fp8_write_k_uses_v_scale(k_pool, v_pool, k_new, v_new, slot_mapping, block_size,
+                                  src_dtype, cache_dtype, k_scale=None, v_scale=None):
+    return paged.write_tokens(k_pool, v_pool, k_new, v_new, slot_mapping, block_size,
+                              src_dtype, cache_dtype, v_scale, v_scale)
+
+
 def _mk_decode(**over):
     """decode() rebuilt on top of possibly broken parts."""
     impl = _impl(**over)
@@ -1036,7 +1099,7 @@ def _mk_decode(**over):
             kr, vr = impl.gather(k_pool, v_pool, block_tables[b], int(context_lens[b]), block_size)
             k = paged.to_f64(kr, cache_dtype)
             v = paged.to_f64(vr, cache_dtype)
-            if cache_dtype == "fp8_e4m3":
+            if cache_dtype in ("fp8_e4m3", "fp8_e5m2"):
                 k = k * np.asarray(k_scale, np.float64)[None, :, None]
                 v = v * np.asarray(v_scale, np.float64)[None, :, None]
             out[b] = impl.attention(q64[b], k, v, scale)
@@ -1072,6 +1135,8 @@ MUTANTS = {
     "int4-v-token-major": dict(int4_v_row=_bad_int4_v_token_major),
     "int4-k-dims-interleaved": dict(int4_k_row=_bad_int4_k_dims_interleaved),
     "int4-block-v-token-major": dict(int4_block_values=_bad_int4_block_v_token_major),
+    "fp8-decode-drops-k-scale": dict(decode=_bad_fp8_decode_drops_k_scale),
+    "fp8-append-k-uses-v-scale": dict(write_tokens=_bad_fp8_write_k_uses_v_scale),
 }
 
 
