@@ -234,8 +234,11 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
  *
  * Caller contract: context_lens[b] <= max_context_len and <=
  * max_blocks_per_seq * block_size, and the table entries read are in
- * [0, num_blocks).  If not, the kernels clamp L to those bounds and read
- * block 0 in place of an out-of-range id, so no access leaves the buffers.
+ * [0, num_blocks).  If not, L is clamped to max_context_len, no token at or
+ * past max_blocks_per_seq * block_size is read (the context ends there; a
+ * range lying wholly past it leaves the empty state: maximum -inf, exp-sum
+ * 0, zero row), and block 0 is read in place of an out-of-range id, so no
+ * access leaves the buffers and the split modes give the unsplit result.
  */
 pa_status pa_decode(void* out, const void* q,
                     const void* k_cache, const void* v_cache,

@@ -54,7 +54,9 @@ struct Target {
 };
 
 // Attention of the G query heads of KV head h of sequence b over tokens
-// [t0, t1) (t0 a multiple of 32).  An empty range writes zeros (final only).
+// [t0, t1) (t0 a multiple of 32).  An empty range -- also one that lies past
+// the table row -- writes zero output rows, or the empty softmax state
+// (maximum -inf, exp-sum 0, zero row), which the merge weighs 0.
 template <int CK, int D, int BS>
 __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const int h, const int t0,
                                        int t1, const Target tgt) {
@@ -69,12 +71,22 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
   const bool head_ok = col < G;
 
   if (t0 >= t1) {
-    if (tgt.final_out && head_ok) {
+    if (head_ok && tgt.final_out) {
       __bf16* o = reinterpret_cast<__bf16*>(a.out) + ((size_t)b * a.num_q_heads + hq) * D;
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[dt * 16 + grp * 4 + r] = (__bf16)0.0f;
+    } else if (head_ok) {
+      const size_t row = tgt.row0 + (size_t)col * tgt.row_stride;
+      float* o = a.part_out + row * D;
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt)
+        *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (grp == 0) {
+        a.part_max[row] = -INFINITY;
+        a.part_sum[row] = 0.f;
+      }
     }
     return;
   }

@@ -63,7 +63,9 @@ struct Target {
 };
 
 // Attention of the G query heads of KV head h of sequence b over tokens
-// [t0, t1) (t0 a multiple of 32).  An empty range writes zeros (final only).
+// [t0, t1) (t0 a multiple of 32).  An empty range -- also one that lies past
+// the table row -- writes zero output rows, or the empty softmax state
+// (maximum -inf, exp-sum 0, zero row), which the merge weighs 0.
 template <typename QT, Elem E, int D, int BS, int G>
 __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const int h, const int t0,
                                        int t1, const Target tgt) {
@@ -88,12 +90,26 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
 
   const int tc = lane % CPR;               // V token chunk of this lane
   if (t0 >= t1) {
-    if (tgt.final_out && tc == 0) {
+    const bool dev = a.counters != nullptr;
+    if (tc == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
-          out[((size_t)b * a.num_q_heads + h * G + g) * D + i * DSTRIDE + lane / CPR] = (QT)0.0f;
+        for (int i = 0; i < NV; ++i) {
+          const int d = i * DSTRIDE + lane / CPR;
+          if (tgt.final_out)
+            out[((size_t)b * a.num_q_heads + h * G + g) * D + d] = (QT)0.0f;
+          else
+            state_store(a.part_out + (tgt.row0 + (size_t)g * tgt.row_stride) * D + d, 0.f, dev);
+        }
+    }
+    if (!tgt.final_out && lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const size_t row = tgt.row0 + (size_t)g * tgt.row_stride;
+        state_store(a.part_max + row, -INFINITY, dev);
+        state_store(a.part_sum + row, 0.f, dev);
+      }
     }
     return;
   }

@@ -316,7 +316,11 @@ pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v
   a.max_blocks = max_blocks_per_seq;
   const long long cap = (long long)max_blocks_per_seq * block_size;
   a.cap_len = (int)std::min<long long>(cap, INT32_MAX);
-  a.max_len = balanced ? max_context_len : (int)std::min<long long>(max_context_len, cap);
+  // lengths are clamped to max_context_len only, as pa_decode_reduce clamps
+  // them, so every partition the merge counts has a state; tokens past the
+  // table row (cap_len) are never read, and a range lying wholly past it
+  // leaves the empty state
+  a.max_len = max_context_len;
   a.num_seqs = num_seqs; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads;
   a.group = group;
   a.partition = balanced ? pa::kAuto : partition_size;
@@ -499,7 +503,7 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
   a.max_blocks = max_blocks_per_seq;
   const long long cap = (long long)max_blocks_per_seq * block_size;
   a.cap_len = (int)std::min<long long>(cap, INT32_MAX);
-  a.max_len = (int)std::min<long long>(max_context_len, cap);
+  a.max_len = max_context_len;  // as the decode: pa_prefill_reduce counts partitions alike
   a.num_seqs = num_seqs; a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads;
   a.group = group;
   a.partition = partition_size;

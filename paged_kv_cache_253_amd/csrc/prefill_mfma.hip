@@ -197,6 +197,7 @@ struct Columns {
 // i0 .. i1-1 (empty if i0 >= nq), tokens [t0, t1) of partition `part`.
 struct TileRange {
   int r0, nq, i0, i1, first_pos, t0, t1, len;
+  int need;  // tokens the tile's rows reach, before the table row's end cuts them
 };
 __device__ __forceinline__ TileRange tile_range(const PrefillArgs& args, int b, int tile, int part,
                                                 int rows_per_tile) {
@@ -208,8 +209,10 @@ __device__ __forceinline__ TileRange tile_range(const PrefillArgs& args, int b, 
   t.i0 = tile * rows_per_tile;
   t.i1 = min(t.i0 + rows_per_tile, t.nq);
   t.first_pos = t.len - t.nq;         // position of query token 0 (negative only if nq > len)
-  // tokens the tile needs: 0 .. position of its last query token
-  const int t_end = min(min(t.first_pos + t.i1, t.len), a.cap_len);
+  // tokens the tile needs: 0 .. position of its last query token, none at
+  // or past the end of the table row
+  t.need = min(t.first_pos + t.i1, t.len);
+  const int t_end = min(t.need, a.cap_len);
   t.t0 = 0;
   t.t1 = t_end;
   if (a.partition > 0) {
@@ -236,7 +239,9 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
   const int grp = lane >> 4;
   const TileRange tr = tile_range(args, b, it.sub, part, 16 * NT / a.group);
   if (tr.i0 >= tr.nq) return;
-  if (a.partition > 0 && tr.t0 >= tr.t1) return;  // no row of the tile reaches this partition
+  // no row of the tile reaches this partition (one that only the table
+  // row's end empties still leaves its empty state for the merge)
+  if (a.partition > 0 && tr.t0 >= tr.need) return;
   const int t0 = tr.t0, t1 = tr.t1;
 
   Columns<CK, D, BS, NT> cols;
