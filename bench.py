@@ -7,13 +7,19 @@ block tables), ``--separate-append`` for ``pa_kv_cache_write`` with the
 slot mapping then ``pa_decode`` -- plus ``pa_decode_reduce`` when the
 context is split and not merged inside the decode launch (``--partition
 -2``, ``PA_PARTITION_AUTO_MERGED``).  Default workload: the
-Llama-3-8B-shaped decode batch (64 sequences, 32 query / 8 KV heads, head
-dim 128, 16-token blocks, bf16 KV, lengths U[512, 4096]).
+Llama-3-70B-shaped decode batch (256 sequences, 64 query / 8 KV heads, head
+dim 128, 16-token blocks, bf16 KV, lognormal lengths, median 1024), the
+largest bf16 configuration; ``--workload 2`` is the Llama-3-8B-shaped one.
 
 Prints one JSON line on stdout.  ``value`` is the step's algorithmic HBM
-bytes divided by the step time (GB/s); ``roofline`` is the decode kernel
-alone, timed with HIP events on the stream it runs on; ``cpu_baseline`` is
-the fp64 CPU oracle on a bounded sample of the same batch.
+bytes divided by the step time (GB/s), K steps back to back; ``roofline``
+is the decode kernel alone and ``roofline.in_step`` the appending decode
+the steps launch, each timed launch by launch with HIP events on the stream
+it runs on after a cache flush (``--flush``), next to the bandwidth a plain
+streaming read attains in the same run; ``cpu_baseline`` is the fp64 CPU
+oracle on a bounded sample of the same batch, one process, and
+``cpu_baseline_all_cores`` the same oracle in a pool of processes over the
+batch's sequences.
 """
 
 from __future__ import annotations
@@ -376,47 +382,174 @@ def with_cache_dtype(w, cache_dtype):
                                name=w.name + ("-e5m2" if cache_dtype == "fp8_e5m2" else ""))
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--partition", type=int, default=None,
-                    help="context split: tokens per partition, 0 unsplit, -1 balanced with "
-                         "a separate merge launch, -2 balanced merged in the decode launch "
-                         "(default: the workload's own, else the library default, -1)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--eager", action="store_true",
-                    help="report the eager step time instead of the HIP graph replay")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--op", choices=["step", "copy", "prefill", "swap"], default="step",
-                    help="step: append + decode (+ merge); copy: a copy-on-write burst "
-                         "of pa_copy_blocks on the workload's pool; prefill: several query "
-                         "tokens per sequence (pa_prefill_chunk), see --case")
-    ap.add_argument("--cache-dtype", choices=["fp8_e4m3", "fp8_e5m2", "int4"], default=None,
-                    help="KV cache format in place of the workload's: the other FP8 format "
-                         "for an FP8 workload, or INT4 (per-token scales, bf16 queries) for "
-                         "any bf16 or FP8 workload")
-    ap.add_argument("--separate-append", action="store_true",
-                    help="step as pa_kv_cache_write + pa_decode (two launches) instead of "
-                         "pa_decode_append")
-    ap.add_argument("--case", default="spec-verify-8b",
-                    help="prefill shape: spec-verify-8b or chunked-prefill-8b")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the library runs on one GPU; it has no multi-GPU path)", file=sys.stderr)
-        return 2
-    if args.op == "copy":
-        return bench_copy(args)
-    if args.op == "prefill":
-        return bench_prefill(args)
-    if args.op == "swap":
-        return bench_swap(args)
+FLUSH_COPY_BYTES = 512 << 20    # device-to-device copy before every timed launch
+FLUSH_READ_BYTES = 1 << 30      # then a streaming read, so the copy's dirty lines leave first
+ATTAINABLE_BYTES = 2 << 30      # the streaming-read buffer (more than the largest decode reads)
 
+
+class Flush:
+    """Run before every per-launch timing: a 512 MiB device-to-device copy,
+    so the memory-side cache (256 MB) and the L2s hold none of the decode's
+    data, then (mode "copy+read", the default) a 1 GiB streaming read of
+    another buffer, so the lines the copy dirtied are written back during
+    the read and not during the timed launch.  Both outside the timed
+    events and outside any captured graph."""
+
+    def __init__(self, torch, pk, mode: str, dev):
+        self.mode, self.pk = mode, pk
+        if mode == "none":
+            return
+        self.src = torch.zeros(FLUSH_COPY_BYTES, dtype=torch.uint8, device=dev)
+        self.dst = torch.empty_like(self.src)
+        if "read" in mode:
+            self.rd = torch.ones(FLUSH_READ_BYTES, dtype=torch.uint8, device=dev)
+            self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        if self.mode == "none":
+            return
+        self.dst.copy_(self.src)
+        if "read" in self.mode:
+            self.pk.stream_read(self.rd, self.sink)
+
+    def describe(self) -> str:
+        return {"none": "none (back to back)",
+                "copy": "512 MiB device copy before each launch",
+                "copy+read": "512 MiB device copy then a 1 GiB streaming read before each launch"
+                }[self.mode]
+
+
+def timed_launches(torch, fn, reps: int, flush) -> np.ndarray:
+    """Milliseconds of each of ``reps`` launches of ``fn``, one HIP event pair
+    around each on torch's current stream (the stream the library launches
+    on), each preceded by ``flush``; one untimed flush and launch first
+    (first-call costs of the flush's and the timed kernels)."""
+    flush()
+    fn()
+    pairs = []
+    for _ in range(reps):
+        flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in pairs])
+
+
+def dist_us(ms: np.ndarray) -> dict:
+    us = np.asarray(ms) * 1e3
+    return {"mean": round(float(us.mean()), 2), "median": round(float(np.median(us)), 2),
+            "p10": round(float(np.percentile(us, 10)), 2),
+            "p90": round(float(np.percentile(us, 90)), 2), "n": int(us.size)}
+
+
+def _oracle_worker(conn):
+    """One process of the CPU-baseline pool: decode its share of the batch's
+    sequences with the oracle, its BLAS on one thread, ``rounds`` times when
+    told to; report (seconds, bytes, tokens, decodes)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged
+
+    meta, shard = conn.recv()
+
+    def decode(sub):
+        paged.decode(sub["q"], sub["k_pool"], sub["v_pool"], sub["block_tables"],
+                     sub["context_lens"], meta["block_size"], meta["scale"], meta["q_dtype"],
+                     meta["cache_dtype"], sub["k_scale"], sub["v_scale"])
+
+    with threadpool_limits(limits=1):
+        if shard:
+            decode(min(shard, key=lambda x: x[1])[0])  # imports and first-call costs
+        conn.send("ready")
+        rounds = conn.recv()
+        nbytes = tokens = count = 0
+        t0 = time.perf_counter()
+        for _ in range(rounds):
+            for sub, b_bytes, b_tokens in shard:
+                decode(sub)
+                nbytes += b_bytes
+                tokens += b_tokens
+                count += 1
+        conn.send((time.perf_counter() - t0, nbytes, tokens, count))
+    conn.close()
+
+
+def cpu_baseline_pool(batch, seconds: float, procs: int, rate_1: float) -> dict:
+    """The oracle as it stands, run by ``procs`` processes at once, each
+    decoding its share of the batch's sequences (shares balanced by bytes),
+    the whole batch ``rounds`` times so that the pool works about
+    ``seconds``.  The value is all processes' algorithmic bytes over the
+    wall time from the start signal to the last result (host copies and
+    process start-up outside it)."""
+    import multiprocessing as mp
+
+    from workloads import decode_bytes, extract_sequences
+
+    w = batch.workload
+    subs = []
+    for b in range(len(batch.context_lens)):
+        acct = decode_bytes(batch.context_lens[b:b + 1], w.num_q_heads, w.num_kv_heads,
+                            w.head_dim, w.block_size, w.cache_dtype, w.q_dtype)
+        subs.append((extract_sequences(batch, [b]), acct["total"], acct["tokens"]))
+    total = sum(x[1] for x in subs)
+    shards = [[] for _ in range(procs)]
+    load = [0] * procs
+    for item in sorted(subs, key=lambda x: -x[1]):  # largest first, to the lightest share
+        i = int(np.argmin(load))
+        shards[i].append(item)
+        load[i] += item[1]
+    rounds = max(1, int(np.ceil(seconds * rate_1 * 1e9 * procs / max(total, 1))))
+    meta = {"block_size": w.block_size, "scale": batch.scale, "q_dtype": w.q_dtype,
+            "cache_dtype": w.cache_dtype}
+    ctx = mp.get_context("spawn")  # fresh interpreters: nothing of this process's GPU state
+    workers = []
+    for shard in shards:
+        parent, child = ctx.Pipe()
+        p = ctx.Process(target=_oracle_worker, args=(child,), daemon=True)
+        p.start()
+        parent.send((meta, shard))
+        workers.append((p, parent))
+
+    def collect(what, timeout_s):
+        got = []
+        for p, conn in workers:
+            if not conn.poll(timeout_s):
+                for q, _ in workers:
+                    q.terminate()
+                raise RuntimeError(f"CPU-baseline worker gave no {what} within {timeout_s}s "
+                                   f"(alive: {p.is_alive()})")
+            got.append(conn.recv())
+        return got
+
+    assert all(r == "ready" for r in collect("ready signal", 300))
+    t0 = time.perf_counter()
+    for _, conn in workers:
+        conn.send(rounds)
+    results = collect("result", max(600, 20 * seconds))
+    wall = time.perf_counter() - t0
+    for p, _ in workers:
+        p.join(timeout=30)
+    nbytes = sum(r[1] for r in results)
+    tokens = sum(r[2] for r in results)
+    count = sum(r[3] for r in results)
+    return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "tokens_per_s": tokens / wall, "seconds": round(wall, 2),
+            "speedup_vs_one_process": round(nbytes / wall / 1e9 / rate_1, 2),
+            "sample": f"process pool of {procs} (one BLAS thread each; "
+                      f"{len(os.sched_getaffinity(0))} cores in this process's affinity), "
+                      f"{count} sequence decodes = {rounds} passes over all "
+                      f"{len(subs)} sequences of the batch ({tokens} context tokens), "
+                      f"fp64 numpy oracle"}
+
+
+def bench_step(args) -> int:
+    """The hot path's step on one batch resident in HBM: ``value`` from K
+    graph-replayed steps; per-kernel times (roofline) from single launches
+    each preceded by the cache flush."""
     import torch
 
     import paged_kv_cache_253_amd as pk
@@ -445,73 +578,64 @@ def main() -> int:
     if part:
         ws = pk.new_workspace(s, hq, w.num_kv_heads, d, batch.max_context_len, part, dev)
 
-    ev = {}
-
-    def rec(name):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        ev.setdefault(name, []).append(e)
-
     one_call = not args.separate_append  # the step calls pa_decode_append
     merge_launch = part not in (0, pk.PARTITION_AUTO_MERGED)  # a pa_decode_reduce per step
+    new_rows = dict(k_new=batch.k_new, v_new=batch.v_new)
 
-    def attend(new_rows):
-        """pa_decode_append (new_rows given) or pa_decode, without the merge."""
+    def write():
+        pk.kv_cache_write(batch.k_new, batch.v_new, batch.k_pool, batch.v_pool, slots,
+                          batch.k_scale, batch.v_scale, cache_dtype=w.cache_dtype)
+
+    def attend(rows):
+        """pa_decode_append (rows given) or pa_decode, without the merge."""
         if part:
             pk.decode_partitions(batch.q, batch.k_pool, batch.v_pool, bt, cl,
                                  batch.max_context_len, part, batch.scale, batch.k_scale,
-                                 batch.v_scale, ws, out=out, cache_dtype=w.cache_dtype,
-                                 **new_rows)
+                                 batch.v_scale, ws, out=out, cache_dtype=w.cache_dtype, **rows)
         else:
             pk.decode(batch.q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len,
                       batch.scale, batch.k_scale, batch.v_scale, 0, out=out,
-                      cache_dtype=w.cache_dtype, **new_rows)
+                      cache_dtype=w.cache_dtype, **rows)
 
-    def step(timed: bool):
-        if timed:
-            rec("write0")
+    def reduce():
+        pk.decode_reduce(out, ws, cl, batch.max_context_len, part, w.num_kv_heads)
+
+    def step():
         if not one_call:
-            pk.kv_cache_write(batch.k_new, batch.v_new, batch.k_pool, batch.v_pool, slots,
-                              batch.k_scale, batch.v_scale, cache_dtype=w.cache_dtype)
-        if timed:
-            rec("write1")
-        attend(dict(k_new=batch.k_new, v_new=batch.v_new) if one_call else {})
-        if timed:
-            rec("decode1")
+            write()
+        attend(new_rows if one_call else {})
         if merge_launch:
-            pk.decode_reduce(out, ws, cl, batch.max_context_len, part, w.num_kv_heads)
-            if timed:
-                rec("reduce1")
+            reduce()
 
+    # ---- the step: K steps back to back, timed as a whole ----------------
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps (partition {part})")
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(args.steps):
-        step(True)
+        step()
     end.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    eager_ms_per_step = ms_per_step
-
+    eager_ms_per_step = start.elapsed_time(end) / args.steps
+    ms_per_step = eager_ms_per_step
     if not args.eager:
         # The same step captured once in a HIP graph and replayed K times
-        # (the step is a fixed launch sequence on one stream; replay removes
-        # the host launch gaps between its kernels).  The replayed result
-        # must match the eager step bit for bit.
+        # (a fixed launch sequence on one stream; replay removes the host
+        # launch gaps).  The replayed result must match the eager step bit
+        # for bit.
         ref = out.clone()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step(False)
+            step()
         for _ in range(3):
             graph.replay()
         torch.cuda.synchronize()
         if not torch.equal(out.view(torch.int16), ref.view(torch.int16)):
             raise RuntimeError("graph replay differs from the eager step")
+        torch.cuda.synchronize()
         g0 = torch.cuda.Event(enable_timing=True)
         g1 = torch.cuda.Event(enable_timing=True)
         g0.record()
@@ -520,33 +644,26 @@ def main() -> int:
         g1.record()
         torch.cuda.synchronize()
         ms_per_step = g0.elapsed_time(g1) / args.steps
-        log(f"[bench] graph replay: {ms_per_step * 1e3:.1f} us per step "
-            f"(eager {eager_ms_per_step * 1e3:.1f} us)")
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us "
+        f"({'eager' if args.eager else 'graph replay'}; eager {eager_ms_per_step * 1e3:.1f} us)")
 
-    def span(a, b):
-        return [x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]
-
-    write_ms = float(np.mean(span("write0", "write1")))
-    decode_ms_list = span("write1", "decode1")
-    decode_ms_in_step = float(np.mean(decode_ms_list))
-    reduce_ms = float(np.mean(span("decode1", "reduce1"))) if merge_launch else 0.0
-
-    # The decode kernel alone: back-to-back launches on the stream it runs on,
-    # one event pair around them, so per-launch event overhead is amortised.
-    def decode_only():
-        attend({})
-
-    reps = max(args.steps, 20)
-    for _ in range(3):
-        decode_only()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        decode_only()
-    e1.record()
-    torch.cuda.synchronize()
-    decode_ms = e0.elapsed_time(e1) / reps
+    # ---- each kernel alone, one launch per flush -------------------------
+    flush = Flush(torch, pk, args.flush, dev)
+    reps = max(args.steps, 30)
+    t_write = timed_launches(torch, write, reps, flush)
+    t_decode = timed_launches(torch, lambda: attend({}), reps, flush)
+    t_append = timed_launches(torch, lambda: attend(new_rows), reps, flush) if one_call else None
+    t_reduce = timed_launches(torch, reduce, reps, flush) if merge_launch else None
+    abuf = torch.ones(ATTAINABLE_BYTES, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    t_read = timed_launches(torch, lambda: pk.stream_read(abuf, sink), reps, flush)
+    del abuf
+    warm = None
+    if args.warm:  # back to back, no flush (a separate figure; not the roofline's)
+        for _ in range(3):
+            attend({})
+        t_warm = timed_launches(torch, lambda: attend({}), reps, lambda: None)
+        warm = dist_us(t_warm)
 
     dec = decode_bytes(batch.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim,
                        w.block_size, w.cache_dtype, w.q_dtype)
@@ -554,15 +671,19 @@ def main() -> int:
                      w.cache_dtype)
     step_bytes = dec["total"] + wr
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    decode_ms = float(t_decode.mean())
     achieved = dec["total"] / (decode_ms * 1e-3) / 1e9
+    attainable = ATTAINABLE_BYTES / (float(np.median(t_read)) * 1e-3) / 1e9
+    in_step_ms = float((t_append if one_call else t_decode).mean())
     in_step_bytes = dec["total"] + (wr if one_call else 0)
-    in_step_gbs = in_step_bytes / (decode_ms_in_step * 1e-3) / 1e9
-    first = (f"append+decode {decode_ms_in_step * 1e3:.1f}" if one_call else
-             f"write {write_ms * 1e3:.1f}, decode {decode_ms_in_step * 1e3:.1f}")
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us ({first}, reduce {reduce_ms * 1e3:.1f}); "
-        f"decode alone "
-        f"{decode_ms * 1e3:.1f} us = {achieved:.0f} GB/s = {100 * achieved / PEAK_HBM_GBS:.1f}% "
-        f"of peak")
+    in_step_gbs = in_step_bytes / (in_step_ms * 1e-3) / 1e9
+    log(f"[bench] decode {decode_ms * 1e3:.1f} us = {achieved:.0f} GB/s = "
+        f"{100 * achieved / PEAK_HBM_GBS:.1f}% of peak, {100 * achieved / attainable:.1f}% of the "
+        f"{attainable:.0f} GB/s streaming read; "
+        + (f"appending decode {in_step_ms * 1e3:.1f} us = {100 * in_step_gbs / PEAK_HBM_GBS:.1f}%; "
+           if one_call else "")
+        + f"write {t_write.mean() * 1e3:.1f} us"
+        + (f", reduce {t_reduce.mean() * 1e3:.1f} us" if merge_launch else ""))
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -599,36 +720,94 @@ def main() -> int:
                    + (" + reduce" if merge_launch else ""),
                    "launch": "eager" if args.eager else "hip graph replay",
                    "eager_ms_per_step": round(eager_ms_per_step, 4)},
-        "kernels_us": {"kv_cache_write": round(write_ms * 1e3, 2) if not one_call else None,
-                       "decode_append" if one_call else "decode": round(decode_ms_in_step * 1e3, 2),
-                       "decode_reduce": round(reduce_ms * 1e3, 2) if merge_launch else None,
-                       "decode_back_to_back": round(decode_ms * 1e3, 2)},
+        # each kernel alone: one launch per flush, HIP events around it
+        "kernels_us": {"flush": flush.describe(),
+                       "kv_cache_write": dist_us(t_write),
+                       "decode": dist_us(t_decode),
+                       "decode_append": dist_us(t_append) if one_call else None,
+                       "decode_reduce": dist_us(t_reduce) if merge_launch else None,
+                       "stream_read_2GiB": dist_us(t_read),
+                       "decode_warm_back_to_back": warm},
         "roofline": {"bound": "hbm", "kernel": "pa_decode", "achieved": round(achieved, 1),
                      "launch_us": round(decode_ms * 1e3, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "algorithmic_bytes": dec["total"],
                      "traffic": traffic,
-                     # the same figure for the launch the timed steps make (eager
-                     # steps' HIP events): pa_decode_append's decode with the
-                     # append inside where the kernels allow, else the append
-                     # launch plus the decode
+                     "algorithmic_bytes": dec["total"],
+                     # what a kernel that only streams reads attains on this device
+                     "attainable": round(attainable, 1),
+                     "frac_of_attainable": round(achieved / attainable, 4),
+                     # the same figures for the decode launch the steps make:
+                     # pa_decode_append, the append inside the decode launch
+                     # where the kernels allow (else the plain decode)
                      "in_step": {"kernel": "pa_decode_append" if one_call else "pa_decode",
-                                 "launch_us": round(decode_ms_in_step * 1e3, 2),
+                                 "launch_us": round(in_step_ms * 1e3, 2),
                                  "achieved": round(in_step_gbs, 1),
                                  "frac": round(in_step_gbs / PEAK_HBM_GBS, 4),
+                                 "frac_of_attainable": round(in_step_gbs / attainable, 4),
                                  "algorithmic_bytes": in_step_bytes}},
     }
     if not args.no_cpu:
         log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f}s")
-        result["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds)
-        cores = host_cores()
-        if cores > 1:  # the same oracle, its BLAS on every core
-            log(f"[bench] timing the CPU oracle on {cores} BLAS threads for about "
-                f"{args.cpu_seconds / 3:.0f}s")
-            result["cpu_baseline_all_cores"] = cpu_baseline(batch, args.cpu_seconds / 3, cores)
+        one = cpu_baseline(batch, args.cpu_seconds)
+        result["cpu_baseline"] = one
+        procs = host_cores()
+        if procs > 1 and not args.no_pool:
+            log(f"[bench] timing the CPU oracle in a pool of {procs} processes")
+            result["cpu_baseline_all_cores"] = cpu_baseline_pool(batch, args.cpu_seconds / 2,
+                                                                 procs, one["value"])
     print(json.dumps(result), flush=True)
     return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--partition", type=int, default=None,
+                    help="context split: tokens per partition, 0 unsplit, -1 balanced with "
+                         "a separate merge launch, -2 balanced merged in the decode launch "
+                         "(default: the workload's own, else the library default, -1)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-pool", action="store_true",
+                    help="skip the CPU baseline's process-pool leg")
+    ap.add_argument("--flush", choices=["copy+read", "copy", "none"], default="copy+read",
+                    help="what runs before each per-kernel timed launch")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time the decode back to back without flushes")
+    ap.add_argument("--eager", action="store_true",
+                    help="report the eager step time instead of the HIP graph replay")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--op", choices=["step", "copy", "prefill", "swap"], default="step",
+                    help="step: append + decode (+ merge); copy: a copy-on-write burst "
+                         "of pa_copy_blocks on the workload's pool; prefill: several query "
+                         "tokens per sequence (pa_prefill_chunk), see --case")
+    ap.add_argument("--cache-dtype", choices=["fp8_e4m3", "fp8_e5m2", "int4"], default=None,
+                    help="KV cache format in place of the workload's: the other FP8 format "
+                         "for an FP8 workload, or INT4 (per-token scales, bf16 queries) for "
+                         "any bf16 or FP8 workload")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="step as pa_kv_cache_write + pa_decode (two launches) instead of "
+                         "pa_decode_append")
+    ap.add_argument("--case", default="spec-verify-8b",
+                    help="prefill shape: spec-verify-8b or chunked-prefill-8b")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library runs on one GPU; it has no multi-GPU path)", file=sys.stderr)
+        return 2
+    if args.op == "copy":
+        return bench_copy(args)
+    if args.op == "prefill":
+        return bench_prefill(args)
+    if args.op == "swap":
+        return bench_swap(args)
+
+    return bench_step(args)
 
 
 if __name__ == "__main__":

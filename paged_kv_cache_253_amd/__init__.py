@@ -27,7 +27,7 @@ import torch
 
 __all__ = ["PagedAttnError", "load", "kv_cache_write", "copy_blocks", "swap_blocks", "decode",
            "decode_append", "decode_partitions",
-           "prefill_chunk",
+           "prefill_chunk", "stream_read",
            "decode_reduce", "workspace_size", "new_workspace", "workspace_views", "default_partition_size",
            "PARTITION_AUTO", "PARTITION_AUTO_MERGED", "LIB_PATH"]
 
@@ -87,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.pa_swap_blocks.restype = i32
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_stream_read.argtypes = [vp, szt, vp, vp]
+    lib.pa_stream_read.restype = i32
     _lib = lib
     return lib
 
@@ -339,6 +341,16 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                       _dtype_code(out), _stream(out))
         _check("pa_prefill_reduce", st)
     return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """``pa_stream_read`` (measurement aid, ``include/pa_measure.h``): read
+    every byte of ``buf`` once with the decode's 16-byte non-temporal loads;
+    ``sink`` is a one-element int32 device tensor the kernel may write."""
+    if sink.numel() < 1 or sink.element_size() != 4:
+        raise ValueError("sink must hold one 4-byte element")
+    nbytes = buf.numel() * buf.element_size()
+    _check("pa_stream_read", load().pa_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf)))
 
 
 def _decode_call(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len,

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
 
 SOURCES = ["pa_api.hip", "cache_write.hip", "decode_mfma.hip", "decode_valu.hip",
-           "decode_reduce.hip", "copy_blocks.hip", "prefill_mfma.hip"]
+           "decode_reduce.hip", "copy_blocks.hip", "prefill_mfma.hip", "stream_read.hip"]
 
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
