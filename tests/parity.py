@@ -24,10 +24,13 @@ TOL = {
     "bf16": dict(atol=5e-3, rtol=1e-2, norm=1e-2),
     "fp8_e4m3": dict(atol=2e-2, rtol=1e-2, norm=1e-2),
     "fp8_e5m2": dict(atol=2e-2, rtol=1e-2, norm=1e-2),   # same codes on both sides
-    # INT4 values reach |code * scale| <= 8 * scale; each token's V scale
-    # rides in its bf16 softmax weight (2^-9 relative), so the budget is the
-    # FP8 one
-    "int4": dict(atol=2e-2, rtol=1e-2, norm=1e-2),
+    # The bf16 atol scaled by the INT4 values' magnitude: the stated 5e-3 is
+    # for N(0, 1) data (rms 1); the INT4 caches hold codes uniform over
+    # -8..7 (E[c^2] = 21.5) times scales uniform in [0.25, 0.5) (E[s^2] =
+    # 7/48), rms sqrt(21.5 * 7/48) = 1.77, and every error term of the
+    # kernels (bf16 softmax weights, bf16 output) is relative to the values
+    # it weighs: 5e-3 * 1.77 = 8.85e-3, rounded up
+    "int4": dict(atol=9e-3, rtol=1e-2, norm=1e-2),
 }
 
 
