@@ -30,7 +30,8 @@
  * Conventions for every entry point:
  *
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The
- *     library allocates no memory and keeps no state between calls.
+ *     library allocates no memory and keeps no state between calls
+ *     (pa_decode_noalloc's static scratch array aside).
  *   - Work is enqueued on `stream` (0 = the null stream) and is
  *     asynchronous; no call synchronizes the device or copies to the host.
  *   - Arguments are checked on the host before anything is launched; on
@@ -488,6 +489,48 @@ pa_status pa_prefill_reduce(void* out, const void* workspace, size_t workspace_b
                             int max_query_len, int num_seqs, int num_q_heads,
                             int num_kv_heads, int head_dim, int partition_size,
                             pa_dtype out_dtype, hipStream_t stream);
+
+/*
+ * pa_decode_noalloc -- for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The decode step of pa_decode_append (k_new and v_new given)
+ * or pa_decode (both NULL) with the balanced split (PA_PARTITION_AUTO),
+ * followed by its merge (pa_decode_reduce), so `out` is complete when the
+ * call's work ends -- the same launches, kernels and result bits as those
+ * calls with a caller's workspace, but the split's partial states live in a
+ * scratch array inside the library.
+ *
+ * Scratch: one static device array of PA_NOALLOC_SCRATCH_BYTES per GPU the
+ * library runs on, held until the process ends; its device address is
+ * looked up once per device, on the first call made with that device
+ * current (make that call before capturing a graph).  A batch whose
+ * balanced-split workspace (pa_decode_workspace_size with PA_PARTITION_AUTO)
+ * is larger returns PA_ERR_WORKSPACE and launches nothing; on a 256-CU
+ * MI355X every supported shape fits (the largest, G = 16 at head_dim 128,
+ * needs 34.1 MB).  Nothing in the array needs to start at zero, and it
+ * keeps the last call's states.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (on different streams, or
+ * from host threads without ordering) race and give wrong results; calls
+ * ordered on one stream are safe.
+ *
+ * This call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  Arguments as pa_decode_append (or pa_decode), without
+ * partition_size and the workspace; src_dtype is ignored when k_new is NULL.
+ * Errors as those calls, plus PA_ERR_INVALID_ARG when only one of k_new and
+ * v_new is given, PA_ERR_WORKSPACE as above, PA_ERR_HIP when the device or
+ * the array's address cannot be queried.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (40u << 20)
+
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache,
+                            const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* context_lens, int max_context_len,
+                            int num_seqs, int num_q_heads, int num_kv_heads,
+                            int head_dim, int block_size, int64_t num_blocks,
+                            float scale, pa_dtype q_dtype, pa_dtype src_dtype,
+                            pa_dtype cache_dtype, const float* k_scale, const float* v_scale,
+                            hipStream_t stream);
 
 /* pa_status_string -- static, human-readable name of a status code. */
 const char* pa_status_string(pa_status status);

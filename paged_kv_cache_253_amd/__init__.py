@@ -26,7 +26,7 @@ import os
 import torch
 
 __all__ = ["PagedAttnError", "load", "kv_cache_write", "copy_blocks", "swap_blocks", "decode",
-           "decode_append", "decode_partitions",
+           "decode_append", "decode_partitions", "decode_noalloc",
            "prefill_chunk", "stream_read",
            "decode_reduce", "workspace_size", "new_workspace", "workspace_views", "default_partition_size",
            "PARTITION_AUTO", "PARTITION_AUTO_MERGED", "LIB_PATH"]
@@ -87,6 +87,9 @@ def load() -> ctypes.CDLL:
     lib.pa_swap_blocks.restype = i32
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                      i32, i32, i64, f32, i32, i32, i32, vp, vp, vp]
+    lib.pa_decode_noalloc.restype = i32
     lib.pa_stream_read.argtypes = [vp, szt, vp, vp]
     lib.pa_stream_read.restype = i32
     _lib = lib
@@ -340,6 +343,38 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                       int(max_query_len), s, hq, hkv, d, int(partition_size),
                                       _dtype_code(out), _stream(out))
         _check("pa_prefill_reduce", st)
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                   scale: float | None = None, k_scale: torch.Tensor | None = None,
+                   v_scale: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                   cache_dtype: str | None = None, k_new: torch.Tensor | None = None,
+                   v_new: torch.Tensor | None = None) -> torch.Tensor:
+    """``pa_decode_noalloc``: the balanced-split decode step (appending
+    ``k_new``/``v_new`` first when given) and its merge, with the split's
+    states in the library's static scratch array -- no workspace and no
+    allocation by the library (give ``out`` to allocate nothing here
+    either).  Calls that overlap on one GPU share that array and race."""
+    s, hq, d = q.shape
+    nb, hkv, bsz, _ = _pool_dims(k_cache, v_cache, cache_dtype, head_dim=d)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if out is None:
+        out = torch.empty_like(q)
+    src = _dtype_code(k_new) if k_new is not None else PA_BF16
+    st = load().pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
+                                  _ptr(context_lens), int(max_context_len), s, hq, hkv, d, bsz,
+                                  nb, float(scale), _dtype_code(q), src,
+                                  _cache_code(k_cache, cache_dtype), _ptr(k_scale), _ptr(v_scale),
+                                  _stream(q))
+    _check("pa_decode_noalloc", st)
     return out
 
 

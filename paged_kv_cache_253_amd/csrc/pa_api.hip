@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "pa_internal.hpp"
 #include "pagedattn.h"
@@ -565,4 +566,72 @@ pa_status pa_prefill_reduce(void* out, const void* workspace, size_t workspace_b
   return from_hip(pa::launch_reduce(a, oe, head_dim, stream));
 }
 
+// ---------------------------------------------------------------------------
+// pa_decode_noalloc: the balanced split's workspace in a static device array
+// ---------------------------------------------------------------------------
+
 }  // extern "C"
+
+// Scratch for pa_decode_noalloc.  Each GPU the library runs on holds its own
+// copy at its own address, until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address is
+// looked up per device (hipGetSymbolAddress) and only that address is used.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current.
+pa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return from_hip(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_decode_noalloc(void* out, const void* q, const void* k_new,
+                                       const void* v_new, void* k_cache, void* v_cache,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* context_lens, int max_context_len,
+                                       int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int64_t num_blocks,
+                                       float scale, pa_dtype q_dtype, pa_dtype src_dtype,
+                                       pa_dtype cache_dtype, const float* k_scale,
+                                       const float* v_scale, hipStream_t stream) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens ||
+      (k_new == nullptr) != (v_new == nullptr))
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      max_context_len < 0 || num_q_heads % num_kv_heads != 0)
+    return PA_ERR_INVALID_ARG;
+  Layout l;
+  if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                        PA_PARTITION_AUTO, &l))
+    return PA_ERR_HIP;  // the arguments passed above: the device could not be queried
+  if (l.total > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  pa_status st = scratch_of_current_device(&ws);
+  if (st != PA_OK) return st;
+  st = decode_impl(out, q, k_new, v_new, k_cache, v_cache, k_cache, v_cache, block_tables,
+                   max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                   num_kv_heads, head_dim, block_size, num_blocks, scale, q_dtype,
+                   k_new ? src_dtype : PA_BF16, cache_dtype, k_scale, v_scale, PA_PARTITION_AUTO,
+                   ws, PA_NOALLOC_SCRATCH_BYTES, stream);
+  if (st != PA_OK) return st;
+  return pa_decode_reduce(out, ws, PA_NOALLOC_SCRATCH_BYTES, context_lens, max_context_len,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, PA_PARTITION_AUTO,
+                          q_dtype, stream);
+}

@@ -43,7 +43,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["pa_copy_blocks", "pa_decode", "pa_decode_append",
-                                    "pa_decode_reduce",
+                                    "pa_decode_noalloc", "pa_decode_reduce",
                                     "pa_decode_workspace_size", "pa_kv_cache_write",
                                     "pa_prefill_chunk", "pa_prefill_reduce", "pa_status_string",
                                     "pa_swap_blocks"]
@@ -283,3 +283,19 @@ def test_product_package_does_not_import_the_oracle():
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
                 assert "oracle/" not in text, f
 
+
+def test_noalloc_rejects_bad_arguments_on_the_host(lib):
+    """Null pointers, one of k_new / v_new, or a bad head count are refused
+    before the device is touched."""
+    p = ctypes.c_void_p(0x1000)
+    args = [p, p, None, None, p, p, p, 4, p, 100, 2, 8, 2, 128, 16, 10, 0.1, BF16, BF16, BF16,
+            None, None, None]
+    bad_out = list(args)
+    bad_out[0] = None
+    assert lib.pa_decode_noalloc(*bad_out) == INVALID
+    half = list(args)
+    half[2] = p
+    assert lib.pa_decode_noalloc(*half) == INVALID
+    heads = list(args)
+    heads[11] = 7  # 7 query heads over 2 KV heads
+    assert lib.pa_decode_noalloc(*heads) == INVALID
