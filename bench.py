@@ -561,8 +561,12 @@ def bench_step(args) -> int:
     dev = "cuda"
     t_gen = time.perf_counter()
     batch = make_batch(w, device=dev)
+    if args.unshare:
+        from workloads import unshare
+        batch = unshare(batch)
     torch.cuda.synchronize()
-    log(f"[bench] workload {w.index} {w.name}: {len(batch.context_lens)} seqs, "
+    log(f"[bench] workload {w.index} {w.name}{' (unshared)' if args.unshare else ''}: "
+        f"{len(batch.context_lens)} seqs, "
         f"{int(batch.context_lens.sum())} tokens, pool {batch.num_blocks} blocks "
         f"(generated in {time.perf_counter() - t_gen:.1f}s)")
 
@@ -711,7 +715,8 @@ def bench_step(args) -> int:
         "data": "synthetic",
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "context_tokens_per_s": round(dec["tokens"] / (ms_per_step * 1e-3), 1),
-        "config": {"workload": w.name, "num_seqs": len(batch.context_lens),
+        "config": {"workload": w.name + ("-unshared" if args.unshare else ""),
+                   "num_seqs": len(batch.context_lens),
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size,
                    "kv_dtype": w.cache_dtype, "context_tokens": dec["tokens"],
@@ -778,6 +783,9 @@ def main() -> int:
                     help="what runs before each per-kernel timed launch")
     ap.add_argument("--warm", action="store_true",
                     help="also time the decode back to back without flushes")
+    ap.add_argument("--unshare", action="store_true",
+                    help="give every sequence private copies of the blocks it shares "
+                         "(the shared-prefix workload without sharing)")
     ap.add_argument("--eager", action="store_true",
                     help="report the eager step time instead of the HIP graph replay")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -282,6 +282,18 @@ constexpr int stream_waves_per_cu() {
 }
 template <int CK>
 constexpr int stream_waves_per_simd() { return CK == kI4 ? 2 : 1; }
+
+// Persistent wavefronts per CU of a launch: the kernel's own choice, except
+// multi-head batches (G = 1: one query head per 16-column MFMA, so a step
+// carries little work per byte), which stream best with one wavefront per
+// SIMD (measured on MI355X, 64-head bf16 batches: 518 vs 535 us at two per
+// CU), or the tuning override.
+template <int CK, int D>
+int launch_waves_per_cu(const DecodeArgs& a) {
+  if (a.waves_per_cu) return a.waves_per_cu;
+  const int own = stream_waves_per_cu<CK, D>();
+  return a.group == 1 && own < 4 ? 4 : own;
+}
 static_assert(stream_waves_per_cu<kI4, 128>() <= kAutoMaxWavesPerCU, "workspace bound");
 
 typedef const __attribute__((address_space(4))) int32_t* const_i32;
@@ -724,7 +736,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     if constexpr (CK == kBF16) {
       if (a.partition != kAuto || a.counters) return hipErrorInvalidValue;
       DecodeArgs b = a;
-      b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : stream_waves_per_cu<CK, D>());
+      b.slices = a.cus * launch_waves_per_cu<CK, D>(a);
       hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, true, false, false>), dim3(b.slices), dim3(64), 0, stream, b);
       return hipGetLastError();
     }
@@ -732,7 +744,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   }
   if (a.partition == kAuto || (a.partition > 0 && a.stream_fixed)) {
     DecodeArgs b = a;
-    b.slices = a.cus * (a.waves_per_cu ? a.waves_per_cu : stream_waves_per_cu<CK, D>());
+    b.slices = a.cus * launch_waves_per_cu<CK, D>(a);
     if (a.partition > 0) {
       if constexpr (CK != kI4)  // INT4 fixed partitions take the grid (host side)
         hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, false, false, true>), dim3(b.slices), dim3(64), 0, stream, b);
