@@ -17,16 +17,22 @@
 // j, and the rows are accumulated in piece order with fused multiply-adds.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 #include "pa_split.hpp"
 
 namespace pa {
 
-// merge_cut_run's fast path: runs of at most kMergeFastPieces pieces, the
-// states of kMergeFastHeads query heads loaded per round.
+// merge_cut_run's paths for runs of up to 64 pieces: NH query heads at a
+// time, their pieces' rows in rounds of NP -- runs of at most 4 pieces 8
+// heads and one round of rows, longer ones (a run cut by the dynamic tail's
+// small chunks) 4 heads and rounds of 16 pieces.
 constexpr int kMergeFastPieces = 4;
 constexpr int kMergeFastHeads = 8;
+constexpr int kMergeMidPieces = 16;
+constexpr int kMergeMidHeads = 4;
 
 // Partial states that a wavefront of the same launch may read from another
 // XCD (the merge inside the decode launch) are stored and loaded at device
@@ -74,46 +80,64 @@ __device__ __forceinline__ void merge_cut_run(const MergeView& v, int b, int h, 
     for (int e = 0; e < PER; ++e) o[lane + 64 * e] = (OT)(acc[e] * inv);
   };
 
-  if (nparts <= kMergeFastPieces) {
-    // Few pieces (the usual cut: 2 or 3): the states of up to kMergeFastHeads
-    // heads are loaded in one round, then merged head by head.
+  // Runs of up to 64 pieces, NH query heads at a time: the pieces' maxima
+  // and exp-sums in one round (piece j on lane j), then the rows in rounds
+  // of NP pieces, accumulated in piece order with the weights on those
+  // lanes; every head's arithmetic is the general path's, in the same order.
+  auto merge_heads = [&](auto np_tag, auto nh_tag) {
+    constexpr int NP = decltype(np_tag)::value;
+    constexpr int NH = decltype(nh_tag)::value;
     const bool mine = lane < nparts;
-    for (int gb = gq0; gb < G; gb += gq_step * kMergeFastHeads) {
-      float pm[kMergeFastHeads], ps[kMergeFastHeads];
-      float rows[kMergeFastHeads][kMergeFastPieces][PER];
+    for (int gb = gq0; gb < G; gb += gq_step * NH) {
+      float w[NH], acc[NH][PER];
 #pragma unroll
-      for (int i = 0; i < kMergeFastHeads; ++i) {
+      for (int i = 0; i < NH; ++i) {
         const int gq = min(gb + i * gq_step, G - 1);
         const size_t rl = row_of(mine ? lane : 0, gq);
-        pm[i] = state_load<DEVICE_SCOPE>(v.part_max + rl);
-        ps[i] = state_load<DEVICE_SCOPE>(v.part_sum + rl);
+        const float pm = state_load<DEVICE_SCOPE>(v.part_max + rl);
+        const float ps = state_load<DEVICE_SCOPE>(v.part_sum + rl);
+        const float mx = xlane<OpMax, 1, 32>(mine ? pm : -INFINITY);
+        w[i] = mine ? ps * __expf(pm - mx) : 0.f;
 #pragma unroll
-        for (int j = 0; j < kMergeFastPieces; ++j) {
-          const float* src = v.part_out + row_of(min(j, nparts - 1), gq) * D + lane;
-#pragma unroll
-          for (int e = 0; e < PER; ++e) rows[i][j][e] = state_load<DEVICE_SCOPE>(src + 64 * e);
-        }
+        for (int e = 0; e < PER; ++e) acc[i][e] = 0.f;
       }
+      for (int j0 = 0; j0 < nparts; j0 += NP) {
+        float rows[NH][NP][PER];
 #pragma unroll
-      for (int i = 0; i < kMergeFastHeads; ++i) {
-        const int gq = gb + i * gq_step;
-        if (gq >= G) continue;
-        const float mx = xlane<OpMax, 1, 32>(mine ? pm[i] : -INFINITY);
-        const float w = mine ? ps[i] * __expf(pm[i] - mx) : 0.f;
-        float acc[PER];
+        for (int i = 0; i < NH; ++i) {
+          const int gq = min(gb + i * gq_step, G - 1);
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+          for (int j = 0; j < NP; ++j) {
+            const float* src = v.part_out + row_of(min(j0 + j, nparts - 1), gq) * D + lane;
 #pragma unroll
-        for (int j = 0; j < kMergeFastPieces; ++j) {
-          if (j < nparts) {
-            const float wj = __int_as_float(readlane(__float_as_int(w), j));
-#pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, rows[i][j][e], acc[e]);
+            for (int e = 0; e < PER; ++e) rows[i][j][e] = state_load<DEVICE_SCOPE>(src + 64 * e);
           }
         }
-        emit(gq, acc, xlane<OpSum, 1, 32>(w));
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+#pragma unroll
+          for (int j = 0; j < NP; ++j) {
+            if (j0 + j < nparts) {
+              const float wj = __int_as_float(readlane(__float_as_int(w[i]), j0 + j));
+#pragma unroll
+              for (int e = 0; e < PER; ++e) acc[i][e] = fmaf(wj, rows[i][j][e], acc[i][e]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NH; ++i) {
+        const int gq = gb + i * gq_step;
+        if (gq < G) emit(gq, acc[i], xlane<OpSum, 1, 32>(w[i]));
       }
     }
+  };
+  if (nparts <= kMergeFastPieces) {  // the usual cut: 2 or 3 pieces, one round of rows
+    merge_heads(std::integral_constant<int, kMergeFastPieces>{}, std::integral_constant<int, kMergeFastHeads>{});
+    return;
+  }
+  if (nparts <= 64) {
+    merge_heads(std::integral_constant<int, kMergeMidPieces>{}, std::integral_constant<int, kMergeMidHeads>{});
     return;
   }
 
@@ -122,40 +146,9 @@ __device__ __forceinline__ void merge_cut_run(const MergeView& v, int b, int h, 
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     float wsum;
-    if (nparts <= 64) {
-      // Lane j takes piece j's maximum and exp-sum; the rows of the first
-      // kBatch pieces are loaded with them, later batches one load round each.
-      const bool mine = lane < nparts;
-      const size_t rl = row_of(mine ? lane : 0, gq);
-      const float pm = state_load<DEVICE_SCOPE>(v.part_max + rl);
-      const float ps = state_load<DEVICE_SCOPE>(v.part_sum + rl);
-      constexpr int kBatch = 8;
-      float rows[kBatch][PER];
-      auto load_batch = [&](int j0) {
-#pragma unroll
-        for (int jj = 0; jj < kBatch; ++jj) {
-          const float* src = v.part_out + row_of(min(j0 + jj, nparts - 1), gq) * D + lane;
-#pragma unroll
-          for (int e = 0; e < PER; ++e) rows[jj][e] = state_load<DEVICE_SCOPE>(src + 64 * e);
-        }
-      };
-      load_batch(0);
-      const float mx = xlane<OpMax, 1, 32>(mine ? pm : -INFINITY);
-      const float w = mine ? ps * __expf(pm - mx) : 0.f;
-      wsum = w;
-      for (int j0 = 0; j0 < nparts; j0 += kBatch) {
-        if (j0 > 0) load_batch(j0);
-#pragma unroll
-        for (int jj = 0; jj < kBatch; ++jj) {
-          if (j0 + jj < nparts) {
-            const float wj = __int_as_float(readlane(__float_as_int(w), j0 + jj));
-#pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, rows[jj][e], acc[e]);
-          }
-        }
-      }
-    } else {
-      // lanes take the pieces' maxima and exp-sums in parallel
+    {
+      // more than 64 pieces: lanes take the pieces' maxima and exp-sums in
+      // parallel
       float mx = -INFINITY;
       for (int j = lane; j < nparts; j += 64)
         mx = fmaxf(mx, state_load<DEVICE_SCOPE>(v.part_max + row_of(j, gq)));
