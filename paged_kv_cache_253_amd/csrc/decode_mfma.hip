@@ -160,14 +160,14 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
   auto compute = [&](StepBuf<CK, D, BS>& sb, int step) {
     const int base = t0 + step * kStep;
     const bool partial = base + kStep > t1;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 s0 = qk_init<CK>(qbias), s1 = s0;
 #pragma unroll
     for (int c = 0; c < C::kChunks; ++c) {
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sb, 0, c), qop[c], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sb, 1, c), qop[c], s1, 0, 0, 0);
     }
     float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    qk_scores<CK>(z, sb, qbias);
+    qk_scores<CK>(z, sb);
     bool zok[8];  // partial step: token of score register i inside the range
     if (partial) {
 #pragma unroll
@@ -314,11 +314,28 @@ struct NewRows<D, true> {
   int64_t tile;  // byte offset of its (block, KV head) tile in either pool
 };
 
+// Where a step's query operands come from.  Per step (loaded with the
+// step's tiles): simple, and no wait at a segment's start, but the loads
+// repeat on every step and every slot of the ring holds a copy.  Per
+// segment (INT4: one copy, loaded when a segment's first step is about to
+// compute): an INT4 step's tiles are a quarter of a bf16 step's, so the
+// repeated query loads were as many bytes through the vector memory path as
+// the tiles themselves and the copies held the registers the kernel needs;
+// the price is one wait for the ring's outstanding loads per segment, which
+// costs the bf16 decode more than it saves (measured on MI355X, 70B-shaped
+// batch: INT4 127 -> 113 us, bf16 283 -> 341 us).
+template <int CK>
+constexpr bool q_per_segment() { return CK == kI4; }
+
+template <int CK, int D, bool PER_STEP>
+struct StepQ { bf16x8 q[D / 32]; };
+template <int CK, int D>
+struct StepQ<CK, D, false> {};
+
 template <int CK, int D, int BS, bool APPEND>
-struct Slot : StepBuf<CK, D, BS> {
+struct Slot : StepBuf<CK, D, BS>, StepQ<CK, D, !q_per_segment<CK>()> {
   using C = Cfg<CK, D, BS>;
   NewRows<D, APPEND> nw;
-  bf16x8 q[C::kChunks];
   // segment descriptor (wave-uniform)
   int base;   // first token of the step
   int t1;     // end of the run's tokens inside this segment
@@ -417,6 +434,8 @@ void decode_mfma_stream(const DecodeArgs a) {
 
   int64_t tile0 = 0, tile1 = 0;  // the last real step's tiles (filler steps reload them)
   const __bf16* qp = qbase;
+  constexpr bool QSEG = q_per_segment<CK>();
+  bf16x8 qseg[QSEG ? C::kChunks : 1];  // per segment: the computing segment's query
 
   auto issue = [&](S& sl) {
     const bool real = pst ? (ci < cseg_end || left > 0) : left > 0;
@@ -493,9 +512,26 @@ void decode_mfma_stream(const DecodeArgs a) {
       ++pending;
     }
     load_step(sl, kc, vc, tile0, tile1, lo, grp);
+    if constexpr (!QSEG) {
 #pragma unroll
-    for (int c = 0; c < C::kChunks; ++c)
-      sl.q[c] = *reinterpret_cast<const bf16x8*>(qp + q_dim<CK, D>(grp, c));
+      for (int c = 0; c < C::kChunks; ++c)
+        sl.q[c] = *reinterpret_cast<const bf16x8*>(qp + q_dim<CK, D>(grp, c));
+    }
+  };
+  // per segment: the query of the segment whose first step computes next,
+  // loaded before the ring's next issue, and used at once (INT4: its operand
+  // bias), so that the wait it takes covers only the loads already in flight
+  // and no later step waits for it again
+  float qbias = 0.f;
+  auto load_q = [&](const S& sl) {
+    const __bf16* p = qbase + ((size_t)sl.b * a.num_q_heads + (size_t)sl.h * G + qhead) * D;
+#pragma unroll
+    for (int c = 0; c < (QSEG ? C::kChunks : 0); ++c)
+      qseg[c] = *reinterpret_cast<const bf16x8*>(p + q_dim<CK, D>(grp, c));
+    if constexpr (QSEG) {
+      static_assert(!QSEG || C::I4, "a per-segment query must be used where it is loaded");
+      qbias = q_bias<C::kChunks>(qseg);
+    }
   };
 
   // ---- finished segments ----------------------------------------------------
@@ -596,9 +632,12 @@ void decode_mfma_stream(const DecodeArgs a) {
   // ---- compute side ---------------------------------------------------------
   f32x4 acc[C::kDTiles];
   f32x4 accb = {0.f, 0.f, 0.f, 0.f};  // INT4: column sums of the PV weights
-  float m_run = -INFINITY, l_run = 0.f, c2 = 0.f, qbias = 0.f;
+  float m_run = -INFINITY, l_run = 0.f, c2 = 0.f;
 
   auto compute = [&](S& sl) {
+    const bf16x8* qop;
+    if constexpr (QSEG) qop = qseg;
+    else qop = sl.q;
     if constexpr (APPEND) {
       // The newest token's rows replace the pool's bytes in the step's
       // registers (K: lanes of its QK row; V: element pos % 8 of the lanes
@@ -651,17 +690,17 @@ void decode_mfma_stream(const DecodeArgs a) {
       float kscale = 1.0f;
       if constexpr (FP8) kscale = ((const_f32)a.k_scale)[sl.h];
       c2 = a.scale * kscale * kLog2e;
-      if constexpr (C::I4) qbias = q_bias<C::kChunks>(sl.q);
+      if constexpr (C::I4 && !QSEG) qbias = q_bias<C::kChunks>(qop);
     }
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 s0 = qk_init<CK>(qbias), s1 = s0;
 #pragma unroll
     for (int c = 0; c < C::kChunks; ++c) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sl, 0, c), sl.q[c], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sl, 1, c), sl.q[c], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sl, 0, c), qop[c], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sl, 1, c), qop[c], s1, 0, 0, 0);
     }
     const bool partial = sl.base + kStepTokens > sl.t1;
     float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    qk_scores<CK>(z, sl, qbias);
+    qk_scores<CK>(z, sl);
     bool zok[8];  // partial step: token of score register i inside the range
     if (partial) {
       const int n = sl.t1 - sl.base;
@@ -713,6 +752,7 @@ void decode_mfma_stream(const DecodeArgs a) {
   while (pending > 0) {
 #pragma unroll
     for (int j = 0; j < kRing; ++j) {
+      if (QSEG && ring[j].real && (ring[j].flags & kFirst)) load_q(ring[j]);
       issue(ring[(j + kRing - 1) % kRing]);
       if (ring[j].real) {
         compute(ring[j]);

@@ -108,9 +108,10 @@ constexpr float kI4Bias = 136.0f;
 // u < 128, so one byte permute per pair builds the bit patterns.  Exact; the
 // consumer subtracts the bias in float32.
 __device__ __forceinline__ u32x4 i4x8_biased_words(uint32_t w) {
-  const uint32_t x = w ^ 0x88888888u;
-  const uint32_t lo = x & 0x0F0F0F0Fu;         // elements 0..3, one per byte
-  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // elements 4..7
+  // offset codes (code + 8 = code ^ 8), one per byte; each line is one
+  // three-input bitwise instruction after the shift
+  const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;         // elements 0..3
+  const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;  // elements 4..7
   constexpr uint32_t k43 = 0x43434343u;
   // v_perm_b32: selector byte 0..3 picks a byte of the second operand, 4..7
   // of the first; {b0, 0x43, b1, 0x43} and {b2, 0x43, b3, 0x43}
@@ -139,6 +140,12 @@ __device__ __forceinline__ int i4_code(float x, float s) {
 
 struct OpSum { __device__ static float f(float a, float b) { return a + b; } };
 struct OpMax { __device__ static float f(float a, float b) { return fmaxf(a, b); } };
+// NaN-propagating maximum (v_maximum3_f32): unlike fmaxf it needs no
+// quieting of its inputs, so a tree of them is one instruction per level.
+// For softmax scores, which hold no NaN unless the inputs did.
+struct OpMaxP {
+  __device__ static float f(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+};
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {

@@ -239,15 +239,23 @@ __device__ __forceinline__ void mask_v(VRaw<CK>& r, int valid) {  // valid = tok
 // softmax weight here can contribute (the largest weight of a row is 1).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Raw QK results (QK register order) -> scores in q.k units.  INT4: remove
-// the operand bias (qbias = 136 * sum of the lane column's q) and apply each
-// token's own K scale.  Other kinds: unchanged (an FP8 K scale is folded
-// into the log2 factor).
+// Initial QK accumulator: zero, or for INT4 minus the operand bias (136 *
+// the sum of the lane column's q, see q_bias), so that the MFMA result is
+// already sum_d q_d code_d.
+template <int CK>
+__device__ __forceinline__ f32x4 qk_init(float qbias) {
+  if constexpr (CK == kI4) return f32x4{-qbias, -qbias, -qbias, -qbias};
+  else return f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// QK results (QK register order, accumulated from qk_init) -> scores in q.k
+// units.  INT4: apply each token's own K scale.  Other kinds: unchanged (an
+// FP8 K scale is folded into the log2 factor).
 template <int CK, class Buf>
-__device__ __forceinline__ void qk_scores(float* z, const Buf& sb, float qbias) {
+__device__ __forceinline__ void qk_scores(float* z, const Buf& sb) {
   if constexpr (CK == kI4) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = (z[i] - qbias) * sb.ts.k[i >> 2][i & 3];
+    for (int i = 0; i < 8; ++i) z[i] *= sb.ts.k[i >> 2][i & 3];
   }
 }
 
@@ -266,9 +274,10 @@ __device__ __forceinline__ bf16x8 softmax_step(float* z, bool partial, const boo
 #pragma unroll
     for (int i = 0; i < 8; ++i) z[i] = ok[i] ? z[i] : -INFINITY;
   }
-  float mx = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-  mx = xlane<OpMax, 16, 32>(mx);
-  const float m_new = fmaxf(m_run, mx);
+  using M = OpMaxP;
+  float mx = M::f(M::f(M::f(z[0], z[1]), M::f(z[2], z[3])), M::f(M::f(z[4], z[5]), M::f(z[6], z[7])));
+  mx = xlane<M, 16, 32>(mx);
+  const float m_new = M::f(m_run, mx);
   if (wave_any(m_new > m_run)) {
     const float alpha = exp2_fast((m_run - m_new) * c2);
     l_run *= alpha;

@@ -107,7 +107,7 @@ struct Columns {
   __device__ __forceinline__ void step(StepBuf<CK, D, BS>& sb, int base, int t1, int grp, float c2) {
     f32x4 s0[NT], s1[NT];
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) { s0[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; s1[ct] = s0[ct]; }
+    for (int ct = 0; ct < NT; ++ct) { s0[ct] = qk_init<CK>(qbias[ct]); s1[ct] = s0[ct]; }
 #pragma unroll
     for (int c = 0; c < C::kChunks; ++c) {
       const bf16x8 ka = k_operand<CK>(sb, 0, c);
@@ -129,7 +129,7 @@ struct Columns {
       const int lim = min(t1 - 1, pos[ct]);  // last token this column may see here
       float z[8] = {s0[ct][0], s0[ct][1], s0[ct][2], s0[ct][3],
                     s1[ct][0], s1[ct][1], s1[ct][2], s1[ct][3]};
-      qk_scores<CK>(z, sb, qbias[ct]);
+      qk_scores<CK>(z, sb);
       // the step is full for every real column unless one stops inside it
       const bool partial = wave_any(cvalid[ct] && base + kStep - 1 > lim);
       bool ok[8];
