@@ -39,6 +39,8 @@
 #include "pa_mfma.hpp"
 #include "pa_split.hpp"
 
+#include <type_traits>
+
 namespace pa {
 namespace {
 
@@ -332,8 +334,9 @@ struct StepQ { bf16x8 q[D / 32]; };
 template <int CK, int D>
 struct StepQ<CK, D, false> {};
 
-template <int CK, int D, int BS, bool APPEND>
-struct Slot : StepBuf<CK, D, BS>, StepQ<CK, D, !q_per_segment<CK>()> {
+template <int CK, int D, int BS, bool APPEND, bool PK>
+struct Slot : std::conditional_t<PK, PkBuf<D, BS>, StepBuf<CK, D, BS>>,
+              StepQ<CK, D, !q_per_segment<CK>()> {
   using C = Cfg<CK, D, BS>;
   NewRows<D, APPEND> nw;
   // segment descriptor (wave-uniform)
@@ -356,16 +359,18 @@ struct Slot : StepBuf<CK, D, BS>, StepQ<CK, D, !q_per_segment<CK>()> {
 //
 // MERGE (PA_PARTITION_AUTO_MERGED): cut runs are merged in this launch by
 // the wavefront that finishes a run's last piece (pa_merge.hpp).  FIXED:
-// fixed partitions (slices of whole partitions).  Template parameters so
-// that each launch carries only its own mode's code.
-template <int CK, int D, int BS, bool APPEND, bool MERGE, bool FIXED>
+// fixed partitions (slices of whole partitions).  PK: INT4 with G <= 8,
+// column-packed steps (pa_mfma.hpp).  Template parameters so that each
+// launch carries only its own mode's code.
+template <int CK, int D, int BS, bool APPEND, bool MERGE, bool FIXED, bool PK = false>
 __global__ __launch_bounds__(64)
 __attribute__((amdgpu_waves_per_eu(stream_waves_per_simd<CK>(), stream_waves_per_simd<CK>())))
 void decode_mfma_stream(const DecodeArgs a) {
   constexpr bool FP8 = one_byte<CK>();
   using C = Cfg<CK, D, BS>;
-  using S = Slot<CK, D, BS, APPEND>;
+  using S = Slot<CK, D, BS, APPEND, PK>;
   static_assert(!APPEND || CK == kBF16, "the decode appends only into bf16 caches");
+  static_assert(!PK || (CK == kI4 && !FIXED), "column packing is for INT4 balanced launches");
   static_assert(!(APPEND && MERGE), "the appending decode uses the separate merge");
   static_assert(!(FIXED && (APPEND || MERGE)), "fixed partitions neither append nor merge");
   const int lane = threadIdx.x;
@@ -427,7 +432,10 @@ void decode_mfma_stream(const DecodeArgs a) {
 
   // per-lane offsets inside a step's tiles (see attend)
   const LaneOffsets<CK, D, BS> lo(grp, col);
-  const int qhead = min(col, G - 1);        // lanes past the group read a real row; unused
+  const PkOffsets<D, BS> plo(grp, col);
+  // lanes past the group read a real row; unused
+  const int qhead = min(PK ? (col & 7) : col, G - 1);
+  const bool pk_on = pk_active(grp, col);  // packed: the lane's q operand is its head's
   const char* kc = reinterpret_cast<const char*>(a.k_cache);
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
   const __bf16* qbase = reinterpret_cast<const __bf16*>(a.q);
@@ -435,7 +443,8 @@ void decode_mfma_stream(const DecodeArgs a) {
   int64_t tile0 = 0, tile1 = 0;  // the last real step's tiles (filler steps reload them)
   const __bf16* qp = qbase;
   constexpr bool QSEG = q_per_segment<CK>();
-  bf16x8 qseg[QSEG ? C::kChunks : 1];  // per segment: the computing segment's query
+  constexpr int kQOps = PK ? D / 16 : C::kChunks;  // q operands (one per QK MFMA of a token group)
+  bf16x8 qseg[QSEG ? kQOps : 1];  // per segment: the computing segment's query
 
   auto issue = [&](S& sl) {
     const bool real = pst ? (ci < cseg_end || left > 0) : left > 0;
@@ -511,7 +520,8 @@ void decode_mfma_stream(const DecodeArgs a) {
       if (!pst) --left;
       ++pending;
     }
-    load_step(sl, kc, vc, tile0, tile1, lo, grp);
+    if constexpr (PK) load_step_pk(sl, kc, vc, tile0, tile1, plo);
+    else load_step(sl, kc, vc, tile0, tile1, lo, grp);
     if constexpr (!QSEG) {
 #pragma unroll
       for (int c = 0; c < C::kChunks; ++c)
@@ -525,12 +535,21 @@ void decode_mfma_stream(const DecodeArgs a) {
   float qbias = 0.f;
   auto load_q = [&](const S& sl) {
     const __bf16* p = qbase + ((size_t)sl.b * a.num_q_heads + (size_t)sl.h * G + qhead) * D;
+    if constexpr (PK) {
+      const bf16x8 zero = {};
 #pragma unroll
-    for (int c = 0; c < (QSEG ? C::kChunks : 0); ++c)
-      qseg[c] = *reinterpret_cast<const bf16x8*>(p + q_dim<CK, D>(grp, c));
+      for (int i = 0; i < kQOps; ++i) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(p + pk_q_dim<D>(grp, i));
+        qseg[i] = pk_on ? v : zero;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < (QSEG ? C::kChunks : 0); ++c)
+        qseg[c] = *reinterpret_cast<const bf16x8*>(p + q_dim<CK, D>(grp, c));
+    }
     if constexpr (QSEG) {
       static_assert(!QSEG || C::I4, "a per-segment query must be used where it is loaded");
-      qbias = q_bias<C::kChunks>(qseg);
+      qbias = q_bias<kQOps>(qseg);
     }
   };
 
@@ -692,32 +711,59 @@ void decode_mfma_stream(const DecodeArgs a) {
       c2 = a.scale * kscale * kLog2e;
       if constexpr (C::I4 && !QSEG) qbias = q_bias<C::kChunks>(qop);
     }
-    f32x4 s0 = qk_init<CK>(qbias), s1 = s0;
-#pragma unroll
-    for (int c = 0; c < C::kChunks; ++c) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sl, 0, c), qop[c], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sl, 1, c), qop[c], s1, 0, 0, 0);
-    }
     const bool partial = sl.base + kStepTokens > sl.t1;
-    float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    qk_scores<CK>(z, sl);
-    bool zok[8];  // partial step: token of score register i inside the range
-    if (partial) {
-      const int n = sl.t1 - sl.base;
+    bf16x8 pop;
+    if constexpr (PK) {
+      // two accumulation chains over the D/16 words of the lane's K row
+      f32x4 s0 = qk_init<CK>(qbias), s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) zok[i] = qk_token(grp, i) < n;
-      const int vvalid = min(max(n - 8 * grp, 0), 8);
+      for (int i = 0; i < kQOps; i += 2) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand_pk(sl, i), qop[i], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand_pk(sl, i + 1), qop[i + 1], s1, 0, 0, 0);
+      }
+      float z[4] = {s0[0] + s1[0], s0[1] + s1[1], s0[2] + s1[2], s0[3] + s1[3]};
+      bool zok[4];  // partial step: token of score j inside the range
+      if (partial) {
+        const int t0 = pk_score_token(grp, col) - (sl.t1 - sl.base);
 #pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sl.v[dt], vvalid);
+        for (int j = 0; j < 4; ++j) zok[j] = t0 + j < 0;
+      }
+      pop = softmax_step_pk<C::kDTiles>(z, partial, zok, sl, c2, m_run, l_run, acc, accb, pk_on);
+    } else {
+      f32x4 s0 = qk_init<CK>(qbias), s1 = s0;
+#pragma unroll
+      for (int c = 0; c < C::kChunks; ++c) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sl, 0, c), qop[c], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<CK>(sl, 1, c), qop[c], s1, 0, 0, 0);
+      }
+      float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      qk_scores<CK>(z, sl);
+      bool zok[8];  // partial step: token of score register i inside the range
+      if (partial) {
+        const int n = sl.t1 - sl.base;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) zok[i] = qk_token(grp, i) < n;
+        const int vvalid = min(max(n - 8 * grp, 0), 8);
+#pragma unroll
+        for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sl.v[dt], vvalid);
+      }
+      pop = softmax_step<CK, C::kDTiles>(z, partial, zok, sl, c2, m_run, l_run, acc, accb);
     }
-    const bf16x8 pop = softmax_step<CK, C::kDTiles>(z, partial, zok, sl, c2, m_run, l_run, acc, accb);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<CK>(sl.v[dt]), pop, acc[dt], 0, 0, 0);
     if constexpr (C::I4) accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop, accb, 0, 0, 0);
 
     if (sl.flags & kLast) {
-      const float l_tot = xlane<OpSum, 16, 32>(l_run);
+      float l_tot = xlane<OpSum, 16, 32>(l_run);
+      if constexpr (PK) {  // columns c and c ^ 8 hold the two token halves of a head
+        l_tot = pk_fold(l_tot);
+#pragma unroll
+        for (int dt = 0; dt < C::kDTiles; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[dt][r] = pk_fold(acc[dt][r]);
+        accb[0] = pk_fold(accb[0]);
+      }
       float vscale = 1.0f;
       if constexpr (FP8) vscale = ((const_f32)a.v_scale)[sl.h];
       const float inv = l_tot > 0.f ? vscale / l_tot : 0.f;  // an empty run writes zeros
@@ -790,6 +836,11 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, false, false, true>), dim3(b.slices), dim3(64), 0, stream, b);
       else
         return hipErrorInvalidValue;
+    } else if (CK == kI4 && a.group <= 8) {  // column-packed INT4 steps
+      if (a.counters)
+        hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, false, true, false, CK == kI4>), dim3(b.slices), dim3(64), 0, stream, b);
+      else
+        hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, false, false, false, CK == kI4>), dim3(b.slices), dim3(64), 0, stream, b);
     } else if (a.counters)
       hipLaunchKernelGGL((decode_mfma_stream<CK, D, BS, false, true, false>), dim3(b.slices), dim3(64), 0, stream, b);
     else

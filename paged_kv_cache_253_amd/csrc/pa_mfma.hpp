@@ -329,5 +329,156 @@ __device__ __forceinline__ float q_bias(const bf16x8* q) {
   return kI4Bias * xlane<OpSum, 16, 32>(s);
 }
 
+// ---------------------------------------------------------------------------
+// Column-packed INT4 steps (G <= 8 query heads per KV head).  Unpacked, a
+// step's QK fills G of the 16 MFMA columns and every lane runs the softmax
+// on 8 scores of which 16 - G columns are padding.  Packed, columns 0..7
+// carry the G heads for the step's first 16 tokens and columns 8..15 the
+// same heads for its last 16: each lane holds 4 scores, and the per-token
+// work (scales, exponentials, sums) halves at the same MFMA count.
+//
+// QK (K rows as the A operand): the 32 k-slots split into two segments of
+// 16 (lane groups 0,1 and 2,3); A row r of segment s is token 16 s + pi(r),
+// and the q operand of column c is zero outside segment c / 8, so column c
+// only sees tokens 16 (c / 8) + pi(r).  Lane group bit grp & 1 selects the
+// head-dimension half a lane supplies: MFMA i takes dimensions
+// (D/2) (grp & 1) + 8 i .. + 7, i.e. word i of the lane's K row.  With
+// pi(4g + j) = 8 (g & 1) + 4 (g >> 1) + j, lane (g, c) ends with the
+// scores of tokens 16 (c / 8) + 8 (g & 1) + 4 (g >> 1) + j (j = 0..3), and
+// the PV weights operand needs one permlane32 swap per register pair.
+//
+// PV (V rows as the A operand, as unpacked): the weights operand of column
+// c is zero outside the k-slots of its token half, so columns c and c + 8
+// accumulate the two halves of every step; pk_fold sums them at the end.
+// ---------------------------------------------------------------------------
+
+template <int D, int BS>
+struct PkBuf {
+  u32x4 k[D / 64];       // the lane's K row: D/2 head dimensions, D/16 octet words
+  VRaw<kI4> v[D / 16];   // as unpacked
+  f32x4 sk, sv;          // K and V scales of the lane's 4 score tokens
+};
+
+// A row r of a segment -> its token within the 16-token half.
+__device__ __forceinline__ int pk_row_token(int r) { return 8 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+// First token (within the step) of the 4 scores lane (grp, col) holds.
+__device__ __forceinline__ int pk_score_token(int grp, int col) {
+  return 16 * (col >> 3) + 8 * (grp & 1) + 4 * (grp >> 1);
+}
+
+// Head dimension of k-slot 0 of QK MFMA i for lane group grp.
+template <int D>
+__device__ __forceinline__ int pk_q_dim(int grp, int i) { return (D / 2) * (grp & 1) + 8 * i; }
+
+// The lane supplies the q operand of its column (else zeros).
+__device__ __forceinline__ bool pk_active(int grp, int col) { return (grp >> 1) == (col >> 3); }
+
+template <int D, int BS>
+struct PkOffsets {
+  uint32_t koff, soff;
+  bool kblk, sblk;  // second tile of the step (block size 16)
+  LaneOffsets<kI4, D, BS> v;
+  __device__ __forceinline__ PkOffsets(int grp, int col) : v(grp, col) {
+    const int ktok = 16 * (grp >> 1) + pk_row_token(col);  // the lane's K row token
+    const int chunk = (D / 64) * (grp & 1);                // first 32-dimension chunk
+    const int t0 = pk_score_token(grp, col);
+    if constexpr (BS == 16) {
+      koff = (uint32_t)((chunk * BS + (ktok & 15)) * 16);
+      kblk = ktok >= 16;
+      soff = (uint32_t)(Cfg<kI4, D, BS>::kCodeBytes + 4 * (t0 & 15));
+      sblk = t0 >= 16;
+    } else {
+      koff = (uint32_t)((chunk * BS + ktok) * 16);
+      kblk = false;
+      soff = (uint32_t)(Cfg<kI4, D, BS>::kCodeBytes + 4 * t0);
+      sblk = false;
+    }
+  }
+};
+
+template <int D, int BS>
+__device__ __forceinline__ void load_step_pk(PkBuf<D, BS>& sb, const char* kc, const char* vc, int64_t tile0,
+                                             int64_t tile1, const PkOffsets<D, BS>& lo) {
+  using C = Cfg<kI4, D, BS>;
+  const char* kp = kc + (lo.kblk ? tile1 : tile0) + lo.koff;
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) sb.k[j] = stream_load<u32x4>(kp + j * BS * 16);
+  const char* vp = vc + (lo.v.vblk ? tile1 : tile0) + lo.v.voff;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) sb.v[dt].w = stream_load<uint32_t>(vp + dt * 16 * C::kRowV);
+  const int64_t st = (lo.sblk ? tile1 : tile0) + lo.soff;
+  sb.sk = stream_load<f32x4>(kc + st);
+  sb.sv = stream_load<f32x4>(vc + st);
+}
+
+template <class Buf>
+__device__ __forceinline__ bf16x8 k_operand_pk(const Buf& sb, int i) {
+  return as_bf16x8(i4x8_biased_words(sb.k[i >> 2][i & 3]));
+}
+
+// One online-softmax step over the lane's 4 scores (q.k units, bias
+// removed, K scales not yet applied): as softmax_step, with the column
+// maximum taken over both column halves of a head, and the PV weights
+// operand zero outside the lane's token half.
+template <int NDT, class Buf>
+__device__ __forceinline__ bf16x8 softmax_step_pk(float* z, bool partial, const bool* ok, const Buf& sb,
+                                                  float c2, float& m_run, float& l_run, f32x4* acc,
+                                                  f32x4& accb, bool active) {
+  using M = OpMaxP;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) z[j] *= sb.sk[j];
+  if (partial) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = ok[j] ? z[j] : -INFINITY;
+  }
+  float mx = M::f(M::f(z[0], z[1]), M::f(z[2], z[3]));
+  mx = M::f(mx, dpp<0x128>(mx));  // row_ror:8 -> column c ^ 8, the same head
+  mx = xlane<M, 16, 32>(mx);
+  const float m_new = M::f(m_run, mx);
+  if (wave_any(m_new > m_run)) {
+    const float alpha = exp2_fast((m_run - m_new) * c2);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+    accb *= alpha;
+    m_run = m_new;
+  }
+  const float mc = m_run * c2;
+  float p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p[j] = exp2_fast(fmaf(z[j], c2, -mc));
+  if (partial) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = ok[j] ? p[j] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) l_run += p[j];
+  float pv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pv[j] = p[j] * sb.sv[j];
+  if (partial) {  // a scale outside the range may be anything, NaN included
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pv[j] = ok[j] ? pv[j] : 0.f;
+  }
+  uint32_t w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    bf16x2 t;
+    t[0] = (__bf16)pv[2 * i];
+    t[1] = (__bf16)pv[2 * i + 1];
+    w[i] = __builtin_bit_cast(uint32_t, t);
+  }
+  // lanes 0..31 keep their own pair and take that of lane + 32 (tokens + 4);
+  // lanes 32..63 take that of lane - 32 (tokens - 4) and keep their own
+  const auto x0 = __builtin_amdgcn_permlane32_swap(w[0], w[0], false, false);
+  const auto x1 = __builtin_amdgcn_permlane32_swap(w[1], w[1], false, false);
+  const u32x4 r = active ? u32x4{x0[0], x1[0], x0[1], x1[1]} : u32x4{0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Sum the two column halves of a head (columns c and c ^ 8).
+__device__ __forceinline__ float pk_fold(float x) { return x + dpp<0x128>(x); }
+
 }  // namespace mfma
 }  // namespace pa

@@ -106,7 +106,7 @@ def test_workload_decode(w):
     seqs = SAMPLE[w.name] or list(range(len(batch.context_lens)))
     print(f"[int4] decode {w.name} seqs={seqs[:6]}", flush=True)
     ref = oracle_decode_seqs(batch, seqs)
-    for p in (0, 512, -1):
+    for p in (0, 512, pk.PARTITION_AUTO, pk.PARTITION_AUTO_MERGED):
         out = gpu_decode(batch, p)
         _sync()
         compare(widen(out)[seqs], ref, "int4", f"{w.name} P={p}")
@@ -134,12 +134,13 @@ EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 511, 512, 513, 1025]
 
 
 @pytest.mark.parametrize("head_dim,block", [(128, 16), (128, 32), (64, 16), (64, 32)])
-@pytest.mark.parametrize("group", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 6, 8, 12, 16])
 def test_shapes_groups_and_edge_lengths(head_dim, block, group):
+    # groups up to 8 take the column-packed steps, larger ones the plain ones
     batch = _custom(head_dim, block, 2 * group, 2, EDGE_LENS)
     k_ref, v_ref = write_and_reference(batch)
     ref = oracle_decode_host(batch, k_ref, v_ref, range(len(EDGE_LENS)))
-    for p in (0, 32, 512, -1):
+    for p in (0, 32, 512, pk.PARTITION_AUTO, pk.PARTITION_AUTO_MERGED):
         out = gpu_decode(batch, p)
         _sync()
         compare(widen(out), ref, "int4", f"int4 d={head_dim} B={block} G={group} P={p}")
@@ -153,9 +154,10 @@ def test_balanced_split_cuts_and_empty_runs():
     batch = _custom(128, 16, 8, 2, lens)
     k_ref, v_ref = write_and_reference(batch)
     ref = oracle_decode_host(batch, k_ref, v_ref, range(len(lens)))
-    out = gpu_decode(batch, -1)
-    _sync()
-    compare(widen(out), ref, "int4", "int4 balanced cuts")
+    for p in (pk.PARTITION_AUTO, pk.PARTITION_AUTO_MERGED):
+        out = gpu_decode(batch, p)
+        _sync()
+        compare(widen(out), ref, "int4", f"int4 balanced cuts P={p}")
 
 
 def test_single_token_returns_its_value_row():

@@ -37,7 +37,9 @@ def _workload(cache, group):
 
 
 def _poison_blocks(batch, ids):
-    nan = 0x7F if batch.workload.cache_dtype.startswith("fp8") else float("nan")
+    # FP8: the E4M3 NaN code; INT4: all-ones bytes make every scale a NaN
+    cd = batch.workload.cache_dtype
+    nan = 0x7F if cd.startswith("fp8") else (0xFF if cd == "int4" else float("nan"))
     idx = torch.as_tensor(ids, dtype=torch.long, device=DEV)
     batch.k_pool[idx] = nan
     batch.v_pool[idx] = nan
@@ -64,6 +66,8 @@ SPLITS = [0, 64, "fixed-grid", pk.PARTITION_AUTO, pk.PARTITION_AUTO_MERGED]
     ("bf16", 4, "valu"),      # vector-unit kernels on a grouped batch
     ("f32", 2, None),         # float32 cache
     ("fp8_e4m3", 4, None),    # FP8 cache, matrix-core kernels
+    ("int4", 4, None),        # INT4 cache, column-packed steps
+    ("int4", 16, None),       # INT4 cache, plain steps
 ])
 @pytest.mark.parametrize("split", SPLITS, ids=str)
 def test_decode_cuts_the_context_at_the_row_end(monkeypatch, cache, group, force, split):
