@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
 
 SOURCES = ["pa_api.hip", "cache_write.hip", "decode_mfma.hip", "decode_valu.hip",
-           "decode_reduce.hip", "copy_blocks.hip", "prefill_mfma.hip", "stream_read.hip"]
+           "decode_reduce.hip", "copy_blocks.hip", "prefill_mfma.hip", "prefill_lds.hip", "stream_read.hip"]
 
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
@@ -38,7 +38,7 @@ FLAGS = [
 # accumulators to VGPRs and back on every 32-token step for the (rare) softmax
 # rescale, a third of the kernel's VALU work; in VGPR form they fit with no
 # spills.
-EXTRA_FLAGS = {"prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] for src in ("prefill_mfma.hip", "prefill_lds.hip")}
 
 
 def hipcc() -> str:

@@ -101,6 +101,14 @@ inline int prefill_query_tiles(int group, int max_query_len, int max_tiles) {
   return (max_query_len + rows_per_tile - 1) / rows_per_tile;
 }
 
+// Chunked prefill with query runs long enough to fill a workgroup of
+// kPrefillLdsWaves wavefronts of kPrefillLdsColumnTiles column tiles
+// (bf16 caches): the LDS-shared kernel (prefill_lds.hip).
+constexpr int kPrefillLdsWaves = 4;
+constexpr int kPrefillLdsColumnTiles = 2;
+bool prefill_uses_lds(Elem cache, int group, int max_query_len);
+hipError_t launch_prefill_lds(const PrefillArgs& p, int head_dim, int block_size, hipStream_t stream);
+
 struct WriteArgs {
   const void* k_new;
   const void* v_new;

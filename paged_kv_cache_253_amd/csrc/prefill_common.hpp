@@ -1,0 +1,209 @@
+// Shared pieces of the multi-query (chunked prefill / speculative verify)
+// kernels: the work-item map, the per-wavefront column tiles with their
+// QK / causal-mask / online-softmax / PV step, and a query tile's context
+// range.  The kernels themselves: prefill_mfma.hip (one wavefront per query
+// tile) and prefill_lds.hip (wavefronts of a workgroup sharing each step's
+// tiles through LDS).
+#pragma once
+
+#include "pa_device.hpp"
+#include "pa_internal.hpp"
+#include "pa_mfma.hpp"
+#include "pa_split.hpp"
+
+namespace pa {
+namespace prefill {
+
+using namespace mfma;
+
+// Work item -> (pair = b * Hkv + h, partition, tile-or-group): pair p runs
+// on XCD p % kXcds; its items (partition-major) take consecutive slots.
+struct Item {
+  int b, h, part, sub;
+  bool ok;
+};
+__device__ __forceinline__ Item locate_item(const DecodeArgs& a, int per_part) {
+  const int parts = a.partition ? a.max_parts : 1;
+  const int items = parts * per_part;
+  const int xcd = (int)(blockIdx.x % kXcds);
+  const int slot = (int)(blockIdx.x / kXcds);
+  const int pair = (slot / items) * kXcds + xcd;
+  Item it;
+  it.ok = pair < a.num_seqs * a.num_kv_heads;
+  const int inner = slot % items;
+  it.part = inner / per_part;
+  it.sub = inner % per_part;
+  it.h = pair % a.num_kv_heads;
+  it.b = pair / a.num_kv_heads;
+  return it;
+}
+
+// The NT column tiles of one wavefront: query rows i0 .. i1-1 of sequence b
+// (positions first_pos + i), KV head h; their q operands, running softmax
+// states and output accumulators.
+template <int CK, int D, int BS, int NT>
+struct Columns {
+  using C = Cfg<CK, D, BS>;
+  int pos[NT];
+  bool cvalid[NT];
+  size_t qrow[NT];                    // row of q / out (query token * Hq + query head)
+  bf16x8 qop[NT][C::kChunks];
+  f32x4 acc[NT][C::kDTiles];
+  f32x4 accb[NT];                     // INT4: column sums of the PV weights
+  float m_run[NT], l_run[NT], qbias[NT];
+
+  // columns: query token qi = i0 + c / G, head g = c % G
+  __device__ __forceinline__ void init(const DecodeArgs& a, int r0, int i0, int i1, int first_pos,
+                                       int h, int col, int grp) {
+    const int G = a.group;
+    const __bf16* qbase = reinterpret_cast<const __bf16*>(a.q);
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      const int c = ct * 16 + col;
+      const int qi = i0 + c / G;
+      cvalid[ct] = qi < i1;
+      pos[ct] = first_pos + qi;
+      qrow[ct] = (size_t)(r0 + (cvalid[ct] ? qi : i0)) * a.num_q_heads + (size_t)h * G + (c % G);
+#pragma unroll
+      for (int cc = 0; cc < C::kChunks; ++cc) {
+        if (cvalid[ct]) {
+          qop[ct][cc] = *reinterpret_cast<const bf16x8*>(qbase + qrow[ct] * D + q_dim<CK, D>(grp, cc));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qop[ct][cc][e] = (__bf16)0.0f;
+        }
+      }
+      m_run[ct] = -INFINITY;
+      l_run[ct] = 0.f;
+      accb[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      qbias[ct] = 0.f;
+      if constexpr (C::I4) qbias[ct] = q_bias<C::kChunks>(qop[ct]);
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt) acc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // One 32-token step starting at token `base`; tokens at or past t1 are
+  // outside this wavefront's range.
+  __device__ __forceinline__ void step(StepBuf<CK, D, BS>& sb, int base, int t1, int grp, float c2) {
+    f32x4 s0[NT], s1[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) { s0[ct] = qk_init<CK>(qbias[ct]); s1[ct] = s0[ct]; }
+#pragma unroll
+    for (int c = 0; c < C::kChunks; ++c) {
+      const bf16x8 ka = k_operand<CK>(sb, 0, c);
+      const bf16x8 kb = k_operand<CK>(sb, 1, c);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        s0[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[ct][c], s0[ct], 0, 0, 0);
+        s1[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qop[ct][c], s1[ct], 0, 0, 0);
+      }
+    }
+    if (base + kStep > t1) {  // PV k-slots of this lane: tokens 8*grp .. +7
+      const int vvalid = min(max(t1 - (base + 8 * grp), 0), 8);
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sb.v[dt], vvalid);
+    }
+    bf16x8 pop[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      // last token this column may see here, relative to the step
+      const int lim = min(t1 - 1, pos[ct]) - base;
+      float z[8] = {s0[ct][0], s0[ct][1], s0[ct][2], s0[ct][3],
+                    s1[ct][0], s1[ct][1], s1[ct][2], s1[ct][3]};
+      qk_scores<CK>(z, sb);
+      // the step is full for every real column unless one stops inside it
+      const bool partial = wave_any(cvalid[ct] && kStep - 1 > lim);
+      bool ok[8];
+      if (partial) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ok[i] = cvalid[ct] && qk_token(grp, i) <= lim;
+      }
+      pop[ct] = softmax_step<CK, C::kDTiles>(z, partial, ok, sb, c2, m_run[ct], l_run[ct], acc[ct],
+                                             accb[ct]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::kDTiles; ++dt) {
+      const bf16x8 vop = v_operand<CK>(sb.v[dt]);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+        acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[ct], acc[ct][dt], 0, 0, 0);
+    }
+    if constexpr (C::I4) {
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+        accb[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop[ct], accb[ct], 0, 0, 0);
+    }
+  }
+
+  // One row per valid column: the output, or the partition's softmax state.
+  __device__ __forceinline__ void finish(const DecodeArgs& a, int part, int grp, float c2,
+                                         float vscale) {
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      const float l_tot = xlane<OpSum, 16, 32>(l_run[ct]);
+      if (!cvalid[ct]) continue;
+      const float inv = l_tot > 0.f ? vscale / l_tot : 0.f;  // a row with no token writes zeros
+      if constexpr (C::I4) {  // remove the operand bias: 136 * sum_t p(t) s_v(t)
+#pragma unroll
+        for (int dt = 0; dt < C::kDTiles; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[ct][dt][r] = fmaf(-kI4Bias, accb[ct][0], acc[ct][dt][r]);
+      }
+      if (a.partition == 0) {
+        __bf16* o = reinterpret_cast<__bf16*>(a.out) + qrow[ct] * D;
+#pragma unroll
+        for (int dt = 0; dt < C::kDTiles; ++dt) {
+          bf16x2 lo, hi;
+          lo[0] = (__bf16)(acc[ct][dt][0] * inv); lo[1] = (__bf16)(acc[ct][dt][1] * inv);
+          hi[0] = (__bf16)(acc[ct][dt][2] * inv); hi[1] = (__bf16)(acc[ct][dt][3] * inv);
+          u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          *reinterpret_cast<u32x2*>(o + dt * 16 + grp * 4) = w;
+        }
+      } else {
+        const size_t row = qrow[ct] * a.max_parts + part;
+        float* o = a.part_out + row * D;
+#pragma unroll
+        for (int dt = 0; dt < C::kDTiles; ++dt)
+          *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = acc[ct][dt] * inv;
+        if (grp == 0) {
+          a.part_max[row] = m_run[ct] * (c2 * kLn2);  // natural units: scale * q.k
+          a.part_sum[row] = l_tot;
+        }
+      }
+    }
+  }
+};
+
+// Query rows and context range of query tile `tile` of sequence b: rows
+// i0 .. i1-1 (empty if i0 >= nq), tokens [t0, t1) of partition `part`.
+struct TileRange {
+  int r0, nq, i0, i1, first_pos, t0, t1, len;
+  int need;  // tokens the tile's rows reach, before the table row's end cuts them
+};
+__device__ __forceinline__ TileRange tile_range(const PrefillArgs& args, int b, int tile, int part,
+                                                int rows_per_tile) {
+  const DecodeArgs& a = args.d;
+  TileRange t;
+  t.len = clamp_len(a.context_lens[b], a.max_len);
+  t.r0 = args.query_start[b];
+  t.nq = max(args.query_start[b + 1] - t.r0, 0);
+  t.i0 = tile * rows_per_tile;
+  t.i1 = min(t.i0 + rows_per_tile, t.nq);
+  t.first_pos = t.len - t.nq;         // position of query token 0 (negative only if nq > len)
+  // tokens the tile needs: 0 .. position of its last query token, none at
+  // or past the end of the table row
+  t.need = min(t.first_pos + t.i1, t.len);
+  const int t_end = min(t.need, a.cap_len);
+  t.t0 = 0;
+  t.t1 = t_end;
+  if (a.partition > 0) {
+    t.t0 = part * a.partition;
+    t.t1 = min(t.t0 + a.partition, t_end);
+  }
+  return t;
+}
+
+
+}  // namespace prefill
+}  // namespace pa
