@@ -561,6 +561,10 @@ def bench_step(args) -> int:
     dev = "cuda"
     t_gen = time.perf_counter()
     batch = make_batch(w, device=dev)
+    if args.equal_lengths:  # same token total, n equal contexts (segment-count studies)
+        n = args.equal_lengths
+        total = int(batch.context_lens.sum())
+        batch = make_batch(w, device=dev, lens=np.full(n, max(1, total // n), np.int32))
     if args.unshare:
         from workloads import unshare
         batch = unshare(batch)
@@ -697,7 +701,8 @@ def bench_step(args) -> int:
         torch.cuda.synchronize()
         log("[bench] copy calibration: 3 x 1 GiB device copies done")
 
-    traffic = measured_traffic(w.name, part, 1)
+    # the counters were taken on the drawn batch only
+    traffic = None if (args.equal_lengths or args.unshare) else measured_traffic(w.name, part, 1)
     split = {0: "unsplit", -1: "balanced", -2: "balanced, merged in the decode launch"}.get(
         part, f"{part}-token partitions")
     result = {
@@ -715,7 +720,8 @@ def bench_step(args) -> int:
         "data": "synthetic",
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "context_tokens_per_s": round(dec["tokens"] / (ms_per_step * 1e-3), 1),
-        "config": {"workload": w.name + ("-unshared" if args.unshare else ""),
+        "config": {"workload": w.name + ("-unshared" if args.unshare else "")
+                   + (f"-equal-lengths-{args.equal_lengths}" if args.equal_lengths else ""),
                    "num_seqs": len(batch.context_lens),
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size,
@@ -801,6 +807,10 @@ def main() -> int:
     ap.add_argument("--separate-append", action="store_true",
                     help="step as pa_kv_cache_write + pa_decode (two launches) instead of "
                          "pa_decode_append")
+    ap.add_argument("--equal-lengths", type=int, default=0, metavar="N",
+                    help="replace the workload's drawn lengths by N equal contexts with the "
+                         "same token total (how the decode's time depends on the number of "
+                         "runs, not on the bytes)")
     ap.add_argument("--case", default="spec-verify-8b",
                     help="prefill shape: spec-verify-8b or chunked-prefill-8b")
     args = ap.parse_args()
