@@ -156,7 +156,8 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
 #pragma unroll
   for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 accb = {0.f, 0.f, 0.f, 0.f};  // INT4: column sums of the PV weights
-  float m_run = -INFINITY;  // running max of the scores (q.k units) of head `col`
+  float m_run = -INFINITY;  // reference max of the scores (q.k units) of head `col`
+  float m_top = -INFINITY;  // their true running max (lazy rescaling)
   float l_run = 0.f;        // this lane's share of sum 2^((z - m_run) * c2)
 
   auto compute = [&](StepBuf<CK, D, BS>& sb, int step) {
@@ -170,15 +171,14 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
     }
     float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     qk_scores<CK>(z, sb);
-    bool zok[8];  // partial step: token of score register i inside the range
+    // partial step: the lane's scores at token offsets <= zlim are in range
+    const int zlim = t1 - base - 1 - 4 * grp;
     if (partial) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) zok[i] = qk_token(grp, i) < t1 - base;
       const int vvalid = min(max(t1 - (base + 8 * grp), 0), 8);  // PV k-slots: tokens 8*grp .. +7
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sb.v[dt], vvalid);
     }
-    const bf16x8 pop = softmax_step<CK, C::kDTiles>(z, partial, zok, sb, c2, m_run, l_run, acc, accb);
+    const bf16x8 pop = softmax_step<CK, C::kDTiles>(z, partial, zlim, sb, c2, m_run, m_top, l_run, acc, accb);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<CK>(sb.v[dt]), pop, acc[dt], 0, 0, 0);
@@ -196,6 +196,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
   }
 
   // ---- epilogue -------------------------------------------------------------
+  lazy_settle<C::kDTiles>(m_run, m_top, c2, l_run, acc, accb);
   const float l_tot = xlane<OpSum, 16, 32>(l_run);
   const float inv = vscale / l_tot;
   if constexpr (C::I4) {  // remove the operand bias: 136 * sum_t p(t) s_v(t)
@@ -651,7 +652,7 @@ void decode_mfma_stream(const DecodeArgs a) {
   // ---- compute side ---------------------------------------------------------
   f32x4 acc[C::kDTiles];
   f32x4 accb = {0.f, 0.f, 0.f, 0.f};  // INT4: column sums of the PV weights
-  float m_run = -INFINITY, l_run = 0.f, c2 = 0.f;
+  float m_run = -INFINITY, m_top = -INFINITY, l_run = 0.f, c2 = 0.f;
 
   auto compute = [&](S& sl) {
     const bf16x8* qop;
@@ -705,6 +706,7 @@ void decode_mfma_stream(const DecodeArgs a) {
       for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       accb = f32x4{0.f, 0.f, 0.f, 0.f};
       m_run = -INFINITY;
+      m_top = -INFINITY;
       l_run = 0.f;
       float kscale = 1.0f;
       if constexpr (FP8) kscale = ((const_f32)a.k_scale)[sl.h];
@@ -722,13 +724,9 @@ void decode_mfma_stream(const DecodeArgs a) {
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand_pk(sl, i + 1), qop[i + 1], s1, 0, 0, 0);
       }
       float z[4] = {s0[0] + s1[0], s0[1] + s1[1], s0[2] + s1[2], s0[3] + s1[3]};
-      bool zok[4];  // partial step: token of score j inside the range
-      if (partial) {
-        const int t0 = pk_score_token(grp, col) - (sl.t1 - sl.base);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) zok[j] = t0 + j < 0;
-      }
-      pop = softmax_step_pk<C::kDTiles>(z, partial, zok, sl, c2, m_run, l_run, acc, accb, pk_on);
+      // partial step: score j (token pk_score_token + j) in range iff j <= zlim
+      const int zlim = sl.t1 - sl.base - 1 - pk_score_token(grp, col);
+      pop = softmax_step_pk<C::kDTiles>(z, partial, zlim, sl, c2, m_run, m_top, l_run, acc, accb, pk_on);
     } else {
       f32x4 s0 = qk_init<CK>(qbias), s1 = s0;
 #pragma unroll
@@ -738,16 +736,14 @@ void decode_mfma_stream(const DecodeArgs a) {
       }
       float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
       qk_scores<CK>(z, sl);
-      bool zok[8];  // partial step: token of score register i inside the range
+      const int n = sl.t1 - sl.base;
+      const int zlim = n - 1 - 4 * grp;  // partial step: offsets <= zlim in range
       if (partial) {
-        const int n = sl.t1 - sl.base;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) zok[i] = qk_token(grp, i) < n;
         const int vvalid = min(max(n - 8 * grp, 0), 8);
 #pragma unroll
         for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sl.v[dt], vvalid);
       }
-      pop = softmax_step<CK, C::kDTiles>(z, partial, zok, sl, c2, m_run, l_run, acc, accb);
+      pop = softmax_step<CK, C::kDTiles>(z, partial, zlim, sl, c2, m_run, m_top, l_run, acc, accb);
     }
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
@@ -755,6 +751,7 @@ void decode_mfma_stream(const DecodeArgs a) {
     if constexpr (C::I4) accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop, accb, 0, 0, 0);
 
     if (sl.flags & kLast) {
+      lazy_settle<C::kDTiles>(m_run, m_top, c2, l_run, acc, accb);
       float l_tot = xlane<OpSum, 16, 32>(l_run);
       if constexpr (PK) {  // columns c and c ^ 8 hold the two token halves of a head
         l_tot = pk_fold(l_tot);

@@ -203,8 +203,9 @@ __device__ __forceinline__ bf16x8 p_operand(const float* p) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// The token of QK result register i (0..7) of lane row grp, within a step.
-__device__ __forceinline__ int qk_token(int grp, int i) { return 4 * grp + (i & 3) + 16 * (i >> 2); }
+// QK result register i (0..7) of lane row grp holds token 4 * grp +
+// qk_token_off(i) of the step.
+__device__ __forceinline__ constexpr int qk_token_off(int i) { return (i & 3) + 16 * (i >> 2); }
 
 template <int CK>
 __device__ __forceinline__ bf16x8 v_operand(const VRaw<CK>& r) {
@@ -239,6 +240,31 @@ __device__ __forceinline__ void mask_v(VRaw<CK>& r, int valid) {  // valid = tok
 // softmax weight here can contribute (the largest weight of a row is 1).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lazy rescaling: the reference maximum m_run (and with it the
+// accumulators) moves only when a step's maximum exceeds it by more than
+// 2^kLazyLog2 in weight, so a weight can reach 2^kLazyLog2 = 256 instead of
+// 1 (a bf16 weight keeps its relative precision at any magnitude).  Most
+// steps then skip the rescale of the accumulators, which moved on a new
+// maximum of any of the wavefront's columns.  The true running maximum
+// m_top is kept beside it, and lazy_settle moves m_run to it once per
+// range, so a range's state (maximum, sum, output) is the plain one.
+constexpr float kLazyLog2 = 8.0f;
+
+template <int NDT>
+__device__ __forceinline__ void lazy_settle(float& m_run, float m_top, float c2, float& l_run,
+                                            f32x4* acc, f32x4& accb) {
+  if (wave_any(m_top > m_run)) {
+    const float alpha = exp2_fast((m_run - m_top) * c2);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+    accb *= alpha;
+    m_run = m_top;
+  }
+}
+
+
+
 // Initial QK accumulator: zero, or for INT4 minus the operand bias (136 *
 // the sum of the lane column's q, see q_bias), so that the MFMA result is
 // already sum_d q_d code_d.
@@ -264,21 +290,26 @@ __device__ __forceinline__ void qk_scores(float* z, const Buf& sb) {
 // column, rescale the accumulators when the max grows, and return the PV
 // weights operand.  c2 = softmax scale * log2(e) (times an FP8 K scale), so
 // a weight is 2^(z*c2 - m*c2).  Only a partial step (one holding tokens
-// outside the range) reads ok[]; every token of a full step is in range.
-// INT4: the weights carry each token's V scale, and accb their column sums.
+// outside the range) reads lim: score register i is kept iff its token's
+// offset from the lane's first token, qk_token_off(i), is at most lim (a
+// lane that keeps nothing passes -1).  The comparisons are made where they
+// are used, so a full step carries no mask.  INT4: the weights carry each
+// token's V scale, and accb their column sums.
 template <int CK, int NDT, class Buf>
-__device__ __forceinline__ bf16x8 softmax_step(float* z, bool partial, const bool* ok, const Buf& sb,
-                                               float c2, float& m_run, float& l_run, f32x4* acc,
-                                               f32x4& accb) {
+__device__ __forceinline__ bf16x8 softmax_step(float* z, bool partial, int lim, const Buf& sb,
+                                               float c2, float& m_run, float& m_top, float& l_run,
+                                               f32x4* acc, f32x4& accb) {
   if (partial) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = ok[i] ? z[i] : -INFINITY;
+    for (int i = 0; i < 8; ++i) z[i] = qk_token_off(i) <= lim ? z[i] : -INFINITY;
   }
   using M = OpMaxP;
   float mx = M::f(M::f(M::f(z[0], z[1]), M::f(z[2], z[3])), M::f(M::f(z[4], z[5]), M::f(z[6], z[7])));
   mx = xlane<M, 16, 32>(mx);
   const float m_new = M::f(m_run, mx);
-  if (wave_any(m_new > m_run)) {
+  m_top = M::f(m_top, mx);
+  // (a -inf running max always moves: inf * c2 is inf, or NaN at c2 = 0)
+  if (wave_any(m_new > m_run && !((m_new - m_run) * c2 <= kLazyLog2))) {
     const float alpha = exp2_fast((m_run - m_new) * c2);
     l_run *= alpha;
 #pragma unroll
@@ -292,7 +323,7 @@ __device__ __forceinline__ bf16x8 softmax_step(float* z, bool partial, const boo
   for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(z[i], c2, -mc));
   if (partial) {  // all-masked rows have m = -inf: select, not rely on exp2(-inf)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = ok[i] ? p[i] : 0.f;
+    for (int i = 0; i < 8; ++i) p[i] = qk_token_off(i) <= lim ? p[i] : 0.f;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) l_run += p[i];
@@ -302,7 +333,7 @@ __device__ __forceinline__ bf16x8 softmax_step(float* z, bool partial, const boo
     for (int i = 0; i < 8; ++i) pv[i] = p[i] * sb.ts.v[i >> 2][i & 3];
     if (partial) {  // a scale outside the range may be anything, NaN included
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] = ok[i] ? pv[i] : 0.f;
+      for (int i = 0; i < 8; ++i) pv[i] = qk_token_off(i) <= lim ? pv[i] : 0.f;
     }
     return p_operand(pv);
   } else {
@@ -420,23 +451,26 @@ __device__ __forceinline__ bf16x8 k_operand_pk(const Buf& sb, int i) {
 // One online-softmax step over the lane's 4 scores (q.k units, bias
 // removed, K scales not yet applied): as softmax_step, with the column
 // maximum taken over both column halves of a head, and the PV weights
-// operand zero outside the lane's token half.
+// operand zero outside the lane's token half.  Partial step: score j is
+// kept iff j <= lim.
 template <int NDT, class Buf>
-__device__ __forceinline__ bf16x8 softmax_step_pk(float* z, bool partial, const bool* ok, const Buf& sb,
-                                                  float c2, float& m_run, float& l_run, f32x4* acc,
-                                                  f32x4& accb, bool active) {
+__device__ __forceinline__ bf16x8 softmax_step_pk(float* z, bool partial, int lim, const Buf& sb,
+                                                  float c2, float& m_run, float& m_top, float& l_run,
+                                                  f32x4* acc, f32x4& accb, bool active) {
   using M = OpMaxP;
 #pragma unroll
   for (int j = 0; j < 4; ++j) z[j] *= sb.sk[j];
   if (partial) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) z[j] = ok[j] ? z[j] : -INFINITY;
+    for (int j = 0; j < 4; ++j) z[j] = j <= lim ? z[j] : -INFINITY;
   }
   float mx = M::f(M::f(z[0], z[1]), M::f(z[2], z[3]));
   mx = M::f(mx, dpp<0x128>(mx));  // row_ror:8 -> column c ^ 8, the same head
   mx = xlane<M, 16, 32>(mx);
   const float m_new = M::f(m_run, mx);
-  if (wave_any(m_new > m_run)) {
+  m_top = M::f(m_top, mx);
+  // (a -inf running max always moves: inf * c2 is inf, or NaN at c2 = 0)
+  if (wave_any(m_new > m_run && !((m_new - m_run) * c2 <= kLazyLog2))) {
     const float alpha = exp2_fast((m_run - m_new) * c2);
     l_run *= alpha;
 #pragma unroll
@@ -450,7 +484,7 @@ __device__ __forceinline__ bf16x8 softmax_step_pk(float* z, bool partial, const 
   for (int j = 0; j < 4; ++j) p[j] = exp2_fast(fmaf(z[j], c2, -mc));
   if (partial) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = ok[j] ? p[j] : 0.f;
+    for (int j = 0; j < 4; ++j) p[j] = j <= lim ? p[j] : 0.f;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) l_run += p[j];
@@ -459,7 +493,7 @@ __device__ __forceinline__ bf16x8 softmax_step_pk(float* z, bool partial, const 
   for (int j = 0; j < 4; ++j) pv[j] = p[j] * sb.sv[j];
   if (partial) {  // a scale outside the range may be anything, NaN included
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pv[j] = ok[j] ? pv[j] : 0.f;
+    for (int j = 0; j < 4; ++j) pv[j] = j <= lim ? pv[j] : 0.f;
   }
   uint32_t w[2];
 #pragma unroll

@@ -50,7 +50,7 @@ struct Columns {
   bf16x8 qop[NT][C::kChunks];
   f32x4 acc[NT][C::kDTiles];
   f32x4 accb[NT];                     // INT4: column sums of the PV weights
-  float m_run[NT], l_run[NT], qbias[NT];
+  float m_run[NT], m_top[NT], l_run[NT], qbias[NT];
 
   // columns: query token qi = i0 + c / G, head g = c % G
   __device__ __forceinline__ void init(const DecodeArgs& a, int r0, int i0, int i1, int first_pos,
@@ -74,6 +74,7 @@ struct Columns {
         }
       }
       m_run[ct] = -INFINITY;
+      m_top[ct] = -INFINITY;
       l_run[ct] = 0.f;
       accb[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       qbias[ct] = 0.f;
@@ -114,12 +115,9 @@ struct Columns {
       qk_scores<CK>(z, sb);
       // the step is full for every real column unless one stops inside it
       const bool partial = wave_any(cvalid[ct] && kStep - 1 > lim);
-      bool ok[8];
-      if (partial) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ok[i] = cvalid[ct] && qk_token(grp, i) <= lim;
-      }
-      pop[ct] = softmax_step<CK, C::kDTiles>(z, partial, ok, sb, c2, m_run[ct], l_run[ct], acc[ct],
+      // kept: offsets from the lane's first token up to this (none for a padding column)
+      const int zlim = cvalid[ct] ? lim - 4 * grp : -1;
+      pop[ct] = softmax_step<CK, C::kDTiles>(z, partial, zlim, sb, c2, m_run[ct], m_top[ct], l_run[ct], acc[ct],
                                              accb[ct]);
     }
 #pragma unroll
@@ -141,6 +139,7 @@ struct Columns {
                                          float vscale) {
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
+      lazy_settle<C::kDTiles>(m_run[ct], m_top[ct], c2, l_run[ct], acc[ct], accb[ct]);
       const float l_tot = xlane<OpSum, 16, 32>(l_run[ct]);
       if (!cvalid[ct]) continue;
       const float inv = l_tot > 0.f ? vscale / l_tot : 0.f;  // a row with no token writes zeros
