@@ -317,14 +317,13 @@ __device__ __forceinline__ bf16x8 softmax_step(float* z, bool partial, int lim, 
     if constexpr (CK == kI4) accb *= alpha;
     m_run = m_new;
   }
-  const float mc = m_run * c2;
+  // a masked score is -inf, so its weight is exp2(-inf) = 0 -- also in a
+  // column that has seen only masked scores, whose running max is -inf
+  // (its offset is taken as 0 there, keeping the exponent -inf, not NaN)
+  const float mc = m_run == -INFINITY ? 0.f : m_run * c2;
   float p[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(z[i], c2, -mc));
-  if (partial) {  // all-masked rows have m = -inf: select, not rely on exp2(-inf)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = qk_token_off(i) <= lim ? p[i] : 0.f;
-  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) l_run += p[i];
   if constexpr (CK == kI4) {
@@ -478,14 +477,10 @@ __device__ __forceinline__ bf16x8 softmax_step_pk(float* z, bool partial, int li
     accb *= alpha;
     m_run = m_new;
   }
-  const float mc = m_run * c2;
+  const float mc = m_run == -INFINITY ? 0.f : m_run * c2;  // as softmax_step
   float p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) p[j] = exp2_fast(fmaf(z[j], c2, -mc));
-  if (partial) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = j <= lim ? p[j] : 0.f;
-  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) l_run += p[j];
   float pv[4];
