@@ -41,28 +41,52 @@ __device__ __forceinline__ Item locate_item(const DecodeArgs& a, int per_part) {
 // The NT column tiles of one wavefront: query rows i0 .. i1-1 of sequence b
 // (positions first_pos + i), KV head h; their q operands, running softmax
 // states and output accumulators.
+//
+// The online softmax here is the decode's (lazy rescaling, masks from a
+// per-lane token limit) with less work per step, as these kernels issue
+// many steps per byte read:
+// * Each lane keeps the running maximum of its own scores (m_lane) and
+//   compares it with the column's rescale threshold thr = m_run + 8 / c2,
+//   so the cross-lane maximum is taken only when some weight would exceed
+//   2^8, i.e. on a rescale, and once per range in finish.
+// * The weights' offset mc = m_run * c2 and the threshold change only on a
+//   rescale.
+// * bf16 and FP8: the exp-sum of a column comes from the matrix cores, as
+//   the product of a ones operand with the step's weights operand (so it
+//   sums the same bf16 weights the PV product does); INT4, whose weights
+//   operand carries the V scales, sums its weights on the vector unit.
+// * Whether a step needs masks is decided per column tile from scalars: the
+//   smallest position of its valid rows against the step's last token.
 template <int CK, int D, int BS, int NT>
 struct Columns {
   using C = Cfg<CK, D, BS>;
   int pos[NT];
+  int pos_min[NT];                    // wave-uniform: smallest valid position (INT_MAX: no valid row)
   bool cvalid[NT];
   size_t qrow[NT];                    // row of q / out (query token * Hq + query head)
   bf16x8 qop[NT][C::kChunks];
   f32x4 acc[NT][C::kDTiles];
+  f32x4 accl[NT];                     // bf16 / FP8: exp-sums of the columns (every register)
   f32x4 accb[NT];                     // INT4: column sums of the PV weights
-  float m_run[NT], m_top[NT], l_run[NT], qbias[NT];
+  float m_run[NT], m_lane[NT], thr[NT], mc[NT], l_run[NT], qbias[NT];
+  float lazy_span;                    // kLazyLog2 / c2: the score span below a weight of 2^8
 
   // columns: query token qi = i0 + c / G, head g = c % G
   __device__ __forceinline__ void init(const DecodeArgs& a, int r0, int i0, int i1, int first_pos,
-                                       int h, int col, int grp) {
+                                       int h, int col, int grp, float c2) {
     const int G = a.group;
     const __bf16* qbase = reinterpret_cast<const __bf16*>(a.q);
+    lazy_span = kLazyLog2 / c2;
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
       const int c = ct * 16 + col;
       const int qi = i0 + c / G;
       cvalid[ct] = qi < i1;
       pos[ct] = first_pos + qi;
+      // the tile's first column holds its smallest position
+      const int qi0 = __builtin_amdgcn_readfirstlane(i0 + (ct * 16) / G);
+      pos_min[ct] = qi0 < __builtin_amdgcn_readfirstlane(i1)
+                        ? __builtin_amdgcn_readfirstlane(first_pos) + qi0 : INT_MAX;
       qrow[ct] = (size_t)(r0 + (cvalid[ct] ? qi : i0)) * a.num_q_heads + (size_t)h * G + (c % G);
 #pragma unroll
       for (int cc = 0; cc < C::kChunks; ++cc) {
@@ -74,13 +98,36 @@ struct Columns {
         }
       }
       m_run[ct] = -INFINITY;
-      m_top[ct] = -INFINITY;
+      m_lane[ct] = -INFINITY;
+      thr[ct] = -INFINITY;
+      mc[ct] = 0.f;
       l_run[ct] = 0.f;
+      accl[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       accb[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       qbias[ct] = 0.f;
       if constexpr (C::I4) qbias[ct] = q_bias<C::kChunks>(qop[ct]);
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) acc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // Move the reference maximum of tile ct to the column maximum so far
+  // (every lane calls; columns whose maximum has not grown keep theirs).
+  __device__ __forceinline__ void rescale(int ct, float c2) {
+    const float m_new = xlane<OpMaxP, 16, 32>(m_lane[ct]);
+    if (m_new > m_run[ct]) {  // (m_run -inf: alpha 0, the accumulators are 0 anyway)
+      const float alpha = exp2_fast((m_run[ct] - m_new) * c2);
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt) acc[ct][dt] *= alpha;
+      if constexpr (C::I4) {
+        accb[ct] *= alpha;
+        l_run[ct] *= alpha;
+      } else {
+        accl[ct] *= alpha;
+      }
+      m_run[ct] = m_new;
+      mc[ct] = m_new * c2;
+      thr[ct] = m_new + lazy_span;
     }
   }
 
@@ -108,17 +155,36 @@ struct Columns {
     bf16x8 pop[NT];
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
-      // last token this column may see here, relative to the step
-      const int lim = min(t1 - 1, pos[ct]) - base;
       float z[8] = {s0[ct][0], s0[ct][1], s0[ct][2], s0[ct][3],
                     s1[ct][0], s1[ct][1], s1[ct][2], s1[ct][3]};
       qk_scores<CK>(z, sb);
-      // the step is full for every real column unless one stops inside it
-      const bool partial = wave_any(cvalid[ct] && kStep - 1 > lim);
-      // kept: offsets from the lane's first token up to this (none for a padding column)
-      const int zlim = cvalid[ct] ? lim - 4 * grp : -1;
-      pop[ct] = softmax_step<CK, C::kDTiles>(z, partial, zlim, sb, c2, m_run[ct], m_top[ct], l_run[ct], acc[ct],
-                                             accb[ct]);
+      // a valid row stops inside the step (its position, or the range end)
+      const bool partial = min(t1 - 1, pos_min[ct]) < base + kStep - 1;
+      // kept: offsets from the lane's first token up to the last token this
+      // column may see (none for a padding column)
+      const int zlim = cvalid[ct] ? min(t1 - 1, pos[ct]) - base - 4 * grp : -1;
+      if (partial) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z[i] = qk_token_off(i) <= zlim ? z[i] : -INFINITY;
+      }
+      using M = OpMaxP;
+      m_lane[ct] = M::f(M::f(M::f(z[0], z[1]), M::f(z[2], z[3])),
+                        M::f(M::f(z[4], z[5]), M::f(M::f(z[6], z[7]), m_lane[ct])));
+      if (wave_any(m_lane[ct] > thr[ct])) rescale(ct, c2);
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(z[i], c2, -mc[ct]));
+      if constexpr (C::I4) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) l_run[ct] += p[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] *= sb.ts.v[i >> 2][i & 3];
+        if (partial) {  // a scale outside the range may be anything, NaN included
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p[i] = qk_token_off(i) <= zlim ? p[i] : 0.f;
+        }
+      }
+      pop[ct] = p_operand(p);
     }
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt) {
@@ -127,10 +193,12 @@ struct Columns {
       for (int ct = 0; ct < NT; ++ct)
         acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[ct], acc[ct][dt], 0, 0, 0);
     }
-    if constexpr (C::I4) {
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
+    for (int ct = 0; ct < NT; ++ct) {
+      if constexpr (C::I4)
         accb[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop[ct], accb[ct], 0, 0, 0);
+      else
+        accl[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop[ct], accl[ct], 0, 0, 0);
     }
   }
 
@@ -139,8 +207,9 @@ struct Columns {
                                          float vscale) {
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
-      lazy_settle<C::kDTiles>(m_run[ct], m_top[ct], c2, l_run[ct], acc[ct], accb[ct]);
-      const float l_tot = xlane<OpSum, 16, 32>(l_run[ct]);
+      // the range's state at its true maximum (the plain softmax state)
+      if (wave_any(m_lane[ct] > m_run[ct])) rescale(ct, c2);
+      const float l_tot = C::I4 ? xlane<OpSum, 16, 32>(l_run[ct]) : accl[ct][0];
       if (!cvalid[ct]) continue;
       const float inv = l_tot > 0.f ? vscale / l_tot : 0.f;  // a row with no token writes zeros
       if constexpr (C::I4) {  // remove the operand bias: 136 * sum_t p(t) s_v(t)

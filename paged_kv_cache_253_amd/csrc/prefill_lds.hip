@@ -67,11 +67,11 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
   const int wi0 = tr.i0 + wave * rows_w;
   const int wi1 = min(wi0 + rows_w, tr.i1);
   const bool mine = wi0 < wi1;
+  const float c2 = a.scale * kLog2e;
   Columns<CK, D, BS, NT> cols;
-  if (mine) cols.init(a, tr.r0, wi0, wi1, tr.first_pos, h, col, grp);
+  if (mine) cols.init(a, tr.r0, wi0, wi1, tr.first_pos, h, col, grp, c2);
   // last token any of this wavefront's rows sees
   const int wlast = mine ? min(tr.first_pos + wi1 - 1, t1 - 1) : -1;
-  const float c2 = a.scale * kLog2e;
 
   __shared__ LdsStep<D> lds[2];
   if (t0 < t1) {

@@ -54,11 +54,11 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
   if (a.partition > 0 && tr.t0 >= tr.need) return;
   const int t0 = tr.t0, t1 = tr.t1;
 
-  Columns<CK, D, BS, NT> cols;
-  cols.init(a, tr.r0, tr.i0, tr.i1, tr.first_pos, h, col, grp);
   float kscale = 1.0f, vscale = 1.0f;
   if constexpr (FP8) { kscale = a.k_scale[h]; vscale = a.v_scale[h]; }
   const float c2 = a.scale * kscale * kLog2e;  // q.k -> log2 units
+  Columns<CK, D, BS, NT> cols;
+  cols.init(a, tr.r0, tr.i0, tr.i1, tr.first_pos, h, col, grp, c2);
 
   if (t0 < t1) {
     const LaneOffsets<CK, D, BS> lo(grp, col);
