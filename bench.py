@@ -283,11 +283,9 @@ def bench_prefill(args) -> int:
     out = torch.empty_like(q)
     part = args.partition
     if part is None:  # the binding's own choice, made once and reused
-        hkv = w.num_kv_heads
-        rows = max(1, 16 * (2 if w.head_dim == 128 and w.cache_dtype in ("bf16", "int4") else 4)
-                   // (w.num_q_heads // hkv))
-        tiles = -(-int(qlens.max()) // rows)
-        part = 0 if len(lens) * hkv * tiles >= 1024 or batch.max_context_len <= 1024 else 512
+        part = pk.prefill_partition(len(lens), w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                    int(qlens.max()), batch.max_context_len,
+                                    w.head_dim == 128 and w.cache_dtype in ("bf16", "int4"), dev)
     ws = pk.new_workspace(int(qs[-1]), w.num_q_heads, w.num_kv_heads, w.head_dim,
                           batch.max_context_len, part, dev) if part else None
 
