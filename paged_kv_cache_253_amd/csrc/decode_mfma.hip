@@ -156,9 +156,8 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
 #pragma unroll
   for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 accb = {0.f, 0.f, 0.f, 0.f};  // INT4: column sums of the PV weights
-  float m_run = -INFINITY;  // reference max of the scores (q.k units) of head `col`
-  float m_top = -INFINITY;  // their true running max (lazy rescaling)
-  float l_run = 0.f;        // this lane's share of sum 2^((z - m_run) * c2)
+  LaneSoftmax st;  // online softmax of head `col` (lazy rescaling)
+  st.reset(c2);
 
   auto compute = [&](StepBuf<CK, D, BS>& sb, int step) {
     const int base = t0 + step * kStep;
@@ -178,7 +177,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sb.v[dt], vvalid);
     }
-    const bf16x8 pop = softmax_step<CK, C::kDTiles>(z, partial, zlim, sb, c2, m_run, m_top, l_run, acc, accb);
+    const bf16x8 pop = softmax_step<CK, C::kDTiles>(z, partial, zlim, sb, c2, st, acc, accb);
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand<CK>(sb.v[dt]), pop, acc[dt], 0, 0, 0);
@@ -196,8 +195,8 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
   }
 
   // ---- epilogue -------------------------------------------------------------
-  lazy_settle<C::kDTiles>(m_run, m_top, c2, l_run, acc, accb);
-  const float l_tot = xlane<OpSum, 16, 32>(l_run);
+  lazy_settle<C::kDTiles, false>(st, c2, acc, accb);
+  const float l_tot = xlane<OpSum, 16, 32>(st.l_run);
   const float inv = vscale / l_tot;
   if constexpr (C::I4) {  // remove the operand bias: 136 * sum_t p(t) s_v(t)
 #pragma unroll
@@ -223,7 +222,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
     for (int dt = 0; dt < C::kDTiles; ++dt)
       *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = acc[dt] * inv;
     if (grp == 0) {
-      a.part_max[row] = m_run * (c2 * kLn2);  // natural units: scale * q.k
+      a.part_max[row] = st.m_run * (c2 * kLn2);  // natural units: scale * q.k
       a.part_sum[row] = l_tot;
     }
   }
@@ -652,7 +651,8 @@ void decode_mfma_stream(const DecodeArgs a) {
   // ---- compute side ---------------------------------------------------------
   f32x4 acc[C::kDTiles];
   f32x4 accb = {0.f, 0.f, 0.f, 0.f};  // INT4: column sums of the PV weights
-  float m_run = -INFINITY, m_top = -INFINITY, l_run = 0.f, c2 = 0.f;
+  LaneSoftmax st;
+  float c2 = 0.f;
 
   auto compute = [&](S& sl) {
     const bf16x8* qop;
@@ -705,12 +705,10 @@ void decode_mfma_stream(const DecodeArgs a) {
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       accb = f32x4{0.f, 0.f, 0.f, 0.f};
-      m_run = -INFINITY;
-      m_top = -INFINITY;
-      l_run = 0.f;
       float kscale = 1.0f;
       if constexpr (FP8) kscale = ((const_f32)a.k_scale)[sl.h];
       c2 = a.scale * kscale * kLog2e;
+      st.reset(c2);
       if constexpr (C::I4 && !QSEG) qbias = q_bias<C::kChunks>(qop);
     }
     const bool partial = sl.base + kStepTokens > sl.t1;
@@ -726,7 +724,7 @@ void decode_mfma_stream(const DecodeArgs a) {
       float z[4] = {s0[0] + s1[0], s0[1] + s1[1], s0[2] + s1[2], s0[3] + s1[3]};
       // partial step: score j (token pk_score_token + j) in range iff j <= zlim
       const int zlim = sl.t1 - sl.base - 1 - pk_score_token(grp, col);
-      pop = softmax_step_pk<C::kDTiles>(z, partial, zlim, sl, c2, m_run, m_top, l_run, acc, accb, pk_on);
+      pop = softmax_step_pk<C::kDTiles>(z, partial, zlim, sl, c2, st, acc, accb, pk_on);
     } else {
       f32x4 s0 = qk_init<CK>(qbias), s1 = s0;
 #pragma unroll
@@ -743,7 +741,7 @@ void decode_mfma_stream(const DecodeArgs a) {
 #pragma unroll
         for (int dt = 0; dt < C::kDTiles; ++dt) mask_v<CK>(sl.v[dt], vvalid);
       }
-      pop = softmax_step<CK, C::kDTiles>(z, partial, zlim, sl, c2, m_run, m_top, l_run, acc, accb);
+      pop = softmax_step<CK, C::kDTiles>(z, partial, zlim, sl, c2, st, acc, accb);
     }
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
@@ -751,8 +749,8 @@ void decode_mfma_stream(const DecodeArgs a) {
     if constexpr (C::I4) accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop, accb, 0, 0, 0);
 
     if (sl.flags & kLast) {
-      lazy_settle<C::kDTiles>(m_run, m_top, c2, l_run, acc, accb);
-      float l_tot = xlane<OpSum, 16, 32>(l_run);
+      lazy_settle<C::kDTiles, PK>(st, c2, acc, accb);
+      float l_tot = xlane<OpSum, 16, 32>(st.l_run);
       if constexpr (PK) {  // columns c and c ^ 8 hold the two token halves of a head
         l_tot = pk_fold(l_tot);
 #pragma unroll
@@ -778,7 +776,7 @@ void decode_mfma_stream(const DecodeArgs a) {
         for (int dt = 0; dt < C::kDTiles; ++dt)
           *reinterpret_cast<f32x4*>(row + dt * 16 + grp * 4) = acc[dt] * inv;
         if (!(sl.flags & kFinal) && grp == 0) {
-          dst[G * kStageRow + col] = m_run * (c2 * kLn2);  // natural units: scale * q.k
+          dst[G * kStageRow + col] = st.m_run * (c2 * kLn2);  // natural units: scale * q.k
           dst[G * kStageRow + G + col] = l_tot;
         }
       }

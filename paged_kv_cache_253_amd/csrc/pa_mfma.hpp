@@ -241,29 +241,63 @@ __device__ __forceinline__ void mask_v(VRaw<CK>& r, int valid) {  // valid = tok
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Lazy rescaling: the reference maximum m_run (and with it the
-// accumulators) moves only when a step's maximum exceeds it by more than
-// 2^kLazyLog2 in weight, so a weight can reach 2^kLazyLog2 = 256 instead of
-// 1 (a bf16 weight keeps its relative precision at any magnitude).  Most
-// steps then skip the rescale of the accumulators, which moved on a new
-// maximum of any of the wavefront's columns.  The true running maximum
-// m_top is kept beside it, and lazy_settle moves m_run to it once per
-// range, so a range's state (maximum, sum, output) is the plain one.
+// accumulators) moves only when a score exceeds it by more than kLazyLog2
+// in log2 units, so a weight can reach 2^kLazyLog2 = 256 instead of 1 (a
+// bf16 weight keeps its relative precision at any magnitude).  Each lane
+// keeps the running maximum of its own scores (m_lane) and compares it with
+// the column's threshold thr = m_run + kLazyLog2 / c2, so the cross-lane
+// maximum is taken only when some column moves, and once at the end of a
+// range (settle), which leaves the range's state (maximum, sum, output) the
+// plain one.  The weights' offset mc = m_run * c2 and thr change only when
+// m_run does.
 constexpr float kLazyLog2 = 8.0f;
 
-template <int NDT>
-__device__ __forceinline__ void lazy_settle(float& m_run, float m_top, float c2, float& l_run,
-                                            f32x4* acc, f32x4& accb) {
-  if (wave_any(m_top > m_run)) {
-    const float alpha = exp2_fast((m_run - m_top) * c2);
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-    accb *= alpha;
-    m_run = m_top;
+struct LaneSoftmax {
+  float m_run;   // reference maximum of the column's scores (q.k units)
+  float m_lane;  // the largest score this lane has seen
+  float thr;     // m_run + span: a score above it would weigh more than 2^kLazyLog2
+  float mc;      // m_run * c2 (0 while m_run is -inf: every weight is then 0)
+  float span;    // kLazyLog2 / c2
+  float l_run;   // this lane's share of sum 2^((z - m_run) * c2)
+
+  __device__ __forceinline__ void reset(float c2) {
+    m_run = m_lane = thr = -INFINITY;
+    mc = 0.f;
+    l_run = 0.f;
+    span = kLazyLog2 * __builtin_amdgcn_rcpf(c2);
   }
+
+  // Move m_run to the column maximum m_col (this lane's column; all lanes
+  // call), rescaling what has been accumulated.
+  template <int NDT, bool SUMS>
+  __device__ __forceinline__ void move_to(float m_col, float c2, f32x4* acc, f32x4& accb) {
+    if (m_col > m_run) {  // (m_run -inf: alpha 0, and nothing has been accumulated)
+      const float alpha = exp2_fast((m_run - m_col) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+      if constexpr (SUMS) accb *= alpha;
+      m_run = m_col;
+      mc = m_col * c2;
+      thr = m_col + span;
+    }
+  }
+};
+
+// The column maximum of m_lane: over the lane groups holding one column
+// (and, packed, over the two column halves of a head).
+template <bool PK>
+__device__ __forceinline__ float column_max(float m_lane) {
+  if constexpr (PK) m_lane = OpMaxP::f(m_lane, dpp<0x128>(m_lane));  // row_ror:8 -> column c ^ 8
+  return xlane<OpMaxP, 16, 32>(m_lane);
 }
 
-
+// End of a range: the state at its true maximum.
+template <int NDT, bool PK>
+__device__ __forceinline__ void lazy_settle(LaneSoftmax& st, float c2, f32x4* acc, f32x4& accb) {
+  const float m_col = column_max<PK>(st.m_lane);
+  if (wave_any(m_col > st.m_run)) st.move_to<NDT, true>(m_col, c2, acc, accb);
+}
 
 // Initial QK accumulator: zero, or for INT4 minus the operand bias (136 *
 // the sum of the lane column's q, see q_bias), so that the MFMA result is
@@ -286,9 +320,9 @@ __device__ __forceinline__ void qk_scores(float* z, const Buf& sb) {
 }
 
 // One online-softmax step over the 8 scores a lane holds (QK register
-// order, q.k units): update the running max m and sum l of the lane's
-// column, rescale the accumulators when the max grows, and return the PV
-// weights operand.  c2 = softmax scale * log2(e) (times an FP8 K scale), so
+// order, q.k units): update the lane's running maximum and sum, rescale the
+// accumulators when a column's reference maximum moves (LaneSoftmax), and
+// return the PV weights operand.  c2 = softmax scale * log2(e) (times an FP8 K scale), so
 // a weight is 2^(z*c2 - m*c2).  Only a partial step (one holding tokens
 // outside the range) reads lim: score register i is kept iff its token's
 // offset from the lane's first token, qk_token_off(i), is at most lim (a
@@ -297,35 +331,22 @@ __device__ __forceinline__ void qk_scores(float* z, const Buf& sb) {
 // token's V scale, and accb their column sums.
 template <int CK, int NDT, class Buf>
 __device__ __forceinline__ bf16x8 softmax_step(float* z, bool partial, int lim, const Buf& sb,
-                                               float c2, float& m_run, float& m_top, float& l_run,
-                                               f32x4* acc, f32x4& accb) {
+                                               float c2, LaneSoftmax& st, f32x4* acc, f32x4& accb) {
   if (partial) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) z[i] = qk_token_off(i) <= lim ? z[i] : -INFINITY;
   }
   using M = OpMaxP;
-  float mx = M::f(M::f(M::f(z[0], z[1]), M::f(z[2], z[3])), M::f(M::f(z[4], z[5]), M::f(z[6], z[7])));
-  mx = xlane<M, 16, 32>(mx);
-  const float m_new = M::f(m_run, mx);
-  m_top = M::f(m_top, mx);
-  // (a -inf running max always moves: inf * c2 is inf, or NaN at c2 = 0)
-  if (wave_any(m_new > m_run && !((m_new - m_run) * c2 <= kLazyLog2))) {
-    const float alpha = exp2_fast((m_run - m_new) * c2);
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-    if constexpr (CK == kI4) accb *= alpha;
-    m_run = m_new;
-  }
+  st.m_lane = M::f(M::f(M::f(z[0], z[1]), M::f(z[2], z[3])),
+                   M::f(M::f(z[4], z[5]), M::f(M::f(z[6], z[7]), st.m_lane)));
+  if (wave_any(st.m_lane > st.thr)) st.move_to<NDT, CK == kI4>(column_max<false>(st.m_lane), c2, acc, accb);
   // a masked score is -inf, so its weight is exp2(-inf) = 0 -- also in a
-  // column that has seen only masked scores, whose running max is -inf
-  // (its offset is taken as 0 there, keeping the exponent -inf, not NaN)
-  const float mc = m_run == -INFINITY ? 0.f : m_run * c2;
+  // column that has seen only masked scores (mc 0 there, not -inf * c2)
   float p[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(z[i], c2, -mc));
+  for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(z[i], c2, -st.mc));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) l_run += p[i];
+  for (int i = 0; i < 8; ++i) st.l_run += p[i];
   if constexpr (CK == kI4) {
     float pv[8];
 #pragma unroll
@@ -454,8 +475,8 @@ __device__ __forceinline__ bf16x8 k_operand_pk(const Buf& sb, int i) {
 // kept iff j <= lim.
 template <int NDT, class Buf>
 __device__ __forceinline__ bf16x8 softmax_step_pk(float* z, bool partial, int lim, const Buf& sb,
-                                                  float c2, float& m_run, float& m_top, float& l_run,
-                                                  f32x4* acc, f32x4& accb, bool active) {
+                                                  float c2, LaneSoftmax& st, f32x4* acc, f32x4& accb,
+                                                  bool active) {
   using M = OpMaxP;
 #pragma unroll
   for (int j = 0; j < 4; ++j) z[j] *= sb.sk[j];
@@ -463,26 +484,13 @@ __device__ __forceinline__ bf16x8 softmax_step_pk(float* z, bool partial, int li
 #pragma unroll
     for (int j = 0; j < 4; ++j) z[j] = j <= lim ? z[j] : -INFINITY;
   }
-  float mx = M::f(M::f(z[0], z[1]), M::f(z[2], z[3]));
-  mx = M::f(mx, dpp<0x128>(mx));  // row_ror:8 -> column c ^ 8, the same head
-  mx = xlane<M, 16, 32>(mx);
-  const float m_new = M::f(m_run, mx);
-  m_top = M::f(m_top, mx);
-  // (a -inf running max always moves: inf * c2 is inf, or NaN at c2 = 0)
-  if (wave_any(m_new > m_run && !((m_new - m_run) * c2 <= kLazyLog2))) {
-    const float alpha = exp2_fast((m_run - m_new) * c2);
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-    accb *= alpha;
-    m_run = m_new;
-  }
-  const float mc = m_run == -INFINITY ? 0.f : m_run * c2;  // as softmax_step
+  st.m_lane = M::f(M::f(z[0], z[1]), M::f(M::f(z[2], z[3]), st.m_lane));
+  if (wave_any(st.m_lane > st.thr)) st.move_to<NDT, true>(column_max<true>(st.m_lane), c2, acc, accb);
   float p[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) p[j] = exp2_fast(fmaf(z[j], c2, -mc));
+  for (int j = 0; j < 4; ++j) p[j] = exp2_fast(fmaf(z[j], c2, -st.mc));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) l_run += p[j];
+  for (int j = 0; j < 4; ++j) st.l_run += p[j];
   float pv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) pv[j] = p[j] * sb.sv[j];

@@ -42,15 +42,9 @@ __device__ __forceinline__ Item locate_item(const DecodeArgs& a, int per_part) {
 // (positions first_pos + i), KV head h; their q operands, running softmax
 // states and output accumulators.
 //
-// The online softmax here is the decode's (lazy rescaling, masks from a
-// per-lane token limit) with less work per step, as these kernels issue
-// many steps per byte read:
-// * Each lane keeps the running maximum of its own scores (m_lane) and
-//   compares it with the column's rescale threshold thr = m_run + 8 / c2,
-//   so the cross-lane maximum is taken only when some weight would exceed
-//   2^8, i.e. on a rescale, and once per range in finish.
-// * The weights' offset mc = m_run * c2 and the threshold change only on a
-//   rescale.
+// The online softmax is the decode's (LaneSoftmax: lazy rescaling checked
+// per lane, masks from a per-lane token limit), with less work per step, as
+// these kernels issue many steps per byte read:
 // * bf16 and FP8: the exp-sum of a column comes from the matrix cores, as
 //   the product of a ones operand with the step's weights operand (so it
 //   sums the same bf16 weights the PV product does); INT4, whose weights
@@ -66,17 +60,17 @@ struct Columns {
   size_t qrow[NT];                    // row of q / out (query token * Hq + query head)
   bf16x8 qop[NT][C::kChunks];
   f32x4 acc[NT][C::kDTiles];
-  f32x4 accl[NT];                     // bf16 / FP8: exp-sums of the columns (every register)
-  f32x4 accb[NT];                     // INT4: column sums of the PV weights
-  float m_run[NT], m_lane[NT], thr[NT], mc[NT], l_run[NT], qbias[NT];
-  float lazy_span;                    // kLazyLog2 / c2: the score span below a weight of 2^8
+  // bf16 / FP8: exp-sums of the columns (every register); INT4: column sums
+  // of the PV weights (the exp-sums are st.l_run)
+  f32x4 sums[NT];
+  LaneSoftmax st[NT];
+  float qbias[NT];
 
   // columns: query token qi = i0 + c / G, head g = c % G
   __device__ __forceinline__ void init(const DecodeArgs& a, int r0, int i0, int i1, int first_pos,
                                        int h, int col, int grp, float c2) {
     const int G = a.group;
     const __bf16* qbase = reinterpret_cast<const __bf16*>(a.q);
-    lazy_span = kLazyLog2 / c2;
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
       const int c = ct * 16 + col;
@@ -97,37 +91,12 @@ struct Columns {
           for (int e = 0; e < 8; ++e) qop[ct][cc][e] = (__bf16)0.0f;
         }
       }
-      m_run[ct] = -INFINITY;
-      m_lane[ct] = -INFINITY;
-      thr[ct] = -INFINITY;
-      mc[ct] = 0.f;
-      l_run[ct] = 0.f;
-      accl[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accb[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st[ct].reset(c2);
+      sums[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       qbias[ct] = 0.f;
       if constexpr (C::I4) qbias[ct] = q_bias<C::kChunks>(qop[ct]);
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt) acc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-
-  // Move the reference maximum of tile ct to the column maximum so far
-  // (every lane calls; columns whose maximum has not grown keep theirs).
-  __device__ __forceinline__ void rescale(int ct, float c2) {
-    const float m_new = xlane<OpMaxP, 16, 32>(m_lane[ct]);
-    if (m_new > m_run[ct]) {  // (m_run -inf: alpha 0, the accumulators are 0 anyway)
-      const float alpha = exp2_fast((m_run[ct] - m_new) * c2);
-#pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt) acc[ct][dt] *= alpha;
-      if constexpr (C::I4) {
-        accb[ct] *= alpha;
-        l_run[ct] *= alpha;
-      } else {
-        accl[ct] *= alpha;
-      }
-      m_run[ct] = m_new;
-      mc[ct] = m_new * c2;
-      thr[ct] = m_new + lazy_span;
     }
   }
 
@@ -168,15 +137,17 @@ struct Columns {
         for (int i = 0; i < 8; ++i) z[i] = qk_token_off(i) <= zlim ? z[i] : -INFINITY;
       }
       using M = OpMaxP;
-      m_lane[ct] = M::f(M::f(M::f(z[0], z[1]), M::f(z[2], z[3])),
-                        M::f(M::f(z[4], z[5]), M::f(M::f(z[6], z[7]), m_lane[ct])));
-      if (wave_any(m_lane[ct] > thr[ct])) rescale(ct, c2);
+      LaneSoftmax& s = st[ct];
+      s.m_lane = M::f(M::f(M::f(z[0], z[1]), M::f(z[2], z[3])),
+                      M::f(M::f(z[4], z[5]), M::f(M::f(z[6], z[7]), s.m_lane)));
+      if (wave_any(s.m_lane > s.thr))
+        s.move_to<C::kDTiles, true>(column_max<false>(s.m_lane), c2, acc[ct], sums[ct]);
       float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(z[i], c2, -mc[ct]));
+      for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(z[i], c2, -s.mc));
       if constexpr (C::I4) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) l_run[ct] += p[i];
+        for (int i = 0; i < 8; ++i) s.l_run += p[i];
 #pragma unroll
         for (int i = 0; i < 8; ++i) p[i] *= sb.ts.v[i >> 2][i & 3];
         if (partial) {  // a scale outside the range may be anything, NaN included
@@ -194,12 +165,8 @@ struct Columns {
         acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[ct], acc[ct][dt], 0, 0, 0);
     }
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      if constexpr (C::I4)
-        accb[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop[ct], accb[ct], 0, 0, 0);
-      else
-        accl[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop[ct], accl[ct], 0, 0, 0);
-    }
+    for (int ct = 0; ct < NT; ++ct)
+      sums[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_operand(), pop[ct], sums[ct], 0, 0, 0);
   }
 
   // One row per valid column: the output, or the partition's softmax state.
@@ -207,16 +174,15 @@ struct Columns {
                                          float vscale) {
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
-      // the range's state at its true maximum (the plain softmax state)
-      if (wave_any(m_lane[ct] > m_run[ct])) rescale(ct, c2);
-      const float l_tot = C::I4 ? xlane<OpSum, 16, 32>(l_run[ct]) : accl[ct][0];
+      lazy_settle<C::kDTiles, false>(st[ct], c2, acc[ct], sums[ct]);
+      const float l_tot = C::I4 ? xlane<OpSum, 16, 32>(st[ct].l_run) : sums[ct][0];
       if (!cvalid[ct]) continue;
       const float inv = l_tot > 0.f ? vscale / l_tot : 0.f;  // a row with no token writes zeros
       if constexpr (C::I4) {  // remove the operand bias: 136 * sum_t p(t) s_v(t)
 #pragma unroll
         for (int dt = 0; dt < C::kDTiles; ++dt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ct][dt][r] = fmaf(-kI4Bias, accb[ct][0], acc[ct][dt][r]);
+          for (int r = 0; r < 4; ++r) acc[ct][dt][r] = fmaf(-kI4Bias, sums[ct][0], acc[ct][dt][r]);
       }
       if (a.partition == 0) {
         __bf16* o = reinterpret_cast<__bf16*>(a.out) + qrow[ct] * D;
@@ -235,7 +201,7 @@ struct Columns {
         for (int dt = 0; dt < C::kDTiles; ++dt)
           *reinterpret_cast<f32x4*>(o + dt * 16 + grp * 4) = acc[ct][dt] * inv;
         if (grp == 0) {
-          a.part_max[row] = m_run[ct] * (c2 * kLn2);  // natural units: scale * q.k
+          a.part_max[row] = st[ct].m_run * (c2 * kLn2);  // natural units: scale * q.k
           a.part_sum[row] = l_tot;
         }
       }
