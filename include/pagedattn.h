@@ -196,7 +196,9 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new,
  *                  (PA_BF16, PA_INT4); FP8 codes are widened exactly,
  *                  times the per-head scales; INT4 scales are applied in
  *                  float32 to the scores and to the softmax weights
- *   k_scale, v_scale   [num_kv_heads] float32, device; FP8 cache only
+ *   k_scale, v_scale   [num_kv_heads] float32, device; FP8 cache only;
+ *                  finite and >= 0 (a scale is an absolute maximum over a
+ *                  code range; the device reads them, the host cannot check)
  *   partition_size selects how contexts are cut into ranges, one range per
  *                  wavefront (split-context decoding; a wavefront's softmax
  *                  state over its range is merged with the others afterwards):

@@ -112,7 +112,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const int b, const i
 
   float kscale = 1.0f, vscale = 1.0f;
   if constexpr (FP8) { kscale = a.k_scale[h]; vscale = a.v_scale[h]; }
-  const float c2 = a.scale * kscale * kLog2e;  // q.k -> log2 units
+  const float c2 = log2_factor(a.scale, kscale);  // q.k -> log2 units
   float qbias = 0.f;
   if constexpr (C::I4) qbias = q_bias<C::kChunks>(qop);
 
@@ -707,7 +707,7 @@ void decode_mfma_stream(const DecodeArgs a) {
       accb = f32x4{0.f, 0.f, 0.f, 0.f};
       float kscale = 1.0f;
       if constexpr (FP8) kscale = ((const_f32)a.k_scale)[sl.h];
-      c2 = a.scale * kscale * kLog2e;
+      c2 = log2_factor(a.scale, kscale);
       st.reset(c2);
       if constexpr (C::I4 && !QSEG) qbias = q_bias<C::kChunks>(qop);
     }

@@ -24,6 +24,8 @@
 // output.  Every token's two scales sit at the end of its tile.
 #pragma once
 
+#include <cfloat>
+
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -252,6 +254,15 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // m_run does.
 constexpr float kLazyLog2 = 8.0f;
 
+// The softmax's log2 factor c2 = scale * log2(e) (times an FP8 K scale), so
+// that a weight is 2^((z - m) * c2) for a score z in q.k units.  A K scale
+// of 0 (a head whose keys were all zero) would make c2 0 and a masked score
+// -inf * 0 = NaN; the smallest normal float instead leaves every finite
+// weight exactly 1, as c2 = 0 would, and every masked one 0.
+__device__ __forceinline__ float log2_factor(float scale, float kscale) {
+  return fmaxf(scale * kscale * kLog2e, FLT_MIN);
+}
+
 struct LaneSoftmax {
   float m_run;   // reference maximum of the column's scores (q.k units)
   float m_lane;  // the largest score this lane has seen
@@ -271,12 +282,16 @@ struct LaneSoftmax {
   // call), rescaling what has been accumulated.
   template <int NDT, bool SUMS>
   __device__ __forceinline__ void move_to(float m_col, float c2, f32x4* acc, f32x4& accb) {
-    if (m_col > m_run) {  // (m_run -inf: alpha 0, and nothing has been accumulated)
-      const float alpha = exp2_fast((m_run - m_col) * c2);
-      l_run *= alpha;
+    if (m_col > m_run) {
+      // with m_run -inf nothing has been accumulated (every weight so far
+      // was 0), and (m_run - m_col) * c2 would be NaN at c2 = 0
+      if (m_run != -INFINITY) {
+        const float alpha = exp2_fast((m_run - m_col) * c2);
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-      if constexpr (SUMS) accb *= alpha;
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        if constexpr (SUMS) accb *= alpha;
+      }
       m_run = m_col;
       mc = m_col * c2;
       thr = m_col + span;

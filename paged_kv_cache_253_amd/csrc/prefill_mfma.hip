@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64) void prefill_mfma(const PrefillArgs args) {
 
   float kscale = 1.0f, vscale = 1.0f;
   if constexpr (FP8) { kscale = a.k_scale[h]; vscale = a.v_scale[h]; }
-  const float c2 = a.scale * kscale * kLog2e;  // q.k -> log2 units
+  const float c2 = log2_factor(a.scale, kscale);  // q.k -> log2 units
   Columns<CK, D, BS, NT> cols;
   cols.init(a, tr.r0, tr.i0, tr.i1, tr.first_pos, h, col, grp, c2);
 

@@ -10,6 +10,8 @@ context and jumps inside steps: the rescales happen mid-range, in some
 columns of a wavefront and not in others, and the range's final state must
 still be the plain softmax ("AI Inference Serving at Scale", section 3:
 paged attention computes the same attention as over a contiguous cache).
+The degenerate end: an FP8 head whose K scale is 0, where the softmax's
+log2 factor is 0 and no maximum ever moves the weights.
 """
 
 from __future__ import annotations
@@ -97,3 +99,52 @@ def test_prefill_with_growing_maxima(qlens, partition):
                               batch.scale, "bf16", "bf16")
     compare(out.float().cpu().numpy().astype(np.float64), ref, "bf16",
             f"ramped prefill q={qlens[:2]} P={partition}")
+
+
+@pytest.mark.parametrize("partition", [0, 512, pk.PARTITION_AUTO, pk.PARTITION_AUTO_MERGED])
+def test_zero_key_scale_gives_uniform_weights(partition):
+    """An FP8 head whose K scale is 0 (its keys were all zero when encoded):
+    every score is 0, so its softmax log2 factor is 0 and every weight 1 --
+    the output is the mean of the values over the context, through every
+    split and merge."""
+    print(f"[rescale] zero K scale P={partition}", flush=True)
+    w = dataclasses.replace(WORKLOADS[5], num_seqs=4, pool="exact", name="fp8-zero-k-scale")
+    batch = make_batch(w, seed=24, device=DEV, lens=np.asarray([3000, 517, 64, 1]))
+    ks = batch.k_scale.clone()
+    ks[0] = 0.0
+    batch = batch.replace(k_scale=ks)
+    bt, cl = device_tables(batch)
+    out = pk.decode(batch.q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len,
+                    batch.scale, batch.k_scale, batch.v_scale, partition_size=partition,
+                    cache_dtype=w.cache_dtype)
+    torch.cuda.synchronize()
+    ref = paged.decode(host_view(batch.q), host_view(batch.k_pool), host_view(batch.v_pool),
+                       batch.block_tables, batch.context_lens, w.block_size, batch.scale,
+                       w.q_dtype, w.cache_dtype, ks.cpu().numpy(), batch.v_scale.cpu().numpy())
+    compare(out.float().cpu().numpy().astype(np.float64), ref, w.cache_dtype,
+            f"zero K scale P={partition}")
+
+
+@pytest.mark.parametrize("partition", [0, 256])
+def test_zero_key_scale_multi_query(partition):
+    """The same head through the multi-query kernel, causal rows included."""
+    print(f"[rescale] zero K scale, several query tokens P={partition}", flush=True)
+    w = dataclasses.replace(WORKLOADS[5], num_seqs=3, pool="exact", name="fp8-zero-k-scale")
+    batch = make_batch(w, seed=25, device=DEV, lens=np.asarray([1200, 300, 40]))
+    ks = batch.k_scale.clone()
+    ks[0] = 0.0
+    qlens = [70, 5, 40]
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    g = torch.Generator(device=DEV).manual_seed(26)
+    q = torch.randn((int(qs[-1]), w.num_q_heads, w.head_dim), generator=g, device=DEV).to(torch.bfloat16)
+    bt, cl = device_tables(batch)
+    out = pk.prefill_chunk(q, batch.k_pool, batch.v_pool, bt, cl, batch.max_context_len,
+                           torch.from_numpy(qs).to(DEV), int(max(qlens)), batch.scale, ks,
+                           batch.v_scale, partition_size=partition, cache_dtype=w.cache_dtype)
+    torch.cuda.synchronize()
+    ref = paged.prefill_chunk(host_view(q), host_view(batch.k_pool), host_view(batch.v_pool),
+                              batch.block_tables, batch.context_lens, qs, w.block_size,
+                              batch.scale, "bf16", w.cache_dtype, ks.cpu().numpy(),
+                              batch.v_scale.cpu().numpy())
+    compare(out.float().cpu().numpy().astype(np.float64), ref, w.cache_dtype,
+            f"zero K scale, several query tokens P={partition}")
