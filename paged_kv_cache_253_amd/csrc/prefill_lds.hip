@@ -2,10 +2,13 @@
 // section 4): the wavefronts of a workgroup share each 32-token step's K
 // and V tiles through LDS (the per-column work is that of prefill_mfma.hip,
 // prefill_common.hpp).  Four wavefronts of two column tiles per workgroup,
-// two workgroups per CU (measured on MI355X, chunked prefill at 8K context:
-// 948 us, against 967 us for eight wavefronts per workgroup, 1,416 us for
-// four column tiles per wavefront with the accumulators in AGPRs, and
-// 1,105 us for one wavefront per query tile without LDS sharing).
+// two workgroups per CU, a barrier every two steps (measured on MI355X,
+// chunked prefill at 8K context: 750 us, against 804 us with a barrier
+// every step; earlier revisions: eight wavefronts per workgroup 967 against
+// 948 us, four column tiles per wavefront with the accumulators in AGPRs
+// 1,416 us, one column tile per wavefront at three workgroups per CU 1,008
+// against 802 us, one wavefront per query tile without LDS sharing
+// 1,105 us).
 #include "prefill_common.hpp"
 
 namespace pa {
@@ -25,9 +28,11 @@ using namespace prefill;
 // lanes of the workgroup (one 16-byte piece each), written to LDS, and
 // every wavefront builds its MFMA operands from LDS in the register layout
 // the streaming loads give (so the QK, softmax and PV code is the one
-// above).  Pieces are loaded two steps ahead into one of two register sets
-// and written to one of two LDS buffers after the step that computes from
-// the other; one barrier per step.
+// above).  Each lane loads its pieces of a step into one of two register
+// sets and writes them to one of four LDS step buffers two steps later,
+// after computing the step before; a barrier every two steps makes the two
+// steps just written visible and frees the two just read (4 x 18 KiB per
+// workgroup, two workgroups per CU).
 //
 // LDS layout (one buffer): K as [token group m][chunk][16 tokens] of 16-byte
 // pieces (chunk = 8 head dimensions), i.e. operand k[m][j] of lane (grp,
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
   // last token any of this wavefront's rows sees
   const int wlast = mine ? min(tr.first_pos + wi1 - 1, t1 - 1) : -1;
 
-  __shared__ LdsStep<D> lds[2];
+  __shared__ LdsStep<D> lds[4];
   if (t0 < t1) {
     const char* kc = reinterpret_cast<const char*>(a.k_cache);
     const char* vc = reinterpret_cast<const char*>(a.v_cache);
@@ -135,20 +140,22 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
         cols.step(sb, base, t1, grp, c2);
       }
     };
-    // step n's pieces travel in set n % 2 and LDS buffer n % 2
+    // step n's pieces travel in set n % 2 and LDS buffer n % 4; a barrier
+    // every two steps
     fetch(set0, 0);
     if (nsteps > 1) fetch(set1, 1);
     store(set0, lds[0]);
+    if (nsteps > 1) store(set1, lds[1]);
+    if (nsteps > 2) fetch(set0, 2);
+    if (nsteps > 3) fetch(set1, 3);
     __syncthreads();
     for (int step = 0; step < nsteps; step += 2) {
-      if (step + 2 < nsteps) fetch(set0, step + 2);
-      compute(lds[0], step);
-      if (step + 1 < nsteps) store(set1, lds[1]);
-      __syncthreads();
-      if (step + 1 >= nsteps) break;
-      if (step + 3 < nsteps) fetch(set1, step + 3);
-      compute(lds[1], step + 1);
-      if (step + 2 < nsteps) store(set0, lds[0]);
+      compute(lds[step & 3], step);
+      if (step + 2 < nsteps) store(set0, lds[(step + 2) & 3]);
+      if (step + 4 < nsteps) fetch(set0, step + 4);
+      if (step + 1 < nsteps) compute(lds[(step + 1) & 3], step + 1);
+      if (step + 3 < nsteps) store(set1, lds[(step + 3) & 3]);
+      if (step + 5 < nsteps) fetch(set1, step + 5);
       __syncthreads();
     }
   }
