@@ -149,14 +149,21 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
     if (nsteps > 2) fetch(set0, 2);
     if (nsteps > 3) fetch(set1, 3);
     __syncthreads();
-    for (int step = 0; step < nsteps; step += 2) {
-      compute(lds[step & 3], step);
-      if (step + 2 < nsteps) store(set0, lds[(step + 2) & 3]);
+    // two steps per barrier, unrolled twice so that every LDS buffer index
+    // is a constant
+    auto two_steps = [&](int step, LdsStep<D>& c0, LdsStep<D>& c1, LdsStep<D>& w0, LdsStep<D>& w1) {
+      compute(c0, step);
+      if (step + 2 < nsteps) store(set0, w0);
       if (step + 4 < nsteps) fetch(set0, step + 4);
-      if (step + 1 < nsteps) compute(lds[(step + 1) & 3], step + 1);
-      if (step + 3 < nsteps) store(set1, lds[(step + 3) & 3]);
+      if (step + 1 < nsteps) compute(c1, step + 1);
+      if (step + 3 < nsteps) store(set1, w1);
       if (step + 5 < nsteps) fetch(set1, step + 5);
       __syncthreads();
+    };
+    for (int step = 0; step < nsteps; step += 4) {
+      two_steps(step, lds[0], lds[1], lds[2], lds[3]);
+      if (step + 2 >= nsteps) break;
+      two_steps(step + 2, lds[2], lds[3], lds[0], lds[1]);
     }
   }
   if (mine) cols.finish(a, part, grp, c2, 1.0f);
