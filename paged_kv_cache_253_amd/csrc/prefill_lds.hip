@@ -107,7 +107,10 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
           const int64_t ko = BS == 16 ? (m ? tile1 : tile0) + (chunk * 16 + tok) * 16
                                       : tile0 + (chunk * 32 + 16 * m + tok) * 16;
           ps.k[i] = stream_load<u32x4>(kc + ko);
-          const int dim = pc / 4, g8 = pc % 4;  // tokens 8 g8 .. + 7 of the step
+          // tokens 8 g8 .. + 7 of dimension dim; 16 consecutive lanes take 16
+          // dimensions of one token group, so their LDS writes (80-byte rows)
+          // fall in distinct banks
+          const int dim = pc % 16 + 16 * (pc / 64), g8 = (pc / 16) % 4;
           const int64_t vo = BS == 16 ? ((g8 >> 1) ? tile1 : tile0) + dim * 32 + (g8 & 1) * 16
                                       : tile0 + dim * 64 + g8 * 16;
           ps.v[i] = stream_load<u32x4>(vc + vo);
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
         if (pc < kPieces) {
           const int m = pc / (kPieces / 2), chunk = (pc / 16) % (D / 8), tok = pc % 16;
           L.k[m][chunk][tok] = ps.k[i];
-          const int dim = pc / 4, g8 = pc % 4;
+          const int dim = pc % 16 + 16 * (pc / 64), g8 = (pc / 16) % 4;
           *reinterpret_cast<u32x4*>(&L.v[dim][8 * g8]) = ps.v[i];
         }
       }
