@@ -3,8 +3,8 @@
 // and V tiles through LDS (the per-column work is that of prefill_mfma.hip,
 // prefill_common.hpp).  Four wavefronts of two column tiles per workgroup,
 // two workgroups per CU, a barrier every two steps (measured on MI355X,
-// chunked prefill at 8K context: 750 us, against 804 us with a barrier
-// every step; earlier revisions: eight wavefronts per workgroup 967 against
+// chunked prefill at 8K context: 716 us; a barrier every step 804 us
+// against 750 us for every two steps at the time; earlier revisions: eight wavefronts per workgroup 967 against
 // 948 us, four column tiles per wavefront with the accumulators in AGPRs
 // 1,416 us, one column tile per wavefront at three workgroups per CU 1,008
 // against 802 us, one wavefront per query tile without LDS sharing
