@@ -3,8 +3,10 @@
 // and V tiles through LDS (the per-column work is that of prefill_mfma.hip,
 // prefill_common.hpp).  Four wavefronts of two column tiles per workgroup,
 // two workgroups per CU, a barrier every two steps (measured on MI355X,
-// chunked prefill at 8K context: 716 us; a barrier every step 804 us
-// against 750 us for every two steps at the time; earlier revisions: eight wavefronts per workgroup 967 against
+// chunked prefill at 8K context: 704 us; a barrier every step 804 us
+// against 750 us for every two steps at the time, the block-table reads
+// of a step's pieces at their issue 721 us against 704 us read a step
+// ahead; earlier revisions: eight wavefronts per workgroup 967 against
 // 948 us, four column tiles per wavefront with the accumulators in AGPRs
 // 1,416 us, one column tile per wavefront at three workgroups per CU 1,008
 // against 802 us, one wavefront per query tile without LDS sharing
@@ -93,12 +95,19 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
       p = (p < 0 || (int64_t)p >= a.num_blocks) ? 0 : p;
       return ((int64_t)p * a.num_kv_heads + h) * C::kTile;
     };
-    // the pieces of step `step` this lane carries: K piece (m, chunk, token),
-    // V piece (dimension, 8-token group)
-    auto fetch = [&](Pieces& ps, int step) {
+    // the tiles of step `step` (table entries read with scalar loads, ahead
+    // of their use: a wait on them also waits on the LDS operations in
+    // flight)
+    struct Tiles { int64_t t0, t1; };
+    auto locate = [&](int step) -> Tiles {
       const int lb0 = (t0 + step * kStep) / BS;
       const int64_t tile0 = tile_of(lb0);
-      const int64_t tile1 = C::kBlocksPerStep == 2 ? tile_of(min(lb0 + 1, lb_last)) : tile0;
+      return {tile0, C::kBlocksPerStep == 2 ? tile_of(min(lb0 + 1, lb_last)) : tile0};
+    };
+    // the pieces of a step this lane carries: K piece (m, chunk, token), V
+    // piece (dimension, 8-token group)
+    auto fetch = [&](Pieces& ps, const Tiles& tl) {
+      const int64_t tile0 = tl.t0, tile1 = tl.t1;
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int pc = tid + i * kThreads;
@@ -145,22 +154,24 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
     };
     // step n's pieces travel in set n % 2 and LDS buffer n % 4; a barrier
     // every two steps
-    fetch(set0, 0);
-    if (nsteps > 1) fetch(set1, 1);
+    fetch(set0, locate(0));
+    if (nsteps > 1) fetch(set1, locate(1));
     store(set0, lds[0]);
     if (nsteps > 1) store(set1, lds[1]);
-    if (nsteps > 2) fetch(set0, 2);
-    if (nsteps > 3) fetch(set1, 3);
+    if (nsteps > 2) fetch(set0, locate(2));
+    if (nsteps > 3) fetch(set1, locate(3));
     __syncthreads();
     // two steps per barrier, unrolled twice so that every LDS buffer index
     // is a constant
     auto two_steps = [&](int step, LdsStep<D>& c0, LdsStep<D>& c1, LdsStep<D>& w0, LdsStep<D>& w1) {
+      const Tiles n0 = step + 4 < nsteps ? locate(step + 4) : Tiles{0, 0};
+      const Tiles n1 = step + 5 < nsteps ? locate(step + 5) : Tiles{0, 0};
       compute(c0, step);
       if (step + 2 < nsteps) store(set0, w0);
-      if (step + 4 < nsteps) fetch(set0, step + 4);
+      if (step + 4 < nsteps) fetch(set0, n0);
       if (step + 1 < nsteps) compute(c1, step + 1);
       if (step + 3 < nsteps) store(set1, w1);
-      if (step + 5 < nsteps) fetch(set1, step + 5);
+      if (step + 5 < nsteps) fetch(set1, n1);
       __syncthreads();
     };
     for (int step = 0; step < nsteps; step += 4) {
