@@ -91,6 +91,12 @@ struct Columns {
           for (int e = 0; e < 8; ++e) qop[ct][cc][e] = (__bf16)0.0f;
         }
       }
+      // the query operands land here: otherwise the compiler, seeing loads
+      // into them before the step loop, waits at their first use in every
+      // step for all loads in flight, the ones issued ahead for later steps
+      // included (an empty asm statement that reads them, no memory clobber)
+#pragma unroll
+      for (int cc = 0; cc < C::kChunks; ++cc) asm volatile("" : : "v"(qop[ct][cc]));
       st[ct].reset(c2);
       sums[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       qbias[ct] = 0.f;

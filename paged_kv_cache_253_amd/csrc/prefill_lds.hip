@@ -84,7 +84,10 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
   if (t0 < t1) {
     const char* kc = reinterpret_cast<const char*>(a.k_cache);
     const char* vc = reinterpret_cast<const char*>(a.v_cache);
-    const int32_t* table = a.block_tables + (size_t)b * a.max_blocks;
+    // block-table entries through the constant address space: scalar loads,
+    // whatever the kernel does before them
+    typedef const __attribute__((address_space(4))) int32_t* const_i32;
+    const const_i32 table = (const_i32)a.block_tables + (size_t)b * a.max_blocks;
     const int nsteps = (t1 - t0 + kStep - 1) / kStep;
     const int lb_last = (t1 - 1) / BS;
     constexpr int kPer = (kPieces + kThreads - 1) / kThreads;  // pieces per lane and tensor
