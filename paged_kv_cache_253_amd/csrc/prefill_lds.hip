@@ -3,7 +3,7 @@
 // and V tiles through LDS (the per-column work is that of prefill_mfma.hip,
 // prefill_common.hpp).  Four wavefronts of two column tiles per workgroup,
 // two workgroups per CU, a barrier every two steps (measured on MI355X,
-// chunked prefill at 8K context: 704 us; a barrier every step 804 us
+// chunked prefill at 8K context: 645 us; a barrier every step 804 us
 // against 750 us for every two steps at the time, the block-table reads
 // of a step's pieces at their issue 721 us against 704 us read a step
 // ahead; earlier revisions: eight wavefronts per workgroup 967 against
