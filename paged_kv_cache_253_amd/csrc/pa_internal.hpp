@@ -101,11 +101,8 @@ inline int prefill_query_tiles(int group, int max_query_len, int max_tiles) {
   return (max_query_len + rows_per_tile - 1) / rows_per_tile;
 }
 
-// Chunked prefill with query runs long enough to fill a workgroup of
-// kPrefillLdsWaves wavefronts of kPrefillLdsColumnTiles column tiles
-// (bf16 caches): the LDS-shared kernel (prefill_lds.hip).
-constexpr int kPrefillLdsWaves = 4;
-constexpr int kPrefillLdsColumnTiles = 2;
+// Chunked prefill with query runs long enough to fill a workgroup of the
+// LDS-shared kernel (bf16 caches; prefill_lds.hip).
 bool prefill_uses_lds(Elem cache, int group, int max_query_len);
 hipError_t launch_prefill_lds(const PrefillArgs& p, int head_dim, int block_size, hipStream_t stream);
 

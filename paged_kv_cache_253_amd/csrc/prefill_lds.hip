@@ -1,10 +1,12 @@
 // Chunked prefill with long query runs ("vLLM & High-Throughput Serving",
 // section 4): the wavefronts of a workgroup share each 32-token step's K
 // and V tiles through LDS (the per-column work is that of prefill_mfma.hip,
-// prefill_common.hpp).  Four wavefronts of two column tiles per workgroup,
-// two workgroups per CU, a barrier every two steps (measured on MI355X,
-// chunked prefill at 8K context: 645 us; a barrier every step 804 us
-// against 750 us for every two steps at the time, the block-table reads
+// prefill_common.hpp).  Eight wavefronts of two column tiles per
+// workgroup, one workgroup per CU, a barrier every four steps (measured on
+// MI355X, chunked prefill at 8K context: 604 us, against 620 us for a
+// barrier every two steps and 647 us for four wavefronts per workgroup at
+// two workgroups per CU; a barrier every step 804 us against 750 us for
+// every two steps at the time, the block-table reads
 // of a step's pieces at their issue 721 us against 704 us read a step
 // ahead; earlier revisions: eight wavefronts per workgroup 967 against
 // 948 us, four column tiles per wavefront with the accumulators in AGPRs
@@ -31,10 +33,10 @@ using namespace prefill;
 // every wavefront builds its MFMA operands from LDS in the register layout
 // the streaming loads give (so the QK, softmax and PV code is the one
 // above).  Each lane loads its pieces of a step into one of two register
-// sets and writes them to one of four LDS step buffers two steps later,
-// after computing the step before; a barrier every two steps makes the two
-// steps just written visible and frees the two just read (4 x 18 KiB per
-// workgroup, two workgroups per CU).
+// sets and writes them to one of eight LDS step buffers two steps later,
+// after computing the step before; a barrier every four steps makes the
+// four steps just written visible and frees the four just read (8 x 18 KiB
+// per workgroup).
 //
 // LDS layout (one buffer): K as [token group m][chunk][16 tokens] of 16-byte
 // pieces (chunk = 8 head dimensions), i.e. operand k[m][j] of lane (grp,
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
   // last token any of this wavefront's rows sees
   const int wlast = mine ? min(tr.first_pos + wi1 - 1, t1 - 1) : -1;
 
-  __shared__ LdsStep<D> lds[4];
+  __shared__ LdsStep<D> lds[8];
   if (t0 < t1) {
     const char* kc = reinterpret_cast<const char*>(a.k_cache);
     const char* vc = reinterpret_cast<const char*>(a.v_cache);
@@ -155,32 +157,45 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
         cols.step(sb, base, t1, grp, c2);
       }
     };
-    // step n's pieces travel in set n % 2 and LDS buffer n % 4; a barrier
-    // every two steps
+    // step n's pieces travel in set n % 2 and LDS buffer n % 8; a barrier
+    // every four steps
     fetch(set0, locate(0));
     if (nsteps > 1) fetch(set1, locate(1));
     store(set0, lds[0]);
     if (nsteps > 1) store(set1, lds[1]);
     if (nsteps > 2) fetch(set0, locate(2));
     if (nsteps > 3) fetch(set1, locate(3));
+    if (nsteps > 2) store(set0, lds[2]);
+    if (nsteps > 3) store(set1, lds[3]);
+    if (nsteps > 4) fetch(set0, locate(4));
+    if (nsteps > 5) fetch(set1, locate(5));
     __syncthreads();
-    // two steps per barrier, unrolled twice so that every LDS buffer index
+    // four steps per barrier, unrolled twice so that every LDS buffer index
     // is a constant
-    auto two_steps = [&](int step, LdsStep<D>& c0, LdsStep<D>& c1, LdsStep<D>& w0, LdsStep<D>& w1) {
-      const Tiles n0 = step + 4 < nsteps ? locate(step + 4) : Tiles{0, 0};
-      const Tiles n1 = step + 5 < nsteps ? locate(step + 5) : Tiles{0, 0};
+    auto four_steps = [&](int step, LdsStep<D>& c0, LdsStep<D>& c1, LdsStep<D>& c2_, LdsStep<D>& c3,
+                          LdsStep<D>& w0, LdsStep<D>& w1, LdsStep<D>& w2, LdsStep<D>& w3) {
+      const Tiles n0 = step + 6 < nsteps ? locate(step + 6) : Tiles{0, 0};
+      const Tiles n1 = step + 7 < nsteps ? locate(step + 7) : Tiles{0, 0};
+      const Tiles n2 = step + 8 < nsteps ? locate(step + 8) : Tiles{0, 0};
+      const Tiles n3 = step + 9 < nsteps ? locate(step + 9) : Tiles{0, 0};
       compute(c0, step);
-      if (step + 2 < nsteps) store(set0, w0);
-      if (step + 4 < nsteps) fetch(set0, n0);
+      if (step + 4 < nsteps) store(set0, w0);
+      if (step + 6 < nsteps) fetch(set0, n0);
       if (step + 1 < nsteps) compute(c1, step + 1);
-      if (step + 3 < nsteps) store(set1, w1);
-      if (step + 5 < nsteps) fetch(set1, n1);
+      if (step + 5 < nsteps) store(set1, w1);
+      if (step + 7 < nsteps) fetch(set1, n1);
+      if (step + 2 < nsteps) compute(c2_, step + 2);
+      if (step + 6 < nsteps) store(set0, w2);
+      if (step + 8 < nsteps) fetch(set0, n2);
+      if (step + 3 < nsteps) compute(c3, step + 3);
+      if (step + 7 < nsteps) store(set1, w3);
+      if (step + 9 < nsteps) fetch(set1, n3);
       __syncthreads();
     };
-    for (int step = 0; step < nsteps; step += 4) {
-      two_steps(step, lds[0], lds[1], lds[2], lds[3]);
-      if (step + 2 >= nsteps) break;
-      two_steps(step + 2, lds[2], lds[3], lds[0], lds[1]);
+    for (int step = 0; step < nsteps; step += 8) {
+      four_steps(step, lds[0], lds[1], lds[2], lds[3], lds[4], lds[5], lds[6], lds[7]);
+      if (step + 4 >= nsteps) break;
+      four_steps(step + 4, lds[4], lds[5], lds[6], lds[7], lds[0], lds[1], lds[2], lds[3]);
     }
   }
   if (mine) cols.finish(a, part, grp, c2, 1.0f);
@@ -188,8 +203,10 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
 
 // Query rows per workgroup of the LDS-shared prefill, and whether a launch
 // takes it: bf16 cache with query runs long enough to fill a workgroup.
-constexpr int kLdsWaves = kPrefillLdsWaves;
-constexpr int kLdsNT = kPrefillLdsColumnTiles;
+// Eight wavefronts of two column tiles per workgroup, one workgroup per CU
+// (230 VGPRs: two wavefronts per SIMD; 144 KiB of LDS).
+constexpr int kLdsWaves = 8;
+constexpr int kLdsNT = 2;
 
 template <int D, int BS>
 hipError_t launch_lds(const PrefillArgs& p, hipStream_t stream) {
@@ -211,7 +228,7 @@ hipError_t launch_lds(const PrefillArgs& p, hipStream_t stream) {
 
 bool prefill_uses_lds(Elem cache, int group, int max_query_len) {
   return cache == Elem::BF16 &&
-         (long long)group * max_query_len >= 16 * kPrefillLdsColumnTiles * kPrefillLdsWaves;
+         (long long)group * max_query_len >= 16 * kLdsNT * kLdsWaves;
 }
 
 hipError_t launch_prefill_lds(const PrefillArgs& p, int head_dim, int block_size, hipStream_t stream) {
