@@ -2,17 +2,19 @@
 // section 4): the wavefronts of a workgroup share each 32-token step's K
 // and V tiles through LDS (the per-column work is that of prefill_mfma.hip,
 // prefill_common.hpp).  Eight wavefronts of two column tiles per
-// workgroup, one workgroup per CU, a barrier every four steps (measured on
-// MI355X, chunked prefill at 8K context: 604 us, against 620 us for a
-// barrier every two steps and 647 us for four wavefronts per workgroup at
-// two workgroups per CU; a barrier every step 804 us against 750 us for
-// every two steps at the time, the block-table reads
-// of a step's pieces at their issue 721 us against 704 us read a step
-// ahead; earlier revisions: eight wavefronts per workgroup 967 against
-// 948 us, four column tiles per wavefront with the accumulators in AGPRs
-// 1,416 us, one column tile per wavefront at three workgroups per CU 1,008
-// against 802 us, one wavefront per query tile without LDS sharing
-// 1,105 us).
+// workgroup, one workgroup per CU, the tiles loaded straight from memory
+// into LDS four steps ahead, a barrier every four steps (measured on
+// MI355X, chunked prefill at 8K context: 588 us, against 598 us with the
+// pieces staged through registers, 620 us for a barrier every two steps
+// and 647 us for four wavefronts per workgroup at two workgroups per CU; a
+// barrier every step 804 us against 750 us for every two steps at the
+// time, the block-table reads of a step's pieces at their issue 721 us
+// against 704 us read a step ahead; earlier revisions: eight wavefronts
+// per workgroup 967 against 948 us, four column tiles per wavefront with
+// the accumulators in AGPRs 1,416 us, one column tile per wavefront at
+// three workgroups per CU 1,008 against 802 us, one wavefront per query
+// tile without LDS sharing 1,105 us; wave priority raised around the
+// matrix-core instructions 592-601 us against 588 us).
 #include "prefill_common.hpp"
 
 namespace pa {
@@ -29,27 +31,27 @@ using namespace prefill;
 // columns, and the L2 delivers the same tiles once per query tile.  Here
 // the W wavefronts of a workgroup take consecutive query tiles of one
 // (sequence, KV head); each step's tiles are read from memory once, by all
-// lanes of the workgroup (one 16-byte piece each), written to LDS, and
+// lanes of the workgroup (one 16-byte piece of K and one of V each), with
+// loads that write LDS directly (global_load_lds_dwordx4: lane l of a
+// wavefront writes the l-th 16 bytes from the wavefront's LDS address), and
 // every wavefront builds its MFMA operands from LDS in the register layout
-// the streaming loads give (so the QK, softmax and PV code is the one
-// above).  Each lane loads its pieces of a step into one of two register
-// sets and writes them to one of eight LDS step buffers two steps later,
-// after computing the step before; a barrier every four steps makes the
-// four steps just written visible and frees the four just read (8 x 18 KiB
-// per workgroup).
-//
-// LDS layout (one buffer): K as [token group m][chunk][16 tokens] of 16-byte
-// pieces (chunk = 8 head dimensions), i.e. operand k[m][j] of lane (grp,
-// col) at [m][grp + 4 j][col]; V as [dimension][32 tokens] bf16 rows padded
-// to 40 elements (80 bytes: the 16 lanes of a lane group read 16 rows
-// without bank conflicts), operand v[dt] of lane (grp, col) at
-// [16 dt + col][8 grp].
+// the streaming loads give (so the QK, softmax and PV code is
+// prefill_common.hpp's).  Eight step buffers: at the start of every four steps each lane
+// issues the loads of the four steps after them, into the buffers the
+// four steps before were read from; before the barrier that ends the four
+// steps it waits for them.
 
+// One LDS step buffer: K as [token group m][chunk][16 tokens] of 16-byte
+// pieces, V as [dimension][4 pieces of 8 tokens] with the pieces of a row
+// permuted (XOR with bits 2-3 of the dimension) so that the 16 rows one
+// lane group reads fall in distinct banks.
 template <int D>
 struct LdsStep {
   u32x4 k[2][D / 8][16];
-  __bf16 v[D][40];
+  u32x4 v[D][4];
 };
+
+typedef __attribute__((address_space(3))) void* lds_void;
 
 template <int CK, int D, int BS, int NT, int W>
 __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
@@ -57,6 +59,7 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
   using C = Cfg<CK, D, BS>;
   constexpr int kThreads = 64 * W;
   constexpr int kPieces = 2 * (D / 8) * 16;  // 16-byte pieces of K (and of V) per step
+  static_assert(kPieces % 64 == 0 && kPieces <= kThreads, "one piece of K and one of V per lane and step");
   const DecodeArgs& a = args.d;
   const Item it = locate_item(a, args.tiles);
   if (!it.ok) return;  // the whole workgroup: uniform
@@ -82,67 +85,49 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
   // last token any of this wavefront's rows sees
   const int wlast = mine ? min(tr.first_pos + wi1 - 1, t1 - 1) : -1;
 
-  __shared__ LdsStep<D> lds[8];
+  // eight buffers as separate variables: the compiler then waits for a
+  // buffer's own loads only
+  __shared__ LdsStep<D> l0, l1, l2, l3, l4, l5, l6, l7;
   if (t0 < t1) {
     const char* kc = reinterpret_cast<const char*>(a.k_cache);
     const char* vc = reinterpret_cast<const char*>(a.v_cache);
-    // block-table entries through the constant address space: scalar loads,
-    // whatever the kernel does before them
+    // block-table entries through the constant address space: scalar loads
     typedef const __attribute__((address_space(4))) int32_t* const_i32;
     const const_i32 table = (const_i32)a.block_tables + (size_t)b * a.max_blocks;
     const int nsteps = (t1 - t0 + kStep - 1) / kStep;
     const int lb_last = (t1 - 1) / BS;
-    constexpr int kPer = (kPieces + kThreads - 1) / kThreads;  // pieces per lane and tensor
-    struct Pieces { u32x4 k[kPer], v[kPer]; };
-    Pieces set0, set1;
     auto tile_of = [&](int lb) -> int64_t {
       int p = table[lb];
       p = (p < 0 || (int64_t)p >= a.num_blocks) ? 0 : p;
       return ((int64_t)p * a.num_kv_heads + h) * C::kTile;
     };
-    // the tiles of step `step` (table entries read with scalar loads, ahead
-    // of their use: a wait on them also waits on the LDS operations in
-    // flight)
     struct Tiles { int64_t t0, t1; };
     auto locate = [&](int step) -> Tiles {
       const int lb0 = (t0 + step * kStep) / BS;
       const int64_t tile0 = tile_of(lb0);
       return {tile0, C::kBlocksPerStep == 2 ? tile_of(min(lb0 + 1, lb_last)) : tile0};
     };
-    // the pieces of a step this lane carries: K piece (m, chunk, token), V
-    // piece (dimension, 8-token group)
-    auto fetch = [&](Pieces& ps, const Tiles& tl) {
-      const int64_t tile0 = tl.t0, tile1 = tl.t1;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int pc = tid + i * kThreads;
-        if (pc < kPieces) {
-          const int m = pc / (kPieces / 2), chunk = (pc / 16) % (D / 8), tok = pc % 16;
-          const int64_t ko = BS == 16 ? (m ? tile1 : tile0) + (chunk * 16 + tok) * 16
-                                      : tile0 + (chunk * 32 + 16 * m + tok) * 16;
-          ps.k[i] = stream_load<u32x4>(kc + ko);
-          // tokens 8 g8 .. + 7 of dimension dim; 16 consecutive lanes take 16
-          // dimensions of one token group, so their LDS writes (80-byte rows)
-          // fall in distinct banks
-          const int dim = pc % 16 + 16 * (pc / 64), g8 = (pc / 16) % 4;
-          const int64_t vo = BS == 16 ? ((g8 >> 1) ? tile1 : tile0) + dim * 32 + (g8 & 1) * 16
-                                      : tile0 + dim * 64 + g8 * 16;
-          ps.v[i] = stream_load<u32x4>(vc + vo);
-        }
+    // This lane's pieces, as slot tid of each tensor's buffer: K piece (m,
+    // chunk, token) = slot; V slot (dimension, position) holds the 8-token
+    // group position ^ bits 2-3 of the dimension.
+    const bool carries = tid < kPieces;  // whole wavefronts
+    const int km = tid / (kPieces / 2), kchunk = (tid / 16) % (D / 8), ktok = tid % 16;
+    const int vdim = tid >> 2, vg8 = (tid & 3) ^ ((vdim >> 2) & 3);
+    const int64_t koff0 = BS == 16 ? (kchunk * 16 + ktok) * 16 : (kchunk * 32 + 16 * km + ktok) * 16;
+    const int64_t voff0 = BS == 16 ? vdim * 32 + (vg8 & 1) * 16 : vdim * 64 + vg8 * 16;
+    const bool k_second = BS == 16 && km;
+    const bool v_second = BS == 16 && (vg8 >> 1);
+    // a step's K and V pieces, straight from memory into buffer L (each
+    // wavefront writes 64 consecutive slots)
+    auto dma = [&](const Tiles& tl, LdsStep<D>& L) {
+      if (carries) {
+        const int64_t kt = k_second ? tl.t1 : tl.t0;
+        const int64_t vt = v_second ? tl.t1 : tl.t0;
+        __builtin_amdgcn_global_load_lds(kc + kt + koff0, (lds_void)(&L.k[0][0][0] + wave * 64), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vc + vt + voff0, (lds_void)(&L.v[0][0] + wave * 64), 16, 0, 0);
       }
     };
-    auto store = [&](const Pieces& ps, LdsStep<D>& L) {
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int pc = tid + i * kThreads;
-        if (pc < kPieces) {
-          const int m = pc / (kPieces / 2), chunk = (pc / 16) % (D / 8), tok = pc % 16;
-          L.k[m][chunk][tok] = ps.k[i];
-          const int dim = pc % 16 + 16 * (pc / 64), g8 = (pc / 16) % 4;
-          *reinterpret_cast<u32x4*>(&L.v[dim][8 * g8]) = ps.v[i];
-        }
-      }
-    };
+    const int vsw = grp ^ (col >> 2);  // this lane's V piece position in its rows
     StepBuf<CK, D, BS> sb;
     auto compute = [&](const LdsStep<D>& L, int step) {
       const int base = t0 + step * kStep;
@@ -152,50 +137,35 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
 #pragma unroll
           for (int j = 0; j < C::kKLoads; ++j) sb.k[m][j] = L.k[m][grp + 4 * j][col];
 #pragma unroll
-        for (int dt = 0; dt < C::kDTiles; ++dt)
-          sb.v[dt].w = *reinterpret_cast<const u32x4*>(&L.v[16 * dt + col][8 * grp]);
+        for (int dt = 0; dt < C::kDTiles; ++dt) sb.v[dt].w = L.v[16 * dt + col][vsw];
         cols.step(sb, base, t1, grp, c2);
       }
     };
-    // step n's pieces travel in set n % 2 and LDS buffer n % 8; a barrier
-    // every four steps
-    fetch(set0, locate(0));
-    if (nsteps > 1) fetch(set1, locate(1));
-    store(set0, lds[0]);
-    if (nsteps > 1) store(set1, lds[1]);
-    if (nsteps > 2) fetch(set0, locate(2));
-    if (nsteps > 3) fetch(set1, locate(3));
-    if (nsteps > 2) store(set0, lds[2]);
-    if (nsteps > 3) store(set1, lds[3]);
-    if (nsteps > 4) fetch(set0, locate(4));
-    if (nsteps > 5) fetch(set1, locate(5));
+    // step n in buffer n % 8; the loads of four steps in flight while the
+    // four before them are computed; a barrier every four steps
+    auto load4 = [&](int s, LdsStep<D>& w0, LdsStep<D>& w1, LdsStep<D>& w2, LdsStep<D>& w3) {
+      if (s < nsteps) dma(locate(s), w0);
+      if (s + 1 < nsteps) dma(locate(s + 1), w1);
+      if (s + 2 < nsteps) dma(locate(s + 2), w2);
+      if (s + 3 < nsteps) dma(locate(s + 3), w3);
+    };
+    load4(0, l0, l1, l2, l3);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // four steps per barrier, unrolled twice so that every LDS buffer index
-    // is a constant
     auto four_steps = [&](int step, LdsStep<D>& c0, LdsStep<D>& c1, LdsStep<D>& c2_, LdsStep<D>& c3,
                           LdsStep<D>& w0, LdsStep<D>& w1, LdsStep<D>& w2, LdsStep<D>& w3) {
-      const Tiles n0 = step + 6 < nsteps ? locate(step + 6) : Tiles{0, 0};
-      const Tiles n1 = step + 7 < nsteps ? locate(step + 7) : Tiles{0, 0};
-      const Tiles n2 = step + 8 < nsteps ? locate(step + 8) : Tiles{0, 0};
-      const Tiles n3 = step + 9 < nsteps ? locate(step + 9) : Tiles{0, 0};
+      load4(step + 4, w0, w1, w2, w3);
       compute(c0, step);
-      if (step + 4 < nsteps) store(set0, w0);
-      if (step + 6 < nsteps) fetch(set0, n0);
       if (step + 1 < nsteps) compute(c1, step + 1);
-      if (step + 5 < nsteps) store(set1, w1);
-      if (step + 7 < nsteps) fetch(set1, n1);
       if (step + 2 < nsteps) compute(c2_, step + 2);
-      if (step + 6 < nsteps) store(set0, w2);
-      if (step + 8 < nsteps) fetch(set0, n2);
       if (step + 3 < nsteps) compute(c3, step + 3);
-      if (step + 7 < nsteps) store(set1, w3);
-      if (step + 9 < nsteps) fetch(set1, n3);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     };
     for (int step = 0; step < nsteps; step += 8) {
-      four_steps(step, lds[0], lds[1], lds[2], lds[3], lds[4], lds[5], lds[6], lds[7]);
+      four_steps(step, l0, l1, l2, l3, l4, l5, l6, l7);
       if (step + 4 >= nsteps) break;
-      four_steps(step + 4, lds[4], lds[5], lds[6], lds[7], lds[0], lds[1], lds[2], lds[3]);
+      four_steps(step + 4, l4, l5, l6, l7, l0, l1, l2, l3);
     }
   }
   if (mine) cols.finish(a, part, grp, c2, 1.0f);
@@ -204,7 +174,7 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
 // Query rows per workgroup of the LDS-shared prefill, and whether a launch
 // takes it: bf16 cache with query runs long enough to fill a workgroup.
 // Eight wavefronts of two column tiles per workgroup, one workgroup per CU
-// (230 VGPRs: two wavefronts per SIMD; 144 KiB of LDS).
+// (218 VGPRs: two wavefronts per SIMD; 128 KiB of LDS).
 constexpr int kLdsWaves = 8;
 constexpr int kLdsNT = 2;
 
