@@ -107,8 +107,14 @@ struct Columns {
   }
 
   // One 32-token step starting at token `base`; tokens at or past t1 are
-  // outside this wavefront's range.
+  // outside this wavefront's range.  kPermRows: the QK A operand's rows
+  // come permuted (row r of sb.k[0] is token 8 (r / 4) + r % 4, of sb.k[1]
+  // that + 4), so score register i of lane row grp is token 8 grp + i: the
+  // scores then sit in the PV weights operand's k-slot order and need no
+  // exchange between lanes.
+  template <bool kPermRows = false>
   __device__ __forceinline__ void step(StepBuf<CK, D, BS>& sb, int base, int t1, int grp, float c2) {
+    static_assert(!(kPermRows && C::I4), "INT4 weights carry token scales in QK register order");
     f32x4 s0[NT], s1[NT];
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) { s0[ct] = qk_init<CK>(qbias[ct]); s1[ct] = s0[ct]; }
@@ -137,10 +143,10 @@ struct Columns {
       const bool partial = min(t1 - 1, pos_min[ct]) < base + kStep - 1;
       // kept: offsets from the lane's first token up to the last token this
       // column may see (none for a padding column)
-      const int zlim = cvalid[ct] ? min(t1 - 1, pos[ct]) - base - 4 * grp : -1;
+      const int zlim = cvalid[ct] ? min(t1 - 1, pos[ct]) - base - (kPermRows ? 8 : 4) * grp : -1;
       if (partial) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) z[i] = qk_token_off(i) <= zlim ? z[i] : -INFINITY;
+        for (int i = 0; i < 8; ++i) z[i] = (kPermRows ? i : qk_token_off(i)) <= zlim ? z[i] : -INFINITY;
       }
       using M = OpMaxP;
       LaneSoftmax& s = st[ct];
@@ -161,7 +167,12 @@ struct Columns {
           for (int i = 0; i < 8; ++i) p[i] = qk_token_off(i) <= zlim ? p[i] : 0.f;
         }
       }
-      pop[ct] = p_operand(p);
+      if constexpr (kPermRows) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pop[ct][i] = (__bf16)p[i];
+      } else {
+        pop[ct] = p_operand(p);
+      }
     }
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt) {

@@ -14,7 +14,8 @@
 // the accumulators in AGPRs 1,416 us, one column tile per wavefront at
 // three workgroups per CU 1,008 against 802 us, one wavefront per query
 // tile without LDS sharing 1,105 us; wave priority raised around the
-// matrix-core instructions 592-601 us against 588 us).
+// matrix-core instructions 592-601 us against 588 us; the QK operand's
+// rows permuted so that the scores need no lane exchange: 600 -> 586 us).
 #include "prefill_common.hpp"
 
 namespace pa {
@@ -42,9 +43,11 @@ using namespace prefill;
 // steps it waits for them.
 
 // One LDS step buffer: K as [token group m][chunk][16 tokens] of 16-byte
-// pieces, V as [dimension][4 pieces of 8 tokens] with the pieces of a row
-// permuted (XOR with bits 2-3 of the dimension) so that the 16 rows one
-// lane group reads fall in distinct banks.
+// pieces, the tokens of group 1 permuted (position ^ 4) so that the tokens
+// t and t + 16 one permuted operand read takes fall in distinct banks; V
+// as [dimension][4 pieces of 8 tokens] with the pieces of a row permuted
+// (XOR with bits 2-3 of the dimension) so that the 16 rows one lane group
+// reads fall in distinct banks.
 template <int D>
 struct LdsStep {
   u32x4 k[2][D / 8][16];
@@ -107,11 +110,12 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
       const int64_t tile0 = tile_of(lb0);
       return {tile0, C::kBlocksPerStep == 2 ? tile_of(min(lb0 + 1, lb_last)) : tile0};
     };
-    // This lane's pieces, as slot tid of each tensor's buffer: K piece (m,
-    // chunk, token) = slot; V slot (dimension, position) holds the 8-token
-    // group position ^ bits 2-3 of the dimension.
+    // This lane's pieces, as slot tid of each tensor's buffer: K slot (m,
+    // chunk, position) holds token position ^ 4 m of token group m; V slot
+    // (dimension, position) holds the 8-token group position ^ bits 2-3 of
+    // the dimension.
     const bool carries = tid < kPieces;  // whole wavefronts
-    const int km = tid / (kPieces / 2), kchunk = (tid / 16) % (D / 8), ktok = tid % 16;
+    const int km = tid / (kPieces / 2), kchunk = (tid / 16) % (D / 8), ktok = (tid % 16) ^ (km << 2);
     const int vdim = tid >> 2, vg8 = (tid & 3) ^ ((vdim >> 2) & 3);
     const int64_t koff0 = BS == 16 ? (kchunk * 16 + ktok) * 16 : (kchunk * 32 + 16 * km + ktok) * 16;
     const int64_t voff0 = BS == 16 ? vdim * 32 + (vg8 & 1) * 16 : vdim * 64 + vg8 * 16;
@@ -128,6 +132,16 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
       }
     };
     const int vsw = grp ^ (col >> 2);  // this lane's V piece position in its rows
+    // QK A-operand rows of this lane, permuted (the step's kPermRows):
+    // tokens 8 (col / 4) + col % 4 and that + 4, as (token group, K slot
+    // position): the 16 lanes of a row then read 16 distinct bank groups
+    int kgm[2], kpos[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int t = 8 * (col >> 2) + 4 * m + (col & 3);
+      kgm[m] = t >> 4;
+      kpos[m] = (t & 15) ^ (kgm[m] << 2);
+    }
     StepBuf<CK, D, BS> sb;
     auto compute = [&](const LdsStep<D>& L, int step) {
       const int base = t0 + step * kStep;
@@ -135,10 +149,10 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int j = 0; j < C::kKLoads; ++j) sb.k[m][j] = L.k[m][grp + 4 * j][col];
+          for (int j = 0; j < C::kKLoads; ++j) sb.k[m][j] = L.k[kgm[m]][grp + 4 * j][kpos[m]];
 #pragma unroll
         for (int dt = 0; dt < C::kDTiles; ++dt) sb.v[dt].w = L.v[16 * dt + col][vsw];
-        cols.step(sb, base, t1, grp, c2);
+        cols.template step<true>(sb, base, t1, grp, c2);
       }
     };
     // step n in buffer n % 8; the loads of four steps in flight while the
