@@ -128,6 +128,7 @@ def test_long_query_runs(w, lens, qlens, partition):
 
 W_B32 = dataclasses.replace(WORKLOADS[2], block_size=32, name="b32-bf16")
 W_G2 = dataclasses.replace(WORKLOADS[2], num_q_heads=16, name="g2-bf16")
+W_D64_B16 = dataclasses.replace(WORKLOADS[2], head_dim=64, name="d64-bf16")
 
 
 @pytest.mark.parametrize("w,lens,qlens", [
@@ -135,10 +136,12 @@ W_G2 = dataclasses.replace(WORKLOADS[2], num_q_heads=16, name="g2-bf16")
     (W4, [2100, 2300], [300, 260]),                       # G = 1, 64 heads
     (W_B32, [1000, 1500, 31], [100, 130, 31]),            # block 32
     (W_G2, [900, 1200], [140, 200]),                      # G = 2
+    (W_D64_B16, [1300, 900, 77], [100, 70, 77]),          # head_dim 64
 ])
 @pytest.mark.parametrize("partition", [0, 256])
 def test_workgroup_shared_tiles(w, lens, qlens, partition):
     """bf16 query runs long enough for the launch whose wavefronts share
     each step's tiles through LDS: every group size's query blocks, block
-    sizes 16 and 32, rows whose contexts end inside a step."""
+    sizes 16 and 32, head_dim 64 and 128, rows whose contexts end inside a
+    step."""
     _run(w, lens, qlens, partition, seed=8)
