@@ -568,8 +568,12 @@ def bench_step(args) -> int:
     if args.unshare:
         from workloads import unshare
         batch = unshare(batch)
+    if args.contiguous_blocks:  # block-layout studies: the unpaged order, same data
+        from workloads import contiguous_layout, unshare
+        batch = contiguous_layout(unshare(batch))
     torch.cuda.synchronize()
-    log(f"[bench] workload {w.index} {w.name}{' (unshared)' if args.unshare else ''}: "
+    log(f"[bench] workload {w.index} {w.name}{' (unshared)' if args.unshare else ''}"
+        f"{' (blocks in sequence order)' if args.contiguous_blocks else ''}: "
         f"{len(batch.context_lens)} seqs, "
         f"{int(batch.context_lens.sum())} tokens, pool {batch.num_blocks} blocks "
         f"(generated in {time.perf_counter() - t_gen:.1f}s)")
@@ -706,7 +710,8 @@ def bench_step(args) -> int:
         log("[bench] copy calibration: 3 x 1 GiB device copies done")
 
     # the counters were taken on the drawn batch only
-    traffic = None if (args.equal_lengths or args.unshare) else measured_traffic(w.name, part, 1)
+    traffic = (None if (args.equal_lengths or args.unshare or args.contiguous_blocks)
+               else measured_traffic(w.name, part, 1))
     split = {0: "unsplit", -1: "balanced", -2: "balanced, merged in the decode launch"}.get(
         part, f"{part}-token partitions")
     result = {
@@ -725,7 +730,8 @@ def bench_step(args) -> int:
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "context_tokens_per_s": round(dec["tokens"] / (ms_per_step * 1e-3), 1),
         "config": {"workload": w.name + ("-unshared" if args.unshare else "")
-                   + (f"-equal-lengths-{args.equal_lengths}" if args.equal_lengths else ""),
+                   + (f"-equal-lengths-{args.equal_lengths}" if args.equal_lengths else "")
+                   + ("-contiguous-blocks" if args.contiguous_blocks else ""),
                    "num_seqs": len(batch.context_lens),
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size,
@@ -817,6 +823,10 @@ def main() -> int:
                     help="replace the workload's drawn lengths by N equal contexts with the "
                          "same token total (how the decode's time depends on the number of "
                          "runs, not on the bytes)")
+    ap.add_argument("--contiguous-blocks", action="store_true",
+                    help="renumber the batch's blocks so each sequence's are consecutive, in "
+                         "sequence order (the unpaged layout, same data): what the scattered "
+                         "physical blocks cost the decode")
     ap.add_argument("--case", default="spec-verify-8b",
                     help="prefill shape: spec-verify-8b or chunked-prefill-8b")
     args = ap.parse_args()

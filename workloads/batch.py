@@ -385,7 +385,8 @@ def contiguous_layout(batch: Batch) -> Batch:
     if np.any(batch.ref_counts > 1):
         raise ValueError("unshare the batch first")
     order = [int(x) for x in batch.block_tables.reshape(-1) if x >= 0]
-    rest = [i for i in range(batch.num_blocks) if i not in set(order)]
+    used = set(order)
+    rest = [i for i in range(batch.num_blocks) if i not in used]
     old_order = np.array(order + rest, dtype=np.int64)
     perm = np.empty(batch.num_blocks, dtype=np.int64)
     perm[old_order] = np.arange(batch.num_blocks)
