@@ -3,19 +3,23 @@
 // and V tiles through LDS (the per-column work is that of prefill_mfma.hip,
 // prefill_common.hpp).  Eight wavefronts of two column tiles per
 // workgroup, one workgroup per CU, the tiles loaded straight from memory
-// into LDS four steps ahead, a barrier every four steps (measured on
-// MI355X, chunked prefill at 8K context: 588 us, against 598 us with the
-// pieces staged through registers, 620 us for a barrier every two steps
-// and 647 us for four wavefronts per workgroup at two workgroups per CU; a
-// barrier every step 804 us against 750 us for every two steps at the
-// time, the block-table reads of a step's pieces at their issue 721 us
-// against 704 us read a step ahead; earlier revisions: eight wavefronts
-// per workgroup 967 against 948 us, four column tiles per wavefront with
-// the accumulators in AGPRs 1,416 us, one column tile per wavefront at
-// three workgroups per CU 1,008 against 802 us, one wavefront per query
-// tile without LDS sharing 1,105 us; wave priority raised around the
-// matrix-core instructions 592-601 us against 588 us; the QK operand's
-// rows permuted so that the scores need no lane exchange: 600 -> 586 us).
+// into LDS four steps ahead, a barrier every four steps.
+//
+// Measured on MI355X, chunked prefill at 8K context (bench events, A/B on
+// one box at each change): one wavefront per query tile without LDS
+// sharing 1,105 us; four wavefronts per workgroup, a barrier every step
+// 804 us, every two steps 750 us; eight wavefronts per workgroup at one
+// workgroup per CU 647 -> 615 us; eight LDS step buffers, a barrier every
+// four steps 620 -> 604 us; the tiles loaded straight into LDS instead of
+// staged through registers 598 -> 588 us; the QK operand's rows permuted so
+// that the scores need no lane exchange 600 -> 586 us, and their K slots
+// permuted against bank conflicts 589 -> 583 us.  Not kept: four column
+// tiles per wavefront with the accumulators in AGPRs (1,416 us), one column
+// tile per wavefront at three workgroups per CU (1,008 against 802 us),
+// wave priority raised around the matrix-core instructions, the second
+// half of the wavefronts delayed or run a phase behind (ping-pong), the
+// operands read from LDS where they are used, and the next step's QK issued
+// among a step's exponentials.
 #include "prefill_common.hpp"
 
 namespace pa {
@@ -36,11 +40,11 @@ using namespace prefill;
 // loads that write LDS directly (global_load_lds_dwordx4: lane l of a
 // wavefront writes the l-th 16 bytes from the wavefront's LDS address), and
 // every wavefront builds its MFMA operands from LDS in the register layout
-// the streaming loads give (so the QK, softmax and PV code is
-// prefill_common.hpp's).  Eight step buffers: at the start of every four steps each lane
-// issues the loads of the four steps after them, into the buffers the
-// four steps before were read from; before the barrier that ends the four
-// steps it waits for them.
+// of the multi-query step (prefill_common.hpp's QK, softmax and PV, with
+// the QK operand's rows permuted).  Eight step buffers: at the start of
+// every four steps each lane issues the loads of the four steps after
+// them, into the buffers the four steps before were read from; before the
+// barrier that ends the four steps it waits for them.
 
 // One LDS step buffer: K as [token group m][chunk][16 tokens] of 16-byte
 // pieces, the tokens of group 1 permuted (position ^ 4) so that the tokens
