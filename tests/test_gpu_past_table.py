@@ -96,14 +96,17 @@ def test_decode_cuts_the_context_at_the_row_end(monkeypatch, cache, group, force
     compare(widen(out), ref, cache, f"{w.name} split={split}")
 
 
+@pytest.mark.parametrize("qlens", [[30, 5, 40], [80, 5, 96]], ids=["tile-per-wave", "lds-shared"])
 @pytest.mark.parametrize("partition", [0, 64])
-def test_prefill_cuts_the_context_at_the_row_end(partition):
+def test_prefill_cuts_the_context_at_the_row_end(partition, qlens):
     """Query rows at positions past the row's end attend to the tokens the
     row addresses; rows before it are unaffected; the split equals the
-    unsplit result within tolerance (stale workspace, NaN past the row)."""
+    unsplit result within tolerance (stale workspace, NaN past the row).
+    Short query runs take one wavefront per query tile, long ones the
+    workgroups that share each step through LDS."""
     w = _workload("bf16", 4)
-    lens, qlens = [230, 100, 300], [30, 5, 40]   # straddles, before, wholly past
-    print(f"[past-table] prefill P={partition}", flush=True)
+    lens = [230, 100, 300]   # straddles, before, wholly past
+    print(f"[past-table] prefill q={qlens} P={partition}", flush=True)
     batch = make_batch(w, seed=32, device=DEV, lens=np.asarray(lens))
     k_host, v_host = host_view(batch.k_pool), host_view(batch.v_pool)
     past = batch.block_tables[:, ROW_BLOCKS:]
