@@ -126,6 +126,16 @@ def test_long_query_runs(w, lens, qlens, partition):
     _run(w, lens, qlens, partition, seed=7)
 
 
+@pytest.mark.parametrize("partition", [0, 64])
+def test_workgroup_step_counts(partition):
+    """The LDS-shared kernel's loop at every step count from 1 to 9 (its
+    loads run four steps ahead in eight buffers, two blocks of four per
+    loop pass): whole contexts of 32 .. 288 new tokens, so the workgroups
+    of each sequence end after different numbers of 32-token steps."""
+    lens = [32 * k for k in range(1, 10)]
+    _run(W2, lens, lens, partition, seed=11)
+
+
 W_B32 = dataclasses.replace(WORKLOADS[2], block_size=32, name="b32-bf16")
 W_G2 = dataclasses.replace(WORKLOADS[2], num_q_heads=16, name="g2-bf16")
 W_D64_B16 = dataclasses.replace(WORKLOADS[2], head_dim=64, name="d64-bf16")
