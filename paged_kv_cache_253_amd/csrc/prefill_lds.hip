@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64 * W) void prefill_lds(const PrefillArgs args) {
 // Query rows per workgroup of the LDS-shared prefill, and whether a launch
 // takes it: bf16 cache with query runs long enough to fill a workgroup.
 // Eight wavefronts of two column tiles per workgroup, one workgroup per CU
-// (218 VGPRs: two wavefronts per SIMD; 128 KiB of LDS).
+// (226 VGPRs: two wavefronts per SIMD; 128 KiB of LDS).
 constexpr int kLdsWaves = 8;
 constexpr int kLdsNT = 2;
 
