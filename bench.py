@@ -828,7 +828,8 @@ def main() -> int:
                          "sequence order (the unpaged layout, same data): what the scattered "
                          "physical blocks cost the decode")
     ap.add_argument("--case", default="spec-verify-8b",
-                    help="prefill shape: spec-verify-8b or chunked-prefill-8b")
+                    help="prefill shape: spec-verify-8b, chunked-prefill-8b or "
+                         "chunked-prefill-8b-fp8")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -121,6 +121,10 @@ PREFILL_WORKLOADS = {
                                     "Chunked prefill: 8 sequences at 8192 cached tokens whose "
                                     "last 512 are the new chunk; Llama-3-8B heads (32/8, d 128), "
                                     "bf16 KV, block 16"), 512),
+    "chunked-prefill-8b-fp8": (Workload(7, "chunked-prefill-fp8", 8, 32, 8, 128, 16, "fp8_e4m3",
+                                        "bf16", ("fixed", 8192), "exact", 0,
+                                        "Chunked prefill as chunked-prefill-8b with an fp8 e4m3 "
+                                        "KV cache (per-KV-head fp32 scales)"), 512),
 }
 
 
