@@ -452,8 +452,11 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void
  *   max_query_len  host upper bound of Q_b (sizes the grid)
  *   other arguments as pa_decode (cache PA_BF16, PA_FP8_E4M3, PA_FP8_E5M2
  *                  or PA_INT4)
- *   partition_size 0: one wavefront per (query tile, KV head, sequence)
- *                     over its whole prefix, `out` written;
+ *   partition_size 0: each query tile over its whole prefix, `out`
+ *                     written: one wavefront per (query tile, KV head,
+ *                     sequence), or for bf16 caches with G * max_query_len
+ *                     >= 256, one workgroup of eight wavefronts per eight
+ *                     consecutive query tiles, sharing K and V through LDS;
  *                  P > 0 (a multiple of 32): fixed partitions of the prefix;
  *                     states to `workspace`, pa_prefill_reduce merges.
  *   workspace      P > 0: at least pa_decode_workspace_size(num_query_tokens,
